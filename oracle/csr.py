@@ -1,0 +1,32 @@
+"""Receiver and sender CSR views of a COO edge list (stable).
+
+The Sobek paper (Sec. 4, the paragraph on layouts and graphs) keeps cached
+stable CSR views, receiver-major and source-major, so that every reduction has
+one owner and one fixed order.  Reading fixed here:
+
+receiver view: edges sorted by receiver, ties by original COO index;
+  rowptr[N+1], col = sender of each slot, eid = COO index of each slot.
+sender view: receiver-view slots sorted by sender, ties by slot;
+  s_rowptr[N+1], s_col = receiver of each sender slot, s_slot = receiver slot.
+
+Pinned by tests/test_oracle_csr.py against a brute-force construction.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def csr_build(n_nodes: int, src, dst):
+    src = np.asarray(src, np.int64)
+    dst = np.asarray(dst, np.int64)
+    perm = np.argsort(dst, kind="stable")
+    col = src[perm]
+    rowptr = np.zeros(n_nodes + 1, np.int64)
+    rowptr[1:] = np.cumsum(np.bincount(dst, minlength=n_nodes))
+    sperm = np.argsort(col, kind="stable")
+    s_col = dst[perm][sperm]
+    s_rowptr = np.zeros(n_nodes + 1, np.int64)
+    s_rowptr[1:] = np.cumsum(np.bincount(src, minlength=n_nodes))
+    i32 = lambda a: a.astype(np.int32)  # noqa: E731
+    return dict(rowptr=i32(rowptr), col=i32(col), eid=i32(perm),
+                s_rowptr=i32(s_rowptr), s_col=i32(s_col), s_slot=i32(sperm))

@@ -1,0 +1,44 @@
+"""Pins for oracle/csr.py against a brute-force construction."""
+import numpy as np
+
+from oracle.csr import csr_build
+
+
+def _brute(n, src, dst):
+    rows = [[] for _ in range(n)]
+    for e in range(len(src)):
+        rows[dst[e]].append(e)            # COO order within a receiver
+    rowptr, col, eid = [0], [], []
+    for i in range(n):
+        for e in rows[i]:
+            col.append(src[e]); eid.append(e)
+        rowptr.append(len(col))
+    srows = [[] for _ in range(n)]
+    for slot in range(len(col)):
+        srows[col[slot]].append(slot)     # receiver-slot order within a sender
+    s_rowptr, s_col, s_slot = [0], [], []
+    for j in range(n):
+        for slot in srows[j]:
+            s_col.append(dst[eid[slot]]); s_slot.append(slot)
+        s_rowptr.append(len(s_col))
+    return dict(rowptr=rowptr, col=col, eid=eid, s_rowptr=s_rowptr, s_col=s_col, s_slot=s_slot)
+
+
+def test_random_graphs(rng):
+    for n, e in [(1, 0), (5, 0), (7, 30), (50, 400), (13, 200)]:
+        src = rng.integers(0, n, e) if e else np.zeros(0, np.int64)
+        dst = rng.integers(0, n, e) if e else np.zeros(0, np.int64)
+        got = csr_build(n, src, dst)
+        want = _brute(n, src, dst)
+        for k in want:
+            assert list(got[k]) == list(want[k]), k
+        assert np.all(np.diff(got["rowptr"]) >= 0) and got["rowptr"][-1] == e
+
+
+def test_all_into_one_and_duplicates():
+    src = np.array([3, 1, 3, 3, 0, 2])
+    dst = np.array([2, 2, 2, 2, 2, 2])
+    got = csr_build(4, src, dst)
+    want = _brute(4, src, dst)
+    for k in want:
+        assert list(got[k]) == list(want[k])
