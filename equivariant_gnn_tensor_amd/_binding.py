@@ -1,0 +1,364 @@
+"""ctypes binding of libetpc.so (argument marshalling only).
+
+Every computation runs in the HIP library; this module converts Python/torch
+arguments to the C ABI of ``include/etpc.h`` and allocates caller-owned buffers
+(outputs, workspaces) with torch on the current device.  Function names mirror
+the C entry points.  If the shared library is missing, importing this module
+raises ImportError: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libetpc.so")
+
+ETPC_OK = 0
+UVW, UVU = 0, 1
+GAUSSIAN, BESSEL = 0, 1
+PASS_FWD, PASS_BWD, PASS_DBL = 0, 1, 2
+_STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "INVALID_PATH", 4: "WORKSPACE", 5: "OVERFLOW",
+           6: "GRAPH", 7: "HIP"}
+
+
+class EtpcError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"etpc {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.name = _STATUS.get(status, str(status))
+
+
+class etpc_irrep(C.Structure):
+    _fields_ = [("mul", C.c_int32), ("l", C.c_int32), ("parity", C.c_int32)]
+
+
+class etpc_instr(C.Structure):
+    _fields_ = [("in_block", C.c_int32), ("l_sh", C.c_int32), ("out_block", C.c_int32)]
+
+
+class etpc_spec(C.Structure):
+    _fields_ = [
+        ("n_in", C.c_int32), ("in_", C.POINTER(etpc_irrep)),
+        ("n_out", C.c_int32), ("out", C.POINTER(etpc_irrep)),
+        ("out_per_path", C.c_int32), ("lmax_sh", C.c_int32), ("mode", C.c_int32),
+        ("n_instr", C.c_int32), ("instr", C.POINTER(etpc_instr)),
+        ("radial", C.c_int32), ("n_basis", C.c_int32), ("r_lo", C.c_float), ("r_hi", C.c_float),
+        ("poly_p", C.c_int32), ("box", C.c_float * 3),
+    ]
+
+
+class etpc_graph(C.Structure):
+    _fields_ = [
+        ("n_nodes", C.c_int32), ("n_edges", C.c_int64),
+        ("rowptr", C.c_void_p), ("col", C.c_void_p),
+        ("s_rowptr", C.c_void_p), ("s_col", C.c_void_p), ("s_slot", C.c_void_p),
+    ]
+
+
+SYMBOLS = (
+    "etpc_plan_create", "etpc_plan_destroy", "etpc_plan_info", "etpc_plan_path", "etpc_plan_out_irrep",
+    "etpc_plan_cg", "etpc_workspace_size", "etpc_csr_workspace_size", "etpc_csr_build", "etpc_graph_validate",
+    "etpc_forward", "etpc_backward", "etpc_double_backward", "etpc_profile_enable", "etpc_profile_read",
+    "etpc_last_error",
+)
+KINDS = ("csr", "fwd_traverse", "channel_gemm", "bwd_traverse", "node_gemm", "aux")
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built (python -m equivariant_gnn_tensor_amd.build)")
+    lib = C.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    P = C.POINTER
+    lib.etpc_last_error.restype = C.c_char_p
+    lib.etpc_last_error.argtypes = []
+    sig = {
+        "etpc_plan_create": [P(etpc_spec), P(vp)],
+        "etpc_plan_info": [vp, P(i64), P(i64), P(i64), P(i32)],
+        "etpc_plan_path": [vp, i32, P(i32), P(i32), P(i32), P(i64), P(i64), P(i32)],
+        "etpc_plan_out_irrep": [vp, i32, P(i32), P(etpc_irrep)],
+        "etpc_plan_cg": [vp, i32, P(C.c_double)],
+        "etpc_workspace_size": [vp, i32, i32, i64, P(sz)],
+        "etpc_csr_workspace_size": [i32, i64, P(sz)],
+        "etpc_csr_build": [i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "etpc_graph_validate": [P(etpc_graph), vp],
+        "etpc_forward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, sz, vp],
+        "etpc_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "etpc_double_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "etpc_profile_enable": [i32],
+        "etpc_profile_read": [i32, P(C.c_double), P(i64)],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = C.c_int
+    lib.etpc_plan_destroy.argtypes = [vp]
+    lib.etpc_plan_destroy.restype = None
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != ETPC_OK:
+        raise EtpcError(status, lib.etpc_last_error().decode())
+
+
+_TOK = re.compile(r"^\s*(?:(\d+)\s*x\s*)?(\d+)([eo])\s*$")
+
+
+def parse_irreps(s) -> List[Tuple[int, int, int]]:
+    if not isinstance(s, str):
+        return [tuple(t) for t in s]
+    out = []
+    for tok in s.split("+"):
+        m = _TOK.match(tok)
+        if not m:
+            raise ValueError(f"bad irrep token {tok!r}")
+        out.append((int(m.group(1) or 1), int(m.group(2)), 1 if m.group(3) == "e" else -1))
+    return out
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=torch.float32) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+class Plan:
+    """Owns an etpc_plan handle (host tables only)."""
+
+    def __init__(self, irreps_in, irreps_out, lmax_sh: int, mode: str = "uvw", radial: str = "gaussian",
+                 n_basis: int = 8, r_lo: float = 0.0, r_hi: float = 5.0, poly_p: int = 6,
+                 box: Optional[Sequence[float]] = None, out_per_path: bool = False,
+                 instructions: Optional[Sequence[Tuple[int, int, int]]] = None):
+        ins, outs = parse_irreps(irreps_in), parse_irreps(irreps_out)
+        self._in = (etpc_irrep * len(ins))(*[etpc_irrep(*t) for t in ins])
+        self._out = (etpc_irrep * len(outs))(*[etpc_irrep(*t) for t in outs])
+        n_instr = 0 if instructions is None else len(instructions)
+        self._instr = (etpc_instr * max(1, n_instr))(*[etpc_instr(*t) for t in (instructions or [])])
+        spec = etpc_spec()
+        spec.n_in, spec.in_ = len(ins), self._in
+        spec.n_out, spec.out = len(outs), self._out
+        spec.out_per_path = 1 if out_per_path else 0
+        spec.lmax_sh = lmax_sh
+        spec.mode = {"uvw": UVW, "uvu": UVU}[mode] if isinstance(mode, str) else int(mode)
+        spec.n_instr = n_instr
+        spec.instr = self._instr if n_instr else None
+        spec.radial = {"gaussian": GAUSSIAN, "bessel": BESSEL}[radial] if isinstance(radial, str) else int(radial)
+        spec.n_basis, spec.r_lo, spec.r_hi, spec.poly_p = n_basis, r_lo, r_hi, poly_p
+        b = (0.0, 0.0, 0.0) if box is None else (tuple(box) if hasattr(box, "__len__") else (box, box, box))
+        spec.box = (C.c_float * 3)(*b)
+        self.spec = spec
+        self.handle = C.c_void_p()
+        self.handle = etpc_plan_create(spec)
+        self.mode = "uvw" if spec.mode == UVW else "uvu"
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            lib.etpc_plan_destroy(h)
+            self.handle = None
+
+    def info(self) -> Dict[str, int]:
+        return etpc_plan_info(self)
+
+    def paths(self) -> List[Dict[str, int]]:
+        return [etpc_plan_path(self, p) for p in range(self.info()["n_paths"])]
+
+    def out_irreps(self) -> List[Tuple[int, int, int]]:
+        return etpc_plan_out_irrep(self)
+
+    def cg(self, p: int):
+        return etpc_plan_cg(self, p)
+
+    def w_blocks(self) -> List[Tuple[int, float]]:
+        return [(q["w_numel"], 1.0 / q["fan_in"] ** 0.5) for q in self.paths()]
+
+
+def etpc_plan_create(spec: etpc_spec) -> C.c_void_p:
+    h = C.c_void_p()
+    _check(lib.etpc_plan_create(C.byref(spec), C.byref(h)))
+    return h
+
+
+def etpc_plan_info(plan: Plan) -> Dict[str, int]:
+    x, z, w = C.c_int64(), C.c_int64(), C.c_int64()
+    n = C.c_int32()
+    _check(lib.etpc_plan_info(plan.handle, C.byref(x), C.byref(z), C.byref(w), C.byref(n)))
+    return dict(x_dim=x.value, z_dim=z.value, w_numel=w.value, n_paths=n.value)
+
+
+def etpc_plan_path(plan: Plan, p: int) -> Dict[str, int]:
+    ib, ls, ob, fi = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int32()
+    wo, wn = C.c_int64(), C.c_int64()
+    _check(lib.etpc_plan_path(plan.handle, p, C.byref(ib), C.byref(ls), C.byref(ob), C.byref(wo), C.byref(wn),
+                              C.byref(fi)))
+    return dict(in_block=ib.value, l_sh=ls.value, out_block=ob.value, w_off=wo.value, w_numel=wn.value,
+                fan_in=fi.value)
+
+
+def etpc_plan_out_irrep(plan: Plan) -> List[Tuple[int, int, int]]:
+    n = C.c_int32()
+    _check(lib.etpc_plan_out_irrep(plan.handle, 0, C.byref(n), None))
+    out = []
+    for b in range(n.value):
+        ir = etpc_irrep()
+        _check(lib.etpc_plan_out_irrep(plan.handle, b, None, C.byref(ir)))
+        out.append((ir.mul, ir.l, ir.parity))
+    return out
+
+
+def etpc_plan_cg(plan: Plan, p: int):
+    import numpy as np
+    q = etpc_plan_path(plan, p)
+    li = parse_irreps_of(plan, "in")[q["in_block"]][1]
+    lo = etpc_plan_out_irrep(plan)[q["out_block"]][1]
+    ls = q["l_sh"]
+    buf = (C.c_double * ((2 * li + 1) * (2 * ls + 1) * (2 * lo + 1)))()
+    _check(lib.etpc_plan_cg(plan.handle, p, buf))
+    return np.array(buf[:], dtype=np.float64).reshape(2 * li + 1, 2 * ls + 1, 2 * lo + 1)
+
+
+def parse_irreps_of(plan: Plan, which: str) -> List[Tuple[int, int, int]]:
+    arr, n = (plan.spec.in_, plan.spec.n_in) if which == "in" else (plan.spec.out, plan.spec.n_out)
+    return [(arr[i].mul, arr[i].l, arr[i].parity) for i in range(n)]
+
+
+def etpc_workspace_size(plan: Plan, pass_: int, n_nodes: int, n_edges: int) -> int:
+    b = C.c_size_t()
+    _check(lib.etpc_workspace_size(plan.handle, pass_, n_nodes, n_edges, C.byref(b)))
+    return b.value
+
+
+def etpc_csr_workspace_size(n_nodes: int, n_edges: int) -> int:
+    b = C.c_size_t()
+    _check(lib.etpc_csr_workspace_size(n_nodes, n_edges, C.byref(b)))
+    return b.value
+
+
+class Graph:
+    """Device CSR views (receiver and sender) of one graph."""
+
+    def __init__(self, n_nodes: int, rowptr, col, s_rowptr, s_col, s_slot, eid=None):
+        self.n_nodes = int(n_nodes)
+        self.rowptr, self.col, self.eid = rowptr, col, eid
+        self.s_rowptr, self.s_col, self.s_slot = s_rowptr, s_col, s_slot
+        self.n_edges = int(col.shape[0])
+        g = etpc_graph()
+        g.n_nodes, g.n_edges = self.n_nodes, self.n_edges
+        g.rowptr = _ptr(rowptr, torch.int32)
+        g.col = _ptr(col, torch.int32) if self.n_edges else None
+        g.s_rowptr = _ptr(s_rowptr, torch.int32)
+        g.s_col = _ptr(s_col, torch.int32) if self.n_edges else None
+        g.s_slot = _ptr(s_slot, torch.int32) if self.n_edges else None
+        self.c = g
+
+
+def _empty_i32(n, device):
+    return torch.empty(max(n, 0), dtype=torch.int32, device=device)
+
+
+def _workspace(nbytes: int, device) -> Tuple[Optional[torch.Tensor], int]:
+    if nbytes <= 0:
+        return None, 0
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return t, nbytes
+
+
+def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> Graph:
+    dev = src.device
+    e = int(src.shape[0])
+    rowptr, s_rowptr = _empty_i32(n_nodes + 1, dev), _empty_i32(n_nodes + 1, dev)
+    col, eid, s_col, s_slot = (_empty_i32(e, dev) for _ in range(4))
+    ws, nb = _workspace(etpc_csr_workspace_size(n_nodes, e), dev)
+    _check(lib.etpc_csr_build(n_nodes, e, _ptr(src, torch.int32), _ptr(dst, torch.int32), _ptr(rowptr, torch.int32),
+                              _ptr(col, torch.int32), _ptr(eid, torch.int32), _ptr(s_rowptr, torch.int32),
+                              _ptr(s_col, torch.int32), _ptr(s_slot, torch.int32),
+                              None if ws is None else ws.data_ptr(), nb, _stream(stream)))
+    return Graph(n_nodes, rowptr, col, s_rowptr, s_col, s_slot, eid=eid)
+
+
+def etpc_graph_validate(graph: Graph, stream=None) -> None:
+    _check(lib.etpc_graph_validate(C.byref(graph.c), _stream(stream)))
+
+
+def _ws_for(plan, pass_, graph, ws):
+    if isinstance(ws, torch.Tensor):
+        return ws.data_ptr(), ws.numel() * ws.element_size(), ws
+    n = etpc_workspace_size(plan, pass_, graph.n_nodes, graph.n_edges)
+    t, nb = _workspace(n, graph.rowptr.device)
+    return (None if t is None else t.data_ptr()), nb, t
+
+
+def etpc_forward(plan: Plan, graph: Graph, x, pos, w, z=None, ws=None, stream=None):
+    if z is None:
+        z = torch.empty(graph.n_nodes, plan.info()["z_dim"], dtype=torch.float32, device=x.device)
+    wp, wn, _keep = _ws_for(plan, PASS_FWD, graph, ws)
+    _check(lib.etpc_forward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z), wp, wn,
+                            _stream(stream)))
+    return z
+
+
+def etpc_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, want=("x", "w", "pos"), outs=None, ws=None,
+                  stream=None):
+    info = plan.info()
+    dev = x.device
+    if outs is None:
+        outs = (
+            torch.empty(graph.n_nodes, info["x_dim"], dtype=torch.float32, device=dev) if "x" in want else None,
+            torch.empty(info["w_numel"], dtype=torch.float32, device=dev) if "w" in want else None,
+            torch.empty(graph.n_nodes, 3, dtype=torch.float32, device=dev) if "pos" in want else None,
+        )
+    xb, wb, pb = outs
+    wp, wn, _keep = _ws_for(plan, PASS_BWD, graph, ws)
+    _check(lib.etpc_backward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z_bar), _ptr(xb),
+                             _ptr(wb), _ptr(pb), wp, wn, _stream(stream)))
+    return xb, wb, pb
+
+
+def etpc_double_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, x_dot=None, w_dot=None, pos_dot=None,
+                         want=("z_bar", "x", "w"), outs=None, ws=None, stream=None):
+    info = plan.info()
+    dev = x.device
+    if outs is None:
+        outs = (
+            torch.empty(graph.n_nodes, info["z_dim"], dtype=torch.float32, device=dev) if "z_bar" in want else None,
+            torch.empty(graph.n_nodes, info["x_dim"], dtype=torch.float32, device=dev) if "x" in want else None,
+            torch.empty(info["w_numel"], dtype=torch.float32, device=dev) if "w" in want else None,
+        )
+    gz, gx, gw = outs
+    wp, wn, _keep = _ws_for(plan, PASS_DBL, graph, ws)
+    _check(lib.etpc_double_backward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z_bar),
+                                    _ptr(x_dot), _ptr(w_dot), _ptr(pos_dot), _ptr(gz), _ptr(gx), _ptr(gw), wp, wn,
+                                    _stream(stream)))
+    return gz, gx, gw
+
+
+def etpc_profile_enable(enable: bool) -> None:
+    _check(lib.etpc_profile_enable(1 if enable else 0))
+
+
+def etpc_profile_read(kind) -> Tuple[float, int]:
+    """(total milliseconds, launches) recorded for one kernel kind since the last enable."""
+    k = KINDS.index(kind) if isinstance(kind, str) else int(kind)
+    ms, n = C.c_double(), C.c_int64()
+    _check(lib.etpc_profile_read(k, C.byref(ms), C.byref(n)))
+    return ms.value, n.value

@@ -1,0 +1,831 @@
+// C ABI: argument validation, workspace carving, chunk scheduling and launches.
+//
+// Schedules (all on the caller's stream, all deterministic for a given workspace):
+//  forward uvw  -- per output group g, per receiver chunk: one receiver traversal per
+//                  path of g builds the receiver state S_g (Sobek paper, Sec. 4, Eq. 33),
+//                  then one MFMA GEMM m_g = S_g W_g writes the output rows (Eq. 34-35).
+//  forward uvu  -- one receiver traversal per path writes the output block (Eq. 7, 17).
+//  backward uvw -- per sender chunk, per input block k: Xt = x W (GEMM, if positions
+//                  are wanted), one sender traversal per path of k (P state and the
+//                  edge position adjoint), x_bar = P W^T and W_bar = x^T P (GEMMs,
+//                  split-K with a fixed-order reduction); finally pos_bar from the
+//                  edge adjoints by a segment sum over both CSR views (Eq. 18-22).
+//  backward uvu -- one sender traversal per path (x_bar, W_bar partials, edge adjoint).
+//  double backward -- the directional program of Eq. 23-31 / 37-39 assembled from the
+//                  same traversals in tangent mode plus the same GEMMs.
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "kernels.hpp"
+#include "plan.hpp"
+#include "profile.hpp"
+
+namespace etpc {
+size_t csr_workspace_bytes(int32_t n_nodes, int64_t n_edges);
+etpc_status csr_build_impl(int32_t n_nodes, int64_t n_edges, const int32_t* src, const int32_t* dst, int32_t* rowptr,
+                           int32_t* col, int32_t* eid, int32_t* s_rowptr, int32_t* s_col, int32_t* s_slot, void* ws,
+                           hipStream_t s);
+etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s);
+}  // namespace etpc
+
+namespace {
+
+using namespace etpc;
+
+constexpr int kMaxSplits = 32;
+
+struct Carver {
+  char* base = nullptr;
+  size_t off = 0;
+  template <class T>
+  T* take(size_t n) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += n * sizeof(T);
+    return p;
+  }
+};
+
+int lane_width(int c, int* ntiles) {
+  if (c > kWave) {
+    *ntiles = (c + kWave - 1) / kWave;
+    return kWave;
+  }
+  int cp = 1;
+  while (cp < c) cp <<= 1;
+  *ntiles = 1;
+  return cp;
+}
+
+// ---------------------------------------------------------------- per-plan derived sizes
+struct Derived {
+  int64_t max_s = 0;                 // max_g o_g * D_g (uvw forward state floats per receiver)
+  std::vector<int64_t> group_d;      // D_g
+  std::vector<int64_t> block_ncols;  // sum over paths of block k of B * C_out
+  std::vector<std::vector<int32_t>> block_col0;
+  int64_t max_state = 0;             // max_k (2l_k+1) * ncols_k
+  int64_t max_wcat = 0;              // max_k C_in_k * ncols_k
+};
+
+Derived derive(const etpc_plan_s* p) {
+  Derived d;
+  d.group_d.assign(p->out.size(), 0);
+  for (size_t g = 0; g < p->out.size(); ++g) {
+    int64_t D = 0;
+    for (int q : p->by_out[g]) D += static_cast<int64_t>(p->n_basis) * p->paths[q].c_in;
+    d.group_d[g] = D;
+    d.max_s = std::max<int64_t>(d.max_s, D * (2 * p->out[g].l + 1));
+  }
+  d.block_ncols.assign(p->in.size(), 0);
+  d.block_col0.assign(p->in.size(), {});
+  for (size_t k = 0; k < p->in.size(); ++k) {
+    int64_t n = 0;
+    for (int q : p->by_in[k]) {
+      d.block_col0[k].push_back(static_cast<int32_t>(n));
+      n += static_cast<int64_t>(p->n_basis) * p->paths[q].c_out;
+    }
+    d.block_ncols[k] = n;
+    d.max_state = std::max<int64_t>(d.max_state, n * (2 * p->in[k].l + 1));
+    d.max_wcat = std::max<int64_t>(d.max_wcat, n * p->in[k].mul);
+  }
+  return d;
+}
+
+// ---------------------------------------------------------------- workspace layouts
+struct FwdLayout {
+  float* S = nullptr;
+};
+void fwd_layout(const etpc_plan_s* p, const Derived& d, int64_t chunk, Carver& c, FwdLayout& L) {
+  if (p->mode == ETPC_UVW) L.S = c.take<float>(static_cast<size_t>(chunk * d.max_s));
+}
+
+struct BwdLayout {
+  float *rbar = nullptr, *wcat = nullptr, *wt = nullptr, *wt2 = nullptr, *wpart = nullptr;
+  float *xt = nullptr, *P = nullptr, *Pd = nullptr;
+};
+// flags: pos = edge adjoint + Xt; p = plain P state; tan = tangent state; wbar = W_bar partials
+// (two sets when wbar2); wt2 = second transposed weight (for w_dot)
+void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t chunk, bool pos, bool need_p,
+                bool tan, bool wbar, bool wbar2, bool xbar, bool wt2, Carver& c, BwdLayout& L) {
+  if (p->mode == ETPC_UVW) {
+    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges));
+    if (pos) L.wcat = c.take<float>(static_cast<size_t>(d.max_wcat));
+    if (xbar) L.wt = c.take<float>(static_cast<size_t>(d.max_wcat));
+    if (wt2) L.wt2 = c.take<float>(static_cast<size_t>(d.max_wcat));
+    if (wbar) L.wpart = c.take<float>(static_cast<size_t>((wbar2 ? 2 : 1) * kMaxSplits * d.max_wcat));
+    if (pos) L.xt = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+    if (need_p) L.P = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+    if (tan) L.Pd = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+  } else {
+    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges));
+    int64_t maxbc = 0;
+    for (auto& q : p->paths) maxbc = std::max<int64_t>(maxbc, static_cast<int64_t>(p->n_basis) * q.c_in);
+    if (wbar) L.wpart = c.take<float>(static_cast<size_t>(chunk * maxbc));  // chunk = uvu grid size here
+  }
+}
+
+constexpr int kUvuGrid = 2048;
+
+size_t fwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t chunk) {
+  Carver c;
+  FwdLayout L;
+  fwd_layout(p, d, chunk, c, L);
+  return c.off;
+}
+
+size_t bwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t chunk) {
+  Carver c;
+  BwdLayout L;
+  bwd_layout(p, d, n_edges, chunk, true, true, false, true, false, true, false, c, L);
+  return c.off;
+}
+
+size_t dbl_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t chunk) {
+  Carver c;
+  BwdLayout L;
+  bwd_layout(p, d, n_edges, chunk, false, true, true, true, true, true, true, c, L);
+  return std::max(c.off, fwd_bytes(p, d, chunk));
+}
+
+// largest chunk in [1, n] whose layout fits
+template <class F>
+int64_t pick_chunk(int64_t n, size_t ws_bytes, F bytes_of) {
+  if (n <= 0) return 0;
+  if (bytes_of(n) <= ws_bytes) return n;
+  const size_t b0 = bytes_of(0), b1 = bytes_of(1);
+  if (b1 > ws_bytes) return -1;
+  const size_t per = std::max<size_t>(1, b1 - b0);
+  int64_t c = std::min<int64_t>(n, static_cast<int64_t>((ws_bytes - b0) / per));
+  while (c > 1 && bytes_of(c) > ws_bytes) --c;
+  return std::max<int64_t>(c, 1);
+}
+
+RowMap plain(int64_t ld) { return RowMap{ld, 0, 1}; }
+RowMap irmul(int32_t m, int64_t width, int64_t mul) { return RowMap{width, mul, m}; }
+
+// ---------------------------------------------------------------- validation
+etpc_status check_common(const etpc_plan_s* p, const etpc_graph* g) {
+  if (p == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null plan");
+  if (g == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null graph");
+  if (g->n_nodes < 0 || g->n_edges < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative graph size");
+  if (g->n_edges >= (int64_t(1) << 31)) ETPC_FAIL(ETPC_ERR_OVERFLOW, "n_edges must be < 2^31");
+  if (static_cast<int64_t>(g->n_nodes) * 7 >= (int64_t(1) << 31))
+    ETPC_FAIL(ETPC_ERR_OVERFLOW, "n_nodes * 7 must be < 2^31");
+  if (g->n_nodes > 0 && (g->rowptr == nullptr || g->s_rowptr == nullptr))
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null row pointers");
+  if (g->n_edges > 0 && (g->col == nullptr || g->s_col == nullptr || g->s_slot == nullptr))
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null CSR index arrays");
+  return ETPC_OK;
+}
+
+etpc_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need > 0 && ws == nullptr) ETPC_FAIL(ETPC_ERR_WORKSPACE, "workspace is null but the pass needs one");
+  if (ws_bytes < need)
+    ETPC_FAIL(ETPC_ERR_WORKSPACE, "workspace too small: need at least " + std::to_string(need) + " bytes");
+  return ETPC_OK;
+}
+
+etpc_status check_channels_bwd(const etpc_plan_s* p) {
+  for (auto& q : p->paths) {
+    const int c = p->mode == ETPC_UVW ? q.c_out : q.c_in;
+    if (c > 64 * 4) ETPC_FAIL(ETPC_ERR_UNSUPPORTED, "backward supports at most 256 channels per block");
+  }
+  return ETPC_OK;
+}
+
+// ---------------------------------------------------------------- forward pieces
+// zero output blocks that receive no path
+hipError_t zero_unreached(const etpc_plan_s* p, float* z, int32_t n, hipStream_t s) {
+  bool any = false;
+  for (size_t g = 0; g < p->out.size(); ++g) any |= p->by_out[g].empty();
+  if (!any) return hipSuccess;
+  return launch_fill(z, static_cast<int64_t>(n) * p->z_dim, 0.f, s);
+}
+
+hipError_t zero_unreached_in(const etpc_plan_s* p, float* x, int32_t n, hipStream_t s) {
+  bool any = false;
+  for (size_t k = 0; k < p->in.size(); ++k) any |= p->by_in[k].empty();
+  if (!any) return hipSuccess;
+  return launch_fill(x, static_cast<int64_t>(n) * p->x_dim, 0.f, s);
+}
+
+// One uvw forward evaluation into z (beta: accumulate into z).  With tangent, the
+// receiver traversal builds dS along pos_dot.  xin / win select the operands.
+etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* xin,
+                        const float* pos, const float* pos_dot, const float* win, float* z, bool beta, bool tangent,
+                        const FwdLayout& L, int64_t chunk, hipStream_t s) {
+  const GeomParams geom = p->geom();
+  const int32_t N = g->n_nodes;
+  for (size_t gi = 0; gi < p->out.size(); ++gi) {
+    const auto& paths = p->by_out[gi];
+    if (paths.empty()) continue;
+    const int no = 2 * p->out[gi].l + 1;
+    const int64_t D = d.group_d[gi];
+    const int c_out = p->out[gi].mul;
+    for (int64_t r0 = 0; r0 < N; r0 += chunk) {
+      const int nrecv = static_cast<int>(std::min<int64_t>(chunk, N - r0));
+      int32_t col0 = 0;
+      for (int qi : paths) {
+        const PathInfo& pi = p->paths[qi];
+        FwdUvwArgs a{};
+        a.rowptr = g->rowptr;
+        a.col = g->col;
+        a.pos = pos;
+        a.pos_dot = pos_dot;
+        a.x = xin;
+        a.S = L.S;
+        a.recv0 = static_cast<int32_t>(r0);
+        a.x_dim = static_cast<int32_t>(p->x_dim);
+        a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
+        int ntiles = 1;
+        a.cp = lane_width(pi.c_in, &ntiles);
+        a.c_in = pi.c_in;
+        a.ls = pi.l_sh;
+        a.s_row_stride = D;
+        a.s_col0 = col0;
+        a.g = geom;
+        a.cg = pi.cgf;
+        ETPC_LAUNCH(ETPC_KIND_FWD_TRAVERSE, launch_fwd_uvw(a, tangent, pi.l_in, pi.l_out, nrecv, ntiles, s));
+        col0 += p->n_basis * pi.c_in;
+      }
+      GemmArgs ga{};
+      ga.A = L.S;
+      ga.amap = plain(D);
+      ga.a_mcontig = 0;
+      ga.B = win + p->paths[paths[0]].w_off;
+      ga.ldb = c_out;
+      ga.C = z + r0 * p->z_dim + p->zoff[gi];
+      ga.cmap = irmul(no, p->z_dim, c_out);
+      ga.beta = beta ? 1 : 0;
+      ga.M = nrecv * no;
+      ga.N = c_out;
+      ga.K = static_cast<int32_t>(D);
+      ga.k_split = static_cast<int32_t>(D);
+      ga.c_split_stride = 0;
+      ETPC_LAUNCH(ETPC_KIND_CHANNEL_GEMM, launch_gemm(ga, 1, s));
+    }
+  }
+  return ETPC_OK;
+}
+
+etpc_status fwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* xin, const float* pos,
+                        const float* pos_dot, const float* win, float* z, bool beta, bool tangent, hipStream_t s) {
+  const GeomParams geom = p->geom();
+  std::vector<int> seen(p->out.size(), 0);
+  for (const PathInfo& pi : p->paths) {
+    FwdUvuArgs a{};
+    a.rowptr = g->rowptr;
+    a.col = g->col;
+    a.pos = pos;
+    a.pos_dot = pos_dot;
+    a.x = xin;
+    a.w = win + pi.w_off;
+    a.z = z;
+    a.x_dim = static_cast<int32_t>(p->x_dim);
+    a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
+    a.z_dim = static_cast<int32_t>(p->z_dim);
+    a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
+    int ntiles = 1;
+    a.cp = lane_width(pi.c_in, &ntiles);
+    a.c = pi.c_in;
+    a.ls = pi.l_sh;
+    a.accumulate = (beta || seen[pi.out_block]) ? 1 : 0;
+    a.g = geom;
+    a.cg = pi.cgf;
+    ETPC_LAUNCH(ETPC_KIND_FWD_TRAVERSE, launch_fwd_uvu(a, tangent, pi.l_in, pi.l_out, g->n_nodes, ntiles, s));
+    seen[pi.out_block] = 1;
+  }
+  return ETPC_OK;
+}
+
+// ---------------------------------------------------------------- backward pieces (uvw)
+struct UvwBwdReq {
+  const float* x;         // features for Xt and W_bar (x^T P)
+  const float* w;         // weights for Xt and x_bar (W^T P)
+  const float* x2;        // second feature operand for W_bar with the plain state (x_dot^T P), or null
+  const float* w2;        // second weight operand for x_bar with the plain state (w_dot^T P), or null
+  const float* pos_dot;   // tangent direction (dbl) or null
+  float* x_out;           // x_bar / x_grad or null
+  float* w_out;           // W_bar / w_grad or null
+  float* rbar;            // edge adjoint (first-order pass) or null
+  bool tangent;           // dbl: the main state is the tangent state dP
+  bool plain_needed;      // dbl: plain P needed for the x2 / w2 terms
+};
+
+void wprep_args(const etpc_plan_s* p, const Derived& d, int k, const float* w, float* wcat, float* wt, WPrepArgs& a) {
+  std::memset(&a, 0, sizeof(a));
+  a.w = w;
+  a.wcat = wcat;
+  a.wt = wt;
+  a.n_paths = static_cast<int32_t>(p->by_in[k].size());
+  a.nb = p->n_basis;
+  a.c_in = p->in[k].mul;
+  a.ncols = static_cast<int32_t>(d.block_ncols[k]);
+  for (int t = 0; t < a.n_paths; ++t) {
+    const PathInfo& pi = p->paths[p->by_in[k][t]];
+    a.path_off[t] = pi.w_off;
+    a.col0[t] = d.block_col0[k][t];
+    a.cout[t] = pi.c_out;
+  }
+}
+
+int pick_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int64_t sp = (1024 + tiles - 1) / tiles;
+  sp = std::min<int64_t>(sp, (K + 255) / 256);
+  sp = std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
+  return static_cast<int>(sp);
+}
+
+// W_out block k (+)= A^T S_state (split-K over the chunk's rows), partials at wpart + slot
+hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float* xa, int64_t j0, int nsend,
+                     const float* state, float* wpart, int* splits_out, hipStream_t s) {
+  const int ni = 2 * p->in[k].l + 1;
+  const int64_t ncols = d.block_ncols[k];
+  const int c_in = p->in[k].mul;
+  const int64_t K = static_cast<int64_t>(nsend) * ni;
+  const int sp = pick_splits(c_in, ncols, K);
+  int64_t ks = (K + sp - 1) / sp;
+  ks = (ks + 15) / 16 * 16;
+  GemmArgs ga{};
+  ga.A = xa + j0 * p->x_dim + p->xoff[k];
+  ga.amap = irmul(ni, p->x_dim, c_in);
+  ga.a_mcontig = 1;
+  ga.B = state;
+  ga.ldb = ncols;
+  ga.C = wpart;
+  ga.cmap = plain(ncols);
+  ga.beta = 0;
+  ga.M = c_in;
+  ga.N = static_cast<int32_t>(ncols);
+  ga.K = static_cast<int32_t>(K);
+  ga.k_split = static_cast<int32_t>(ks);
+  ga.c_split_stride = static_cast<int64_t>(c_in) * ncols;
+  *splits_out = sp;
+  return launch_gemm(ga, sp, s);
+}
+
+hipError_t xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float* state, const float* wt, float* xo,
+                     int64_t j0, int nsend, bool beta, hipStream_t s) {
+  const int ni = 2 * p->in[k].l + 1;
+  const int64_t ncols = d.block_ncols[k];
+  const int c_in = p->in[k].mul;
+  GemmArgs ga{};
+  ga.A = state;
+  ga.amap = plain(ncols);
+  ga.a_mcontig = 0;
+  ga.B = wt;
+  ga.ldb = c_in;
+  ga.C = xo + j0 * p->x_dim + p->xoff[k];
+  ga.cmap = irmul(ni, p->x_dim, c_in);
+  ga.beta = beta ? 1 : 0;
+  ga.M = nsend * ni;
+  ga.N = c_in;
+  ga.K = static_cast<int32_t>(ncols);
+  ga.k_split = static_cast<int32_t>(ncols);
+  ga.c_split_stride = 0;
+  return launch_gemm(ga, 1, s);
+}
+
+etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* pos,
+                        const float* z_bar, const UvwBwdReq& R, const BwdLayout& L, int64_t chunk, hipStream_t s) {
+  const GeomParams geom = p->geom();
+  const int32_t N = g->n_nodes;
+  const bool want_pos = R.rbar != nullptr;
+  const bool main_state = R.tangent || (R.x_out || R.w_out);        // P (plain) or dP (tangent)
+  const bool need_plain = R.tangent ? R.plain_needed : main_state;   // plain P
+  float* Pmain = R.tangent ? L.Pd : L.P;
+  bool rbar_started = false;
+  if (R.x_out) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
+  for (int64_t j0 = 0; j0 < N; j0 += chunk) {
+    const int nsend = static_cast<int>(std::min<int64_t>(chunk, N - j0));
+    for (size_t k = 0; k < p->in.size(); ++k) {
+      const auto& paths = p->by_in[k];
+      if (paths.empty()) continue;
+      const int ni = 2 * p->in[k].l + 1;
+      const int64_t ncols = d.block_ncols[k];
+      const int c_in = p->in[k].mul;
+      WPrepArgs wa;
+      if (want_pos || R.x_out) {
+        wprep_args(p, d, static_cast<int>(k), R.w, want_pos ? L.wcat : nullptr, R.x_out ? L.wt : nullptr, wa);
+        ETPC_LAUNCH(ETPC_KIND_AUX, launch_wprep(wa, s));
+      }
+      if (R.x_out && R.w2) {
+        wprep_args(p, d, static_cast<int>(k), R.w2, nullptr, L.wt2, wa);
+        ETPC_LAUNCH(ETPC_KIND_AUX, launch_wprep(wa, s));
+      }
+      if (want_pos) {  // Xt = x W
+        GemmArgs ga{};
+        ga.A = R.x + j0 * p->x_dim + p->xoff[k];
+        ga.amap = irmul(ni, p->x_dim, c_in);
+        ga.a_mcontig = 0;
+        ga.B = L.wcat;
+        ga.ldb = ncols;
+        ga.C = L.xt;
+        ga.cmap = plain(ncols);
+        ga.beta = 0;
+        ga.M = nsend * ni;
+        ga.N = static_cast<int32_t>(ncols);
+        ga.K = c_in;
+        ga.k_split = c_in;
+        ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, launch_gemm(ga, 1, s));
+      }
+      for (size_t t = 0; t < paths.size(); ++t) {
+        const PathInfo& pi = p->paths[paths[t]];
+        BwdUvwArgs a{};
+        a.s_rowptr = g->s_rowptr;
+        a.s_col = g->s_col;
+        a.s_slot = g->s_slot;
+        a.pos = pos;
+        a.pos_dot = R.pos_dot;
+        a.z_bar = z_bar;
+        a.xt = L.xt;
+        a.P = L.P;
+        a.Pdot = L.Pd;
+        a.rbar = R.rbar;
+        a.send0 = static_cast<int32_t>(j0);
+        a.z_dim = static_cast<int32_t>(p->z_dim);
+        a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
+        int ntiles = 1;
+        a.cp = lane_width(pi.c_out, &ntiles);
+        a.c_out = pi.c_out;
+        a.ls = pi.l_sh;
+        a.ld_state = ncols;
+        a.state_col0 = d.block_col0[k][t];
+        a.rbar_accumulate = rbar_started ? 1 : 0;
+        a.g = geom;
+        a.cg = pi.cgf;
+        const bool np = R.tangent ? need_plain : main_state;
+        ETPC_LAUNCH(ETPC_KIND_BWD_TRAVERSE, launch_bwd_uvw(a, np, want_pos, R.tangent, pi.l_in, pi.l_out, nsend, ntiles, s));
+        if (want_pos) rbar_started = true;
+      }
+      if (R.x_out) {
+        if (main_state) ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, xbar_gemm(p, d, static_cast<int>(k), Pmain, L.wt, R.x_out, j0, nsend, false, s));
+        if (R.tangent && R.w2)
+          ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, xbar_gemm(p, d, static_cast<int>(k), L.P, L.wt2, R.x_out, j0, nsend, true, s));
+      }
+      if (R.w_out) {
+        int sp1 = 0, sp2 = 0;
+        ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, wbar_gemm(p, d, static_cast<int>(k), R.x, j0, nsend, Pmain, L.wpart, &sp1, s));
+        if (R.tangent && R.x2)
+          ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, wbar_gemm(p, d, static_cast<int>(k), R.x2, j0, nsend, L.P,
+                             L.wpart + static_cast<int64_t>(sp1) * c_in * ncols, &sp2, s));
+        int64_t poff[kMaxPaths];
+        int32_t col0[kMaxPaths], cout[kMaxPaths];
+        for (size_t t = 0; t < paths.size(); ++t) {
+          poff[t] = p->paths[paths[t]].w_off;
+          col0[t] = d.block_col0[k][t];
+          cout[t] = p->paths[paths[t]].c_out;
+        }
+        ETPC_LAUNCH(ETPC_KIND_AUX, launch_reduce_wbar(L.wpart, sp1 + sp2, c_in, static_cast<int>(paths.size()), p->n_basis, poff, col0,
+                                    cout, static_cast<int>(ncols), R.w_out, j0 > 0, s));
+      }
+    }
+  }
+  return ETPC_OK;
+}
+
+// ---------------------------------------------------------------- backward pieces (uvu)
+struct UvuBwdReq {
+  const float* x;
+  const float* w;
+  const float* pos_dot;
+  float* x_out;
+  float* w_out;
+  float* rbar;
+  bool tangent;
+  bool x_acc;   // accumulate into x_out from the first path on
+  bool w_acc;   // accumulate into w_out
+};
+
+etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* pos, const float* z_bar,
+                        const UvuBwdReq& R, const BwdLayout& L, hipStream_t s) {
+  const GeomParams geom = p->geom();
+  const int32_t N = g->n_nodes;
+  const int grid = static_cast<int>(std::min<int64_t>(N, kUvuGrid));
+  if (R.x_out && !R.x_acc) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
+  std::vector<int> seen(p->in.size(), 0);
+  bool rbar_started = false;
+  for (const PathInfo& pi : p->paths) {
+    BwdUvuArgs a{};
+    a.s_rowptr = g->s_rowptr;
+    a.s_col = g->s_col;
+    a.s_slot = g->s_slot;
+    a.pos = pos;
+    a.pos_dot = R.pos_dot;
+    a.x = R.x;
+    a.w = R.w + pi.w_off;
+    a.z_bar = z_bar;
+    a.x_bar = R.x_out;
+    a.wbar_part = R.w_out ? L.wpart : nullptr;
+    a.rbar = R.rbar;
+    a.n_nodes = N;
+    a.x_dim = static_cast<int32_t>(p->x_dim);
+    a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
+    a.z_dim = static_cast<int32_t>(p->z_dim);
+    a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
+    int ntiles = 1;
+    a.cp = lane_width(pi.c_in, &ntiles);
+    a.c = pi.c_in;
+    a.ls = pi.l_sh;
+    a.xbar_accumulate = (R.x_acc || seen[pi.in_block]) ? 1 : 0;
+    a.rbar_accumulate = rbar_started ? 1 : 0;
+    a.g = geom;
+    a.cg = pi.cgf;
+    ETPC_LAUNCH(ETPC_KIND_BWD_TRAVERSE, launch_bwd_uvu(a, R.tangent, pi.l_in, pi.l_out, grid, ntiles, s));
+    seen[pi.in_block] = 1;
+    if (R.rbar) rbar_started = true;
+    if (R.w_out) {
+      int64_t poff[1] = {pi.w_off};
+      int32_t col0[1] = {0}, cout[1] = {pi.c_in};
+      ETPC_LAUNCH(ETPC_KIND_AUX, launch_reduce_wbar(L.wpart, grid, 1, 1, p->n_basis, poff, col0, cout, p->n_basis * pi.c_in, R.w_out,
+                                  R.w_acc, s));
+    }
+  }
+  return ETPC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+etpc_status etpc_workspace_size(etpc_plan p, int32_t pass, int32_t n_nodes, int64_t n_edges, size_t* bytes) {
+  if (p == nullptr || bytes == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null plan or output");
+  if (n_nodes < 0 || n_edges < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative graph size");
+  const Derived d = derive(p);
+  const int64_t chunk = p->mode == ETPC_UVW ? n_nodes : kUvuGrid;
+  switch (pass) {
+    case ETPC_PASS_FWD: *bytes = fwd_bytes(p, d, chunk); break;
+    case ETPC_PASS_BWD: *bytes = bwd_bytes(p, d, n_edges, chunk); break;
+    case ETPC_PASS_DBL: *bytes = dbl_bytes(p, d, n_edges, chunk); break;
+    default: ETPC_FAIL(ETPC_ERR_INVALID_ARG, "unknown pass");
+  }
+  return ETPC_OK;
+}
+
+etpc_status etpc_csr_workspace_size(int32_t n_nodes, int64_t n_edges, size_t* bytes) {
+  if (bytes == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null output");
+  if (n_nodes < 0 || n_edges < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative graph size");
+  *bytes = csr_workspace_bytes(n_nodes, n_edges);
+  return ETPC_OK;
+}
+
+etpc_status etpc_csr_build(int32_t n_nodes, int64_t n_edges, const int32_t* src, const int32_t* dst, int32_t* rowptr,
+                           int32_t* col, int32_t* eid, int32_t* s_rowptr, int32_t* s_col, int32_t* s_slot, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  if (n_nodes < 0 || n_edges < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative graph size");
+  if (n_edges >= (int64_t(1) << 31)) ETPC_FAIL(ETPC_ERR_OVERFLOW, "n_edges must be < 2^31");
+  if (rowptr == nullptr || s_rowptr == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null row pointer outputs");
+  if (n_edges > 0 && (src == nullptr || dst == nullptr || col == nullptr || eid == nullptr || s_col == nullptr ||
+                      s_slot == nullptr))
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null edge arrays");
+  if (n_edges > 0 && n_nodes == 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "edges on an empty node set");
+  etpc_status st = check_ws(ws, ws_bytes, csr_workspace_bytes(n_nodes, n_edges));
+  if (st != ETPC_OK) return st;
+  ::etpc::ProfScope ps(ETPC_KIND_CSR, stream);
+  return csr_build_impl(n_nodes, n_edges, src, dst, rowptr, col, eid, s_rowptr, s_col, s_slot, ws, stream);
+}
+
+etpc_status etpc_graph_validate(const etpc_graph* g, hipStream_t stream) {
+  if (g == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null graph");
+  if (g->n_nodes < 0 || g->n_edges < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative graph size");
+  if (g->n_edges >= (int64_t(1) << 31)) ETPC_FAIL(ETPC_ERR_OVERFLOW, "n_edges must be < 2^31");
+  if (g->rowptr == nullptr || g->s_rowptr == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null row pointers");
+  if (g->n_edges > 0 && (g->col == nullptr || g->s_col == nullptr || g->s_slot == nullptr))
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null CSR index arrays");
+  return graph_validate_impl(*g, stream);
+}
+
+etpc_status etpc_forward(etpc_plan p, const etpc_graph* g, const float* x, const float* pos, const float* w, float* z,
+                         void* ws, size_t ws_bytes, hipStream_t s) {
+  etpc_status st = check_common(p, g);
+  if (st != ETPC_OK) return st;
+  if (g->n_nodes == 0) return ETPC_OK;
+  if (x == nullptr || pos == nullptr || w == nullptr || z == nullptr)
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null x, pos, w or z");
+  const Derived d = derive(p);
+  const int64_t chunk = pick_chunk(g->n_nodes, ws_bytes, [&](int64_t c) { return fwd_bytes(p, d, c); });
+  if (p->mode == ETPC_UVW) {
+    st = check_ws(ws, ws_bytes, fwd_bytes(p, d, 1));
+    if (st != ETPC_OK) return st;
+  }
+  Carver c{static_cast<char*>(ws), 0};
+  FwdLayout L;
+  fwd_layout(p, d, std::max<int64_t>(chunk, 0), c, L);
+  ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached(p, z, g->n_nodes, s));
+  if (p->mode == ETPC_UVW) return fwd_uvw_run(p, d, g, x, pos, nullptr, w, z, false, false, L, chunk, s);
+  return fwd_uvu_run(p, g, x, pos, nullptr, w, z, false, false, s);
+}
+
+etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, const float* pos, const float* w,
+                          const float* z_bar, float* x_bar, float* w_bar, float* pos_bar, void* ws, size_t ws_bytes,
+                          hipStream_t s) {
+  etpc_status st = check_common(p, g);
+  if (st != ETPC_OK) return st;
+  if (x == nullptr || pos == nullptr || w == nullptr || z_bar == nullptr)
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null x, pos, w or z_bar");
+  st = check_channels_bwd(p);
+  if (st != ETPC_OK) return st;
+  if (x_bar == nullptr && w_bar == nullptr && pos_bar == nullptr) return ETPC_OK;
+  const Derived d = derive(p);
+  const bool want_pos = pos_bar != nullptr;
+  const bool need_p = x_bar || w_bar;
+  const int32_t N = g->n_nodes;
+  if (N == 0) {
+    if (w_bar) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_bar, p->w_numel, 0.f, s));
+    return ETPC_OK;
+  }
+  auto bytes_of = [&](int64_t c) {
+    Carver cv;
+    BwdLayout L;
+    bwd_layout(p, d, g->n_edges, p->mode == ETPC_UVW ? c : kUvuGrid, want_pos, need_p, false, w_bar != nullptr,
+               false, x_bar != nullptr, false, cv, L);
+    return cv.off;
+  };
+  const int64_t chunk = pick_chunk(N, ws_bytes, bytes_of);
+  st = check_ws(ws, ws_bytes, bytes_of(1));
+  if (st != ETPC_OK) return st;
+  Carver cv{static_cast<char*>(ws), 0};
+  BwdLayout L;
+  bwd_layout(p, d, g->n_edges, p->mode == ETPC_UVW ? chunk : kUvuGrid, want_pos, need_p, false, w_bar != nullptr,
+             false, x_bar != nullptr, false, cv, L);
+  if (p->mode == ETPC_UVW) {
+    UvwBwdReq R{};
+    R.x = x;
+    R.w = w;
+    R.x_out = x_bar;
+    R.w_out = w_bar;
+    R.rbar = want_pos ? L.rbar : nullptr;
+    st = bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, s);
+  } else {
+    UvuBwdReq R{};
+    R.x = x;
+    R.w = w;
+    R.x_out = x_bar;
+    R.w_out = w_bar;
+    R.rbar = want_pos ? L.rbar : nullptr;
+    st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
+  }
+  if (st != ETPC_OK) return st;
+  if (want_pos) {
+    if (g->n_edges == 0 || p->paths.empty()) {
+      ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(pos_bar, 3 * static_cast<int64_t>(N), 0.f, s));
+    } else {
+      ETPC_LAUNCH(ETPC_KIND_AUX, launch_pos_bar(g->rowptr, g->s_rowptr, g->s_slot, L.rbar, pos_bar, N, s));
+    }
+  }
+  if (w_bar && p->paths.empty()) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_bar, p->w_numel, 0.f, s));
+  return ETPC_OK;
+}
+
+etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* x, const float* pos, const float* w,
+                                 const float* z_bar, const float* x_dot, const float* w_dot, const float* pos_dot,
+                                 float* z_bar_grad, float* x_grad, float* w_grad, void* ws, size_t ws_bytes,
+                                 hipStream_t s) {
+  etpc_status st = check_common(p, g);
+  if (st != ETPC_OK) return st;
+  if (x == nullptr || pos == nullptr || w == nullptr || z_bar == nullptr)
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null x, pos, w or z_bar");
+  st = check_channels_bwd(p);
+  if (st != ETPC_OK) return st;
+  const int32_t N = g->n_nodes;
+  if (N == 0) {
+    if (w_grad) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
+    return ETPC_OK;
+  }
+  const Derived d = derive(p);
+  const bool tan = pos_dot != nullptr;
+  const bool plain = x_dot != nullptr || w_dot != nullptr;
+  auto bytes_of = [&](int64_t c) {
+    Carver cv;
+    BwdLayout L;
+    const int64_t ch = p->mode == ETPC_UVW ? c : kUvuGrid;
+    bwd_layout(p, d, g->n_edges, ch, false, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
+               x_grad && w_dot && tan, cv, L);
+    return std::max(cv.off, z_bar_grad ? fwd_bytes(p, d, c) : size_t(0));
+  };
+  const int64_t chunk = pick_chunk(N, ws_bytes, bytes_of);
+  st = check_ws(ws, ws_bytes, bytes_of(1));
+  if (st != ETPC_OK) return st;
+
+  // d/dz_bar = z_dot = J_pos pos_dot + J_x x_dot + J_W w_dot (forward tangents)
+  if (z_bar_grad) {
+    Carver cv{static_cast<char*>(ws), 0};
+    FwdLayout L;
+    fwd_layout(p, d, chunk, cv, L);
+    if (!tan && !plain) {
+      ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(z_bar_grad, static_cast<int64_t>(N) * p->z_dim, 0.f, s));
+    } else {
+      ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached(p, z_bar_grad, N, s));
+      bool beta = false;
+      for (int term = 0; term < 3; ++term) {
+        const float* xin = x;
+        const float* win = w;
+        bool tangent = false;
+        if (term == 0) {
+          if (!tan) continue;
+          tangent = true;
+        } else if (term == 1) {
+          if (!x_dot) continue;
+          xin = x_dot;
+        } else {
+          if (!w_dot) continue;
+          win = w_dot;
+        }
+        if (p->mode == ETPC_UVW)
+          st = fwd_uvw_run(p, d, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, L, chunk, s);
+        else
+          st = fwd_uvu_run(p, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, s);
+        if (st != ETPC_OK) return st;
+        beta = true;
+      }
+    }
+  }
+  if (!x_grad && !w_grad) return ETPC_OK;
+  if (!tan && !plain) {
+    if (x_grad) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
+    if (w_grad) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
+    return ETPC_OK;
+  }
+  Carver cv{static_cast<char*>(ws), 0};
+  BwdLayout L;
+  const int64_t ch = p->mode == ETPC_UVW ? chunk : kUvuGrid;
+  bwd_layout(p, d, g->n_edges, ch, false, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
+             x_grad && w_dot && tan, cv, L);
+  if (p->mode == ETPC_UVW) {
+    // d/dx = W^T dP + w_dot^T P ;  d/dW = x^T dP + x_dot^T P
+    UvwBwdReq R{};
+    R.pos_dot = pos_dot;
+    if (tan) {
+      R.x = x;
+      R.w = w;
+      R.x2 = x_dot;
+      R.w2 = w_dot;
+      R.tangent = true;
+      R.plain_needed = plain;
+    } else {
+      // only plain terms: x_grad = w_dot^T P, w_grad = x_dot^T P (zero where the cotangent is absent)
+      R.x = x_dot;
+      R.w = w_dot;
+      R.tangent = false;
+    }
+    R.x_out = x_grad;
+    R.w_out = w_grad;
+    if (!tan) {
+      if (x_grad && !w_dot) {
+        ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
+        R.x_out = nullptr;
+      }
+      if (w_grad && !x_dot) {
+        ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
+        R.w_out = nullptr;
+      }
+      if (!R.x_out && !R.w_out) return ETPC_OK;
+      // the plain pass reads x (for W_bar) and w (for x_bar); feed the cotangents in their place
+      R.x = x_dot ? x_dot : x;
+      R.w = w_dot ? w_dot : w;
+    }
+    return bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, s);
+  }
+  // uvu: tangent pass (pos_dot) then plain passes with w -> w_dot (x_grad) and x -> x_dot (w_grad)
+  bool xs = false, wsd = false;
+  if (tan) {
+    UvuBwdReq R{};
+    R.x = x;
+    R.w = w;
+    R.pos_dot = pos_dot;
+    R.tangent = true;
+    R.x_out = x_grad;
+    R.w_out = w_grad;
+    st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
+    if (st != ETPC_OK) return st;
+    xs = x_grad != nullptr;
+    wsd = w_grad != nullptr;
+  }
+  if (x_grad && w_dot) {
+    UvuBwdReq R{};
+    R.x = x;
+    R.w = w_dot;
+    R.x_out = x_grad;
+    R.x_acc = xs;
+    st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
+    if (st != ETPC_OK) return st;
+    xs = true;
+  }
+  if (w_grad && x_dot) {
+    UvuBwdReq R{};
+    R.x = x_dot;
+    R.w = w;
+    R.w_out = w_grad;
+    R.w_acc = wsd;
+    st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
+    if (st != ETPC_OK) return st;
+    wsd = true;
+  }
+  if (x_grad && !xs) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
+  if (w_grad && !wsd) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
+  return ETPC_OK;
+}
+
+}  // extern "C"

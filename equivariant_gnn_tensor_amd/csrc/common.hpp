@@ -1,0 +1,65 @@
+// Shared host/device definitions for the etpc library (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+#include <string>
+
+#include "../../include/etpc.h"
+
+namespace etpc {
+
+constexpr int kMaxL = 3;
+constexpr int kMaxBasis = 16;
+constexpr int kMaxPaths = 64;
+constexpr int kWave = 64;
+
+// Row offset map: row r of a logical matrix lives at (r / div) * s1 + (r % div) * s2.
+// Covers plain row-major matrices (div = 1) and ir_mul blocks, whose rows are
+// (node, m) pairs: node stride = feature width, m stride = multiplicity.
+struct RowMap {
+  int64_t s1;
+  int64_t s2;
+  int32_t div;
+};
+
+// Edge geometry parameters shared by every traversal kernel.
+struct GeomParams {
+  int32_t radial;     // etpc_radial
+  int32_t nb;         // number of radial bases B
+  float r_lo, r_hi;
+  float gauss_d;      // Gaussian spacing D
+  float gauss_inv2d2; // 1 / (2 D^2)
+  int32_t poly_p;
+  int32_t periodic;
+  float box[3];
+  float inv_box[3];
+};
+
+// Dense real coupling tensor of one path, stored [NI][7][NO] (m_sh stride fixed at 7).
+struct CGTable {
+  float c[7 * 7 * 7];
+};
+
+}  // namespace etpc
+
+// thread-local error message used by the C ABI
+namespace etpc {
+void set_error(const std::string& msg);
+const char* last_error();
+}  // namespace etpc
+
+#define ETPC_FAIL(code, msg)         \
+  do {                               \
+    ::etpc::set_error(msg);          \
+    return (code);                   \
+  } while (0)
+
+#define ETPC_HIP(call)                                                                      \
+  do {                                                                                      \
+    hipError_t _e = (call);                                                                 \
+    if (_e != hipSuccess) {                                                                 \
+      ::etpc::set_error(std::string("HIP error: ") + hipGetErrorString(_e) + " at " #call); \
+      return ETPC_ERR_HIP;                                                                  \
+    }                                                                                       \
+  } while (0)

@@ -1,0 +1,8 @@
+// Instantiation unit: uvu forward traversal, tangent=false.
+#include "fwd_impl.hpp"
+
+namespace etpc {
+namespace fwd_detail {
+template hipError_t launch_fwd_uvu_t<false>(const FwdUvuArgs&, int, int, int, int, hipStream_t);
+}  // namespace fwd_detail
+}  // namespace etpc

@@ -1,0 +1,157 @@
+// Edge geometry device functions (fused into every traversal kernel; never stored).
+//
+// Edge vector r_e = p_sender - p_receiver (Sobek paper, Sec. 2, Eq. 8), minimum
+// image in an orthorhombic box; distance r and direction u = r_e / r.
+//
+// Harmonics: real, component-normalized, evaluated from their homogeneous
+// polynomial forms P_l at the unit vector (on the sphere P_l(u) = Y_l(u)).  The
+// gradient with respect to the edge vector uses homogeneity of degree l:
+//   dY_l/dr_e = (grad P_l(u) - l Y_l(u) u) / r.
+// Radial bases: Gaussian  phi_b = exp(-(r - mu_b)^2 / (2 D^2));
+//   Bessel  phi_b = sqrt(2/r_c) sin(b pi r / r_c) / r * f_p(r / r_c), b = 1..B,
+//   f_p(t) = 1 - (p+1)(p+2)/2 t^p + p(p+2) t^(p+1) - p(p+1)/2 t^(p+2) (t < 1), else 0.
+#pragma once
+
+#include "common.hpp"
+
+namespace etpc {
+
+constexpr float kS3 = 1.7320508075688772f;
+constexpr float kS5 = 2.23606797749979f;
+constexpr float kS7 = 2.6457513110645907f;
+constexpr float kS15 = 3.872983346207417f;
+constexpr float kS42 = 6.48074069840786f;
+constexpr float kS70 = 8.366600265340756f;
+constexpr float kS105 = 10.246950765959598f;
+
+__device__ inline void edge_vector(const GeomParams& g, const float* __restrict__ pos, int j, int i, float& rx,
+                                   float& ry, float& rz) {
+  rx = pos[3 * j + 0] - pos[3 * i + 0];
+  ry = pos[3 * j + 1] - pos[3 * i + 1];
+  rz = pos[3 * j + 2] - pos[3 * i + 2];
+  if (g.periodic) {
+    rx -= g.box[0] * rintf(rx * g.inv_box[0]);
+    ry -= g.box[1] * rintf(ry * g.inv_box[1]);
+    rz -= g.box[2] * rintf(rz * g.inv_box[2]);
+  }
+}
+
+// Y_l(u) for one degree l (runtime), written into y[0..2l].
+__device__ inline void sh_eval(int l, float x, float y, float z, float* __restrict__ out) {
+  if (l == 0) {
+    out[0] = 1.f;
+  } else if (l == 1) {
+    out[0] = kS3 * y;
+    out[1] = kS3 * z;
+    out[2] = kS3 * x;
+  } else if (l == 2) {
+    out[0] = kS15 * x * y;
+    out[1] = kS15 * y * z;
+    out[2] = 0.5f * kS5 * (2.f * z * z - x * x - y * y);
+    out[3] = kS15 * x * z;
+    out[4] = 0.5f * kS15 * (x * x - y * y);
+  } else {
+    const float x2 = x * x, y2 = y * y, z2 = z * z;
+    out[0] = 0.25f * kS70 * y * (3.f * x2 - y2);
+    out[1] = kS105 * x * y * z;
+    out[2] = 0.25f * kS42 * y * (4.f * z2 - x2 - y2);
+    out[3] = 0.5f * kS7 * z * (2.f * z2 - 3.f * x2 - 3.f * y2);
+    out[4] = 0.25f * kS42 * x * (4.f * z2 - x2 - y2);
+    out[5] = 0.5f * kS105 * z * (x2 - y2);
+    out[6] = 0.25f * kS70 * x * (x2 - 3.f * y2);
+  }
+}
+
+// Gradient of the homogeneous polynomial P_l at u: g[m][d], d = x,y,z.
+__device__ inline void sh_poly_grad(int l, float x, float y, float z, float (*__restrict__ g)[3]) {
+  if (l == 0) {
+    g[0][0] = g[0][1] = g[0][2] = 0.f;
+  } else if (l == 1) {
+    g[0][0] = 0.f; g[0][1] = kS3; g[0][2] = 0.f;
+    g[1][0] = 0.f; g[1][1] = 0.f; g[1][2] = kS3;
+    g[2][0] = kS3; g[2][1] = 0.f; g[2][2] = 0.f;
+  } else if (l == 2) {
+    g[0][0] = kS15 * y; g[0][1] = kS15 * x; g[0][2] = 0.f;
+    g[1][0] = 0.f; g[1][1] = kS15 * z; g[1][2] = kS15 * y;
+    g[2][0] = -kS5 * x; g[2][1] = -kS5 * y; g[2][2] = 2.f * kS5 * z;
+    g[3][0] = kS15 * z; g[3][1] = 0.f; g[3][2] = kS15 * x;
+    g[4][0] = kS15 * x; g[4][1] = -kS15 * y; g[4][2] = 0.f;
+  } else {
+    const float x2 = x * x, y2 = y * y, z2 = z * z;
+    const float a70 = 0.25f * kS70, a42 = 0.25f * kS42, a7 = 0.5f * kS7, a105 = 0.5f * kS105;
+    g[0][0] = a70 * 6.f * x * y; g[0][1] = a70 * 3.f * (x2 - y2); g[0][2] = 0.f;
+    g[1][0] = kS105 * y * z; g[1][1] = kS105 * x * z; g[1][2] = kS105 * x * y;
+    g[2][0] = -a42 * 2.f * x * y; g[2][1] = a42 * (4.f * z2 - x2 - 3.f * y2); g[2][2] = a42 * 8.f * y * z;
+    g[3][0] = -a7 * 6.f * x * z; g[3][1] = -a7 * 6.f * y * z; g[3][2] = a7 * (6.f * z2 - 3.f * x2 - 3.f * y2);
+    g[4][0] = a42 * (4.f * z2 - 3.f * x2 - y2); g[4][1] = -a42 * 2.f * x * y; g[4][2] = a42 * 8.f * x * z;
+    g[5][0] = a105 * 2.f * x * z; g[5][1] = -a105 * 2.f * y * z; g[5][2] = a105 * (x2 - y2);
+    g[6][0] = a70 * 3.f * (x2 - y2); g[6][1] = -a70 * 6.f * x * y; g[6][2] = 0.f;
+  }
+}
+
+// dY_l/dr_e[m][d] = (grad P_l(u) - l Y_l(u) u) / r
+__device__ inline void sh_grad_r(int l, float x, float y, float z, float inv_r, const float* __restrict__ yv,
+                                 float (*__restrict__ dy)[3]) {
+  sh_poly_grad(l, x, y, z, dy);
+  const int n = 2 * l + 1;
+  for (int m = 0; m < n; ++m) {
+    const float s = static_cast<float>(l) * yv[m];
+    dy[m][0] = (dy[m][0] - s * x) * inv_r;
+    dy[m][1] = (dy[m][1] - s * y) * inv_r;
+    dy[m][2] = (dy[m][2] - s * z) * inv_r;
+  }
+}
+
+// phi[0..NB) (zero-padded beyond nb); if dphi != nullptr also d phi / d r.
+template <int NB>
+__device__ inline void radial_eval(const GeomParams& g, float r, float* __restrict__ phi, float* __restrict__ dphi) {
+  if (g.radial == ETPC_RADIAL_GAUSSIAN) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < g.nb) {
+        const float t = r - (g.r_lo + b * g.gauss_d);
+        const float e = __expf(-t * t * g.gauss_inv2d2);
+        phi[b] = e;
+        if (dphi) dphi[b] = -2.f * g.gauss_inv2d2 * t * e;
+      } else {
+        phi[b] = 0.f;
+        if (dphi) dphi[b] = 0.f;
+      }
+    }
+  } else {
+    const float rc = g.r_hi;
+    const float t = r / rc;
+    float f = 0.f, fp = 0.f;
+    if (t < 1.f) {
+      const int p = g.poly_p;
+      const float pf = static_cast<float>(p);
+      const float tp1 = __powf(t, pf - 1.f);  // t^(p-1), t > 0
+      const float tp = tp1 * t;
+      const float a = 0.5f * (pf + 1.f) * (pf + 2.f), bb = pf * (pf + 2.f), c = 0.5f * pf * (pf + 1.f);
+      f = 1.f - a * tp + bb * tp * t - c * tp * t * t;
+      fp = (-a * pf * tp1 + bb * (pf + 1.f) * tp - c * (pf + 2.f) * tp * t) / rc;
+    }
+    const float amp = sqrtf(2.f / rc);
+    const float inv_r = 1.f / r;
+    const float w = 3.14159265358979323846f / rc;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b < g.nb) {
+        const float k = w * (b + 1);
+        float sn, cs;
+        sincosf(k * r, &sn, &cs);
+        const float bare = amp * sn * inv_r;
+        phi[b] = bare * f;
+        if (dphi) {
+          const float dbare = amp * (k * cs - sn * inv_r) * inv_r;
+          dphi[b] = dbare * f + bare * fp;
+        }
+      } else {
+        phi[b] = 0.f;
+        if (dphi) dphi[b] = 0.f;
+      }
+    }
+  }
+}
+
+}  // namespace etpc

@@ -1,0 +1,140 @@
+// Small memory-bound helpers: fill, weight re-layout, fixed-order reductions.
+#include "kernels.hpp"
+
+namespace etpc {
+namespace {
+
+__global__ void fill_kernel(float* p, int64_t n, float v) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+// one path per blockIdx.y: wcat[u][col0 + q*cout + w], wt[(col0 + q*cout + w)][u] from W[q][u][w]
+__global__ void wprep_kernel(const WPrepArgs a) {
+  const int t = blockIdx.y;
+  const int cout = a.cout[t];
+  const int64_t per_path = static_cast<int64_t>(a.nb) * a.c_in * cout;
+  const float* w = a.w + a.path_off[t];
+  for (int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; r < per_path;
+       r += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int q = static_cast<int>(r / (static_cast<int64_t>(a.c_in) * cout));
+    const int64_t rr = r - static_cast<int64_t>(q) * a.c_in * cout;
+    const int u = static_cast<int>(rr / cout);
+    const int wch = static_cast<int>(rr - static_cast<int64_t>(u) * cout);
+    const float v = w[r];
+    const int64_t col = a.col0[t] + static_cast<int64_t>(q) * cout + wch;
+    if (a.wcat) a.wcat[static_cast<int64_t>(u) * a.ncols + col] = v;
+    if (a.wt) a.wt[col * a.c_in + u] = v;
+  }
+}
+
+struct ReduceWArgs {
+  const float* part;
+  int32_t splits, rows, ncols, nb;
+  int32_t accumulate;
+  float* out;
+  int64_t path_off[kMaxPaths];
+  int32_t col0[kMaxPaths];
+  int32_t cout[kMaxPaths];
+};
+
+// one path per blockIdx.y; element r of the path block = (q, u, w) in W order
+__global__ void reduce_wbar_kernel(const ReduceWArgs a) {
+  const int t = blockIdx.y;
+  const int cout = a.cout[t];
+  const int64_t per_path = static_cast<int64_t>(a.nb) * a.rows * cout;
+  const int64_t split_stride = static_cast<int64_t>(a.rows) * a.ncols;
+  for (int64_t r = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; r < per_path;
+       r += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int q = static_cast<int>(r / (static_cast<int64_t>(a.rows) * cout));
+    const int64_t rr = r - static_cast<int64_t>(q) * a.rows * cout;
+    const int u = static_cast<int>(rr / cout);
+    const int w = static_cast<int>(rr - static_cast<int64_t>(u) * cout);
+    const int64_t src = static_cast<int64_t>(u) * a.ncols + a.col0[t] + static_cast<int64_t>(q) * cout + w;
+    float s = 0.f;
+    for (int z = 0; z < a.splits; ++z) s += a.part[z * split_stride + src];
+    float* o = a.out + a.path_off[t] + r;
+    *o = a.accumulate ? (*o + s) : s;
+  }
+}
+
+__global__ void pos_bar_kernel(const int32_t* __restrict__ rowptr, const int32_t* __restrict__ s_rowptr,
+                               const int32_t* __restrict__ s_slot, const float* __restrict__ rbar,
+                               float* __restrict__ pos_bar, int n) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= n) return;
+  float sx = 0.f, sy = 0.f, sz = 0.f;
+  for (int k = s_rowptr[v]; k < s_rowptr[v + 1]; ++k) {
+    const int64_t e = s_slot[k];
+    sx += rbar[3 * e + 0];
+    sy += rbar[3 * e + 1];
+    sz += rbar[3 * e + 2];
+  }
+  for (int64_t e = rowptr[v]; e < rowptr[v + 1]; ++e) {
+    sx -= rbar[3 * e + 0];
+    sy -= rbar[3 * e + 1];
+    sz -= rbar[3 * e + 2];
+  }
+  pos_bar[3 * v + 0] = sx;
+  pos_bar[3 * v + 1] = sy;
+  pos_bar[3 * v + 2] = sz;
+}
+
+int grid_for(int64_t n, int block) {
+  int64_t g = (n + block - 1) / block;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+}  // namespace
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_wprep(const WPrepArgs& a, hipStream_t s) {
+  if (a.n_paths <= 0) return hipSuccess;
+  int maxc = 1;
+  for (int t = 0; t < a.n_paths; ++t) maxc = a.cout[t] > maxc ? a.cout[t] : maxc;
+  const int64_t per = static_cast<int64_t>(a.nb) * a.c_in * maxc;
+  hipLaunchKernelGGL(wprep_kernel, dim3(grid_for(per, 256), a.n_paths), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_wbar(const float* part, int splits, int c_in, int n_paths, int nb, const int64_t* path_off,
+                              const int32_t* col0, const int32_t* cout, int ncols, float* out, bool accumulate,
+                              hipStream_t s) {
+  if (n_paths <= 0) return hipSuccess;
+  ReduceWArgs a{};
+  a.part = part;
+  a.splits = splits;
+  a.rows = c_in;
+  a.ncols = ncols;
+  a.nb = nb;
+  a.accumulate = accumulate ? 1 : 0;
+  a.out = out;
+  int maxc = 1;
+  for (int t = 0; t < n_paths && t < kMaxPaths; ++t) {
+    a.path_off[t] = path_off[t];
+    a.col0[t] = col0[t];
+    a.cout[t] = cout[t];
+    maxc = cout[t] > maxc ? cout[t] : maxc;
+  }
+  const int64_t per = static_cast<int64_t>(nb) * c_in * maxc;
+  hipLaunchKernelGGL(reduce_wbar_kernel, dim3(grid_for(per, 256), n_paths), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pos_bar(const int32_t* rowptr, const int32_t* s_rowptr, const int32_t* s_slot, const float* rbar,
+                          float* pos_bar, int n_nodes, hipStream_t s) {
+  if (n_nodes <= 0) return hipSuccess;
+  hipLaunchKernelGGL(pos_bar_kernel, dim3((n_nodes + 255) / 256), dim3(256), 0, s, rowptr, s_rowptr, s_slot, rbar,
+                     pos_bar, n_nodes);
+  return hipGetLastError();
+}
+
+}  // namespace etpc

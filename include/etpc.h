@@ -1,0 +1,190 @@
+/*
+ * etpc.h -- streaming edge-conditioned O(3) tensor-product convolution for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the edge-conditioned equivariant convolution of the Sobek
+ * paper ("Sobek: Streaming Equivariant Tensor Product Convolutions", Sec. 2,
+ * Eq. 6-13):
+ *
+ *   z_i = sum_{e=(j->i)} sum_{paths pi} sum_{u,w} w_e,pi[u,w] (x_j,u (x)_CG Y(r_e))_pi
+ *   w_e,pi = sum_b phi_b(|r_e|) W_pi[b]                     (radial projection, Eq. 12)
+ *   r_e = p_j - p_i   (sender minus receiver, Eq. 8; minimum image in a periodic box)
+ *
+ * in two connection modes: fully connected "uvw" (Eq. 6) and channelwise "uvu"
+ * (Eq. 7).  It is evaluated in the streaming order of Sec. 3-4 (Eq. 15-17,
+ * 32-36): per-edge weights, messages and weight adjoints are never stored.
+ *
+ * Conventions (the paper leaves them open; these are this library's readings):
+ *  - harmonics: real, component-normalized (sum_m Y_lm^2 = 2l+1), m = -l..l,
+ *    l = 1 ordered (y, z, x); degree l has parity (-1)^l; l <= 3.
+ *  - coupling c^pi[m_in][m_sh][m_out]: real-basis SO(3) intertwiner, each output
+ *    column of unit norm, first nonzero entry (C order) positive; no extra path
+ *    normalization factor.
+ *  - radial: Gaussian  phi_b = exp(-(r-mu_b)^2/(2D^2)), mu_b = r_lo + b D,
+ *    D = (r_hi-r_lo)/(B-1);  Bessel  phi_b = sqrt(2/r_c) sin(b pi r/r_c)/r f_p(r/r_c),
+ *    b = 1..B, r_c = r_hi, polynomial envelope f_p of degree p+2 (zero beyond r_c).
+ *  - layouts, all row-major fp32 with int32 graph indices:
+ *      x, x_bar, x_grad, x_dot : [N][x_dim]   ir_mul: block k stored [2l+1][C], channel fastest
+ *      z, z_bar, z_bar_grad    : [N][z_dim]   ir_mul
+ *      pos, pos_bar, pos_dot   : [N][3]
+ *      w, w_bar, w_grad, w_dot : paths in plan order (out_block, in_block, l_sh),
+ *                                uvw block [B][C_in][C_out], uvu block [B][C_in].
+ *
+ * Ownership: the caller allocates every data and workspace buffer; the library
+ * allocates nothing in a compute call.  A plan is host memory only (its tables
+ * travel to the GPU as kernel arguments) and is immutable after creation, so it
+ * may be shared across streams; concurrent calls need distinct workspaces.
+ * Inputs are read-only; outputs are overwritten (never accumulated into).
+ * Every call validates its arguments on the host first; on a non-OK status no
+ * kernel has been enqueued and etpc_last_error() describes the problem.
+ * Compute calls are asynchronous on the given stream; results are
+ * deterministic for a given workspace size (fixed reduction owners and orders,
+ * no floating-point atomics).
+ */
+#ifndef ETPC_H
+#define ETPC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct etpc_plan_s* etpc_plan;
+
+typedef enum {
+  ETPC_OK = 0,
+  ETPC_ERR_INVALID_ARG = 1,   /* null required pointer, bad size, bad enum */
+  ETPC_ERR_UNSUPPORTED = 2,   /* l > 3, B > 16, more than 64 paths, ... */
+  ETPC_ERR_INVALID_PATH = 3,  /* instruction violates the selection rule (Eq. 5) or uvu C_out != C_in */
+  ETPC_ERR_WORKSPACE = 4,     /* workspace smaller than etpc_workspace_size() asks for */
+  ETPC_ERR_OVERFLOW = 5,      /* N, E or an internal index would exceed int32 */
+  ETPC_ERR_GRAPH = 6,         /* etpc_graph_validate found an inconsistent CSR */
+  ETPC_ERR_HIP = 7            /* a HIP runtime call failed */
+} etpc_status;
+
+typedef enum { ETPC_UVW = 0, ETPC_UVU = 1 } etpc_mode;
+typedef enum { ETPC_RADIAL_GAUSSIAN = 0, ETPC_RADIAL_BESSEL_POLY = 1 } etpc_radial;
+typedef enum { ETPC_PASS_FWD = 0, ETPC_PASS_BWD = 1, ETPC_PASS_DBL = 2 } etpc_pass;
+
+/* One irrep block: multiplicity, degree l (0..3) and parity (+1 'e', -1 'o'). */
+typedef struct { int32_t mul, l, parity; } etpc_irrep;
+/* One instruction (path): input block, harmonic degree, output block. */
+typedef struct { int32_t in_block, l_sh, out_block; } etpc_instr;
+
+typedef struct {
+  int32_t n_in;  const etpc_irrep* in;        /* [host] input irreps (Eq. 3) */
+  int32_t n_out; const etpc_irrep* out;       /* [host] output irreps, or allowed outputs (see below) */
+  int32_t out_per_path;  /* uvu only: nonzero = one output block per valid (in, l_sh, allowed out)
+                            in that nested order, multiplicity tied to the input (Eq. 7);
+                            `out` then lists the allowed (l, parity), `mul` ignored */
+  int32_t lmax_sh;                            /* 0..3 */
+  int32_t mode;                               /* etpc_mode */
+  int32_t n_instr; const etpc_instr* instr;   /* [host] NULL/0 = every valid (in, l_sh, out) */
+  int32_t radial;                             /* etpc_radial */
+  int32_t n_basis;                            /* B: 1..16 (Gaussian needs >= 2) */
+  float r_lo, r_hi;                           /* Gaussian range; Bessel cutoff = r_hi */
+  int32_t poly_p;                             /* Bessel envelope exponent p >= 1 */
+  float box[3];                               /* all zero = open; else orthorhombic minimum image */
+} etpc_spec;
+
+/* Receiver-sorted CSR plus the sender (source) view; all DEVICE pointers.
+ * rowptr[N+1], col[E] = sender of each receiver slot;
+ * s_rowptr[N+1], s_col[E] = receiver of each sender slot, s_slot[E] = the receiver slot.
+ * Preconditions (checked only by etpc_graph_validate): indices in range, both views
+ * describe the same edge multiset, no self loops, |r_e| > 0 on every edge. */
+typedef struct {
+  int32_t n_nodes;
+  int64_t n_edges;
+  const int32_t* rowptr;
+  const int32_t* col;
+  const int32_t* s_rowptr;
+  const int32_t* s_col;
+  const int32_t* s_slot;
+} etpc_graph;
+
+/* Planner (host only).  Parses the spec, enumerates the valid paths (selection
+ * rule, Eq. 5), builds the real coupling tensors in float64 (Racah's formula moved
+ * to the real basis) and the block offsets.  Sec. 4, the paragraph on the kernel
+ * generator: it enumerates valid paths and sparse CG terms from the irreps. */
+etpc_status etpc_plan_create(const etpc_spec* spec, etpc_plan* out);
+void etpc_plan_destroy(etpc_plan plan);
+/* Widths: x_dim = sum C(2l+1) (Eq. 4), z_dim likewise, w_numel = B * sum n_pi (Eq. 9-10). */
+etpc_status etpc_plan_info(etpc_plan plan, int64_t* x_dim, int64_t* z_dim, int64_t* w_numel,
+                           int32_t* n_paths);
+/* Path p in plan order.  fan_in = B * (sum of C_in over the output group) for uvw, B for uvu. */
+etpc_status etpc_plan_path(etpc_plan plan, int32_t p, int32_t* in_block, int32_t* l_sh, int32_t* out_block,
+                           int64_t* w_off, int64_t* w_numel, int32_t* fan_in);
+/* Output block b (useful when out_per_path built the output list). */
+etpc_status etpc_plan_out_irrep(etpc_plan plan, int32_t b, int32_t* n_out, etpc_irrep* irrep);
+/* [host] dense coupling tensor of path p, [2l_in+1][2l_sh+1][2l_out+1] doubles (Eq. 32). */
+etpc_status etpc_plan_cg(etpc_plan plan, int32_t p, double* out);
+
+/* Workspace bytes a compute pass needs for a graph of n_nodes / n_edges.  Grows with
+ * N (node-side states) and by 12 B per edge for backward and double backward (the
+ * per-edge position adjoint); it never scales with E times a channel width. */
+etpc_status etpc_workspace_size(etpc_plan plan, int32_t pass, int32_t n_nodes, int64_t n_edges,
+                                size_t* bytes);
+
+/* Build both CSR views from a COO list (src[e] -> dst[e]), stable: receiver view sorted
+ * by receiver with ties in COO order; sender view sorted by sender with ties in
+ * receiver-slot order (Sec. 4: cached stable CSR views give receiver and source
+ * reductions fixed ownership).  eid[slot] = COO index.  All arrays are device int32.
+ * Bit-exact and deterministic.  Workspace from etpc_csr_workspace_size. */
+etpc_status etpc_csr_workspace_size(int32_t n_nodes, int64_t n_edges, size_t* bytes);
+etpc_status etpc_csr_build(int32_t n_nodes, int64_t n_edges, const int32_t* src, const int32_t* dst,
+                           int32_t* rowptr, int32_t* col, int32_t* eid,
+                           int32_t* s_rowptr, int32_t* s_col, int32_t* s_slot,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+/* Debug check of the graph preconditions; synchronizes the stream.  Needs no workspace. */
+etpc_status etpc_graph_validate(const etpc_graph* graph, hipStream_t stream);
+
+/* Forward: z = conv(x, pos, W) (Eq. 11-13), streaming order Eq. 32-35 (uvw: receiver
+ * state S then a channel GEMM; uvu: edge-local weights, Eq. 17). */
+etpc_status etpc_forward(etpc_plan plan, const etpc_graph* graph, const float* x, const float* pos,
+                         const float* w, float* z, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Backward: gradients of <z_bar, z> with respect to x, W and positions (Eq. 18-22 and
+ * the chain rule through Eq. 8).  Each output pointer may be NULL to skip it. */
+etpc_status etpc_backward(etpc_plan plan, const etpc_graph* graph, const float* x, const float* pos,
+                          const float* w, const float* z_bar,
+                          float* x_bar, float* w_bar, float* pos_bar,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Double backward: vector-Jacobian product of backward (x, W, pos, z_bar) -> (x_bar, W_bar,
+ * pos_bar) with cotangents (x_dot, w_dot, pos_dot) (directional second adjoints, Eq. 23-31,
+ * channel identities Eq. 37-39).  Returns d/dz_bar, d/dx and d/dW; any cotangent may be NULL
+ * (= zero) and any output may be NULL (skipped).  The d/dpos term (second derivatives of the
+ * harmonics and radial basis) is not provided. */
+etpc_status etpc_double_backward(etpc_plan plan, const etpc_graph* graph, const float* x,
+                                 const float* pos, const float* w, const float* z_bar,
+                                 const float* x_dot, const float* w_dot, const float* pos_dot,
+                                 float* z_bar_grad, float* x_grad, float* w_grad,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Kernel timing (off by default).  While enabled, every kernel the library enqueues is
+ * bracketed by a pair of HIP events recorded on its launch stream, grouped by kind.
+ * etpc_profile_read synchronizes on the recorded events and returns the summed
+ * durations (milliseconds) and launch count of one kind since the last enable.
+ * Process-wide; not meant for concurrent use from several threads. */
+typedef enum {
+  ETPC_KIND_CSR = 0,          /* CSR build kernels */
+  ETPC_KIND_FWD_TRAVERSE = 1, /* receiver traversals (uvw state S, uvu outputs) */
+  ETPC_KIND_CHANNEL_GEMM = 2, /* m = S W */
+  ETPC_KIND_BWD_TRAVERSE = 3, /* sender traversals (P state, edge position adjoint) */
+  ETPC_KIND_NODE_GEMM = 4,    /* Xt = x W, x_bar = P W^T, W_bar = x^T P */
+  ETPC_KIND_AUX = 5,          /* weight re-layout, fixed-order reductions, fills, pos_bar */
+  ETPC_KIND_COUNT = 6
+} etpc_kind;
+etpc_status etpc_profile_enable(int32_t enable);
+etpc_status etpc_profile_read(int32_t kind, double* total_ms, int64_t* launches);
+
+/* Thread-local description of the last non-OK status (empty string if none). */
+const char* etpc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ETPC_H */

@@ -1,0 +1,212 @@
+"""GPU parity: HIP path (through the C ABI) vs the float64 oracle.
+
+Tolerance: max|d| / max|ref| <= 1e-4 for forward and backward, 1e-3 for double
+backward, per output tensor (fp32 arithmetic on the GPU, float64 oracle).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import conv
+from oracle.csr import csr_build
+from tests.gpu_helpers import make_case, note, rel_err
+from workloads import CONFIGS, small_variant
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+TOL_DBL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import equivariant_gnn_tensor_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _etpc():
+    import equivariant_gnn_tensor_amd as etpc
+    return etpc
+
+
+# ---------------------------------------------------------------- CSR
+def _csr_cases(rng):
+    yield "empty", 5, np.zeros(0, np.int32), np.zeros(0, np.int32)
+    yield "single-node-no-edges", 1, np.zeros(0, np.int32), np.zeros(0, np.int32)
+    yield "all-into-one", 7, rng.integers(0, 7, 3000).astype(np.int32), np.full(3000, 3, np.int32)
+    yield "duplicates", 4, np.array([1, 1, 1, 0, 2, 2], np.int32), np.array([0, 0, 0, 1, 0, 0], np.int32)
+    for n, e in [(100, 5000), (70000, 300000), (300, 20000)]:
+        yield f"random-{n}-{e}", n, rng.integers(0, n, e).astype(np.int32), rng.integers(0, n, e).astype(np.int32)
+
+
+def test_csr_bit_exact():
+    etpc = _etpc()
+    rng = np.random.default_rng(5)
+    for name, n, src, dst in _csr_cases(rng):
+        note(f"csr {name} n={n} e={len(src)}")
+        g = etpc.etpc_csr_build(n, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+        want = csr_build(n, src, dst)
+        got = dict(rowptr=g.rowptr, col=g.col, eid=g.eid, s_rowptr=g.s_rowptr, s_col=g.s_col, s_slot=g.s_slot)
+        for k, v in want.items():
+            assert np.array_equal(got[k].cpu().numpy(), v), (name, k)
+
+
+def test_graph_validate_accepts_built_and_rejects_broken():
+    etpc = _etpc()
+    rng = np.random.default_rng(6)
+    n, e = 50, 400
+    src = rng.integers(0, n, e).astype(np.int32)
+    dst = (src + rng.integers(1, n, e).astype(np.int32)) % n
+    g = etpc.etpc_csr_build(n, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    etpc.etpc_graph_validate(g)
+    bad_col = g.col.clone()
+    bad_col[3] = n + 5                       # out of range, caught on the host side of the check
+    gb = etpc.Graph(n, g.rowptr, bad_col, g.s_rowptr, g.s_col, g.s_slot)
+    with pytest.raises(etpc.EtpcError):
+        etpc.etpc_graph_validate(gb)
+    bad_slot = g.s_slot.clone()
+    bad_slot[[0, 1]] = bad_slot[[1, 0]]      # breaks the stable order within a sender row or the mapping
+    gs = etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, bad_slot)
+    with pytest.raises(etpc.EtpcError):
+        etpc.etpc_graph_validate(gs)
+
+
+# ---------------------------------------------------------------- forward / backward parity
+FWD_CASES = [
+    ("cfg1", None, None),
+    ("cfg2", 256, None),
+    ("cfg3", 256, None),
+    ("cfg4_d16", 600, None),
+    ("cfg4_d64", 300, None),
+    ("cfg5", 256, None),
+]
+
+
+def _cfg(name, n, d):
+    return CONFIGS[name] if n is None else small_variant(name, n, d)
+
+
+@pytest.mark.parametrize("name,n,d", FWD_CASES)
+def test_forward_parity(name, n, d):
+    etpc = _etpc()
+    cfg = _cfg(name, n, d)
+    note(f"forward {cfg.name} N={cfg.n_nodes}")
+    c = make_case(cfg)
+    z = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w)
+    torch.cuda.synchronize()
+    ref = conv.forward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst)
+    err = rel_err(z, ref)
+    note(f"forward {cfg.name} rel err {err:.2e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("name,n,d", [c for c in FWD_CASES if c[0] != "cfg1"])
+def test_backward_parity(name, n, d):
+    etpc = _etpc()
+    cfg = _cfg(name, n, d)
+    note(f"backward {cfg.name} N={cfg.n_nodes}")
+    c = make_case(cfg)
+    xb, wb, pb = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar)
+    torch.cuda.synchronize()
+    rx, rw, rp = conv.backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, c.wl.z_bar)
+    errs = (rel_err(xb, rx), rel_err(wb, rw), rel_err(pb, rp))
+    note(f"backward {cfg.name} rel err x {errs[0]:.2e} w {errs[1]:.2e} pos {errs[2]:.2e}")
+    assert max(errs) <= TOL
+    # subsets of outputs give the same values
+    xb2, _, pb2 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, want=("x", "pos"))
+    _, _, pb3 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, want=("pos",))
+    _, wb4, _ = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, want=("w",))
+    assert torch.equal(xb2, xb) and torch.equal(pb2, pb) and torch.equal(pb3, pb) and torch.equal(wb4, wb)
+
+
+@pytest.mark.parametrize("name,n", [("cfg5", 256), ("cfg3", 128)])
+def test_double_backward_force_loss(name, n):
+    """L = <c, F> with F = -pos_bar: outputs d/dz_bar, d/dx, d/dW along pos_dot = -c."""
+    etpc = _etpc()
+    cfg = small_variant(name, n)
+    note(f"double backward {cfg.name} N={cfg.n_nodes}")
+    c = make_case(cfg)
+    fc = c.wl.force_c if c.wl.force_c is not None else np.random.default_rng(9).standard_normal(
+        (cfg.n_nodes, 3)).astype(np.float32)
+    pos_dot = torch.from_numpy(-fc).cuda()
+    gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot)
+    torch.cuda.synchronize()
+    rz, rx, rw, _ = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, c.wl.z_bar,
+                                         pos_dot=-fc.astype(np.float64))
+    errs = (rel_err(gz, rz), rel_err(gx, rx), rel_err(gw, rw))
+    note(f"double backward {cfg.name} rel err z_bar {errs[0]:.2e} x {errs[1]:.2e} w {errs[2]:.2e}")
+    assert max(errs) <= TOL_DBL
+
+
+@pytest.mark.parametrize("name,n", [("cfg5", 128), ("cfg3", 128)])
+def test_double_backward_all_cotangents(name, n):
+    etpc = _etpc()
+    cfg = small_variant(name, n)
+    note(f"double backward (all cotangents) {cfg.name}")
+    c = make_case(cfg)
+    rng = np.random.default_rng(11)
+    xd = rng.standard_normal(c.wl.x.shape).astype(np.float32)
+    wd = rng.standard_normal(c.wl.w.shape).astype(np.float32)
+    pd = rng.standard_normal(c.wl.pos.shape).astype(np.float32)
+    zb = rng.standard_normal((cfg.n_nodes, c.spec.plan.z_dim)).astype(np.float32)
+    T = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, T(zb), x_dot=T(xd), w_dot=T(wd),
+                                           pos_dot=T(pd))
+    torch.cuda.synchronize()
+    rz, rx, rw, _ = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, zb,
+                                         x_dot=xd, w_dot=wd, pos_dot=pd)
+    errs = (rel_err(gz, rz), rel_err(gx, rx), rel_err(gw, rw))
+    note(f"double backward all {cfg.name} rel err {errs}")
+    assert max(errs) <= TOL_DBL
+    # each cotangent alone
+    for kw, ref_kw in ((dict(x_dot=T(xd)), dict(x_dot=xd)), (dict(w_dot=T(wd)), dict(w_dot=wd))):
+        gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, T(zb), **kw)
+        rz, rx, rw, _ = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, zb, **ref_kw)
+        for got, ref in ((gz, rz), (gx, rx), (gw, rw)):
+            if np.abs(ref).max() == 0:
+                assert torch.count_nonzero(got) == 0
+            else:
+                assert rel_err(got, ref) <= TOL_DBL
+
+
+def test_determinism_and_chunked_workspace():
+    etpc = _etpc()
+    cfg = small_variant("cfg2", 256)
+    c = make_case(cfg)
+    note("determinism / chunking")
+    z1 = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w)
+    z2 = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w)
+    b1 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar)
+    b2 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar)
+    assert torch.equal(z1, z2) and all(torch.equal(a, b) for a, b in zip(b1, b2))
+    # a workspace a fifth of the full size forces receiver/sender chunks
+    full = etpc.etpc_workspace_size(c.plan, etpc.PASS_FWD, cfg.n_nodes, c.graph.n_edges)
+    ws = torch.empty(full // 5, dtype=torch.uint8, device="cuda")
+    z3 = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, ws=ws)
+    assert torch.equal(z3, z1)
+    fullb = etpc.etpc_workspace_size(c.plan, etpc.PASS_BWD, cfg.n_nodes, c.graph.n_edges)
+    wsb = torch.empty(fullb // 3, dtype=torch.uint8, device="cuda")
+    b3 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, ws=wsb)
+    assert torch.equal(b3[0], b1[0]) and torch.equal(b3[2], b1[2])
+    assert rel_err(b3[1], b1[1].cpu().numpy()) < 1e-6
+    with pytest.raises(etpc.EtpcError) as ei:
+        etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert ei.value.name == "WORKSPACE"
+
+
+def test_isolated_nodes_and_empty_graph():
+    etpc = _etpc()
+    cfg = dataclasses.replace(CONFIGS["cfg1"], n_nodes=64)
+    c = make_case(cfg)
+    note("empty graph")
+    empty = etpc.etpc_csr_build(cfg.n_nodes, torch.zeros(0, dtype=torch.int32, device="cuda"),
+                                torch.zeros(0, dtype=torch.int32, device="cuda"))
+    z = etpc.etpc_forward(c.plan, empty, c.x, c.pos, c.w)
+    zb = torch.randn(cfg.n_nodes, c.plan.info()["z_dim"], device="cuda")
+    xb, wb, pb = etpc.etpc_backward(c.plan, empty, c.x, c.pos, c.w, zb)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(z) == 0 and torch.count_nonzero(xb) == 0
+    assert torch.count_nonzero(wb) == 0 and torch.count_nonzero(pb) == 0
