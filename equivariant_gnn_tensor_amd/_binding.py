@@ -150,6 +150,7 @@ class Plan:
                  box: Optional[Sequence[float]] = None, out_per_path: bool = False,
                  instructions: Optional[Sequence[Tuple[int, int, int]]] = None):
         ins, outs = parse_irreps(irreps_in), parse_irreps(irreps_out)
+        self.irreps_in = ins
         self._in = (etpc_irrep * len(ins))(*[etpc_irrep(*t) for t in ins])
         self._out = (etpc_irrep * len(outs))(*[etpc_irrep(*t) for t in outs])
         n_instr = 0 if instructions is None else len(instructions)

@@ -30,12 +30,35 @@ FLAGS = [
 ]
 
 
+GENERATOR = "gen_cg.cpp"
+CG_INC = os.path.join(CSRC, "cg_tables.inc")
+
+
 def _sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    return [s for s in srcs if os.path.basename(s) != GENERATOR]
+
+
+def _gen_cg_tables(force: bool) -> None:
+    """Compile and run the coupling-table generator (host code) -> csrc/cg_tables.inc."""
+    gen_src = [os.path.join(CSRC, GENERATOR), os.path.join(CSRC, "plan.cpp")]
+    exe = os.path.join(BUILD, "gen_cg")
+    newest_src = max(os.path.getmtime(p) for p in gen_src + [os.path.join(CSRC, "plan.hpp")])
+    if not force and os.path.exists(CG_INC) and os.path.getmtime(CG_INC) >= newest_src:
+        return
+    cmd = [HIPCC, "-xhip", "-O2", "-std=c++17", "-I", os.path.join(ROOT, "include"), *gen_src, "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("building the coupling-table generator failed:\n" + r.stderr)
+    r = subprocess.run([exe, CG_INC + ".tmp"], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("coupling-table generator failed:\n" + r.stderr)
+    os.replace(CG_INC + ".tmp", CG_INC)
 
 
 def _headers():
-    return glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(ROOT, "include", "*.h"))
+    return (glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(CSRC, "*.inc"))
+            + glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _compile(src: str, force: bool, newest_header: float) -> str:
@@ -59,6 +82,7 @@ def _compile(src: str, force: bool, newest_header: float) -> str:
 def build(force: bool = False, jobs: int = 0, verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
+    _gen_cg_tables(force)
     srcs = _sources()
     hdr = max((os.path.getmtime(h) for h in _headers()), default=0.0)
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 4)))

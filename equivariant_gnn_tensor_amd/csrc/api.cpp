@@ -66,6 +66,8 @@ struct Derived {
   std::vector<std::vector<int32_t>> block_col0;
   int64_t max_state = 0;             // max_k (2l_k+1) * ncols_k
   int64_t max_wcat = 0;              // max_k C_in_k * ncols_k
+  int64_t max_zrow = 0;              // max_g o_g * C_out_g (channel GEMM output floats per receiver)
+  int64_t max_xrow = 0;              // max_k i_k * C_in_k (x_bar GEMM output floats per sender)
 };
 
 Derived derive(const etpc_plan_s* p) {
@@ -76,6 +78,7 @@ Derived derive(const etpc_plan_s* p) {
     for (int q : p->by_out[g]) D += static_cast<int64_t>(p->n_basis) * p->paths[q].c_in;
     d.group_d[g] = D;
     d.max_s = std::max<int64_t>(d.max_s, D * (2 * p->out[g].l + 1));
+    d.max_zrow = std::max<int64_t>(d.max_zrow, static_cast<int64_t>(2 * p->out[g].l + 1) * p->out[g].mul);
   }
   d.block_ncols.assign(p->in.size(), 0);
   d.block_col0.assign(p->in.size(), {});
@@ -88,21 +91,32 @@ Derived derive(const etpc_plan_s* p) {
     d.block_ncols[k] = n;
     d.max_state = std::max<int64_t>(d.max_state, n * (2 * p->in[k].l + 1));
     d.max_wcat = std::max<int64_t>(d.max_wcat, n * p->in[k].mul);
+    d.max_xrow = std::max<int64_t>(d.max_xrow, static_cast<int64_t>(2 * p->in[k].l + 1) * p->in[k].mul);
   }
   return d;
 }
 
 // ---------------------------------------------------------------- workspace layouts
+constexpr int kGemmSplits = 8;   // split-K partial sets kept for the long-K channel / x_bar GEMMs
+
 struct FwdLayout {
   float* S = nullptr;
+  float* part = nullptr;
+  int64_t part_cap = 0;
 };
 void fwd_layout(const etpc_plan_s* p, const Derived& d, int64_t chunk, Carver& c, FwdLayout& L) {
-  if (p->mode == ETPC_UVW) L.S = c.take<float>(static_cast<size_t>(chunk * d.max_s));
+  if (p->mode == ETPC_UVW) {
+    L.S = c.take<float>(static_cast<size_t>(chunk * d.max_s));
+    L.part_cap = kGemmSplits * chunk * d.max_zrow;
+    L.part = c.take<float>(static_cast<size_t>(L.part_cap));
+  }
 }
 
 struct BwdLayout {
   float *rbar = nullptr, *wcat = nullptr, *wt = nullptr, *wt2 = nullptr, *wpart = nullptr;
   float *xt = nullptr, *P = nullptr, *Pd = nullptr;
+  float* xpart = nullptr;
+  int64_t xpart_cap = 0;
 };
 // flags: pos = edge adjoint + Xt; p = plain P state; tan = tangent state; wbar = W_bar partials
 // (two sets when wbar2); wt2 = second transposed weight (for w_dot)
@@ -117,6 +131,10 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t
     if (pos) L.xt = c.take<float>(static_cast<size_t>(chunk * d.max_state));
     if (need_p) L.P = c.take<float>(static_cast<size_t>(chunk * d.max_state));
     if (tan) L.Pd = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+    if (xbar) {
+      L.xpart_cap = kGemmSplits * chunk * d.max_xrow;
+      L.xpart = c.take<float>(static_cast<size_t>(L.xpart_cap));
+    }
   } else {
     if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges));
     int64_t maxbc = 0;
@@ -163,6 +181,53 @@ int64_t pick_chunk(int64_t n, size_t ws_bytes, F bytes_of) {
 
 RowMap plain(int64_t ld) { return RowMap{ld, 0, 1}; }
 RowMap irmul(int32_t m, int64_t width, int64_t mul) { return RowMap{width, mul, m}; }
+
+int pick_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int64_t sp = (1024 + tiles - 1) / tiles;
+  sp = std::min<int64_t>(sp, (K + 255) / 256);
+  sp = std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
+  return static_cast<int>(sp);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool map4(const RowMap& m) { return m.s1 % 4 == 0 && (m.div == 1 || m.s2 % 4 == 0); }
+
+void set_vec4(GemmArgs& ga) {
+  ga.vec4 = (aligned16(ga.A) && map4(ga.amap) && aligned16(ga.B) && ga.ldb % 4 == 0) ? 1 : 0;
+}
+
+// Launch ga (final destination C / cmap / beta).  When K is long relative to the number
+// of output tiles, split K across workgroups into `part` (capacity part_cap floats) and
+// sum the partial tiles in a fixed order into C.
+etpc_status gemm_auto(GemmArgs ga, float* part, int64_t part_cap, int max_splits, int kind, hipStream_t s) {
+  set_vec4(ga);
+  int sp = std::min(pick_splits(ga.M, ga.N, ga.K), max_splits);
+  const int64_t mn = static_cast<int64_t>(ga.M) * ga.N;
+  if (part == nullptr || mn <= 0) sp = 1;
+  while (sp > 1 && static_cast<int64_t>(sp) * mn > part_cap) --sp;
+  if (sp <= 1) {
+    ga.k_split = ga.K;
+    ga.c_split_stride = 0;
+    ETPC_LAUNCH(kind, launch_gemm(ga, 1, s));
+    return ETPC_OK;
+  }
+  int64_t ks = (ga.K + sp - 1) / sp;
+  ks = (ks + 31) / 32 * 32;
+  sp = static_cast<int>((ga.K + ks - 1) / ks);
+  float* C = ga.C;
+  const RowMap cmap = ga.cmap;
+  const bool beta = ga.beta != 0;
+  ga.C = part;
+  ga.cmap = plain(ga.N);
+  ga.beta = 0;
+  ga.k_split = static_cast<int32_t>(ks);
+  ga.c_split_stride = mn;
+  ETPC_LAUNCH(kind, launch_gemm(ga, sp, s));
+  ETPC_LAUNCH(ETPC_KIND_AUX, launch_splitk_reduce(part, sp, ga.M, ga.N, C, cmap, beta, s));
+  return ETPC_OK;
+}
 
 // ---------------------------------------------------------------- validation
 etpc_status check_common(const etpc_plan_s* p, const etpc_graph* g) {
@@ -261,9 +326,8 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       ga.M = nrecv * no;
       ga.N = c_out;
       ga.K = static_cast<int32_t>(D);
-      ga.k_split = static_cast<int32_t>(D);
-      ga.c_split_stride = 0;
-      ETPC_LAUNCH(ETPC_KIND_CHANNEL_GEMM, launch_gemm(ga, 1, s));
+      etpc_status st = gemm_auto(ga, L.part, L.part_cap, kGemmSplits, ETPC_KIND_CHANNEL_GEMM, s);
+      if (st != ETPC_OK) return st;
     }
   }
   return ETPC_OK;
@@ -330,14 +394,6 @@ void wprep_args(const etpc_plan_s* p, const Derived& d, int k, const float* w, f
   }
 }
 
-int pick_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
-  int64_t sp = (1024 + tiles - 1) / tiles;
-  sp = std::min<int64_t>(sp, (K + 255) / 256);
-  sp = std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
-  return static_cast<int>(sp);
-}
-
 // W_out block k (+)= A^T S_state (split-K over the chunk's rows), partials at wpart + slot
 hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float* xa, int64_t j0, int nsend,
                      const float* state, float* wpart, int* splits_out, hipStream_t s) {
@@ -347,7 +403,7 @@ hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float*
   const int64_t K = static_cast<int64_t>(nsend) * ni;
   const int sp = pick_splits(c_in, ncols, K);
   int64_t ks = (K + sp - 1) / sp;
-  ks = (ks + 15) / 16 * 16;
+  ks = (ks + 31) / 32 * 32;
   GemmArgs ga{};
   ga.A = xa + j0 * p->x_dim + p->xoff[k];
   ga.amap = irmul(ni, p->x_dim, c_in);
@@ -362,12 +418,13 @@ hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float*
   ga.K = static_cast<int32_t>(K);
   ga.k_split = static_cast<int32_t>(ks);
   ga.c_split_stride = static_cast<int64_t>(c_in) * ncols;
+  set_vec4(ga);
   *splits_out = sp;
   return launch_gemm(ga, sp, s);
 }
 
-hipError_t xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float* state, const float* wt, float* xo,
-                     int64_t j0, int nsend, bool beta, hipStream_t s) {
+etpc_status xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float* state, const float* wt, float* xo,
+                      int64_t j0, int nsend, bool beta, const BwdLayout& L, hipStream_t s) {
   const int ni = 2 * p->in[k].l + 1;
   const int64_t ncols = d.block_ncols[k];
   const int c_in = p->in[k].mul;
@@ -383,9 +440,7 @@ hipError_t xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float*
   ga.M = nsend * ni;
   ga.N = c_in;
   ga.K = static_cast<int32_t>(ncols);
-  ga.k_split = static_cast<int32_t>(ncols);
-  ga.c_split_stride = 0;
-  return launch_gemm(ga, 1, s);
+  return gemm_auto(ga, L.xpart, L.xpart_cap, kGemmSplits, ETPC_KIND_NODE_GEMM, s);
 }
 
 etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* pos,
@@ -429,6 +484,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         ga.N = static_cast<int32_t>(ncols);
         ga.K = c_in;
         ga.k_split = c_in;
+        set_vec4(ga);
         ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, launch_gemm(ga, 1, s));
       }
       for (size_t t = 0; t < paths.size(); ++t) {
@@ -461,9 +517,14 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         if (want_pos) rbar_started = true;
       }
       if (R.x_out) {
-        if (main_state) ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, xbar_gemm(p, d, static_cast<int>(k), Pmain, L.wt, R.x_out, j0, nsend, false, s));
-        if (R.tangent && R.w2)
-          ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, xbar_gemm(p, d, static_cast<int>(k), L.P, L.wt2, R.x_out, j0, nsend, true, s));
+        if (main_state) {
+          etpc_status st = xbar_gemm(p, d, static_cast<int>(k), Pmain, L.wt, R.x_out, j0, nsend, false, L, s);
+          if (st != ETPC_OK) return st;
+        }
+        if (R.tangent && R.w2) {
+          etpc_status st = xbar_gemm(p, d, static_cast<int>(k), L.P, L.wt2, R.x_out, j0, nsend, true, L, s);
+          if (st != ETPC_OK) return st;
+        }
       }
       if (R.w_out) {
         int sp1 = 0, sp2 = 0;

@@ -22,102 +22,115 @@
 #pragma once
 #include "geom.hpp"
 #include "kernels.hpp"
+#include "wave.hpp"
+#include "cg_tables.inc"
+#include "triples.hpp"
 
 namespace etpc {
 namespace bwd_detail {
 
 constexpr int kMaxTiles = 4;
 
-// LDS edge record offsets
-template <int NB, int NI, int NO, bool POS, bool TAN>
-struct BwdLds {
-  static constexpr int CY = NI * NO;
+// Per-edge partial of a lane-distributed sum: for slots of >= 16 lanes every lane gets its
+// 16-lane row sum (the rows of a slot are combined later through LDS); narrower slots are
+// summed completely.
+__device__ inline float edge_partial_sum(float v, int cp) {
+  return cp >= 16 ? row_sum16(v) : small_slot_sum(v, cp);
+}
+
+// rows of 16 lanes per slot that hold partial sums (1 for slots narrower than 16 lanes)
+__device__ inline int rows_per_slot(int cp) { return cp >= 16 ? cp / 16 : 1; }
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// Compact per-edge record for the sender traversals (LDS, one per edge of a chunk):
+// phi[NB], phi'[NB] (positions), dphi[NB] (tangent), Y[NS], dY/dr[3][NS] (positions),
+// dY[NS] along pos_dot (tangent), u[3] (positions).  The coupling tensor is not stored
+// per edge: its compile-time sparse form is applied per lane (CgTab).
+template <int NB, int NS, bool POS, bool TAN>
+struct BwdRec {
   static constexpr int kPhi = 0;
-  static constexpr int kDphi = NB;                       // radial derivative (POS)
-  static constexpr int kPhiDot = 2 * NB;                 // tangent
-  static constexpr int kCy = 3 * NB;
-  static constexpr int kCdy = kCy + CY;                  // 3 x CY (POS)
-  static constexpr int kCyDot = kCdy + 3 * CY;           // tangent
-  static constexpr int kU = kCyDot + CY;                 // unit vector (POS)
-  static constexpr int kStride = kU + 3 + 1;
+  static constexpr int kDphi = NB;
+  static constexpr int kPhiDot = kDphi + (POS ? NB : 0);
+  static constexpr int kY = kPhiDot + (TAN ? NB : 0);
+  static constexpr int kDY = kY + NS;
+  static constexpr int kYDot = kDY + (POS ? 3 * NS : 0);
+  static constexpr int kU = kYDot + (TAN ? NS : 0);
+  static constexpr int kStride = kU + (POS ? 3 : 0) + 1;
 };
 
-template <int NB, int NI, int NO, bool POS, bool TAN>
-__device__ inline void bwd_fill_edge(const GeomParams& g, const CGTable& cg, int ls, const float* __restrict__ pos,
-                                     const float* __restrict__ pos_dot, int j, int i, float* __restrict__ e) {
-  using L = BwdLds<NB, NI, NO, POS, TAN>;
+template <int LS, int NB, bool POS, bool TAN, bool NEED_D>
+__device__ inline void bwd_fill_rec(const GeomParams& g, const float* __restrict__ pos,
+                                    const float* __restrict__ pos_dot, int j, int i, float* __restrict__ e) {
+  constexpr int NS = 2 * LS + 1;
+  using R = BwdRec<NB, NS, POS, TAN>;
   float rx, ry, rz;
   edge_vector(g, pos, j, i, rx, ry, rz);
   const float r = sqrtf(rx * rx + ry * ry + rz * rz);
   const float ir = 1.f / r;
   const float ux = rx * ir, uy = ry * ir, uz = rz * ir;
-  constexpr bool NEED_D = POS || TAN;
   float phi[NB], dphi[NB];
   radial_eval<NB>(g, r, phi, NEED_D ? dphi : nullptr);
   float y[7];
-  sh_eval(ls, ux, uy, uz, y);
-  const int nsh = 2 * ls + 1;
+  sh_eval(LS, ux, uy, uz, y);
   float gy[7][3];
-  if constexpr (NEED_D) sh_grad_r(ls, ux, uy, uz, ir, y, gy);
+  if constexpr (POS || TAN) sh_grad_r(LS, ux, uy, uz, ir, y, gy);
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
-    e[L::kPhi + q] = phi[q];
-    if constexpr (POS) e[L::kDphi + q] = dphi[q];
+    e[R::kPhi + q] = phi[q];
+    if constexpr (POS) e[R::kDphi + q] = dphi[q];
   }
-  float ydot[7];
+#pragma unroll
+  for (int m = 0; m < NS; ++m) {
+    e[R::kY + m] = y[m];
+    if constexpr (POS) {
+      e[R::kDY + m] = gy[m][0];
+      e[R::kDY + NS + m] = gy[m][1];
+      e[R::kDY + 2 * NS + m] = gy[m][2];
+    }
+  }
   if constexpr (TAN) {
     const float dx = pos_dot[3 * j + 0] - pos_dot[3 * i + 0];
     const float dy = pos_dot[3 * j + 1] - pos_dot[3 * i + 1];
     const float dz = pos_dot[3 * j + 2] - pos_dot[3 * i + 2];
     const float rdot = ux * dx + uy * dy + uz * dz;
 #pragma unroll
-    for (int q = 0; q < NB; ++q) e[L::kPhiDot + q] = dphi[q] * rdot;
-    for (int m = 0; m < nsh; ++m) ydot[m] = gy[m][0] * dx + gy[m][1] * dy + gy[m][2] * dz;
+    for (int q = 0; q < NB; ++q) e[R::kPhiDot + q] = dphi[q] * rdot;
+#pragma unroll
+    for (int m = 0; m < NS; ++m) e[R::kYDot + m] = gy[m][0] * dx + gy[m][1] * dy + gy[m][2] * dz;
   }
   if constexpr (POS) {
-    e[L::kU + 0] = ux;
-    e[L::kU + 1] = uy;
-    e[L::kU + 2] = uz;
+    e[R::kU + 0] = ux;
+    e[R::kU + 1] = uy;
+    e[R::kU + 2] = uz;
   }
+}
+
+// V[m_in][m_sh] = sum_m_out c[m_in][m_sh][m_out] zb[m_out] with the compile-time sparse table
+template <int LI, int LS, int LO>
+__device__ inline void cg_contract_out(const float* __restrict__ zb, float (*__restrict__ V)[2 * LS + 1]) {
+  using C = CgTab<LI, LS, LO>;
 #pragma unroll
-  for (int a = 0; a < NI; ++a)
+  for (int a = 0; a < 2 * LI + 1; ++a)
 #pragma unroll
-    for (int m = 0; m < NO; ++m) {
-      float s = 0.f, s0 = 0.f, s1 = 0.f, s2 = 0.f, sd = 0.f;
-      for (int b = 0; b < nsh; ++b) {
-        const float c = cg.c[(a * 7 + b) * NO + m];
-        s += c * y[b];
-        if constexpr (POS) {
-          s0 += c * gy[b][0];
-          s1 += c * gy[b][1];
-          s2 += c * gy[b][2];
-        }
-        if constexpr (TAN) sd += c * ydot[b];
-      }
-      e[L::kCy + a * NO + m] = s;
-      if constexpr (POS) {
-        e[L::kCdy + a * NO + m] = s0;
-        e[L::kCdy + L::CY + a * NO + m] = s1;
-        e[L::kCdy + 2 * L::CY + a * NO + m] = s2;
-      }
-      if constexpr (TAN) e[L::kCyDot + a * NO + m] = sd;
+    for (int b = 0; b < 2 * LS + 1; ++b) {
+      float s = 0.f;
+#pragma unroll
+      for (int m = 0; m < 2 * LO + 1; ++m)
+        if (C::v[a][b][m] != 0.f) s += C::v[a][b][m] * zb[m];
+      V[a][b] = s;
     }
 }
 
-// sum over the cp lanes of one slot (cp a power of two); every lane of the slot gets the sum
-__device__ inline float slot_sum(float v, int cp) {
-  for (int off = 1; off < cp; off <<= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-template <int LI, int LO, int NBQ, bool NEED_P, bool POS, bool TAN>
+// Sender traversal for one uvw path (compile-time l_in, l_sh, l_out).
+template <int LI, int LS, int LO, int NBQ, bool NEED_P, bool POS, bool TAN>
 __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
-  constexpr int NI = 2 * LI + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
-  using L = BwdLds<NB, NI, NO, POS, TAN>;
-  __shared__ float s_edge[64 * L::kStride];
+  constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
+  using R = BwdRec<NB, NS, POS, TAN>;
+  __shared__ float s_edge[64 * R::kStride];
   __shared__ int s_i[64];
   __shared__ int s_sl[64];
-  __shared__ float s_rb[kMaxTiles][64][3];
+  extern __shared__ float s_dyn[];   // [nwaves][64][rows][3] edge-adjoint partials
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int j = a.send0 + blockIdx.x;
   const int cp = a.cp;
@@ -125,6 +138,10 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   const int slot = lane / cp;
   const int w = wave * cp + (lane - slot * cp);
   const bool wvalid = w < a.c_out;
+  const int rows = rows_per_slot(cp);
+  const int row_in_slot = (lane - slot * cp) >> 4;
+  const bool row_leader = cp >= 16 ? (lane & 15) == 0 : lane == slot * cp;
+  const int q4 = lane & 3;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * NI;
   float xt[NB][NI];
   if constexpr (POS) {
@@ -136,89 +153,102 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
                         ? a.xt[(row0 + mi) * a.ld_state + a.state_col0 + static_cast<int64_t>(q) * a.c_out + w]
                         : 0.f;
   }
-  float P[NB][NI], Pd[NB][NI];
+  f4v P[NI][NBQ], Pd[NI][NBQ];
 #pragma unroll
-  for (int q = 0; q < NB; ++q)
+  for (int mi = 0; mi < NI; ++mi)
 #pragma unroll
-    for (int mi = 0; mi < NI; ++mi) {
-      P[q][mi] = 0.f;
-      Pd[q][mi] = 0.f;
+    for (int qq = 0; qq < NBQ; ++qq) {
+      P[mi][qq] = f4v{0.f, 0.f, 0.f, 0.f};
+      Pd[mi][qq] = f4v{0.f, 0.f, 0.f, 0.f};
     }
   const int k0 = a.s_rowptr[j], k1 = a.s_rowptr[j + 1];
   for (int base = k0; base < k1; base += kWave) {
     const int ne = min(kWave, k1 - base);
     if (tid < ne) {
       const int i = a.s_col[base + tid];
-      bwd_fill_edge<NB, NI, NO, POS, TAN>(a.g, a.cg, a.ls, a.pos, a.pos_dot, j, i, s_edge + tid * L::kStride);
+      bwd_fill_rec<LS, NB, POS, TAN, POS || TAN>(a.g, a.pos, a.pos_dot, j, i, s_edge + tid * R::kStride);
       s_i[tid] = i;
       s_sl[tid] = a.s_slot[base + tid];
     }
     __syncthreads();
     const int trips = (ne + nslots - 1) / nslots;
+    float zn[NO];
+    {
+      const bool v0 = slot < ne && wvalid;
+      const float* zr = a.z_bar + static_cast<int64_t>(v0 ? s_i[slot] : 0) * a.z_dim + a.zoff + w;
+#pragma unroll
+      for (int mo = 0; mo < NO; ++mo) zn[mo] = v0 ? zr[mo * a.c_out] : 0.f;
+    }
     for (int it = 0; it < trips; ++it) {
       const int t = it * nslots + slot;
       const bool tvalid = t < ne;
-      const float* e = s_edge + (tvalid ? t : 0) * L::kStride;
+      const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
       float zb[NO];
-      const float* zr = a.z_bar + static_cast<int64_t>(tvalid ? s_i[t] : 0) * a.z_dim + a.zoff + w;
 #pragma unroll
-      for (int mo = 0; mo < NO; ++mo) zb[mo] = (tvalid && wvalid) ? zr[mo * a.c_out] : 0.f;
+      for (int mo = 0; mo < NO; ++mo) zb[mo] = zn[mo];
+      {
+        const int tn = t + nslots;
+        const bool vn = tn < ne && wvalid;
+        const float* zr = a.z_bar + static_cast<int64_t>(vn ? s_i[tn] : 0) * a.z_dim + a.zoff + w;
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo) zn[mo] = vn ? zr[mo * a.c_out] : 0.f;
+      }
+      float V[NI][NS];
+      cg_contract_out<LI, LS, LO>(zb, V);
       float Q[NI], Qd[NI];
 #pragma unroll
       for (int mi = 0; mi < NI; ++mi) {
         float s = 0.f, sd = 0.f;
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) {
-          s += e[L::kCy + mi * NO + mo] * zb[mo];
-          if constexpr (TAN) sd += e[L::kCyDot + mi * NO + mo] * zb[mo];
+        for (int my = 0; my < NS; ++my) {
+          s += e[R::kY + my] * V[mi][my];
+          if constexpr (TAN) sd += e[R::kYDot + my] * V[mi][my];
         }
         Q[mi] = s;
         Qd[mi] = sd;
       }
 #pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        const float ph = e[L::kPhi + q];
+      for (int qq = 0; qq < NBQ; ++qq) {
+        const float ph = e[R::kPhi + 4 * qq + q4];
         if constexpr (NEED_P) {
 #pragma unroll
-          for (int mi = 0; mi < NI; ++mi) P[q][mi] += ph * Q[mi];
+          for (int mi = 0; mi < NI; ++mi)
+            P[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, Q[mi], P[mi][qq], 0, 0, 0);
         }
         if constexpr (TAN) {
-          const float phd = e[L::kPhiDot + q];
+          const float phd = e[R::kPhiDot + 4 * qq + q4];
 #pragma unroll
-          for (int mi = 0; mi < NI; ++mi) Pd[q][mi] += phd * Q[mi] + ph * Qd[mi];
+          for (int mi = 0; mi < NI; ++mi) {
+            Pd[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(phd, Q[mi], Pd[mi][qq], 0, 0, 0);
+            Pd[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, Qd[mi], Pd[mi][qq], 0, 0, 0);
+          }
         }
       }
       if constexpr (POS) {
         float srad = 0.f;
-        float T[NI];
+        float rb[3] = {0.f, 0.f, 0.f};
 #pragma unroll
         for (int mi = 0; mi < NI; ++mi) {
-          float gq = 0.f, tq = 0.f;
+          float tq = 0.f, gq = 0.f;
 #pragma unroll
           for (int q = 0; q < NB; ++q) {
-            gq += e[L::kDphi + q] * xt[q][mi];
-            tq += e[L::kPhi + q] * xt[q][mi];
+            tq += e[R::kPhi + q] * xt[q][mi];
+            gq += e[R::kDphi + q] * xt[q][mi];
           }
           srad += gq * Q[mi];
-          T[mi] = tq;
-        }
-        float rb[3];
 #pragma unroll
-        for (int d = 0; d < 3; ++d) {
-          float s = 0.f;
-#pragma unroll
-          for (int mi = 0; mi < NI; ++mi) {
+          for (int d = 0; d < 3; ++d) {
             float zc = 0.f;
 #pragma unroll
-            for (int mo = 0; mo < NO; ++mo) zc += e[L::kCdy + d * L::CY + mi * NO + mo] * zb[mo];
-            s += T[mi] * zc;
+            for (int my = 0; my < NS; ++my) zc += e[R::kDY + d * NS + my] * V[mi][my];
+            rb[d] += tq * zc;
           }
-          rb[d] = slot_sum(srad * e[L::kU + d] + s, cp);
         }
-        if (tvalid && lane == slot * cp) {
-          s_rb[wave][t][0] = rb[0];
-          s_rb[wave][t][1] = rb[1];
-          s_rb[wave][t][2] = rb[2];
+        float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          const float v = edge_partial_sum(srad * e[R::kU + d] + rb[d], cp);
+          if (tvalid && row_leader) sr[d] = v;
         }
       }
     }
@@ -226,11 +256,13 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
     if constexpr (POS) {
       if (tid < ne) {
         float r0 = 0.f, r1 = 0.f, r2 = 0.f;
-        for (int wv = 0; wv < nwaves; ++wv) {
-          r0 += s_rb[wv][tid][0];
-          r1 += s_rb[wv][tid][1];
-          r2 += s_rb[wv][tid][2];
-        }
+        for (int w2 = 0; w2 < nwaves; ++w2)
+          for (int r = 0; r < rows; ++r) {
+            const float* src = s_dyn + ((w2 * 64 + tid) * rows + r) * 3;
+            r0 += src[0];
+            r1 += src[1];
+            r2 += src[2];
+          }
         float* dst = a.rbar + 3 * static_cast<int64_t>(s_sl[tid]);
         if (a.rbar_accumulate) {
           dst[0] += r0;
@@ -248,40 +280,48 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   // combine the edge slots of the wave (different edges of the same sender)
   for (int off = cp; off < kWave; off <<= 1)
 #pragma unroll
-    for (int q = 0; q < NB; ++q)
+    for (int mi = 0; mi < NI; ++mi)
 #pragma unroll
-      for (int mi = 0; mi < NI; ++mi) {
-        if constexpr (NEED_P) P[q][mi] += __shfl_xor(P[q][mi], off);
-        if constexpr (TAN) Pd[q][mi] += __shfl_xor(Pd[q][mi], off);
-      }
+      for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (NEED_P) P[mi][qq][r] += __shfl_xor(P[mi][qq][r], off);
+          if constexpr (TAN) Pd[mi][qq][r] += __shfl_xor(Pd[mi][qq][r], off);
+        }
   if (slot == 0 && wvalid) {
 #pragma unroll
-    for (int q = 0; q < NB; ++q)
-      if (q < a.g.nb)
+    for (int qq = 0; qq < NBQ; ++qq)
 #pragma unroll
-        for (int mi = 0; mi < NI; ++mi) {
-          const int64_t o = (row0 + mi) * a.ld_state + a.state_col0 + static_cast<int64_t>(q) * a.c_out + w;
-          if constexpr (NEED_P) a.P[o] = P[q][mi];
-          if constexpr (TAN) a.Pdot[o] = Pd[q][mi];
-        }
+      for (int r = 0; r < 4; ++r)
+        if (4 * qq + r < a.g.nb)
+#pragma unroll
+          for (int mi = 0; mi < NI; ++mi) {
+            const int64_t o =
+                (row0 + mi) * a.ld_state + a.state_col0 + static_cast<int64_t>(4 * qq + r) * a.c_out + w;
+            if constexpr (NEED_P) a.P[o] = P[mi][qq][r];
+            if constexpr (TAN) a.Pdot[o] = Pd[mi][qq][r];
+          }
   }
 }
 
-template <int LI, int LO, int NBQ, bool TAN>
+template <int LI, int LS, int LO, int NBQ, bool TAN>
 __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
-  constexpr int NI = 2 * LI + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
+  constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
   constexpr bool POS = !TAN;   // position adjoint only in the first-order pass
-  using L = BwdLds<NB, NI, NO, true, TAN>;
-  __shared__ float s_edge[64 * L::kStride];
+  using R = BwdRec<NB, NS, true, TAN>;
+  __shared__ float s_edge[64 * R::kStride];
   __shared__ int s_i[64];
   __shared__ int s_sl[64];
-  __shared__ float s_rb[kMaxTiles][64][3];
+  extern __shared__ float s_dyn[];   // [nwaves][64][rows][3]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int cp = a.cp;
   const int nslots = kWave / cp;
   const int slot = lane / cp;
   const int u = wave * cp + (lane - slot * cp);
   const bool uvalid = u < a.c;
+  const int rows = rows_per_slot(cp);
+  const int row_in_slot = (lane - slot * cp) >> 4;
+  const bool row_leader = cp >= 16 ? (lane & 15) == 0 : lane == slot * cp;
   const bool want_pos = POS && a.rbar != nullptr;
   float wv[NB], wbar[NB];
 #pragma unroll
@@ -302,29 +342,44 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
       const int ne = min(kWave, k1 - base);
       if (tid < ne) {
         const int i = a.s_col[base + tid];
-        bwd_fill_edge<NB, NI, NO, true, TAN>(a.g, a.cg, a.ls, a.pos, a.pos_dot, j, i, s_edge + tid * L::kStride);
+        bwd_fill_rec<LS, NB, true, TAN, true>(a.g, a.pos, a.pos_dot, j, i, s_edge + tid * R::kStride);
         s_i[tid] = i;
         s_sl[tid] = a.s_slot[base + tid];
       }
       __syncthreads();
       const int trips = (ne + nslots - 1) / nslots;
+      float zn[NO];
+      {
+        const bool v0 = slot < ne && uvalid;
+        const float* zr = a.z_bar + static_cast<int64_t>(v0 ? s_i[slot] : 0) * a.z_dim + a.zoff + u;
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo) zn[mo] = v0 ? zr[mo * a.c] : 0.f;
+      }
       for (int it = 0; it < trips; ++it) {
         const int t = it * nslots + slot;
         const bool tvalid = t < ne;
-        const float* e = s_edge + (tvalid ? t : 0) * L::kStride;
+        const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
         float zb[NO];
-        const float* zr = a.z_bar + static_cast<int64_t>(tvalid ? s_i[t] : 0) * a.z_dim + a.zoff + u;
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) zb[mo] = (tvalid && uvalid) ? zr[mo * a.c] : 0.f;
+        for (int mo = 0; mo < NO; ++mo) zb[mo] = zn[mo];
+        {
+          const int tn = t + nslots;
+          const bool vn = tn < ne && uvalid;
+          const float* zr = a.z_bar + static_cast<int64_t>(vn ? s_i[tn] : 0) * a.z_dim + a.zoff + u;
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo) zn[mo] = vn ? zr[mo * a.c] : 0.f;
+        }
+        float V[NI][NS];
+        cg_contract_out<LI, LS, LO>(zb, V);
         float Q[NI], Qd[NI];
         float h = 0.f, hd = 0.f;
 #pragma unroll
         for (int mi = 0; mi < NI; ++mi) {
           float s = 0.f, sd = 0.f;
 #pragma unroll
-          for (int mo = 0; mo < NO; ++mo) {
-            s += e[L::kCy + mi * NO + mo] * zb[mo];
-            if constexpr (TAN) sd += e[L::kCyDot + mi * NO + mo] * zb[mo];
+          for (int my = 0; my < NS; ++my) {
+            s += e[R::kY + my] * V[mi][my];
+            if constexpr (TAN) sd += e[R::kYDot + my] * V[mi][my];
           }
           Q[mi] = s;
           Qd[mi] = sd;
@@ -334,34 +389,32 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
         float we = 0.f, wed = 0.f, wdr = 0.f;
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
-          we += e[L::kPhi + q] * wv[q];
-          if constexpr (TAN) wed += e[L::kPhiDot + q] * wv[q];
-          wdr += e[L::kDphi + q] * wv[q];
+          we += e[R::kPhi + q] * wv[q];
+          if constexpr (TAN) wed += e[R::kPhiDot + q] * wv[q];
+          wdr += e[R::kDphi + q] * wv[q];
         }
 #pragma unroll
         for (int mi = 0; mi < NI; ++mi) xb[mi] += TAN ? (wed * Q[mi] + we * Qd[mi]) : we * Q[mi];
 #pragma unroll
         for (int q = 0; q < NB; ++q)
-          wbar[q] += TAN ? (e[L::kPhiDot + q] * h + e[L::kPhi + q] * hd) : e[L::kPhi + q] * h;
+          wbar[q] += TAN ? (e[R::kPhiDot + q] * h + e[R::kPhi + q] * hd) : e[R::kPhi + q] * h;
         if (want_pos) {
           const float srad = wdr * h;
-          float rb[3];
+          float rb[3] = {0.f, 0.f, 0.f};
 #pragma unroll
-          for (int d = 0; d < 3; ++d) {
-            float s = 0.f;
+          for (int mi = 0; mi < NI; ++mi)
 #pragma unroll
-            for (int mi = 0; mi < NI; ++mi) {
+            for (int d = 0; d < 3; ++d) {
               float zc = 0.f;
 #pragma unroll
-              for (int mo = 0; mo < NO; ++mo) zc += e[L::kCdy + d * L::CY + mi * NO + mo] * zb[mo];
-              s += xj[mi] * zc;
+              for (int my = 0; my < NS; ++my) zc += e[R::kDY + d * NS + my] * V[mi][my];
+              rb[d] += xj[mi] * zc;
             }
-            rb[d] = slot_sum(srad * e[L::kU + d] + we * s, cp);
-          }
-          if (tvalid && lane == slot * cp) {
-            s_rb[wave][t][0] = rb[0];
-            s_rb[wave][t][1] = rb[1];
-            s_rb[wave][t][2] = rb[2];
+          float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+#pragma unroll
+          for (int d = 0; d < 3; ++d) {
+            const float v = edge_partial_sum(srad * e[R::kU + d] + we * rb[d], cp);
+            if (tvalid && row_leader) sr[d] = v;
           }
         }
       }
@@ -369,11 +422,13 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
       if (want_pos) {
         if (tid < ne) {
           float r0 = 0.f, r1 = 0.f, r2 = 0.f;
-          for (int w2 = 0; w2 < nwaves; ++w2) {
-            r0 += s_rb[w2][tid][0];
-            r1 += s_rb[w2][tid][1];
-            r2 += s_rb[w2][tid][2];
-          }
+          for (int w2 = 0; w2 < nwaves; ++w2)
+            for (int r = 0; r < rows; ++r) {
+              const float* src = s_dyn + ((w2 * 64 + tid) * rows + r) * 3;
+              r0 += src[0];
+              r1 += src[1];
+              r2 += src[2];
+            }
           float* dst = a.rbar + 3 * static_cast<int64_t>(s_sl[tid]);
           if (a.rbar_accumulate) {
             dst[0] += r0;
@@ -412,61 +467,41 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
   }
 }
 
-template <int LI, int LO, bool NEED_P, bool POS, bool TAN>
+template <int LI, int LS, int LO, bool NEED_P, bool POS, bool TAN>
 hipError_t bwd_uvw_nb(const BwdUvwArgs& a, int nsend, int ntiles, hipStream_t s) {
   dim3 grid(nsend), block(64 * ntiles);
-  switch ((a.g.nb + 3) / 4) {
-    case 1: hipLaunchKernelGGL((bwd_uvw_kernel<LI, LO, 1, NEED_P, POS, TAN>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((bwd_uvw_kernel<LI, LO, 2, NEED_P, POS, TAN>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((bwd_uvw_kernel<LI, LO, 3, NEED_P, POS, TAN>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((bwd_uvw_kernel<LI, LO, 4, NEED_P, POS, TAN>), grid, block, 0, s, a); break;
-  }
+  const int rows = a.cp >= 16 ? a.cp / 16 : 1;
+  const size_t dyn = POS ? sizeof(float) * 64 * 3 * rows * ntiles : 0;
+  if (a.g.nb <= 8)
+    hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 2, NEED_P, POS, TAN>), grid, block, dyn, s, a);
+  else
+    hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 4, NEED_P, POS, TAN>), grid, block, dyn, s, a);
   return hipGetLastError();
 }
 
-template <int LI, int LO, bool TAN>
+template <int LI, int LS, int LO, bool TAN>
 hipError_t bwd_uvu_nb(const BwdUvuArgs& a, int nblocks, int ntiles, hipStream_t s) {
   dim3 grid(nblocks), block(64 * ntiles);
-  switch ((a.g.nb + 3) / 4) {
-    case 1: hipLaunchKernelGGL((bwd_uvu_kernel<LI, LO, 1, TAN>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((bwd_uvu_kernel<LI, LO, 2, TAN>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((bwd_uvu_kernel<LI, LO, 3, TAN>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((bwd_uvu_kernel<LI, LO, 4, TAN>), grid, block, 0, s, a); break;
-  }
+  const int rows = a.cp >= 16 ? a.cp / 16 : 1;
+  const size_t dyn = sizeof(float) * 64 * 3 * rows * ntiles;
+  if (a.g.nb <= 8)
+    hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 2, TAN>), grid, block, dyn, s, a);
+  else
+    hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 4, TAN>), grid, block, dyn, s, a);
   return hipGetLastError();
 }
-
-#define ETPC_LL_DISPATCH(CALL)                 \
-  switch (li * 4 + lo) {                       \
-    case 0: return CALL(0, 0);                 \
-    case 1: return CALL(0, 1);                 \
-    case 2: return CALL(0, 2);                 \
-    case 3: return CALL(0, 3);                 \
-    case 4: return CALL(1, 0);                 \
-    case 5: return CALL(1, 1);                 \
-    case 6: return CALL(1, 2);                 \
-    case 7: return CALL(1, 3);                 \
-    case 8: return CALL(2, 0);                 \
-    case 9: return CALL(2, 1);                 \
-    case 10: return CALL(2, 2);                \
-    case 11: return CALL(2, 3);                \
-    case 12: return CALL(3, 0);                \
-    case 13: return CALL(3, 1);                \
-    case 14: return CALL(3, 2);                \
-    default: return CALL(3, 3);                \
-  }
 
 template <bool NEED_P, bool POS, bool TAN>
 hipError_t launch_bwd_uvw_t(const BwdUvwArgs& a, int li, int lo, int nsend, int ntiles, hipStream_t s) {
-#define ETPC_CALL(LI, LO) bwd_uvw_nb<LI, LO, NEED_P, POS, TAN>(a, nsend, ntiles, s)
-  ETPC_LL_DISPATCH(ETPC_CALL)
+#define ETPC_CALL(LI, LS, LO) bwd_uvw_nb<LI, LS, LO, NEED_P, POS, TAN>(a, nsend, ntiles, s)
+  ETPC_TRIPLE_DISPATCH(li, a.ls, lo, ETPC_CALL)
 #undef ETPC_CALL
 }
 
 template <bool TAN>
 hipError_t launch_bwd_uvu_t(const BwdUvuArgs& a, int li, int lo, int nblocks, int ntiles, hipStream_t s) {
-#define ETPC_CALL(LI, LO) bwd_uvu_nb<LI, LO, TAN>(a, nblocks, ntiles, s)
-  ETPC_LL_DISPATCH(ETPC_CALL)
+#define ETPC_CALL(LI, LS, LO) bwd_uvu_nb<LI, LS, LO, TAN>(a, nblocks, ntiles, s)
+  ETPC_TRIPLE_DISPATCH(li, a.ls, lo, ETPC_CALL)
 #undef ETPC_CALL
 }
 

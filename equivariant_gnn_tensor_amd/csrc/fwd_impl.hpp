@@ -75,8 +75,14 @@ __device__ inline void fill_edge(const GeomParams& g, const CGTable& cg, int ls,
     }
 }
 
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// The radial outer product S[q][m_out] += phi_q C[m_out] runs on the matrix cores:
+// v_mfma_f32_4x4x1f32 with A = phi[4 qq + (lane & 3)] (per-lane LDS read) and
+// B = C[m_out] of the lane's channel gives, in lane l and register r, phi[4 qq + r] C_l[m_out],
+// i.e. each lane accumulates its own channel's S[4 qq .. 4 qq + 3][m_out].
 template <int LI, int LO, int NBQ, bool TANGENT>
-__global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
+__global__ __launch_bounds__(64, 3) void fwd_uvw_kernel(const FwdUvwArgs a) {
   constexpr int NI = 2 * LI + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
   using L = EdgeLds<NB, NI * NO, TANGENT>;
   __shared__ float s_edge[64 * L::kStride];
@@ -88,11 +94,12 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
   const int slot = lane / cp;
   const int u = blockIdx.y * cp + (lane - slot * cp);
   const bool uvalid = u < a.c_in;
-  float acc[NB][NO];
+  const int q4 = lane & 3;
+  f4v acc[NO][NBQ];
 #pragma unroll
-  for (int q = 0; q < NB; ++q)
+  for (int m = 0; m < NO; ++m)
 #pragma unroll
-    for (int m = 0; m < NO; ++m) acc[q][m] = 0.f;
+    for (int qq = 0; qq < NBQ; ++qq) acc[m][qq] = f4v{0.f, 0.f, 0.f, 0.f};
   const int e0 = a.rowptr[i], e1 = a.rowptr[i + 1];
   for (int base = e0; base < e1; base += kWave) {
     const int ne = min(kWave, e1 - base);
@@ -102,36 +109,55 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
       s_j[lane] = j;
     }
     __syncthreads();
-    if (uvalid) {
-      for (int t = slot; t < ne; t += nslots) {
-        const float* e = s_edge + t * L::kStride;
-        const float* xr = a.x + static_cast<int64_t>(s_j[t]) * a.x_dim + a.xoff + u;
-        float xv[NI];
+    const int trips = (ne + nslots - 1) / nslots;
+    // gathered sender rows, one edge ahead (zero for lanes without a channel or an edge)
+    float xn[NI];
+    {
+      const bool v = uvalid && slot < ne;
+      const float* xr = a.x + static_cast<int64_t>(v ? s_j[slot] : 0) * a.x_dim + a.xoff + u;
 #pragma unroll
-        for (int mi = 0; mi < NI; ++mi) xv[mi] = xr[mi * a.c_in];
-        float cm[NO], cmd[NO];
+      for (int mi = 0; mi < NI; ++mi) xn[mi] = v ? xr[mi * a.c_in] : 0.f;
+    }
+    for (int it = 0; it < trips; ++it) {
+      const int t = it * nslots + slot;
+      const bool tvalid = t < ne;
+      const float* e = s_edge + (tvalid ? t : 0) * L::kStride;
+      float xv[NI];
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) {
-          float s = 0.f, sd = 0.f;
+      for (int mi = 0; mi < NI; ++mi) xv[mi] = xn[mi];
+      {
+        const int tn = t + nslots;
+        const bool v = uvalid && tn < ne;
+        const float* xr = a.x + static_cast<int64_t>(v ? s_j[tn] : 0) * a.x_dim + a.xoff + u;
 #pragma unroll
-          for (int mi = 0; mi < NI; ++mi) {
-            s += xv[mi] * e[L::kCy + mi * NO + mo];
-            if constexpr (TANGENT) sd += xv[mi] * e[L::kCyDot + mi * NO + mo];
-          }
-          cm[mo] = s;
-          cmd[mo] = sd;
+        for (int mi = 0; mi < NI; ++mi) xn[mi] = v ? xr[mi * a.c_in] : 0.f;
+      }
+      float cm[NO], cmd[NO];
+#pragma unroll
+      for (int mo = 0; mo < NO; ++mo) {
+        float s = 0.f, sd = 0.f;
+#pragma unroll
+        for (int mi = 0; mi < NI; ++mi) {
+          s += xv[mi] * e[L::kCy + mi * NO + mo];
+          if constexpr (TANGENT) sd += xv[mi] * e[L::kCyDot + mi * NO + mo];
         }
+        cm[mo] = tvalid ? s : 0.f;
+        cmd[mo] = tvalid ? sd : 0.f;
+      }
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-          const float ph = e[L::kPhi + q];
-          if constexpr (TANGENT) {
-            const float phd = e[L::kPhiDot + q];
+      for (int qq = 0; qq < NBQ; ++qq) {
+        const float ph = e[L::kPhi + 4 * qq + q4];
+        if constexpr (TANGENT) {
+          const float phd = e[L::kPhiDot + 4 * qq + q4];
 #pragma unroll
-            for (int mo = 0; mo < NO; ++mo) acc[q][mo] += phd * cm[mo] + ph * cmd[mo];
-          } else {
-#pragma unroll
-            for (int mo = 0; mo < NO; ++mo) acc[q][mo] += ph * cm[mo];
+          for (int mo = 0; mo < NO; ++mo) {
+            acc[mo][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(phd, cm[mo], acc[mo][qq], 0, 0, 0);
+            acc[mo][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, cmd[mo], acc[mo][qq], 0, 0, 0);
           }
+        } else {
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo)
+            acc[mo][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, cm[mo], acc[mo][qq], 0, 0, 0);
         }
       }
     }
@@ -139,16 +165,20 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
   }
   for (int off = cp; off < kWave; off <<= 1)
 #pragma unroll
-    for (int q = 0; q < NB; ++q)
+    for (int m = 0; m < NO; ++m)
 #pragma unroll
-      for (int m = 0; m < NO; ++m) acc[q][m] += __shfl_xor(acc[q][m], off);
+      for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][qq][r] += __shfl_xor(acc[m][qq][r], off);
   if (slot == 0 && uvalid) {
     float* srow = a.S + static_cast<int64_t>(blockIdx.x) * NO * a.s_row_stride + a.s_col0 + u;
 #pragma unroll
-    for (int q = 0; q < NB; ++q)
-      if (q < a.g.nb)
+    for (int qq = 0; qq < NBQ; ++qq)
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) srow[mo * a.s_row_stride + q * a.c_in] = acc[q][mo];
+      for (int r = 0; r < 4; ++r)
+        if (4 * qq + r < a.g.nb)
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo) srow[mo * a.s_row_stride + (4 * qq + r) * a.c_in] = acc[mo][qq][r];
   }
 }
 
@@ -180,13 +210,23 @@ __global__ __launch_bounds__(64) void fwd_uvu_kernel(const FwdUvuArgs a) {
       s_j[lane] = j;
     }
     __syncthreads();
-    if (uvalid) {
+    if (uvalid && slot < ne) {
+      float xn[NI];
+      {
+        const float* xr = a.x + static_cast<int64_t>(s_j[slot]) * a.x_dim + a.xoff + u;
+#pragma unroll
+        for (int mi = 0; mi < NI; ++mi) xn[mi] = xr[mi * a.c];
+      }
       for (int t = slot; t < ne; t += nslots) {
         const float* e = s_edge + t * L::kStride;
-        const float* xr = a.x + static_cast<int64_t>(s_j[t]) * a.x_dim + a.xoff + u;
         float xv[NI];
 #pragma unroll
-        for (int mi = 0; mi < NI; ++mi) xv[mi] = xr[mi * a.c];
+        for (int mi = 0; mi < NI; ++mi) xv[mi] = xn[mi];
+        if (t + nslots < ne) {
+          const float* xr = a.x + static_cast<int64_t>(s_j[t + nslots]) * a.x_dim + a.xoff + u;
+#pragma unroll
+          for (int mi = 0; mi < NI; ++mi) xn[mi] = xr[mi * a.c];
+        }
         float we = 0.f, wed = 0.f;
 #pragma unroll
         for (int q = 0; q < NB; ++q) {

@@ -5,7 +5,9 @@
 // backward: Xt = x W, x_bar = P W^T, W_bar = x^T P.  Rows of A and C are given
 // through a RowMap so ir_mul feature blocks ((node, m) rows) are read and written
 // in place.  A 64x64 output tile per 256-thread workgroup, four wavefronts of
-// 32x32, K staged through LDS in slices of 16 (double-buffered through registers).
+// 32x32, K staged through LDS in slices of 32 with the next slice's global loads
+// in flight during the current slice's MFMAs.  Long-K products split K across
+// workgroups; the partial tiles are summed in a fixed order by a second kernel.
 #include "kernels.hpp"
 
 namespace etpc {
@@ -13,13 +15,15 @@ namespace {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 64, BN = 64, BK = 16;
+constexpr int BM = 64, BN = 64, BK = 32;
 
 __device__ inline int64_t rowoff(const RowMap& m, int r) {
   const int q = r / m.div;
   return static_cast<int64_t>(q) * m.s1 + static_cast<int64_t>(r - q * m.div) * m.s2;
 }
 
+// A(m, k) and B(k, n) tiles: each of the 256 threads moves 8 elements of A and 8 of B
+// per K slice, as two groups of 4 consecutive elements (float4 when aligned).
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
@@ -30,63 +34,90 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
   const int kz1 = min(a.K, kz0 + a.k_split);
   float* C = a.C + static_cast<int64_t>(blockIdx.z) * a.c_split_stride;
 
-  // load assignments
-  const int a_row = tid >> 2, a_k4 = (tid & 3) * 4;      // K-contiguous A: row, 4 k's
-  const int t_k = tid >> 4, t_c4 = (tid & 15) * 4;       // k-major: k, 4 columns
-  int64_t a_rowoff = 0;
-  const bool a_row_ok = (m0 + a_row) < a.M;
-  if (!a.a_mcontig && a_row_ok) a_rowoff = rowoff(a.amap, m0 + a_row);
+  // K-contiguous A: rows a_row and a_row + 32, k offset a_k4 (4 consecutive k)
+  const int a_row = tid >> 3, a_k4 = (tid & 7) * 4;
+  // k-major tiles: k rows t_k and t_k + 16, 4 consecutive columns at t_c4
+  const int t_k = tid >> 4, t_c4 = (tid & 15) * 4;
+  int64_t a_off[2] = {0, 0};
+  bool a_ok[2] = {false, false};
+  if (!a.a_mcontig) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = m0 + a_row + 32 * h;
+      a_ok[h] = m < a.M;
+      if (a_ok[h]) a_off[h] = rowoff(a.amap, m);
+    }
+  }
+  const bool vec = a.vec4 != 0;
 
-  float ra[4], rb[4];
+  float ra[8], rb[8];
+  auto load4 = [&](const float* p, bool full, int valid, float* dst) {
+    if (full && vec) {
+      const float4 v = *reinterpret_cast<const float4*>(p);
+      dst[0] = v.x;
+      dst[1] = v.y;
+      dst[2] = v.z;
+      dst[3] = v.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[t] = t < valid ? p[t] : 0.f;
+    }
+  };
   auto load = [&](int k0) {
     if (!a.a_mcontig) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int k = k0 + a_k4 + t;
-        ra[t] = (a_row_ok && k < kz1) ? a.A[a_rowoff + k] : 0.f;
+      for (int h = 0; h < 2; ++h) {
+        const int k = k0 + a_k4;
+        const int valid = a_ok[h] ? min(4, kz1 - k) : 0;
+        load4(a.A + a_off[h] + k, valid == 4, valid, ra + 4 * h);
       }
     } else {
-      const int k = k0 + t_k;
-      const bool kok = k < kz1;
-      const int64_t ko = kok ? rowoff(a.amap, k) : 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int m = m0 + t_c4 + t;
-        ra[t] = (kok && m < a.M) ? a.A[ko + m] : 0.f;
+      for (int h = 0; h < 2; ++h) {
+        const int k = k0 + t_k + 16 * h;
+        const int m = m0 + t_c4;
+        const int valid = k < kz1 ? min(4, a.M - m) : 0;
+        load4(a.A + (valid > 0 ? rowoff(a.amap, k) : 0) + m, valid == 4, valid, ra + 4 * h);
       }
     }
-    const int k = k0 + t_k;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int n = n0 + t_c4 + t;
-      rb[t] = (k < kz1 && n < a.N) ? a.B[static_cast<int64_t>(k) * a.ldb + n] : 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + t_k + 16 * h;
+      const int n = n0 + t_c4;
+      const int valid = k < kz1 ? min(4, a.N - n) : 0;
+      load4(a.B + static_cast<int64_t>(k < kz1 ? k : 0) * a.ldb + n, valid == 4, valid, rb + 4 * h);
     }
   };
   auto store = [&]() {
     if (!a.a_mcontig) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) As[a_k4 + t][a_row] = ra[t];
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) As[a_k4 + t][a_row + 32 * h] = ra[4 * h + t];
     } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) As[t_k][t_c4 + t] = ra[t];
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) As[t_k + 16 * h][t_c4 + t] = ra[4 * h + t];
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) Bs[t_k][t_c4 + t] = rb[t];
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Bs[t_k + 16 * h][t_c4 + t] = rb[4 * h + t];
   };
 
   f16v acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   if (kz0 < kz1) load(kz0);
+  const int am = wm * 32 + (lane & 31), bn = wn * 32 + (lane & 31), kh = lane >> 5;
   for (int k0 = kz0; k0 < kz1; k0 += BK) {
     store();
     __syncthreads();
     if (k0 + BK < kz1) load(k0 + BK);
-    const int am = wm * 32 + (lane & 31), bn = wn * 32 + (lane & 31), kh = lane >> 5;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
+    for (int kk = 0; kk < BK; kk += 2)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + kh][am], Bs[kk + kh][bn], acc, 0, 0, 0);
-    }
     __syncthreads();
   }
   const int n = n0 + wn * 32 + (lane & 31);
@@ -102,12 +133,38 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
   }
 }
 
+// C(m, n) (+)= sum_s part[s][m][n], fixed order in s
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, float* __restrict__ C,
+                                     RowMap cmap, int beta) {
+  const int64_t total = static_cast<int64_t>(M) * N;
+  for (int64_t idx = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; idx < total;
+       idx += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float s = 0.f;
+    for (int z = 0; z < splits; ++z) s += part[z * total + idx];
+    const int m = static_cast<int>(idx / N);
+    const int n = static_cast<int>(idx - static_cast<int64_t>(m) * N);
+    float* p = C + rowoff(cmap, m) + n;
+    *p = beta ? (*p + s) : s;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, int splits, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   dim3 grid((a.M + BM - 1) / BM, (a.N + BN - 1) / BN, splits), block(256);
   hipLaunchKernelGGL(gemm_f32_kernel, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, float* C, RowMap cmap, bool beta,
+                                hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(M) * N;
+  if (total <= 0) return hipSuccess;
+  int64_t g = (total + 255) / 256;
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(static_cast<unsigned>(g)), dim3(256), 0, s, part, splits, M, N, C,
+                     cmap, beta ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -134,22 +134,31 @@ __device__ inline void radial_eval(const GeomParams& g, float r, float* __restri
     const float amp = sqrtf(2.f / rc);
     const float inv_r = 1.f / r;
     const float w = 3.14159265358979323846f / rc;
+    // sin(b w r), cos(b w r) for b = 1..B by the Chebyshev recurrence
+    // s_(b+1) = 2 cos(w r) s_b - s_(b-1), and the same for the cosines
+    float s1, c1;
+    sincosf(w * r, &s1, &c1);
+    float sp = 0.f, sc = s1, cpv = 1.f, cc = c1;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (b < g.nb) {
         const float k = w * (b + 1);
-        float sn, cs;
-        sincosf(k * r, &sn, &cs);
-        const float bare = amp * sn * inv_r;
+        const float bare = amp * sc * inv_r;
         phi[b] = bare * f;
         if (dphi) {
-          const float dbare = amp * (k * cs - sn * inv_r) * inv_r;
+          const float dbare = amp * (k * cc - sc * inv_r) * inv_r;
           dphi[b] = dbare * f + bare * fp;
         }
       } else {
         phi[b] = 0.f;
         if (dphi) dphi[b] = 0.f;
       }
+      const float sn = 2.f * c1 * sc - sp;
+      const float cn = 2.f * c1 * cc - cpv;
+      sp = sc;
+      sc = sn;
+      cpv = cc;
+      cc = cn;
     }
   }
 }

@@ -59,26 +59,38 @@ __global__ void reduce_wbar_kernel(const ReduceWArgs a) {
   }
 }
 
-__global__ void pos_bar_kernel(const int32_t* __restrict__ rowptr, const int32_t* __restrict__ s_rowptr,
-                               const int32_t* __restrict__ s_slot, const float* __restrict__ rbar,
-                               float* __restrict__ pos_bar, int n) {
-  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+// one wavefront per node: lanes stride over the node's sender and receiver slots; the lane
+// partials are combined by a fixed reduction tree (deterministic)
+__global__ __launch_bounds__(256) void pos_bar_kernel(const int32_t* __restrict__ rowptr,
+                                                     const int32_t* __restrict__ s_rowptr,
+                                                     const int32_t* __restrict__ s_slot,
+                                                     const float* __restrict__ rbar, float* __restrict__ pos_bar,
+                                                     int n) {
+  const int v = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (v >= n) return;
   float sx = 0.f, sy = 0.f, sz = 0.f;
-  for (int k = s_rowptr[v]; k < s_rowptr[v + 1]; ++k) {
+  for (int k = s_rowptr[v] + lane; k < s_rowptr[v + 1]; k += 64) {
     const int64_t e = s_slot[k];
     sx += rbar[3 * e + 0];
     sy += rbar[3 * e + 1];
     sz += rbar[3 * e + 2];
   }
-  for (int64_t e = rowptr[v]; e < rowptr[v + 1]; ++e) {
+  for (int64_t e = rowptr[v] + lane; e < rowptr[v + 1]; e += 64) {
     sx -= rbar[3 * e + 0];
     sy -= rbar[3 * e + 1];
     sz -= rbar[3 * e + 2];
   }
-  pos_bar[3 * v + 0] = sx;
-  pos_bar[3 * v + 1] = sy;
-  pos_bar[3 * v + 2] = sz;
+  for (int off = 32; off > 0; off >>= 1) {
+    sx += __shfl_xor(sx, off);
+    sy += __shfl_xor(sy, off);
+    sz += __shfl_xor(sz, off);
+  }
+  if (lane == 0) {
+    pos_bar[3 * v + 0] = sx;
+    pos_bar[3 * v + 1] = sy;
+    pos_bar[3 * v + 2] = sz;
+  }
 }
 
 int grid_for(int64_t n, int block) {
@@ -132,7 +144,7 @@ hipError_t launch_reduce_wbar(const float* part, int splits, int c_in, int n_pat
 hipError_t launch_pos_bar(const int32_t* rowptr, const int32_t* s_rowptr, const int32_t* s_slot, const float* rbar,
                           float* pos_bar, int n_nodes, hipStream_t s) {
   if (n_nodes <= 0) return hipSuccess;
-  hipLaunchKernelGGL(pos_bar_kernel, dim3((n_nodes + 255) / 256), dim3(256), 0, s, rowptr, s_rowptr, s_slot, rbar,
+  hipLaunchKernelGGL(pos_bar_kernel, dim3((n_nodes + 3) / 4), dim3(256), 0, s, rowptr, s_rowptr, s_slot, rbar,
                      pos_bar, n_nodes);
   return hipGetLastError();
 }

@@ -119,8 +119,12 @@ struct GemmArgs {
   int32_t M, N, K;
   int32_t k_split;
   int64_t c_split_stride;
+  int32_t vec4;           // 1: every A row / B row start is 16-byte aligned (float4 loads allowed)
 };
 hipError_t launch_gemm(const GemmArgs& a, int splits, hipStream_t s);
+// C(m, n) (+)= sum_{s < splits} part[s][m][n] (fixed order), C rows through cmap
+hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, float* C, RowMap cmap, bool beta,
+                                hipStream_t s);
 
 // ---------------------------------------------------------------- small helpers
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);

@@ -115,11 +115,12 @@ def test_backward_parity(name, n, d):
     errs = (rel_err(xb, rx), rel_err(wb, rw), rel_err(pb, rp))
     note(f"backward {cfg.name} rel err x {errs[0]:.2e} w {errs[1]:.2e} pos {errs[2]:.2e}")
     assert max(errs) <= TOL
-    # subsets of outputs give the same values
+    # subsets of outputs give the same values (kernel variants may differ in the last bits)
     xb2, _, pb2 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, want=("x", "pos"))
     _, _, pb3 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, want=("pos",))
     _, wb4, _ = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, want=("w",))
-    assert torch.equal(xb2, xb) and torch.equal(pb2, pb) and torch.equal(pb3, pb) and torch.equal(wb4, wb)
+    for got, ref in ((xb2, xb), (pb2, pb), (pb3, pb), (wb4, wb)):
+        assert rel_err(got, ref.double().cpu().numpy()) <= 1e-6
 
 
 @pytest.mark.parametrize("name,n", [("cfg5", 256), ("cfg3", 128)])
