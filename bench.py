@@ -32,7 +32,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def flop_model(plan, n_nodes, n_edges, radial_b):
+def flop_model(plan, n_nodes, n_edges, radial_b, force_step=False):
     """Algorithmic FLOPs per step by kernel kind (2 per multiply-add).
 
     Per path pi: i = 2l_in+1, o = 2l_out+1, kappa = i*o.
@@ -41,6 +41,8 @@ def flop_model(plan, n_nodes, n_edges, radial_b):
       bwd traversal   E * sum C_out (2 kappa + 3 B i)       (x_bar, W_bar and pos_bar)
       node GEMMs      3 N * sum B C_in C_out i              (Xt, x_bar, W_bar)
     uvu: fwd E * sum C (B + kappa + min(i, o)), bwd E * sum C (3B + 3i + 2 kappa).
+    Force step (forward, pos_bar-only backward, double backward along pos_dot for d/dx, d/dW):
+      bwd traversal   E * sum C_out (2 kappa + 2 B i) twice, node GEMMs 3 N * sum B C_in C_out i.
     """
     ins = plan.irreps_in
     outs = plan.out_irreps()
@@ -51,7 +53,12 @@ def flop_model(plan, n_nodes, n_edges, radial_b):
         co, lo, _ = outs[q["out_block"]]
         i, o = 2 * li + 1, 2 * lo + 1
         k = i * o
-        if plan.mode == "uvw":
+        if plan.mode == "uvw" and force_step:
+            f["fwd_traverse"] += n_edges * ci * (k + B * o)
+            f["channel_gemm"] += n_nodes * B * ci * co * o
+            f["bwd_traverse"] += 2 * n_edges * co * (2 * k + 2 * B * i)
+            f["node_gemm"] += 3 * n_nodes * B * ci * co * i
+        elif plan.mode == "uvw":
             f["fwd_traverse"] += n_edges * ci * (k + B * o)
             f["channel_gemm"] += n_nodes * B * ci * co * o
             f["bwd_traverse"] += n_edges * co * (2 * k + 3 * B * i)
@@ -158,16 +165,25 @@ def main():
     torch.cuda.synchronize()
     csr_ms = (time.perf_counter() - t0) / 3 * 1e3
 
+    force_step = "dbl" in cfg.passes
     ws_f = torch.empty(etpc.etpc_workspace_size(plan, etpc.PASS_FWD, N, E), dtype=torch.uint8, device=dev)
     ws_b = torch.empty(etpc.etpc_workspace_size(plan, etpc.PASS_BWD, N, E), dtype=torch.uint8, device=dev)
+    ws_d = (torch.empty(etpc.etpc_workspace_size(plan, etpc.PASS_DBL, N, E), dtype=torch.uint8, device=dev)
+            if force_step else torch.empty(0, dtype=torch.uint8, device=dev))
     z = torch.empty(N, info["z_dim"], device=dev)
     outs = (torch.empty(N, info["x_dim"], device=dev), torch.empty(info["w_numel"], device=dev),
             torch.empty(N, 3, device=dev))
+    if force_step:
+        pos_dot = T(-wl.force_c)
+        outs = (None, None, torch.empty(N, 3, device=dev))
+        douts = (None, torch.empty(N, info["x_dim"], device=dev), torch.empty(info["w_numel"], device=dev))
     resident = torch.cuda.memory_allocated()
 
     def step():
         etpc.etpc_forward(plan, graph, x, pos, w, z=z, ws=ws_f)
         etpc.etpc_backward(plan, graph, x, pos, w, zb, outs=outs, ws=ws_b)
+        if force_step:
+            etpc.etpc_double_backward(plan, graph, x, pos, w, zb, pos_dot=pos_dot, outs=douts, ws=ws_d)
 
     for _ in range(args.warmup):
         step()
@@ -195,7 +211,7 @@ def main():
         tot, n = etpc.etpc_profile_read(k)
         kinds[k] = dict(ms_per_step=tot / args.steps, launches_per_step=n / args.steps)
     etpc.etpc_profile_enable(False)
-    flops = flop_model(plan, N, E, cfg.n_basis)
+    flops = flop_model(plan, N, E, cfg.n_basis, force_step)
     log(f"step {ms:.3f} ms (profiled pass {prof_ms:.3f} ms); csr build {csr_ms:.3f} ms")
     for k, v in kinds.items():
         tf = flops.get(k, 0.0) / (v["ms_per_step"] * 1e-3) / 1e12 if v["ms_per_step"] > 0 and k in flops else 0.0
@@ -210,7 +226,8 @@ def main():
     log(f"whole step: {total_tf:.2f} TFLOP/s algorithmic ({total_tf / PEAK_FP32_TFLOPS:.1%} of fp32 peak)")
 
     result = {
-        "metric": "edges/s fwd+bwd (uvw, 64x0e+1o+2e)" if cfg.index == 2 else f"edges/s fwd+bwd ({cfg.name})",
+        "metric": "edges/s fwd+bwd (uvw, 64x0e+1o+2e)" if cfg.index == 2 else
+                  (f"edges/s fwd+bwd+dbl ({cfg.name})" if force_step else f"edges/s fwd+bwd ({cfg.name})"),
         "value": value,
         "unit": "edges/s",
         "n_gpus": 1,
@@ -230,7 +247,8 @@ def main():
             "n_nodes": N,
             "n_edges": E,
             "mode": cfg.mode,
-            "pass": "forward + backward (x_bar, W_bar, pos_bar)",
+            "pass": ("forward + backward (pos_bar) + double backward along pos_dot (d/dx, d/dW)" if force_step
+                     else "forward + backward (x_bar, W_bar, pos_bar)"),
         },
         "roofline": {
             "kernel": dom,
@@ -248,7 +266,7 @@ def main():
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kinds.items()},
         "csr_build_ms": csr_ms,
         "peak_mib": peak / 2 ** 20,
-        "workspace_mib": (ws_f.numel() + ws_b.numel()) / 2 ** 20,
+        "workspace_mib": (ws_f.numel() + ws_b.numel() + ws_d.numel()) / 2 ** 20,
         "resident_mib": resident / 2 ** 20,
     }
     if not args.no_cpu_baseline:

@@ -96,6 +96,14 @@ Derived derive(const etpc_plan_s* p) {
   return d;
 }
 
+int pick_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int64_t sp = (1024 + tiles - 1) / tiles;
+  sp = std::min<int64_t>(sp, (K + 255) / 256);
+  sp = std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
+  return static_cast<int>(sp);
+}
+
 // ---------------------------------------------------------------- workspace layouts
 constexpr int kGemmSplits = 8;   // split-K partial sets kept for the long-K channel / x_bar GEMMs
 
@@ -127,7 +135,17 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t
     if (pos) L.wcat = c.take<float>(static_cast<size_t>(d.max_wcat));
     if (xbar) L.wt = c.take<float>(static_cast<size_t>(d.max_wcat));
     if (wt2) L.wt2 = c.take<float>(static_cast<size_t>(d.max_wcat));
-    if (wbar) L.wpart = c.take<float>(static_cast<size_t>((wbar2 ? 2 : 1) * kMaxSplits * d.max_wcat));
+    if (wbar) {
+      // split-K partial tiles of W_bar: as many splits as wbar_gemm picks for this chunk
+      int64_t need = 0;
+      for (size_t k = 0; k < p->in.size(); ++k) {
+        if (p->by_in[k].empty()) continue;
+        const int ni = 2 * p->in[k].l + 1;
+        const int sp = pick_splits(p->in[k].mul, d.block_ncols[k], std::max<int64_t>(chunk, 1) * ni);
+        need = std::max<int64_t>(need, static_cast<int64_t>(sp) * p->in[k].mul * d.block_ncols[k]);
+      }
+      L.wpart = c.take<float>(static_cast<size_t>((wbar2 ? 2 : 1) * need));
+    }
     if (pos) L.xt = c.take<float>(static_cast<size_t>(chunk * d.max_state));
     if (need_p) L.P = c.take<float>(static_cast<size_t>(chunk * d.max_state));
     if (tan) L.Pd = c.take<float>(static_cast<size_t>(chunk * d.max_state));
@@ -182,13 +200,6 @@ int64_t pick_chunk(int64_t n, size_t ws_bytes, F bytes_of) {
 RowMap plain(int64_t ld) { return RowMap{ld, 0, 1}; }
 RowMap irmul(int32_t m, int64_t width, int64_t mul) { return RowMap{width, mul, m}; }
 
-int pick_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
-  int64_t sp = (1024 + tiles - 1) / tiles;
-  sp = std::min<int64_t>(sp, (K + 255) / 256);
-  sp = std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
-  return static_cast<int>(sp);
-}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -455,6 +466,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   if (R.x_out) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
   for (int64_t j0 = 0; j0 < N; j0 += chunk) {
     const int nsend = static_cast<int>(std::min<int64_t>(chunk, N - j0));
+    rbar_started = false;  // the edges of this sender chunk are first written by its first path
     for (size_t k = 0; k < p->in.size(); ++k) {
       const auto& paths = p->by_in[k];
       if (paths.empty()) continue;

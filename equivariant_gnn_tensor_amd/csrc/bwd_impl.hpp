@@ -225,8 +225,12 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
         }
       }
       if constexpr (POS) {
+        // radial part: sum_q phi'_q phi_bar_q = sum_m_in G[m_in] Q[m_in], G = sum_q phi'_q Xt[q];
+        // angular part: sum_m_sh dY[d][m_sh] Wy[m_sh], Wy = sum_m_in T[m_in] V[m_in][m_sh], T = sum_q phi_q Xt[q]
         float srad = 0.f;
-        float rb[3] = {0.f, 0.f, 0.f};
+        float wy[NS];
+#pragma unroll
+        for (int my = 0; my < NS; ++my) wy[my] = 0.f;
 #pragma unroll
         for (int mi = 0; mi < NI; ++mi) {
           float tq = 0.f, gq = 0.f;
@@ -237,12 +241,15 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
           }
           srad += gq * Q[mi];
 #pragma unroll
-          for (int d = 0; d < 3; ++d) {
-            float zc = 0.f;
+          for (int my = 0; my < NS; ++my) wy[my] += tq * V[mi][my];
+        }
+        float rb[3];
 #pragma unroll
-            for (int my = 0; my < NS; ++my) zc += e[R::kDY + d * NS + my] * V[mi][my];
-            rb[d] += tq * zc;
-          }
+        for (int d = 0; d < 3; ++d) {
+          float s = 0.f;
+#pragma unroll
+          for (int my = 0; my < NS; ++my) s += e[R::kDY + d * NS + my] * wy[my];
+          rb[d] = s;
         }
         float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
 #pragma unroll
@@ -400,16 +407,22 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
           wbar[q] += TAN ? (e[R::kPhiDot + q] * h + e[R::kPhi + q] * hd) : e[R::kPhi + q] * h;
         if (want_pos) {
           const float srad = wdr * h;
-          float rb[3] = {0.f, 0.f, 0.f};
+          float wy[NS];
 #pragma unroll
-          for (int mi = 0; mi < NI; ++mi)
+          for (int my = 0; my < NS; ++my) {
+            float s = 0.f;
 #pragma unroll
-            for (int d = 0; d < 3; ++d) {
-              float zc = 0.f;
+            for (int mi = 0; mi < NI; ++mi) s += xj[mi] * V[mi][my];
+            wy[my] = s;
+          }
+          float rb[3];
 #pragma unroll
-              for (int my = 0; my < NS; ++my) zc += e[R::kDY + d * NS + my] * V[mi][my];
-              rb[d] += xj[mi] * zc;
-            }
+          for (int d = 0; d < 3; ++d) {
+            float s = 0.f;
+#pragma unroll
+            for (int my = 0; my < NS; ++my) s += e[R::kDY + d * NS + my] * wy[my];
+            rb[d] = s;
+          }
           float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
 #pragma unroll
           for (int d = 0; d < 3; ++d) {
