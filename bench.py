@@ -11,6 +11,16 @@ data, resident in HBM before timing starts.
 Prints one JSON line (see the "metric" key); diagnostics go to stderr.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload cfg2] [--no-cpu-baseline]
+
+Counter summaries for the `traffic` field (rocprofv3 runs of this same script; the
+--copy-calibration-mib run adds a plain device copy of known size whose counter reading
+gives the scale factor):
+
+    rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace_cfg2 -o run -- \
+        python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration-mib 256
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch_cfg2 -o run -- python3 bench.py <same>
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write_cfg2 -o run -- python3 bench.py <same>
+    python bench.py --summarize-profile DIR --steps 3 --warmup 1 --workload cfg2 --copy-calibration-mib 256
 """
 from __future__ import annotations
 
@@ -121,6 +131,120 @@ def cpu_baseline(cfg, wl, seconds):
                        f"({done / wl.n_edges:.1%} of the graph) in {dt:.1f} s")
 
 
+KERNEL_FAMILIES = (
+    ("fwd_traverse", ("fwd_uvw_kernel", "fwd_uvu_kernel")),
+    ("bwd_traverse", ("bwd_uvw_kernel", "bwd_uvu_kernel")),
+    ("gemm", ("gemm_f32_kernel",)),
+    ("csr", ("radix_", "scan_", "lower_bound", "validate_", "iota_", "gather_", "copy_kernel")),
+    ("aux", ("fill_kernel", "wprep_kernel", "reduce_wbar_kernel", "segment_sum_kernel", "pos_bar_kernel",
+             "splitk_reduce_kernel")),
+)
+
+
+def kernel_family(name):
+    if "etpc::" not in name:
+        return "other"
+    for fam, keys in KERNEL_FAMILIES:
+        if any(k in name for k in keys):
+            return fam
+    return "other"
+
+
+def summarize_profile(d, workload, steps, warmup, copy_mib):
+    """Turn the three rocprofv3 runs (kernel trace, FETCH_SIZE, WRITE_SIZE) into
+    profiles/trace_<workload>.md and profiles/pmc_<kind>_<workload>.json."""
+    import csv
+    import glob
+    import collections
+    execs = warmup + 2 * steps            # timed pass + event-profiled pass
+    stats = glob.glob(os.path.join(d, f"trace_{workload}", "**", "*kernel_stats.csv"), recursive=True)
+    if not stats:
+        raise SystemExit(f"no kernel_stats.csv under {d}/trace_{workload}")
+    fam_t = collections.defaultdict(lambda: [0.0, 0])
+    rows = []
+    for r in csv.DictReader(open(stats[0])):
+        f = kernel_family(r["Name"])
+        fam_t[f][0] += float(r["TotalDurationNs"])
+        fam_t[f][1] += int(r["Calls"])
+        rows.append((float(r["TotalDurationNs"]), int(r["Calls"]), float(r["AverageNs"]), f, r["Name"]))
+    rows.sort(reverse=True)
+
+    def counters(kind):
+        files = glob.glob(os.path.join(d, f"{kind}_{workload}", "**", "*counter_collection.csv"), recursive=True)
+        per = collections.defaultdict(list)     # family -> [KiB per dispatch]
+        copy = []
+        for fn in files:
+            for r in csv.DictReader(open(fn)):
+                name = r.get("Kernel_Name", "")
+                v = float(r["Counter_Value"])
+                if "copy" in name.lower() and kernel_family(name) == "other":
+                    copy.append(v)
+                else:
+                    per[kernel_family(name)].append(v)
+        return per, copy
+
+    fetch, fcopy = counters("fetch")
+    write, wcopy = counters("write")
+    known_kib = copy_mib * 1024.0
+    # the calibration copy is the largest copy dispatch; its reading should be copy_mib
+    f_scale = known_kib / max(fcopy) if fcopy else None
+    w_scale = known_kib / max(wcopy) if wcopy else None
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    cmd_args = f"--steps {steps} --warmup {warmup} --no-cpu-baseline --workload {workload} " \
+               f"--copy-calibration-mib {copy_mib}"
+    lines = [f"# rocprofv3 kernel trace, workload {workload}", "",
+             "Commands (repo root, one MI355X):", "",
+             "```",
+             f"rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace_{workload} -o run -- "
+             f"python3 bench.py {cmd_args}",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch_{workload} -o run -- "
+             f"python3 bench.py {cmd_args}",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write_{workload} -o run -- "
+             f"python3 bench.py {cmd_args}",
+             f"python bench.py --summarize-profile DIR --steps {steps} --warmup {warmup} --workload {workload} "
+             f"--copy-calibration-mib {copy_mib}",
+             "```", "",
+             f"Each run executes {execs} steps (warmup {warmup} + timed {steps} + event-profiled {steps}).", "",
+             "| family | launches/step | ms/step (trace) | avg us/launch | HBM MB/step (calibrated) |",
+             "|---|---|---|---|---|"]
+    out = {}
+    for fam in ("fwd_traverse", "bwd_traverse", "gemm", "aux", "csr"):
+        if fam not in fam_t:
+            continue
+        tot_ns, calls = fam_t[fam]
+        fk = sum(fetch.get(fam, [])) * (f_scale or 0.0)
+        wk = sum(write.get(fam, [])) * (w_scale or 0.0)
+        nd = max(len(fetch.get(fam, [])), 1)
+        mb_step = (fk + wk) * 1024.0 / execs / 1e6 if f_scale and w_scale else None
+        lines.append(f"| {fam} | {calls / execs:.1f} | {tot_ns / execs / 1e6:.4f} | {tot_ns / max(calls, 1) / 1e3:.1f} | "
+                     f"{mb_step if mb_step is None else round(mb_step, 1)} |")
+        out[fam] = dict(launches_per_step=calls / execs, ms_per_step=tot_ns / execs / 1e6,
+                        hbm_bytes_per_step=None if mb_step is None else mb_step * 1e6,
+                        hbm_bytes_per_launch=None if mb_step is None else (fk + wk) * 1024.0 / nd,
+                        fetch_kib_raw_per_dispatch=sum(fetch.get(fam, [])) / nd,
+                        write_kib_raw_per_dispatch=sum(write.get(fam, [])) / nd)
+    lines += ["", f"Copy calibration: a {copy_mib} MiB device-to-device copy read FETCH_SIZE "
+                  f"{max(fcopy) if fcopy else 'n/a'} KiB and WRITE_SIZE {max(wcopy) if wcopy else 'n/a'} KiB; "
+                  f"scale factors {f_scale} (fetch), {w_scale} (write).", "",
+              "Top kernels by total time (all executions):", "",
+              "| total ms | calls | avg us | family | kernel |", "|---|---|---|---|---|"]
+    for tot, calls, avg, fam, name in rows[:16]:
+        short = name if len(name) < 110 else name[:107] + "..."
+        lines.append(f"| {tot / 1e6:.3f} | {calls} | {avg / 1e3:.1f} | {fam} | `{short}` |")
+    with open(os.path.join(ROOT, "profiles", f"trace_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    kind_of = {"fwd_traverse": "fwd_traverse", "bwd_traverse": "bwd_traverse"}
+    for fam, kind in kind_of.items():
+        if fam in out and out[fam]["hbm_bytes_per_step"] is not None:
+            rec = dict(out[fam], kind=kind, workload=workload, kernel_src_sha=kernel_source_hash(kind),
+                       fetch_scale=f_scale, write_scale=w_scale, copy_calibration_mib=copy_mib,
+                       command=f"python bench.py --summarize-profile DIR --steps {steps} --warmup {warmup} "
+                               f"--workload {workload} --copy-calibration-mib {copy_mib}")
+            with open(os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.json"), "w") as fh:
+                json.dump(rec, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,7 +253,14 @@ def main():
     ap.add_argument("--workload", default="cfg2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="summarize rocprofv3 output under DIR into profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload, args.steps, args.warmup, args.copy_calibration_mib)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on exactly one GPU (no multi-GPU path); "
@@ -269,6 +400,14 @@ def main():
         "workspace_mib": (ws_f.numel() + ws_b.numel() + ws_d.numel()) / 2 ** 20,
         "resident_mib": resident / 2 ** 20,
     }
+    if args.copy_calibration_mib > 0:
+        nel = args.copy_calibration_mib * 2 ** 20 // 4
+        a_src = torch.ones(nel, device=dev)
+        a_dst = torch.empty_like(a_src)
+        for _ in range(3):
+            a_dst.copy_(a_src)
+        torch.cuda.synchronize()
+        del a_src, a_dst
     if not args.no_cpu_baseline:
         log("timing the oracle on the host ...")
         result["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_seconds)

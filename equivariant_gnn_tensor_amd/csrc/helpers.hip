@@ -31,13 +31,27 @@ __global__ void wprep_kernel(const WPrepArgs a) {
 
 struct ReduceWArgs {
   const float* part;
-  int32_t splits, rows, ncols, nb;
+  int32_t splits, split_step, rows, ncols, nb;
   int32_t accumulate;
   float* out;
   int64_t path_off[kMaxPaths];
   int32_t col0[kMaxPaths];
   int32_t cout[kMaxPaths];
 };
+
+// First stage for many partial copies: copy g = blockIdx.y sums copies [g*seg, (g+1)*seg)
+// of each element in order and stores the sum over copy g*seg (only this thread reads or
+// writes that element's copies in the segment, so the update is in place).
+__global__ void segment_sum_kernel(float* __restrict__ part, int splits, int seg, int64_t stride) {
+  const int64_t c = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+  if (c >= stride) return;
+  const int z0 = blockIdx.y * seg;
+  const int z1 = min(splits, z0 + seg);
+  float* p = part + static_cast<int64_t>(z0) * stride + c;
+  float s = 0.f;
+  for (int z = z0; z < z1; ++z) s += p[static_cast<int64_t>(z - z0) * stride];
+  *p = s;
+}
 
 // one path per blockIdx.y; element r of the path block = (q, u, w) in W order
 __global__ void reduce_wbar_kernel(const ReduceWArgs a) {
@@ -53,7 +67,7 @@ __global__ void reduce_wbar_kernel(const ReduceWArgs a) {
     const int w = static_cast<int>(rr - static_cast<int64_t>(u) * cout);
     const int64_t src = static_cast<int64_t>(u) * a.ncols + a.col0[t] + static_cast<int64_t>(q) * cout + w;
     float s = 0.f;
-    for (int z = 0; z < a.splits; ++z) s += a.part[z * split_stride + src];
+    for (int z = 0; z < a.splits; ++z) s += a.part[static_cast<int64_t>(z) * a.split_step * split_stride + src];
     float* o = a.out + a.path_off[t] + r;
     *o = a.accumulate ? (*o + s) : s;
   }
@@ -117,13 +131,25 @@ hipError_t launch_wprep(const WPrepArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_wbar(const float* part, int splits, int c_in, int n_paths, int nb, const int64_t* path_off,
+hipError_t launch_reduce_wbar(float* part, int splits, int c_in, int n_paths, int nb, const int64_t* path_off,
                               const int32_t* col0, const int32_t* cout, int ncols, float* out, bool accumulate,
                               hipStream_t s) {
   if (n_paths <= 0) return hipSuccess;
   ReduceWArgs a{};
   a.part = part;
   a.splits = splits;
+  a.split_step = 1;
+  constexpr int kSeg = 32;
+  if (splits > 2 * kSeg) {
+    // many copies (one per persistent workgroup): sum segments of kSeg copies in place
+    // first, so the final pass reads splits / kSeg copies with full parallelism
+    const int64_t stride = static_cast<int64_t>(c_in) * ncols;
+    const int groups = (splits + kSeg - 1) / kSeg;
+    hipLaunchKernelGGL(segment_sum_kernel, dim3(static_cast<unsigned>((stride + 255) / 256), groups), dim3(256), 0,
+                       s, part, splits, kSeg, stride);
+    a.splits = groups;
+    a.split_step = kSeg;
+  }
   a.rows = c_in;
   a.ncols = ncols;
   a.nb = nb;

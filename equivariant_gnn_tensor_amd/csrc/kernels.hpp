@@ -129,8 +129,9 @@ hipError_t launch_splitk_reduce(const float* part, int splits, int M, int N, flo
 // ---------------------------------------------------------------- small helpers
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 // W_bar scatter: out[path_off[t] + q*c_in*cout_t + u*cout_t + w] (+)= sum_{s < splits} part[s][u][col0_t + q*cout_t + w]
-// (fixed summation order over the split-K partials; part rows have ncols columns)
-hipError_t launch_reduce_wbar(const float* part, int splits, int c_in, int n_paths, int nb, const int64_t* path_off,
+// (fixed summation order over the split-K partials; part rows have ncols columns).  With
+// more than 64 copies, segments of 32 are summed first, in place, so part is clobbered.
+hipError_t launch_reduce_wbar(float* part, int splits, int c_in, int n_paths, int nb, const int64_t* path_off,
                               const int32_t* col0, const int32_t* cout, int ncols, float* out, bool accumulate,
                               hipStream_t s);
 // pos_bar[n] = sum_{sender slots of n} rbar[s_slot] - sum_{receiver slots of n} rbar[slot]
