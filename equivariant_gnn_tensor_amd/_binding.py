@@ -15,7 +15,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libetpc.so")
+_LIB_PATH = os.environ.get("ETPC_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib",
+                                                            "libetpc.so")
 
 ETPC_OK = 0
 UVW, UVU = 0, 1
@@ -70,7 +71,7 @@ KINDS = ("csr", "fwd_traverse", "channel_gemm", "bwd_traverse", "node_gemm", "au
 
 def _load():
     if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"{_LIB_PATH} is not built (python -m equivariant_gnn_tensor_amd.build)")
+        raise ImportError(f"{_LIB_PATH} is not built (python equivariant_gnn_tensor_amd/build.py)")
     lib = C.CDLL(_LIB_PATH)
     vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
     P = C.POINTER

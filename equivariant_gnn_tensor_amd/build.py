@@ -1,10 +1,13 @@
 """Build libetpc.so for gfx950 with hipcc (in-tree, parallel, one object per source).
 
-    python -m equivariant_gnn_tensor_amd.build [--force] [--jobs N]
+    python equivariant_gnn_tensor_amd/build.py [--force] [--jobs N]
+        [--define NAME=VALUE ...] [--build-dir DIR --lib PATH]
 
 Objects go to <repo>/_build/, the library to equivariant_gnn_tensor_amd/_lib/libetpc.so.
 Without --force, a source is recompiled only when it or any header is newer than
-its object.
+its object.  --define passes tuning macros (e.g. ETPC_BWD_PREFETCH=3) to every
+kernel source; use it with a separate --build-dir and --lib so the default
+library is left alone (the binding loads $ETPC_LIBRARY when set).
 """
 from __future__ import annotations
 
@@ -61,13 +64,13 @@ def _headers():
             + glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
-def _compile(src: str, force: bool, newest_header: float) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src: str, force: bool, newest_header: float, build_dir: str, defines) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     if not force and os.path.exists(obj):
         t = os.path.getmtime(obj)
         if t >= os.path.getmtime(src) and t >= newest_header:
             return obj
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -79,34 +82,41 @@ def _compile(src: str, force: bool, newest_header: float) -> str:
     return obj
 
 
-def build(force: bool = False, jobs: int = 0, verbose: bool = True) -> str:
+def build(force: bool = False, jobs: int = 0, verbose: bool = True, defines=(), build_dir: str = BUILD,
+          lib: str = LIB) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(os.path.abspath(lib)), exist_ok=True)
     _gen_cg_tables(force)
     srcs = _sources()
     hdr = max((os.path.getmtime(h) for h in _headers()), default=0.0)
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, force, hdr), srcs))
+        objs = list(ex.map(lambda s: _compile(s, force, hdr, build_dir, defines), srcs))
     newest = max(os.path.getmtime(o) for o in objs)
-    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < newest:
-        tmp = LIB + ".tmp"
+    if force or not os.path.exists(lib) or os.path.getmtime(lib) < newest:
+        tmp = lib + ".tmp"
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stderr)
-        os.replace(tmp, LIB)
+        os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--force", action="store_true")
     ap.add_argument("--jobs", type=int, default=0)
+    ap.add_argument("--define", action="append", default=[])
+    ap.add_argument("--build-dir", default=BUILD)
+    ap.add_argument("--lib", default=LIB)
     a = ap.parse_args()
-    build(force=a.force, jobs=a.jobs)
+    if (a.define or a.lib != LIB) and (a.build_dir == BUILD or a.lib == LIB):
+        ap.error("--define and --lib need their own --build-dir and --lib")
+    build(force=a.force, jobs=a.jobs, defines=a.define, build_dir=a.build_dir, lib=a.lib)
 
 
 if __name__ == "__main__":

@@ -47,12 +47,16 @@ struct Carver {
   }
 };
 
-int lane_width(int c, int* ntiles) {
+// Lanes per edge slot: the channel count rounded up to a power of two (whole waves above
+// 64), at least min_cp.  The sender traversals take min_cp = 16: their per-edge lane sums
+// are DPP row sums, and their 4x4x1 matrix-core updates combine groups of four lanes,
+// which must belong to one edge slot.
+int lane_width(int c, int* ntiles, int min_cp = 1) {
   if (c > kWave) {
     *ntiles = (c + kWave - 1) / kWave;
     return kWave;
   }
-  int cp = 1;
+  int cp = min_cp;
   while (cp < c) cp <<= 1;
   *ntiles = 1;
   return cp;
@@ -516,7 +520,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.z_dim = static_cast<int32_t>(p->z_dim);
         a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
         int ntiles = 1;
-        a.cp = lane_width(pi.c_out, &ntiles);
+        a.cp = lane_width(pi.c_out, &ntiles, 16);
         a.c_out = pi.c_out;
         a.ls = pi.l_sh;
         a.ld_state = ncols;
@@ -599,7 +603,7 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
     a.z_dim = static_cast<int32_t>(p->z_dim);
     a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
     int ntiles = 1;
-    a.cp = lane_width(pi.c_in, &ntiles);
+    a.cp = lane_width(pi.c_in, &ntiles, 16);
     a.c = pi.c_in;
     a.ls = pi.l_sh;
     a.xbar_accumulate = (R.x_acc || seen[pi.in_block]) ? 1 : 0;

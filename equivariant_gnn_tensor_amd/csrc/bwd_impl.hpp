@@ -31,15 +31,16 @@ namespace bwd_detail {
 
 constexpr int kMaxTiles = 4;
 
-// Per-edge partial of a lane-distributed sum: for slots of >= 16 lanes every lane gets its
-// 16-lane row sum (the rows of a slot are combined later through LDS); narrower slots are
-// summed completely.
-__device__ inline float edge_partial_sum(float v, int cp) {
-  return cp >= 16 ? row_sum16(v) : small_slot_sum(v, cp);
-}
+// z_bar gathers kept in flight per edge slot in the sender traversals
+#ifndef ETPC_BWD_PREFETCH
+#define ETPC_BWD_PREFETCH 2
+#endif
+constexpr int kPrefetch = ETPC_BWD_PREFETCH;
 
-// rows of 16 lanes per slot that hold partial sums (1 for slots narrower than 16 lanes)
-__device__ inline int rows_per_slot(int cp) { return cp >= 16 ? cp / 16 : 1; }
+// Edge slots of the sender traversals are at least 16 lanes wide (the host rounds the
+// channel count up), so a per-edge lane sum is a DPP row sum per 16 lanes (no branch, no
+// LDS round trip) plus a sum over the cp/16 rows of the slot, done through LDS.
+__device__ inline int rows_per_slot(int cp) { return cp / 16; }
 
 typedef float f4v __attribute__((ext_vector_type(4)));
 
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   const bool wvalid = w < a.c_out;
   const int rows = rows_per_slot(cp);
   const int row_in_slot = (lane - slot * cp) >> 4;
-  const bool row_leader = cp >= 16 ? (lane & 15) == 0 : lane == slot * cp;
+  const bool row_leader = (lane & 15) == 0;
   const int q4 = lane & 3;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * NI;
   float xt[NB][NI];
@@ -172,90 +173,108 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
     }
     __syncthreads();
     const int trips = (ne + nslots - 1) / nslots;
-    float zn[NO];
-    {
-      const bool v0 = slot < ne && wvalid;
-      const float* zr = a.z_bar + static_cast<int64_t>(v0 ? s_i[slot] : 0) * a.z_dim + a.zoff + w;
+    // z_bar rows of the next kPrefetch edges of this slot are in flight while one is used
+    float zq[kPrefetch][NO];
+    // Unconditional loads from a clamped in-bounds address (no branch per load); lanes
+    // without an edge are zeroed when the row is consumed, not here, so nothing waits
+    // on the load before its own trip.
+    auto gather = [&](int t, float* dst) {
+      const int i = s_i[t < ne ? t : 0];
+      const float* zr = a.z_bar + static_cast<int64_t>(t < ne ? i : 0) * a.z_dim + a.zoff + (wvalid ? w : 0);
 #pragma unroll
-      for (int mo = 0; mo < NO; ++mo) zn[mo] = v0 ? zr[mo * a.c_out] : 0.f;
+      for (int mo = 0; mo < NO; ++mo) dst[mo] = zr[mo * a.c_out];
+    };
+#pragma unroll
+    for (int pf = 0; pf < kPrefetch; ++pf) {
+      gather(pf * nslots + slot, zq[pf]);
+      // Pass the first rows through an arithmetic op: when every value entering the
+      // loop-carried registers is a plain load, the optimizer merges them into one load
+      // at the top of the loop, which undoes the prefetch.
+#pragma unroll
+      for (int mo = 0; mo < NO; ++mo) zq[pf][mo] += 0.f;
     }
-    for (int it = 0; it < trips; ++it) {
-      const int t = it * nslots + slot;
-      const bool tvalid = t < ne;
-      const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
-      float zb[NO];
+    for (int it0 = 0; it0 < trips; it0 += kPrefetch) {
 #pragma unroll
-      for (int mo = 0; mo < NO; ++mo) zb[mo] = zn[mo];
-      {
-        const int tn = t + nslots;
-        const bool vn = tn < ne && wvalid;
-        const float* zr = a.z_bar + static_cast<int64_t>(vn ? s_i[tn] : 0) * a.z_dim + a.zoff + w;
+      for (int pf = 0; pf < kPrefetch; ++pf) {
+        // trips run in whole groups of kPrefetch (no exit inside the unrolled body, which
+        // would make the compiler copy the loop-carried registers and wait on the loads);
+        // a padding trip has t >= ne, gathers zeros and adds exact zeros
+        const int it = it0 + pf;
+        const int t = it * nslots + slot;
+        const bool tvalid = t < ne;
+        const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
+        float zb[NO];
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) zn[mo] = vn ? zr[mo * a.c_out] : 0.f;
-      }
-      float V[NI][NS];
-      cg_contract_out<LI, LS, LO>(zb, V);
-      float Q[NI], Qd[NI];
-#pragma unroll
-      for (int mi = 0; mi < NI; ++mi) {
-        float s = 0.f, sd = 0.f;
-#pragma unroll
-        for (int my = 0; my < NS; ++my) {
-          s += e[R::kY + my] * V[mi][my];
-          if constexpr (TAN) sd += e[R::kYDot + my] * V[mi][my];
-        }
-        Q[mi] = s;
-        Qd[mi] = sd;
-      }
-#pragma unroll
-      for (int qq = 0; qq < NBQ; ++qq) {
-        const float ph = e[R::kPhi + 4 * qq + q4];
-        if constexpr (NEED_P) {
-#pragma unroll
-          for (int mi = 0; mi < NI; ++mi)
-            P[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, Q[mi], P[mi][qq], 0, 0, 0);
-        }
-        if constexpr (TAN) {
-          const float phd = e[R::kPhiDot + 4 * qq + q4];
-#pragma unroll
-          for (int mi = 0; mi < NI; ++mi) {
-            Pd[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(phd, Q[mi], Pd[mi][qq], 0, 0, 0);
-            Pd[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, Qd[mi], Pd[mi][qq], 0, 0, 0);
-          }
-        }
-      }
-      if constexpr (POS) {
-        // radial part: sum_q phi'_q phi_bar_q = sum_m_in G[m_in] Q[m_in], G = sum_q phi'_q Xt[q];
-        // angular part: sum_m_sh dY[d][m_sh] Wy[m_sh], Wy = sum_m_in T[m_in] V[m_in][m_sh], T = sum_q phi_q Xt[q]
-        float srad = 0.f;
-        float wy[NS];
-#pragma unroll
-        for (int my = 0; my < NS; ++my) wy[my] = 0.f;
+        for (int mo = 0; mo < NO; ++mo) zb[mo] = (tvalid && wvalid) ? zq[pf][mo] : 0.f;
+        float V[NI][NS];
+        cg_contract_out<LI, LS, LO>(zb, V);
+        // the row is consumed: its registers take the gather kPrefetch trips ahead (no
+        // register copy, so nothing waits for that load until its own trip); the
+        // scheduling barrier keeps the loads here instead of sunk to the loop end
+        gather(t + kPrefetch * nslots, zq[pf]);
+        __builtin_amdgcn_sched_barrier(0);
+        float Q[NI], Qd[NI];
 #pragma unroll
         for (int mi = 0; mi < NI; ++mi) {
-          float tq = 0.f, gq = 0.f;
+          float s = 0.f, sd = 0.f;
 #pragma unroll
-          for (int q = 0; q < NB; ++q) {
-            tq += e[R::kPhi + q] * xt[q][mi];
-            gq += e[R::kDphi + q] * xt[q][mi];
+          for (int my = 0; my < NS; ++my) {
+            s += e[R::kY + my] * V[mi][my];
+            if constexpr (TAN) sd += e[R::kYDot + my] * V[mi][my];
           }
-          srad += gq * Q[mi];
-#pragma unroll
-          for (int my = 0; my < NS; ++my) wy[my] += tq * V[mi][my];
+          Q[mi] = s;
+          Qd[mi] = sd;
         }
-        float rb[3];
 #pragma unroll
-        for (int d = 0; d < 3; ++d) {
-          float s = 0.f;
+        for (int qq = 0; qq < NBQ; ++qq) {
+          const float ph = e[R::kPhi + 4 * qq + q4];
+          if constexpr (NEED_P) {
 #pragma unroll
-          for (int my = 0; my < NS; ++my) s += e[R::kDY + d * NS + my] * wy[my];
-          rb[d] = s;
+            for (int mi = 0; mi < NI; ++mi)
+              P[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, Q[mi], P[mi][qq], 0, 0, 0);
+          }
+          if constexpr (TAN) {
+            const float phd = e[R::kPhiDot + 4 * qq + q4];
+#pragma unroll
+            for (int mi = 0; mi < NI; ++mi) {
+              Pd[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(phd, Q[mi], Pd[mi][qq], 0, 0, 0);
+              Pd[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, Qd[mi], Pd[mi][qq], 0, 0, 0);
+            }
+          }
         }
-        float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+        if constexpr (POS) {
+          // radial part: sum_q phi'_q phi_bar_q = sum_m_in G[m_in] Q[m_in], G = sum_q phi'_q Xt[q];
+          // angular part: sum_m_sh dY[d][m_sh] Wy[m_sh], Wy = sum_m_in T[m_in] V[m_in][m_sh], T = sum_q phi_q Xt[q]
+          float srad = 0.f;
+          float wy[NS];
 #pragma unroll
-        for (int d = 0; d < 3; ++d) {
-          const float v = edge_partial_sum(srad * e[R::kU + d] + rb[d], cp);
-          if (tvalid && row_leader) sr[d] = v;
+          for (int my = 0; my < NS; ++my) wy[my] = 0.f;
+#pragma unroll
+          for (int mi = 0; mi < NI; ++mi) {
+            float tq = 0.f, gq = 0.f;
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+              tq += e[R::kPhi + q] * xt[q][mi];
+              gq += e[R::kDphi + q] * xt[q][mi];
+            }
+            srad += gq * Q[mi];
+#pragma unroll
+            for (int my = 0; my < NS; ++my) wy[my] += tq * V[mi][my];
+          }
+          float rb[3];
+#pragma unroll
+          for (int d = 0; d < 3; ++d) {
+            float s = 0.f;
+#pragma unroll
+            for (int my = 0; my < NS; ++my) s += e[R::kDY + d * NS + my] * wy[my];
+            rb[d] = s;
+          }
+          float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+#pragma unroll
+          for (int d = 0; d < 3; ++d) {
+            const float v = row_sum16(srad * e[R::kU + d] + rb[d]);
+            if (tvalid && row_leader) sr[d] = v;
+          }
         }
       }
     }
@@ -328,7 +347,7 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
   const bool uvalid = u < a.c;
   const int rows = rows_per_slot(cp);
   const int row_in_slot = (lane - slot * cp) >> 4;
-  const bool row_leader = cp >= 16 ? (lane & 15) == 0 : lane == slot * cp;
+  const bool row_leader = (lane & 15) == 0;
   const bool want_pos = POS && a.rbar != nullptr;
   float wv[NB], wbar[NB];
 #pragma unroll
@@ -426,7 +445,7 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
           float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
 #pragma unroll
           for (int d = 0; d < 3; ++d) {
-            const float v = edge_partial_sum(srad * e[R::kU + d] + we * rb[d], cp);
+            const float v = row_sum16(srad * e[R::kU + d] + we * rb[d]);
             if (tvalid && row_leader) sr[d] = v;
           }
         }
@@ -483,7 +502,7 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
 template <int LI, int LS, int LO, bool NEED_P, bool POS, bool TAN>
 hipError_t bwd_uvw_nb(const BwdUvwArgs& a, int nsend, int ntiles, hipStream_t s) {
   dim3 grid(nsend), block(64 * ntiles);
-  const int rows = a.cp >= 16 ? a.cp / 16 : 1;
+  const int rows = a.cp / 16;
   const size_t dyn = POS ? sizeof(float) * 64 * 3 * rows * ntiles : 0;
   if (a.g.nb <= 8)
     hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 2, NEED_P, POS, TAN>), grid, block, dyn, s, a);
@@ -495,7 +514,7 @@ hipError_t bwd_uvw_nb(const BwdUvwArgs& a, int nsend, int ntiles, hipStream_t s)
 template <int LI, int LS, int LO, bool TAN>
 hipError_t bwd_uvu_nb(const BwdUvuArgs& a, int nblocks, int ntiles, hipStream_t s) {
   dim3 grid(nblocks), block(64 * ntiles);
-  const int rows = a.cp >= 16 ? a.cp / 16 : 1;
+  const int rows = a.cp / 16;
   const size_t dyn = sizeof(float) * 64 * 3 * rows * ntiles;
   if (a.g.nb <= 8)
     hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 2, TAN>), grid, block, dyn, s, a);

@@ -23,6 +23,12 @@
 namespace etpc {
 namespace fwd_detail {
 
+// sender-row gathers kept in flight per edge slot
+#ifndef ETPC_FWD_PREFETCH
+#define ETPC_FWD_PREFETCH 2
+#endif
+constexpr int kPrefetch = ETPC_FWD_PREFETCH;
+
 // LDS per edge: phi[NB], (dphi[NB]), cY[NI*NO], (dcY[NI*NO]), padded by one float.
 template <int NB, int CY, bool TANGENT>
 struct EdgeLds {
@@ -109,24 +115,40 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
       s_j[lane] = j;
     }
     __syncthreads();
-    if (uvalid && slot < ne) {
-      // gathered sender rows, one edge ahead
-      float xn[NI];
-      {
-        const float* xr = a.x + static_cast<int64_t>(s_j[slot]) * a.x_dim + a.xoff + u;
+    const int trips = (ne + nslots - 1) / nslots;
+    // sender rows of the next kPrefetch edges of this slot are in flight while one is used
+    float xq[kPrefetch][NI];
+    // Unconditional loads from a clamped in-bounds address (no branch per load); lanes
+    // without an edge are zeroed when the row is consumed, not here, so nothing waits
+    // on the load before its own trip.
+    auto gather = [&](int t, float* dst) {
+      const int j = s_j[t < ne ? t : 0];
+      const float* xr = a.x + static_cast<int64_t>(t < ne ? j : 0) * a.x_dim + a.xoff + (uvalid ? u : 0);
 #pragma unroll
-        for (int mi = 0; mi < NI; ++mi) xn[mi] = xr[mi * a.c_in];
-      }
-      for (int t = slot; t < ne; t += nslots) {
-        const float* e = s_edge + t * L::kStride;
+      for (int mi = 0; mi < NI; ++mi) dst[mi] = xr[mi * a.c_in];
+    };
+#pragma unroll
+    for (int pf = 0; pf < kPrefetch; ++pf) {
+      gather(pf * nslots + slot, xq[pf]);
+      // Pass the first rows through an arithmetic op: when every value entering the
+      // loop-carried registers is a plain load, the optimizer merges them into one load
+      // at the top of the loop, which undoes the prefetch.
+#pragma unroll
+      for (int mi = 0; mi < NI; ++mi) xq[pf][mi] += 0.f;
+    }
+    for (int it0 = 0; it0 < trips; it0 += kPrefetch) {
+#pragma unroll
+      for (int pf = 0; pf < kPrefetch; ++pf) {
+        // trips run in whole groups of kPrefetch (no exit inside the unrolled body, which
+        // would make the compiler copy the loop-carried registers and wait on the loads);
+        // a padding trip has t >= ne, gathers zeros and adds exact zeros
+        const int it = it0 + pf;
+        const int t = it * nslots + slot;
+        const float* e = s_edge + (t < ne ? t : 0) * L::kStride;
+        const bool tv = t < ne && uvalid;
         float xv[NI];
 #pragma unroll
-        for (int mi = 0; mi < NI; ++mi) xv[mi] = xn[mi];
-        if (t + nslots < ne) {
-          const float* xr = a.x + static_cast<int64_t>(s_j[t + nslots]) * a.x_dim + a.xoff + u;
-#pragma unroll
-          for (int mi = 0; mi < NI; ++mi) xn[mi] = xr[mi * a.c_in];
-        }
+        for (int mi = 0; mi < NI; ++mi) xv[mi] = tv ? xq[pf][mi] : 0.f;
         float cm[NO], cmd[NO];
 #pragma unroll
         for (int mo = 0; mo < NO; ++mo) {
@@ -139,6 +161,11 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
           cm[mo] = s;
           cmd[mo] = sd;
         }
+        // the row is consumed: its registers take the gather kPrefetch trips ahead (no
+        // register copy, so nothing waits for that load until its own trip); the
+        // scheduling barrier keeps the loads here instead of sunk to the loop end
+        gather(t + kPrefetch * nslots, xq[pf]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
           const float ph = e[L::kPhi + q];

@@ -19,11 +19,4 @@ __device__ inline float row_sum16(float v) {
   return v;
 }
 
-// Sum over the cp consecutive lanes of a slot (cp a power of two <= 16); every lane of
-// the slot receives the sum.
-__device__ inline float small_slot_sum(float v, int cp) {
-  for (int off = 1; off < cp; off <<= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
 }  // namespace etpc

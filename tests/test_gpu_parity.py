@@ -211,3 +211,43 @@ def test_isolated_nodes_and_empty_graph():
     torch.cuda.synchronize()
     assert torch.count_nonzero(z) == 0 and torch.count_nonzero(xb) == 0
     assert torch.count_nonzero(wb) == 0 and torch.count_nonzero(pb) == 0
+
+
+# ---------------------------------------------------------------- ragged channel counts
+# Multiplicities below 4 (slots narrower than a matrix-core lane group), odd widths, and
+# widths above one wave with a ragged last tile; 12 radial bases (partial basis quads).
+RAGGED = [
+    ("uvw_small", "cfg5", dict(irreps_in="3x0e+1x1o+2x2e+1x3o", irreps_out="2x0e+1x1o+5x2e+1x3o")),
+    ("uvw_wide", "cfg5", dict(irreps_in="70x0e+65x1o", irreps_out="33x0e+66x1o+1x2e", lmax_sh=2, n_basis=12)),
+    ("uvu_small", "cfg3", dict(irreps_in="1x0e+3x1o+2x2e+5x3o")),
+    ("uvu_wide", "cfg3", dict(irreps_in="70x0e+129x1o", lmax_sh=2, n_basis=12)),
+]
+
+
+@pytest.mark.parametrize("tag,base,kw", RAGGED, ids=[r[0] for r in RAGGED])
+def test_ragged_channels(tag, base, kw):
+    etpc = _etpc()
+    cfg = dataclasses.replace(small_variant(base, 128), name=f"ragged_{tag}", **kw)
+    if cfg.mode == "uvu":
+        cfg = dataclasses.replace(cfg, irreps_out="0e+1o+2e+3o" if cfg.lmax_sh == 3 else "0e+1o+2e")
+    note(f"ragged {tag}: {cfg.irreps_in} -> {cfg.irreps_out}")
+    c = make_case(cfg)
+    wl = c.wl
+    z = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w)
+    xb, wb, pb = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar)
+    torch.cuda.synchronize()
+    rz = conv.forward(c.spec, wl.x, wl.pos, wl.w, wl.src, wl.dst)
+    rx, rw, rp = conv.backward(c.spec, wl.x, wl.pos, wl.w, wl.src, wl.dst, wl.z_bar)
+    errs = [rel_err(z, rz), rel_err(xb, rx), rel_err(wb, rw), rel_err(pb, rp)]
+    note(f"  fwd/bwd rel err {['%.2e' % e for e in errs]}")
+    assert max(errs) <= TOL
+    rng = np.random.default_rng(5)
+    pd = rng.standard_normal(wl.pos.shape).astype(np.float32)
+    xd = rng.standard_normal(wl.x.shape).astype(np.float32)
+    T = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
+    gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, x_dot=T(xd), pos_dot=T(pd))
+    torch.cuda.synchronize()
+    r = conv.double_backward(c.spec, wl.x, wl.pos, wl.w, wl.src, wl.dst, wl.z_bar, x_dot=xd, pos_dot=pd)
+    derrs = [rel_err(gz, r[0]), rel_err(gx, r[1]), rel_err(gw, r[2])]
+    note(f"  double backward rel err {['%.2e' % e for e in derrs]}")
+    assert max(derrs) <= TOL_DBL
