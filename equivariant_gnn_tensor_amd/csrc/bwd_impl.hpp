@@ -374,79 +374,84 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
       }
       __syncthreads();
       const int trips = (ne + nslots - 1) / nslots;
-      float zn[NO];
-      {
-        const bool v0 = slot < ne && uvalid;
-        const float* zr = a.z_bar + static_cast<int64_t>(v0 ? s_i[slot] : 0) * a.z_dim + a.zoff + u;
+      // same software pipeline as the uvw sender traversal
+      float zq[kPrefetch][NO];
+      auto gather = [&](int t, float* dst) {
+        const int i = s_i[t < ne ? t : 0];
+        const float* zr = a.z_bar + static_cast<int64_t>(t < ne ? i : 0) * a.z_dim + a.zoff + (uvalid ? u : 0);
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) zn[mo] = v0 ? zr[mo * a.c] : 0.f;
+        for (int mo = 0; mo < NO; ++mo) dst[mo] = zr[mo * a.c];
+      };
+#pragma unroll
+      for (int pf = 0; pf < kPrefetch; ++pf) {
+        gather(pf * nslots + slot, zq[pf]);
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo) zq[pf][mo] += 0.f;   // not a plain load
       }
-      for (int it = 0; it < trips; ++it) {
-        const int t = it * nslots + slot;
-        const bool tvalid = t < ne;
-        const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
-        float zb[NO];
+      for (int it0 = 0; it0 < trips; it0 += kPrefetch) {
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) zb[mo] = zn[mo];
-        {
-          const int tn = t + nslots;
-          const bool vn = tn < ne && uvalid;
-          const float* zr = a.z_bar + static_cast<int64_t>(vn ? s_i[tn] : 0) * a.z_dim + a.zoff + u;
+        for (int pf = 0; pf < kPrefetch; ++pf) {
+          const int t = (it0 + pf) * nslots + slot;
+          const bool tvalid = t < ne;
+          const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
+          float zb[NO];
 #pragma unroll
-          for (int mo = 0; mo < NO; ++mo) zn[mo] = vn ? zr[mo * a.c] : 0.f;
-        }
-        float V[NI][NS];
-        cg_contract_out<LI, LS, LO>(zb, V);
-        float Q[NI], Qd[NI];
-        float h = 0.f, hd = 0.f;
+          for (int mo = 0; mo < NO; ++mo) zb[mo] = (tvalid && uvalid) ? zq[pf][mo] : 0.f;
+          gather(t + kPrefetch * nslots, zq[pf]);
+          __builtin_amdgcn_sched_barrier(0);
+          float V[NI][NS];
+          cg_contract_out<LI, LS, LO>(zb, V);
+          float Q[NI], Qd[NI];
+          float h = 0.f, hd = 0.f;
 #pragma unroll
-        for (int mi = 0; mi < NI; ++mi) {
-          float s = 0.f, sd = 0.f;
+          for (int mi = 0; mi < NI; ++mi) {
+            float s = 0.f, sd = 0.f;
 #pragma unroll
-          for (int my = 0; my < NS; ++my) {
-            s += e[R::kY + my] * V[mi][my];
-            if constexpr (TAN) sd += e[R::kYDot + my] * V[mi][my];
+            for (int my = 0; my < NS; ++my) {
+              s += e[R::kY + my] * V[mi][my];
+              if constexpr (TAN) sd += e[R::kYDot + my] * V[mi][my];
+            }
+            Q[mi] = s;
+            Qd[mi] = sd;
+            h += xj[mi] * s;
+            hd += xj[mi] * sd;
           }
-          Q[mi] = s;
-          Qd[mi] = sd;
-          h += xj[mi] * s;
-          hd += xj[mi] * sd;
-        }
-        float we = 0.f, wed = 0.f, wdr = 0.f;
+          float we = 0.f, wed = 0.f, wdr = 0.f;
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-          we += e[R::kPhi + q] * wv[q];
-          if constexpr (TAN) wed += e[R::kPhiDot + q] * wv[q];
-          wdr += e[R::kDphi + q] * wv[q];
-        }
-#pragma unroll
-        for (int mi = 0; mi < NI; ++mi) xb[mi] += TAN ? (wed * Q[mi] + we * Qd[mi]) : we * Q[mi];
-#pragma unroll
-        for (int q = 0; q < NB; ++q)
-          wbar[q] += TAN ? (e[R::kPhiDot + q] * h + e[R::kPhi + q] * hd) : e[R::kPhi + q] * h;
-        if (want_pos) {
-          const float srad = wdr * h;
-          float wy[NS];
-#pragma unroll
-          for (int my = 0; my < NS; ++my) {
-            float s = 0.f;
-#pragma unroll
-            for (int mi = 0; mi < NI; ++mi) s += xj[mi] * V[mi][my];
-            wy[my] = s;
+          for (int q = 0; q < NB; ++q) {
+            we += e[R::kPhi + q] * wv[q];
+            if constexpr (TAN) wed += e[R::kPhiDot + q] * wv[q];
+            wdr += e[R::kDphi + q] * wv[q];
           }
-          float rb[3];
 #pragma unroll
-          for (int d = 0; d < 3; ++d) {
-            float s = 0.f;
+          for (int mi = 0; mi < NI; ++mi) xb[mi] += TAN ? (wed * Q[mi] + we * Qd[mi]) : we * Q[mi];
 #pragma unroll
-            for (int my = 0; my < NS; ++my) s += e[R::kDY + d * NS + my] * wy[my];
-            rb[d] = s;
-          }
-          float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+          for (int q = 0; q < NB; ++q)
+            wbar[q] += TAN ? (e[R::kPhiDot + q] * h + e[R::kPhi + q] * hd) : e[R::kPhi + q] * h;
+          if (want_pos) {
+            const float srad = wdr * h;
+            float wy[NS];
 #pragma unroll
-          for (int d = 0; d < 3; ++d) {
-            const float v = row_sum16(srad * e[R::kU + d] + we * rb[d]);
-            if (tvalid && row_leader) sr[d] = v;
+            for (int my = 0; my < NS; ++my) {
+              float s = 0.f;
+#pragma unroll
+              for (int mi = 0; mi < NI; ++mi) s += xj[mi] * V[mi][my];
+              wy[my] = s;
+            }
+            float rb[3];
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+              float s = 0.f;
+#pragma unroll
+              for (int my = 0; my < NS; ++my) s += e[R::kDY + d * NS + my] * wy[my];
+              rb[d] = s;
+            }
+            float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+              const float v = row_sum16(srad * e[R::kU + d] + we * rb[d]);
+              if (tvalid && row_leader) sr[d] = v;
+            }
           }
         }
       }

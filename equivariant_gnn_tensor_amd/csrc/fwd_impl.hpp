@@ -225,23 +225,33 @@ __global__ __launch_bounds__(64) void fwd_uvu_kernel(const FwdUvuArgs a) {
       s_j[lane] = j;
     }
     __syncthreads();
-    if (uvalid && slot < ne) {
-      float xn[NI];
-      {
-        const float* xr = a.x + static_cast<int64_t>(s_j[slot]) * a.x_dim + a.xoff + u;
+    const int trips = (ne + nslots - 1) / nslots;
+    float xq[kPrefetch][NI];
+    // same software pipeline as the uvw traversal: clamped unconditional loads, rows
+    // zeroed when consumed, whole groups of kPrefetch trips
+    auto gather = [&](int t, float* dst) {
+      const int j = s_j[t < ne ? t : 0];
+      const float* xr = a.x + static_cast<int64_t>(t < ne ? j : 0) * a.x_dim + a.xoff + (uvalid ? u : 0);
 #pragma unroll
-        for (int mi = 0; mi < NI; ++mi) xn[mi] = xr[mi * a.c];
-      }
-      for (int t = slot; t < ne; t += nslots) {
-        const float* e = s_edge + t * L::kStride;
+      for (int mi = 0; mi < NI; ++mi) dst[mi] = xr[mi * a.c];
+    };
+#pragma unroll
+    for (int pf = 0; pf < kPrefetch; ++pf) {
+      gather(pf * nslots + slot, xq[pf]);
+#pragma unroll
+      for (int mi = 0; mi < NI; ++mi) xq[pf][mi] += 0.f;   // not a plain load (see above)
+    }
+    for (int it0 = 0; it0 < trips; it0 += kPrefetch) {
+#pragma unroll
+      for (int pf = 0; pf < kPrefetch; ++pf) {
+        const int t = (it0 + pf) * nslots + slot;
+        const bool tv = t < ne && uvalid;
+        const float* e = s_edge + (t < ne ? t : 0) * L::kStride;
         float xv[NI];
 #pragma unroll
-        for (int mi = 0; mi < NI; ++mi) xv[mi] = xn[mi];
-        if (t + nslots < ne) {
-          const float* xr = a.x + static_cast<int64_t>(s_j[t + nslots]) * a.x_dim + a.xoff + u;
-#pragma unroll
-          for (int mi = 0; mi < NI; ++mi) xn[mi] = xr[mi * a.c];
-        }
+        for (int mi = 0; mi < NI; ++mi) xv[mi] = tv ? xq[pf][mi] : 0.f;
+        gather(t + kPrefetch * nslots, xq[pf]);
+        __builtin_amdgcn_sched_barrier(0);
         float we = 0.f, wed = 0.f;
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
