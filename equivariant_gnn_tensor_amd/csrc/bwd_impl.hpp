@@ -36,6 +36,9 @@ constexpr int kMaxTiles = 4;
 #define ETPC_BWD_PREFETCH 2
 #endif
 constexpr int kPrefetch = ETPC_BWD_PREFETCH;
+// What may cross the scheduling barrier placed after each pipelined gather: LDS reads and
+// writes (0x80 | 0x100 | 0x200), so record reads can be hoisted; global loads never.
+constexpr int kSchedMask = 0x380;
 
 // Edge slots of the sender traversals are at least 16 lanes wide (the host rounds the
 // channel count up), so a per-edge lane sum is a DPP row sum per 16 lanes (no branch, no
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
         // register copy, so nothing waits for that load until its own trip); the
         // scheduling barrier keeps the loads here instead of sunk to the loop end
         gather(t + kPrefetch * nslots, zq[pf]);
-        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(kSchedMask);
         float Q[NI], Qd[NI];
 #pragma unroll
         for (int mi = 0; mi < NI; ++mi) {
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
 #pragma unroll
           for (int mo = 0; mo < NO; ++mo) zb[mo] = (tvalid && uvalid) ? zq[pf][mo] : 0.f;
           gather(t + kPrefetch * nslots, zq[pf]);
-          __builtin_amdgcn_sched_barrier(0);
+          __builtin_amdgcn_sched_barrier(kSchedMask);
           float V[NI][NS];
           cg_contract_out<LI, LS, LO>(zb, V);
           float Q[NI], Qd[NI];
