@@ -201,8 +201,8 @@ int64_t pick_chunk(int64_t n, size_t ws_bytes, F bytes_of) {
   return std::max<int64_t>(c, 1);
 }
 
-RowMap plain(int64_t ld) { return RowMap{ld, 0, 1}; }
-RowMap irmul(int32_t m, int64_t width, int64_t mul) { return RowMap{width, mul, m}; }
+RowMap plain(int64_t ld) { return make_rowmap(ld, 0, 1); }
+RowMap irmul(int32_t m, int64_t width, int64_t mul) { return make_rowmap(width, mul, m); }
 
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }

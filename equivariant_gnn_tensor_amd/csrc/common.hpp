@@ -21,7 +21,20 @@ struct RowMap {
   int64_t s1;
   int64_t s2;
   int32_t div;
+  uint32_t magic;   // r / div = (umulhi(r, magic) + r) >> shift for 0 <= r < 2^31
+  int32_t shift;
 };
+
+// Row map for row r = (r / div, r % div) -> (r / div) * s1 + (r % div) * s2, with the
+// division by an invariant integer done as a multiply-high (round-up method: shift =
+// ceil(log2 div), magic = floor(2^32 (2^shift - div) / div) + 1).
+inline RowMap make_rowmap(int64_t s1, int64_t s2, int32_t div) {
+  int32_t l = 0;
+  while ((int64_t{1} << l) < div) ++l;
+  const uint64_t magic = ((uint64_t{1} << 32) * ((uint64_t{1} << l) - static_cast<uint64_t>(div))) /
+                             static_cast<uint64_t>(div) + 1;
+  return RowMap{s1, s2, div, static_cast<uint32_t>(magic), l};
+}
 
 // Edge geometry parameters shared by every traversal kernel.
 struct GeomParams {

@@ -18,7 +18,7 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 constexpr int BM = 64, BN = 64, BK = 32;
 
 __device__ inline int64_t rowoff(const RowMap& m, int r) {
-  const int q = r / m.div;
+  const int q = static_cast<int>((__umulhi(static_cast<uint32_t>(r), m.magic) + static_cast<uint32_t>(r)) >> m.shift);
   return static_cast<int64_t>(q) * m.s1 + static_cast<int64_t>(r - q * m.div) * m.s2;
 }
 
