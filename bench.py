@@ -90,6 +90,8 @@ def kernel_source_hash(kind):
     for f in files:
         with open(os.path.join(ROOT, "equivariant_gnn_tensor_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(ROOT, "equivariant_gnn_tensor_amd", "build.py"), "rb") as fh:   # compiler flags
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

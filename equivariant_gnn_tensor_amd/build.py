@@ -1,7 +1,7 @@
 """Build libetpc.so for gfx950 with hipcc (in-tree, parallel, one object per source).
 
     python equivariant_gnn_tensor_amd/build.py [--force] [--jobs N]
-        [--define NAME=VALUE ...] [--build-dir DIR --lib PATH]
+        [--define NAME=VALUE ...] [--flag HIPCC_FLAG ...] [--build-dir DIR --lib PATH]
 
 Objects go to <repo>/_build/, the library to equivariant_gnn_tensor_amd/_lib/libetpc.so.
 Without --force, a source is recompiled only when it or any header is newer than
@@ -29,6 +29,9 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results and accumulators in ordinary VGPRs: the traversals read their
+    # 4x4x1 results with VALU code, and AGPR<->VGPR copies cost more than they save
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 
@@ -64,13 +67,13 @@ def _headers():
             + glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
-def _compile(src: str, force: bool, newest_header: float, build_dir: str, defines) -> str:
+def _compile(src: str, force: bool, newest_header: float, build_dir: str, defines, extra=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     if not force and os.path.exists(obj):
         t = os.path.getmtime(obj)
         if t >= os.path.getmtime(src) and t >= newest_header:
             return obj
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -83,7 +86,7 @@ def _compile(src: str, force: bool, newest_header: float, build_dir: str, define
 
 
 def build(force: bool = False, jobs: int = 0, verbose: bool = True, defines=(), build_dir: str = BUILD,
-          lib: str = LIB) -> str:
+          lib: str = LIB, extra=()) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(build_dir, exist_ok=True)
     os.makedirs(os.path.dirname(os.path.abspath(lib)), exist_ok=True)
@@ -92,7 +95,7 @@ def build(force: bool = False, jobs: int = 0, verbose: bool = True, defines=(), 
     hdr = max((os.path.getmtime(h) for h in _headers()), default=0.0)
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, force, hdr, build_dir, defines), srcs))
+        objs = list(ex.map(lambda s: _compile(s, force, hdr, build_dir, defines, extra), srcs))
     newest = max(os.path.getmtime(o) for o in objs)
     if force or not os.path.exists(lib) or os.path.getmtime(lib) < newest:
         tmp = lib + ".tmp"
@@ -113,10 +116,11 @@ def main():
     ap.add_argument("--define", action="append", default=[])
     ap.add_argument("--build-dir", default=BUILD)
     ap.add_argument("--lib", default=LIB)
+    ap.add_argument("--flag", action="append", default=[], help="extra hipcc flag for every kernel source")
     a = ap.parse_args()
-    if (a.define or a.lib != LIB) and (a.build_dir == BUILD or a.lib == LIB):
-        ap.error("--define and --lib need their own --build-dir and --lib")
-    build(force=a.force, jobs=a.jobs, defines=a.define, build_dir=a.build_dir, lib=a.lib)
+    if (a.define or a.flag or a.lib != LIB) and (a.build_dir == BUILD or a.lib == LIB):
+        ap.error("--define, --flag and --lib need their own --build-dir and --lib")
+    build(force=a.force, jobs=a.jobs, defines=a.define, build_dir=a.build_dir, lib=a.lib, extra=a.flag)
 
 
 if __name__ == "__main__":
