@@ -96,16 +96,16 @@ def kernel_source_hash(kind):
 
 
 def traffic_from_profiles(kind, workload):
-    """HBM bytes per step for one kernel kind from committed rocprofv3 counter summaries,
-    or None when absent or taken on a different kernel source."""
+    """(HBM bytes per launch, per step) for one kernel kind from the committed rocprofv3
+    counter summaries, or (None, None) when absent or taken on a different kernel build."""
     path = os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as fh:
         d = json.load(fh)
     if d.get("kernel_src_sha") != kernel_source_hash(kind):
-        return None
-    return d.get("hbm_bytes_per_step")
+        return None, None
+    return d.get("hbm_bytes_per_launch"), d.get("hbm_bytes_per_step")
 
 
 def cpu_baseline(cfg, wl, seconds):
@@ -354,7 +354,7 @@ def main():
     dom_ms = kinds[dom]["ms_per_step"]
     achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
     bound = "mfma" if dom.endswith("gemm") else "alu"
-    traffic = traffic_from_profiles(dom, args.workload)
+    traffic, traffic_step = traffic_from_profiles(dom, args.workload)
     total_tf = sum(flops.values()) / (ms * 1e-3) / 1e12
     log(f"whole step: {total_tf:.2f} TFLOP/s algorithmic ({total_tf / PEAK_FP32_TFLOPS:.1%} of fp32 peak)")
 
@@ -391,6 +391,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_FP32_TFLOPS,
             "traffic": traffic,
+            "traffic_per_step": traffic_step,
             "launches_per_step": kinds[dom]["launches_per_step"],
             "kernel_ms_per_step": dom_ms,
         },

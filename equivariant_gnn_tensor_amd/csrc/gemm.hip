@@ -4,10 +4,11 @@
 // m = S W (forward), and the node-side products of the sender-factorized
 // backward: Xt = x W, x_bar = P W^T, W_bar = x^T P.  Rows of A and C are given
 // through a RowMap so ir_mul feature blocks ((node, m) rows) are read and written
-// in place.  A 64x64 output tile per 256-thread workgroup, four wavefronts of
-// 32x32, K staged through LDS in slices of 32 with the next slice's global loads
-// in flight during the current slice's MFMAs.  Long-K products split K across
-// workgroups; the partial tiles are summed in a fixed order by a second kernel.
+// in place.  Four 32x32 wavefront blocks per 256-thread workgroup (64x64, or 128x32 /
+// 32x128 against a 32-channel side), K staged through LDS in slices of 32 with the
+// next slice's global loads in flight during the current slice's MFMAs.  Long-K
+// products split K across workgroups; the partial tiles are summed in a fixed order by
+// a second kernel.
 #include "kernels.hpp"
 
 namespace etpc {
@@ -15,7 +16,7 @@ namespace {
 
 typedef float f16v __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 64, BN = 64, BK = 32;
+constexpr int BK = 32;
 
 __device__ inline int64_t rowoff(const RowMap& m, int r) {
   const int q = static_cast<int>((__umulhi(static_cast<uint32_t>(r), m.magic) + static_cast<uint32_t>(r)) >> m.shift);
@@ -25,6 +26,7 @@ __device__ inline int64_t rowoff(const RowMap& m, int r) {
 // A(m, k) and B(k, n) tiles: each of the 256 threads moves 8 elements of A and 8 of B
 // per K slice, as two groups of 4 consecutive elements (float4 when aligned).
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
+  constexpr int BM = 64, BN = 64;
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -133,6 +135,120 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
   }
 }
 
+// The same scheme with the four wavefronts arranged WGM x WGN (4 x 1 or 1 x 4): 128 x 32 or
+// 32 x 128 tiles for products with a 32-channel side.
+// Per K slice each thread moves groups of 4 consecutive elements of A and B (float4 when
+// aligned): BM / 32 groups of A and BN / 32 of B.
+template <int WGM, int WGN>
+__global__ __launch_bounds__(256) void gemm_f32_narrow_kernel(const GemmArgs a) {
+  constexpr int BM = 32 * WGM, BN = 32 * WGN;
+  constexpr int AG = BM / 32, BG = BN / 32;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid % WGM, wn = wid / WGM;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int kz0 = blockIdx.z * a.k_split;
+  const int kz1 = min(a.K, kz0 + a.k_split);
+  float* C = a.C + static_cast<int64_t>(blockIdx.z) * a.c_split_stride;
+  const bool vec = a.vec4 != 0;
+
+  // group h of this thread (g = tid + 256 h): K-contiguous A -> row g / 8, k4 = 4 (g % 8);
+  // m-contiguous A -> k = g / (BM / 4), m4 = 4 (g % (BM / 4)); B (k-major) -> k = g / (BN / 4),
+  // n4 = 4 (g % (BN / 4)).  Only the A row offsets are kept; the rest is recomputed.
+  int64_t a_off[AG];
+  bool a_ok[AG];
+  if (!a.a_mcontig) {
+#pragma unroll
+    for (int h = 0; h < AG; ++h) {
+      const int m = m0 + ((tid + 256 * h) >> 3);
+      a_ok[h] = m < a.M;
+      a_off[h] = a_ok[h] ? rowoff(a.amap, m) : 0;
+    }
+  }
+  float ra[AG][4], rb[BG][4];
+  auto load4 = [&](const float* p, int valid, float* dst) {
+    if (valid == 4 && vec) {
+      const float4 v = *reinterpret_cast<const float4*>(p);
+      dst[0] = v.x;
+      dst[1] = v.y;
+      dst[2] = v.z;
+      dst[3] = v.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[t] = t < valid ? p[t] : 0.f;
+    }
+  };
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < AG; ++h) {
+      const int g = tid + 256 * h;
+      if (!a.a_mcontig) {
+        const int k = k0 + (g & 7) * 4;
+        load4(a.A + a_off[h] + k, a_ok[h] ? min(4, kz1 - k) : 0, ra[h]);
+      } else {
+        const int k = k0 + g / (BM / 4);
+        const int m = m0 + (g % (BM / 4)) * 4;
+        const int valid = k < kz1 ? min(4, a.M - m) : 0;
+        load4(a.A + (valid > 0 ? rowoff(a.amap, k) : 0) + m, valid, ra[h]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < BG; ++h) {
+      const int g = tid + 256 * h;
+      const int k = k0 + g / (BN / 4);
+      const int n = n0 + (g % (BN / 4)) * 4;
+      const int valid = k < kz1 ? min(4, a.N - n) : 0;
+      load4(a.B + static_cast<int64_t>(k < kz1 ? k : 0) * a.ldb + n, valid, rb[h]);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int h = 0; h < AG; ++h) {
+      const int g = tid + 256 * h;
+      if (!a.a_mcontig) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) As[(g & 7) * 4 + t][g >> 3] = ra[h][t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) As[g / (BM / 4)][(g % (BM / 4)) * 4 + t] = ra[h][t];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < BG; ++h) {
+      const int g = tid + 256 * h;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Bs[g / (BN / 4)][(g % (BN / 4)) * 4 + t] = rb[h][t];
+    }
+  };
+
+  f16v acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  if (kz0 < kz1) load(kz0);
+  const int am = wm * 32 + (lane & 31), bn = wn * 32 + (lane & 31), kh = lane >> 5;
+  for (int k0 = kz0; k0 < kz1; k0 += BK) {
+    store();
+    __syncthreads();
+    if (k0 + BK < kz1) load(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + kh][am], Bs[kk + kh][bn], acc, 0, 0, 0);
+    __syncthreads();
+  }
+  const int n = n0 + wn * 32 + (lane & 31);
+  if (n < a.N) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (m < a.M) {
+        float* p = C + rowoff(a.cmap, m) + n;
+        *p = a.beta ? (*p + acc[r]) : acc[r];
+      }
+    }
+  }
+}
+
 // C(m, n) (+)= sum_s part[s][m][n], fixed order in s
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, float* __restrict__ C,
                                      RowMap cmap, int beta) {
@@ -152,8 +268,18 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 
 hipError_t launch_gemm(const GemmArgs& a, int splits, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  dim3 grid((a.M + BM - 1) / BM, (a.N + BN - 1) / BN, splits), block(256);
-  hipLaunchKernelGGL(gemm_f32_kernel, grid, block, 0, s, a);
+  // a side of at most 32 (a 32-channel operand) gets a 32-wide tile, so no half tile of
+  // MFMA work and loads is wasted on padding
+  if (a.N <= 32 && a.M > 32) {
+    dim3 grid((a.M + 127) / 128, (a.N + 31) / 32, splits);
+    hipLaunchKernelGGL((gemm_f32_narrow_kernel<4, 1>), grid, dim3(256), 0, s, a);
+  } else if (a.M <= 32 && a.N > 32) {
+    dim3 grid((a.M + 31) / 32, (a.N + 127) / 128, splits);
+    hipLaunchKernelGGL((gemm_f32_narrow_kernel<1, 4>), grid, dim3(256), 0, s, a);
+  } else {
+    dim3 grid((a.M + 63) / 64, (a.N + 63) / 64, splits);
+    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
