@@ -255,6 +255,8 @@ def main():
     ap.add_argument("--workload", default="cfg2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--workspace-mib", type=float, default=0.0,
+                    help="cap each pass's workspace (0 = the full size; smaller runs in node chunks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (counter calibration)")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
@@ -299,9 +301,12 @@ def main():
     csr_ms = (time.perf_counter() - t0) / 3 * 1e3
 
     force_step = "dbl" in cfg.passes
-    ws_f = torch.empty(etpc.etpc_workspace_size(plan, etpc.PASS_FWD, N, E), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(etpc.etpc_workspace_size(plan, etpc.PASS_BWD, N, E), dtype=torch.uint8, device=dev)
-    ws_d = (torch.empty(etpc.etpc_workspace_size(plan, etpc.PASS_DBL, N, E), dtype=torch.uint8, device=dev)
+    def ws_bytes(pass_):
+        full = etpc.etpc_workspace_size(plan, pass_, N, E)
+        return min(full, int(args.workspace_mib * 2 ** 20)) if args.workspace_mib > 0 else full
+    ws_f = torch.empty(ws_bytes(etpc.PASS_FWD), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(ws_bytes(etpc.PASS_BWD), dtype=torch.uint8, device=dev)
+    ws_d = (torch.empty(ws_bytes(etpc.PASS_DBL), dtype=torch.uint8, device=dev)
             if force_step else torch.empty(0, dtype=torch.uint8, device=dev))
     z = torch.empty(N, info["z_dim"], device=dev)
     outs = (torch.empty(N, info["x_dim"], device=dev), torch.empty(info["w_numel"], device=dev),
