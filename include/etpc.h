@@ -59,7 +59,9 @@ typedef enum {
   ETPC_ERR_INVALID_ARG = 1,   /* null required pointer, bad size, bad enum */
   ETPC_ERR_UNSUPPORTED = 2,   /* l > 3, B > 16, more than 64 paths, ... */
   ETPC_ERR_INVALID_PATH = 3,  /* instruction violates the selection rule (Eq. 5) or uvu C_out != C_in */
-  ETPC_ERR_WORKSPACE = 4,     /* workspace smaller than etpc_workspace_size() asks for */
+  ETPC_ERR_WORKSPACE = 4,     /* workspace below the minimum of a pass (one node's state plus its
+                                 fixed parts; backward adds 12 B per edge); smaller than
+                                 etpc_workspace_size() but above that minimum runs in node chunks */
   ETPC_ERR_OVERFLOW = 5,      /* N, E or an internal index would exceed int32 */
   ETPC_ERR_GRAPH = 6,         /* etpc_graph_validate found an inconsistent CSR */
   ETPC_ERR_HIP = 7            /* a HIP runtime call failed */
@@ -122,9 +124,11 @@ etpc_status etpc_plan_out_irrep(etpc_plan plan, int32_t b, int32_t* n_out, etpc_
 /* [host] dense coupling tensor of path p, [2l_in+1][2l_sh+1][2l_out+1] doubles (Eq. 32). */
 etpc_status etpc_plan_cg(etpc_plan plan, int32_t p, double* out);
 
-/* Workspace bytes a compute pass needs for a graph of n_nodes / n_edges.  Grows with
- * N (node-side states) and by 12 B per edge for backward and double backward (the
- * per-edge position adjoint); it never scales with E times a channel width. */
+/* Workspace bytes for a compute pass over a graph of n_nodes / n_edges with every node
+ * in one chunk (the fastest schedule).  Grows with N (node-side states) and by 12 B per
+ * edge for backward and double backward (the per-edge position adjoint); it never scales
+ * with E times a channel width.  A compute call given less (down to one node's state)
+ * runs the nodes in chunks that fit, with the same results up to summation order. */
 etpc_status etpc_workspace_size(etpc_plan plan, int32_t pass, int32_t n_nodes, int64_t n_edges,
                                 size_t* bytes);
 
