@@ -86,3 +86,15 @@ def test_csr_workspace_size_and_argument_errors():
     assert etpc.etpc_csr_workspace_size(10, 100) > 0
     with pytest.raises(etpc.EtpcError):
         etpc.etpc_csr_workspace_size(-1, 10)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """With the HIP library absent the package refuses to import (there is no CPU path)."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ, ETPC_LIBRARY=str(tmp_path / "absent" / "libetpc.so"))
+    r = subprocess.run([sys.executable, "-c", "import equivariant_gnn_tensor_amd"], cwd=os.path.dirname(
+        os.path.dirname(os.path.abspath(__file__))), env=env, capture_output=True, text=True)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "not built" in r.stderr
