@@ -89,7 +89,7 @@ def _load():
         "etpc_graph_validate": [P(etpc_graph), vp],
         "etpc_forward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, sz, vp],
         "etpc_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
-        "etpc_double_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "etpc_double_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_profile_enable": [i32],
         "etpc_profile_read": [i32, P(C.c_double), P(i64)],
     }
@@ -337,7 +337,8 @@ def etpc_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, want=("x", "w", "p
 
 
 def etpc_double_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, x_dot=None, w_dot=None, pos_dot=None,
-                         want=("z_bar", "x", "w"), outs=None, ws=None, stream=None):
+                         want=("z_bar", "x", "w", "pos"), outs=None, ws=None, stream=None):
+    """Returns (d/dz_bar, d/dx, d/dW, d/dpos); outputs not in ``want`` are None."""
     info = plan.info()
     dev = x.device
     if outs is None:
@@ -345,13 +346,16 @@ def etpc_double_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, x_dot=None,
             torch.empty(graph.n_nodes, info["z_dim"], dtype=torch.float32, device=dev) if "z_bar" in want else None,
             torch.empty(graph.n_nodes, info["x_dim"], dtype=torch.float32, device=dev) if "x" in want else None,
             torch.empty(info["w_numel"], dtype=torch.float32, device=dev) if "w" in want else None,
+            torch.empty(graph.n_nodes, 3, dtype=torch.float32, device=dev) if "pos" in want else None,
         )
-    gz, gx, gw = outs
+    if len(outs) == 3:
+        outs = tuple(outs) + (None,)
+    gz, gx, gw, gp = outs
     wp, wn, _keep = _ws_for(plan, PASS_DBL, graph, ws)
     _check(lib.etpc_double_backward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z_bar),
-                                    _ptr(x_dot), _ptr(w_dot), _ptr(pos_dot), _ptr(gz), _ptr(gx), _ptr(gw), wp, wn,
-                                    _stream(stream)))
-    return gz, gx, gw
+                                    _ptr(x_dot), _ptr(w_dot), _ptr(pos_dot), _ptr(gz), _ptr(gx), _ptr(gw), _ptr(gp),
+                                    wp, wn, _stream(stream)))
+    return gz, gx, gw, gp
 
 
 def etpc_profile_enable(enable: bool) -> None:

@@ -184,7 +184,7 @@ size_t bwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_
 size_t dbl_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t chunk) {
   Carver c;
   BwdLayout L;
-  bwd_layout(p, d, n_edges, chunk, false, true, true, true, true, true, true, c, L);
+  bwd_layout(p, d, n_edges, chunk, true, true, true, true, true, true, true, c, L);   // every output
   return std::max(c.off, fwd_bytes(p, d, chunk));
 }
 
@@ -390,6 +390,8 @@ struct UvwBwdReq {
   float* rbar;            // edge adjoint (first-order pass) or null
   bool tangent;           // dbl: the main state is the tangent state dP
   bool plain_needed;      // dbl: plain P needed for the x2 / w2 terms
+  bool hess;              // dbl: rbar receives the position-Hessian term along pos_dot
+  bool rbar_acc;          // add into rbar from the first path on (earlier passes wrote it)
 };
 
 void wprep_args(const etpc_plan_s* p, const Derived& d, int k, const float* w, float* wcat, float* wt, WPrepArgs& a) {
@@ -470,7 +472,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   if (R.x_out) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
   for (int64_t j0 = 0; j0 < N; j0 += chunk) {
     const int nsend = static_cast<int>(std::min<int64_t>(chunk, N - j0));
-    rbar_started = false;  // the edges of this sender chunk are first written by its first path
+    rbar_started = R.rbar_acc;  // the edges of this sender chunk are first written by its first path
     for (size_t k = 0; k < p->in.size(); ++k) {
       const auto& paths = p->by_in[k];
       if (paths.empty()) continue;
@@ -529,7 +531,8 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.g = geom;
         a.cg = pi.cgf;
         const bool np = R.tangent ? need_plain : main_state;
-        ETPC_LAUNCH(ETPC_KIND_BWD_TRAVERSE, launch_bwd_uvw(a, np, want_pos, R.tangent, pi.l_in, pi.l_out, nsend, ntiles, s));
+        ETPC_LAUNCH(ETPC_KIND_BWD_TRAVERSE,
+                    launch_bwd_uvw(a, R.hess ? false : np, want_pos, R.tangent, R.hess, pi.l_in, pi.l_out, nsend, ntiles, s));
         if (want_pos) rbar_started = true;
       }
       if (R.x_out) {
@@ -572,8 +575,10 @@ struct UvuBwdReq {
   float* w_out;
   float* rbar;
   bool tangent;
-  bool x_acc;   // accumulate into x_out from the first path on
-  bool w_acc;   // accumulate into w_out
+  bool x_acc;     // accumulate into x_out from the first path on
+  bool w_acc;     // accumulate into w_out
+  bool hess;      // rbar receives the position-Hessian term along pos_dot (no x_out / w_out)
+  bool rbar_acc;  // add into rbar from the first path on
 };
 
 etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* pos, const float* z_bar,
@@ -583,7 +588,7 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
   const int grid = static_cast<int>(std::min<int64_t>(N, kUvuGrid));
   if (R.x_out && !R.x_acc) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
   std::vector<int> seen(p->in.size(), 0);
-  bool rbar_started = false;
+  bool rbar_started = R.rbar_acc;
   for (const PathInfo& pi : p->paths) {
     BwdUvuArgs a{};
     a.s_rowptr = g->s_rowptr;
@@ -610,7 +615,7 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
     a.rbar_accumulate = rbar_started ? 1 : 0;
     a.g = geom;
     a.cg = pi.cgf;
-    ETPC_LAUNCH(ETPC_KIND_BWD_TRAVERSE, launch_bwd_uvu(a, R.tangent, pi.l_in, pi.l_out, grid, ntiles, s));
+    ETPC_LAUNCH(ETPC_KIND_BWD_TRAVERSE, launch_bwd_uvu(a, R.tangent, R.hess, pi.l_in, pi.l_out, grid, ntiles, s));
     seen[pi.in_block] = 1;
     if (R.rbar) rbar_started = true;
     if (R.w_out) {
@@ -758,8 +763,8 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
 
 etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* x, const float* pos, const float* w,
                                  const float* z_bar, const float* x_dot, const float* w_dot, const float* pos_dot,
-                                 float* z_bar_grad, float* x_grad, float* w_grad, void* ws, size_t ws_bytes,
-                                 hipStream_t s) {
+                                 float* z_bar_grad, float* x_grad, float* w_grad, float* pos_grad, void* ws,
+                                 size_t ws_bytes, hipStream_t s) {
   etpc_status st = check_common(p, g);
   if (st != ETPC_OK) return st;
   if (x == nullptr || pos == nullptr || w == nullptr || z_bar == nullptr)
@@ -771,6 +776,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     if (w_grad) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
     return ETPC_OK;
   }
+  const bool want_pos = pos_grad != nullptr;
   const Derived d = derive(p);
   const bool tan = pos_dot != nullptr;
   const bool plain = x_dot != nullptr || w_dot != nullptr;
@@ -778,7 +784,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     Carver cv;
     BwdLayout L;
     const int64_t ch = p->mode == ETPC_UVW ? c : kUvuGrid;
-    bwd_layout(p, d, g->n_edges, ch, false, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
+    bwd_layout(p, d, g->n_edges, ch, want_pos, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
                x_grad && w_dot && tan, cv, L);
     return std::max(cv.off, z_bar_grad ? fwd_bytes(p, d, c) : size_t(0));
   };
@@ -819,89 +825,146 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
       }
     }
   }
-  if (!x_grad && !w_grad) return ETPC_OK;
-  if (!tan && !plain) {
-    if (x_grad) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
-    if (w_grad) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
-    return ETPC_OK;
-  }
-  Carver cv{static_cast<char*>(ws), 0};
-  BwdLayout L;
-  const int64_t ch = p->mode == ETPC_UVW ? chunk : kUvuGrid;
-  bwd_layout(p, d, g->n_edges, ch, false, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
-             x_grad && w_dot && tan, cv, L);
-  if (p->mode == ETPC_UVW) {
-    // d/dx = W^T dP + w_dot^T P ;  d/dW = x^T dP + x_dot^T P
-    UvwBwdReq R{};
-    R.pos_dot = pos_dot;
+  // d/dx and d/dW
+  auto xw_part = [&]() -> etpc_status {
+    if (!x_grad && !w_grad) return ETPC_OK;
+    if (!tan && !plain) {
+      if (x_grad) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
+      if (w_grad) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
+      return ETPC_OK;
+    }
+    Carver cv{static_cast<char*>(ws), 0};
+    BwdLayout L;
+    const int64_t ch = p->mode == ETPC_UVW ? chunk : kUvuGrid;
+    bwd_layout(p, d, g->n_edges, ch, want_pos, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
+               x_grad && w_dot && tan, cv, L);
+    if (p->mode == ETPC_UVW) {
+      // d/dx = W^T dP + w_dot^T P ;  d/dW = x^T dP + x_dot^T P
+      UvwBwdReq R{};
+      R.pos_dot = pos_dot;
+      if (tan) {
+        R.x = x;
+        R.w = w;
+        R.x2 = x_dot;
+        R.w2 = w_dot;
+        R.tangent = true;
+        R.plain_needed = plain;
+      } else {
+        // only plain terms: x_grad = w_dot^T P, w_grad = x_dot^T P (zero where the cotangent is absent)
+        R.x = x_dot;
+        R.w = w_dot;
+        R.tangent = false;
+      }
+      R.x_out = x_grad;
+      R.w_out = w_grad;
+      if (!tan) {
+        if (x_grad && !w_dot) {
+          ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
+          R.x_out = nullptr;
+        }
+        if (w_grad && !x_dot) {
+          ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
+          R.w_out = nullptr;
+        }
+        if (!R.x_out && !R.w_out) return ETPC_OK;
+        // the plain pass reads x (for W_bar) and w (for x_bar); feed the cotangents in their place
+        R.x = x_dot ? x_dot : x;
+        R.w = w_dot ? w_dot : w;
+      }
+      return bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, s);
+    }
+    // uvu: tangent pass (pos_dot) then plain passes with w -> w_dot (x_grad) and x -> x_dot (w_grad)
+    bool xs = false, wsd = false;
     if (tan) {
+      UvuBwdReq R{};
       R.x = x;
       R.w = w;
-      R.x2 = x_dot;
-      R.w2 = w_dot;
+      R.pos_dot = pos_dot;
       R.tangent = true;
-      R.plain_needed = plain;
-    } else {
-      // only plain terms: x_grad = w_dot^T P, w_grad = x_dot^T P (zero where the cotangent is absent)
-      R.x = x_dot;
+      R.x_out = x_grad;
+      R.w_out = w_grad;
+      st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
+      if (st != ETPC_OK) return st;
+      xs = x_grad != nullptr;
+      wsd = w_grad != nullptr;
+    }
+    if (x_grad && w_dot) {
+      UvuBwdReq R{};
+      R.x = x;
       R.w = w_dot;
-      R.tangent = false;
+      R.x_out = x_grad;
+      R.x_acc = xs;
+      st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
+      if (st != ETPC_OK) return st;
+      xs = true;
     }
-    R.x_out = x_grad;
-    R.w_out = w_grad;
-    if (!tan) {
-      if (x_grad && !w_dot) {
-        ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
-        R.x_out = nullptr;
-      }
-      if (w_grad && !x_dot) {
-        ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
-        R.w_out = nullptr;
-      }
-      if (!R.x_out && !R.w_out) return ETPC_OK;
-      // the plain pass reads x (for W_bar) and w (for x_bar); feed the cotangents in their place
-      R.x = x_dot ? x_dot : x;
-      R.w = w_dot ? w_dot : w;
+    if (w_grad && x_dot) {
+      UvuBwdReq R{};
+      R.x = x_dot;
+      R.w = w;
+      R.w_out = w_grad;
+      R.w_acc = wsd;
+      st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
+      if (st != ETPC_OK) return st;
+      wsd = true;
     }
-    return bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, s);
+    if (x_grad && !xs) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
+    if (w_grad && !wsd) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
+  return ETPC_OK;
+  };
+  st = xw_part();
+  if (st != ETPC_OK) return st;
+  if (!want_pos) return ETPC_OK;
+
+  // d/dpos: pos_bar of the backward with x -> x_dot and with W -> w_dot (the x_bar and
+  // W_bar cotangents enter <z_bar, z> linearly), plus the edge Hessian H_e r_dot_e of
+  // the pos_dot term; all three accumulate into the per-edge buffer, then one segment sum.
+  if ((!tan && !plain) || g->n_edges == 0 || p->paths.empty()) {
+    ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(pos_grad, 3 * static_cast<int64_t>(N), 0.f, s));
+    return ETPC_OK;
   }
-  // uvu: tangent pass (pos_dot) then plain passes with w -> w_dot (x_grad) and x -> x_dot (w_grad)
-  bool xs = false, wsd = false;
-  if (tan) {
-    UvuBwdReq R{};
-    R.x = x;
-    R.w = w;
-    R.pos_dot = pos_dot;
-    R.tangent = true;
-    R.x_out = x_grad;
-    R.w_out = w_grad;
-    st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
+  Carver cvp{static_cast<char*>(ws), 0};
+  BwdLayout Lp;
+  const int64_t chp = p->mode == ETPC_UVW ? chunk : kUvuGrid;
+  bwd_layout(p, d, g->n_edges, chp, true, false, false, false, false, false, false, cvp, Lp);
+  bool acc = false;
+  for (int term = 0; term < 3; ++term) {
+    const float* xin = x;
+    const float* win = w;
+    bool hess = false;
+    if (term == 0) {
+      if (!x_dot) continue;
+      xin = x_dot;
+    } else if (term == 1) {
+      if (!w_dot) continue;
+      win = w_dot;
+    } else {
+      if (!tan) continue;
+      hess = true;
+    }
+    if (p->mode == ETPC_UVW) {
+      UvwBwdReq R{};
+      R.x = xin;
+      R.w = win;
+      R.pos_dot = hess ? pos_dot : nullptr;
+      R.rbar = Lp.rbar;
+      R.hess = hess;
+      R.rbar_acc = acc;
+      st = bwd_uvw_run(p, d, g, pos, z_bar, R, Lp, chunk, s);
+    } else {
+      UvuBwdReq R{};
+      R.x = xin;
+      R.w = win;
+      R.pos_dot = hess ? pos_dot : nullptr;
+      R.rbar = Lp.rbar;
+      R.hess = hess;
+      R.rbar_acc = acc;
+      st = bwd_uvu_run(p, g, pos, z_bar, R, Lp, s);
+    }
     if (st != ETPC_OK) return st;
-    xs = x_grad != nullptr;
-    wsd = w_grad != nullptr;
+    acc = true;
   }
-  if (x_grad && w_dot) {
-    UvuBwdReq R{};
-    R.x = x;
-    R.w = w_dot;
-    R.x_out = x_grad;
-    R.x_acc = xs;
-    st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
-    if (st != ETPC_OK) return st;
-    xs = true;
-  }
-  if (w_grad && x_dot) {
-    UvuBwdReq R{};
-    R.x = x_dot;
-    R.w = w;
-    R.w_out = w_grad;
-    R.w_acc = wsd;
-    st = bwd_uvu_run(p, g, pos, z_bar, R, L, s);
-    if (st != ETPC_OK) return st;
-    wsd = true;
-  }
-  if (x_grad && !xs) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(x_grad, static_cast<int64_t>(N) * p->x_dim, 0.f, s));
-  if (w_grad && !wsd) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_grad, p->w_numel, 0.f, s));
+  ETPC_LAUNCH(ETPC_KIND_AUX, launch_pos_bar(g->rowptr, g->s_rowptr, g->s_slot, Lp.rbar, pos_grad, N, s));
   return ETPC_OK;
 }
 

@@ -48,33 +48,39 @@ __device__ inline int rows_per_slot(int cp) { return cp / 16; }
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 // Compact per-edge record for the sender traversals (LDS, one per edge of a chunk):
-// phi[NB], phi'[NB] (positions), dphi[NB] (tangent), Y[NS], dY/dr[3][NS] (positions),
-// dY[NS] along pos_dot (tangent), u[3] (positions).  The coupling tensor is not stored
-// per edge: its compile-time sparse form is applied per lane (CgTab).
-template <int NB, int NS, bool POS, bool TAN>
+// phi[NB], phi'[NB] (positions), dphi[NB] along pos_dot (tangent), phi''[NB] (Hessian),
+// Y[NS], dY/dr[3][NS] (positions), dY[NS] along pos_dot (tangent, Hessian),
+// d(dY/dr)[3][NS] along pos_dot (Hessian), u[3] (positions), du[3] and d|r| along
+// pos_dot (Hessian).  The coupling tensor is not stored per edge: its compile-time
+// sparse form is applied per lane (CgTab).
+template <int NB, int NS, bool POS, bool TAN, bool HESS = false>
 struct BwdRec {
   static constexpr int kPhi = 0;
   static constexpr int kDphi = NB;
   static constexpr int kPhiDot = kDphi + (POS ? NB : 0);
-  static constexpr int kY = kPhiDot + (TAN ? NB : 0);
+  static constexpr int kDDphi = kPhiDot + (TAN ? NB : 0);
+  static constexpr int kY = kDDphi + (HESS ? NB : 0);
   static constexpr int kDY = kY + NS;
   static constexpr int kYDot = kDY + (POS ? 3 * NS : 0);
-  static constexpr int kU = kYDot + (TAN ? NS : 0);
-  static constexpr int kStride = kU + (POS ? 3 : 0) + 1;
+  static constexpr int kDDY = kYDot + ((TAN || HESS) ? NS : 0);
+  static constexpr int kU = kDDY + (HESS ? 3 * NS : 0);
+  static constexpr int kUDot = kU + (POS ? 3 : 0);
+  static constexpr int kRhoDot = kUDot + (HESS ? 3 : 0);
+  static constexpr int kStride = kRhoDot + (HESS ? 1 : 0) + 1;
 };
 
-template <int LS, int NB, bool POS, bool TAN, bool NEED_D>
+template <int LS, int NB, bool POS, bool TAN, bool NEED_D, bool HESS = false>
 __device__ inline void bwd_fill_rec(const GeomParams& g, const float* __restrict__ pos,
                                     const float* __restrict__ pos_dot, int j, int i, float* __restrict__ e) {
   constexpr int NS = 2 * LS + 1;
-  using R = BwdRec<NB, NS, POS, TAN>;
+  using R = BwdRec<NB, NS, POS, TAN, HESS>;
   float rx, ry, rz;
   edge_vector(g, pos, j, i, rx, ry, rz);
   const float r = sqrtf(rx * rx + ry * ry + rz * rz);
   const float ir = 1.f / r;
   const float ux = rx * ir, uy = ry * ir, uz = rz * ir;
-  float phi[NB], dphi[NB];
-  radial_eval<NB>(g, r, phi, NEED_D ? dphi : nullptr);
+  float phi[NB], dphi[NB], ddphi[NB];
+  radial_eval<NB>(g, r, phi, NEED_D ? dphi : nullptr, HESS ? ddphi : nullptr);
   float y[7];
   sh_eval(LS, ux, uy, uz, y);
   float gy[7][3];
@@ -83,6 +89,7 @@ __device__ inline void bwd_fill_rec(const GeomParams& g, const float* __restrict
   for (int q = 0; q < NB; ++q) {
     e[R::kPhi + q] = phi[q];
     if constexpr (POS) e[R::kDphi + q] = dphi[q];
+    if constexpr (HESS) e[R::kDDphi + q] = ddphi[q];
   }
 #pragma unroll
   for (int m = 0; m < NS; ++m) {
@@ -93,15 +100,33 @@ __device__ inline void bwd_fill_rec(const GeomParams& g, const float* __restrict
       e[R::kDY + 2 * NS + m] = gy[m][2];
     }
   }
-  if constexpr (TAN) {
+  if constexpr (TAN || HESS) {
+    // edge-vector tangent r_dot = pos_dot_sender - pos_dot_receiver (Eq. 8 differentiated)
     const float dx = pos_dot[3 * j + 0] - pos_dot[3 * i + 0];
     const float dy = pos_dot[3 * j + 1] - pos_dot[3 * i + 1];
     const float dz = pos_dot[3 * j + 2] - pos_dot[3 * i + 2];
     const float rdot = ux * dx + uy * dy + uz * dz;
+    if constexpr (TAN) {
 #pragma unroll
-    for (int q = 0; q < NB; ++q) e[R::kPhiDot + q] = dphi[q] * rdot;
+      for (int q = 0; q < NB; ++q) e[R::kPhiDot + q] = dphi[q] * rdot;
+    }
 #pragma unroll
     for (int m = 0; m < NS; ++m) e[R::kYDot + m] = gy[m][0] * dx + gy[m][1] * dy + gy[m][2] * dz;
+    if constexpr (HESS) {
+      const float udx = (dx - ux * rdot) * ir, udy = (dy - uy * rdot) * ir, udz = (dz - uz * rdot) * ir;
+      float ddy[7][3];
+      sh_grad_r_dir(LS, ux, uy, uz, ir, y, gy, udx, udy, udz, rdot, ddy);
+#pragma unroll
+      for (int m = 0; m < NS; ++m) {
+        e[R::kDDY + m] = ddy[m][0];
+        e[R::kDDY + NS + m] = ddy[m][1];
+        e[R::kDDY + 2 * NS + m] = ddy[m][2];
+      }
+      e[R::kUDot + 0] = udx;
+      e[R::kUDot + 1] = udy;
+      e[R::kUDot + 2] = udz;
+      e[R::kRhoDot] = rdot;
+    }
   }
   if constexpr (POS) {
     e[R::kU + 0] = ux;
@@ -126,11 +151,15 @@ __device__ inline void cg_contract_out(const float* __restrict__ zb, float (*__r
     }
 }
 
-// Sender traversal for one uvw path (compile-time l_in, l_sh, l_out).
-template <int LI, int LS, int LO, int NBQ, bool NEED_P, bool POS, bool TAN>
+// Sender traversal for one uvw path (compile-time l_in, l_sh, l_out).  With HESS (and
+// POS) the per-edge output is not r_bar_e but its directional derivative along
+// r_dot_e = pos_dot_sender - pos_dot_receiver, i.e. H_e r_dot_e with H_e the Hessian of the
+// edge's term of <z_bar, z> in the edge vector: the position term of double backward.
+template <int LI, int LS, int LO, int NBQ, bool NEED_P, bool POS, bool TAN, bool HESS = false>
 __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
-  using R = BwdRec<NB, NS, POS, TAN>;
+  static_assert(!HESS || (POS && !TAN && !NEED_P), "the Hessian pass is a position-only pass");
+  using R = BwdRec<NB, NS, POS, TAN, HESS>;
   __shared__ float s_edge[64 * R::kStride];
   __shared__ int s_i[64];
   __shared__ int s_sl[64];
@@ -170,7 +199,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
     const int ne = min(kWave, k1 - base);
     if (tid < ne) {
       const int i = a.s_col[base + tid];
-      bwd_fill_rec<LS, NB, POS, TAN, POS || TAN>(a.g, a.pos, a.pos_dot, j, i, s_edge + tid * R::kStride);
+      bwd_fill_rec<LS, NB, POS, TAN, POS || TAN, HESS>(a.g, a.pos, a.pos_dot, j, i, s_edge + tid * R::kStride);
       s_i[tid] = i;
       s_sl[tid] = a.s_slot[base + tid];
     }
@@ -223,7 +252,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
 #pragma unroll
           for (int my = 0; my < NS; ++my) {
             s += e[R::kY + my] * V[mi][my];
-            if constexpr (TAN) sd += e[R::kYDot + my] * V[mi][my];
+            if constexpr (TAN || HESS) sd += e[R::kYDot + my] * V[mi][my];
           }
           Q[mi] = s;
           Qd[mi] = sd;
@@ -248,34 +277,48 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
         if constexpr (POS) {
           // radial part: sum_q phi'_q phi_bar_q = sum_m_in G[m_in] Q[m_in], G = sum_q phi'_q Xt[q];
           // angular part: sum_m_sh dY[d][m_sh] Wy[m_sh], Wy = sum_m_in T[m_in] V[m_in][m_sh], T = sum_q phi_q Xt[q]
-          float srad = 0.f;
-          float wy[NS];
+          float srad = 0.f, sradd = 0.f;
+          float wy[NS], wg[NS];
 #pragma unroll
-          for (int my = 0; my < NS; ++my) wy[my] = 0.f;
+          for (int my = 0; my < NS; ++my) wy[my] = wg[my] = 0.f;
 #pragma unroll
           for (int mi = 0; mi < NI; ++mi) {
-            float tq = 0.f, gq = 0.f;
+            float tq = 0.f, gq = 0.f, g2 = 0.f;
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
               tq += e[R::kPhi + q] * xt[q][mi];
               gq += e[R::kDphi + q] * xt[q][mi];
+              if constexpr (HESS) g2 += e[R::kDDphi + q] * xt[q][mi];
             }
             srad += gq * Q[mi];
+            // Hessian pass: d srad = sum (rho_dot G2 Q + G dQ), dQ = dY . V
+            if constexpr (HESS) sradd += e[R::kRhoDot] * g2 * Q[mi] + gq * Qd[mi];
 #pragma unroll
-            for (int my = 0; my < NS; ++my) wy[my] += tq * V[mi][my];
+            for (int my = 0; my < NS; ++my) {
+              wy[my] += tq * V[mi][my];
+              if constexpr (HESS) wg[my] += gq * V[mi][my];   // dT = rho_dot G, so dWy = rho_dot Wg
+            }
           }
           float rb[3];
 #pragma unroll
           for (int d = 0; d < 3; ++d) {
             float s = 0.f;
 #pragma unroll
-            for (int my = 0; my < NS; ++my) s += e[R::kDY + d * NS + my] * wy[my];
+            for (int my = 0; my < NS; ++my) {
+              if constexpr (HESS)
+                s += e[R::kDDY + d * NS + my] * wy[my] + e[R::kRhoDot] * e[R::kDY + d * NS + my] * wg[my];
+              else
+                s += e[R::kDY + d * NS + my] * wy[my];
+            }
             rb[d] = s;
           }
           float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
 #pragma unroll
           for (int d = 0; d < 3; ++d) {
-            const float v = row_sum16(srad * e[R::kU + d] + rb[d]);
+            // r_bar = srad u + dY^T Wy; its tangent = d srad u + srad du + d(dY)^T Wy + dY^T dWy
+            const float lanev = HESS ? sradd * e[R::kU + d] + srad * e[R::kUDot + d] + rb[d]
+                                     : srad * e[R::kU + d] + rb[d];
+            const float v = row_sum16(lanev);
             if (tvalid && row_leader) sr[d] = v;
           }
         }
@@ -333,11 +376,14 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   }
 }
 
-template <int LI, int LS, int LO, int NBQ, bool TAN>
+// With HESS the per-edge output is the tangent of r_bar_e along r_dot_e (the position
+// term of double backward, as in the uvw traversal); x_bar and W_bar are not formed.
+template <int LI, int LS, int LO, int NBQ, bool TAN, bool HESS = false>
 __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
   constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
-  constexpr bool POS = !TAN;   // position adjoint only in the first-order pass
-  using R = BwdRec<NB, NS, true, TAN>;
+  constexpr bool POS = !TAN;   // position adjoint only in the first-order and Hessian passes
+  static_assert(!(HESS && TAN), "the Hessian pass has no tangent state");
+  using R = BwdRec<NB, NS, true, TAN, HESS>;
   __shared__ float s_edge[64 * R::kStride];
   __shared__ int s_i[64];
   __shared__ int s_sl[64];
@@ -371,7 +417,7 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
       const int ne = min(kWave, k1 - base);
       if (tid < ne) {
         const int i = a.s_col[base + tid];
-        bwd_fill_rec<LS, NB, true, TAN, true>(a.g, a.pos, a.pos_dot, j, i, s_edge + tid * R::kStride);
+        bwd_fill_rec<LS, NB, true, TAN, true, HESS>(a.g, a.pos, a.pos_dot, j, i, s_edge + tid * R::kStride);
         s_i[tid] = i;
         s_sl[tid] = a.s_slot[base + tid];
       }
@@ -412,25 +458,28 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
 #pragma unroll
             for (int my = 0; my < NS; ++my) {
               s += e[R::kY + my] * V[mi][my];
-              if constexpr (TAN) sd += e[R::kYDot + my] * V[mi][my];
+              if constexpr (TAN || HESS) sd += e[R::kYDot + my] * V[mi][my];
             }
             Q[mi] = s;
             Qd[mi] = sd;
             h += xj[mi] * s;
             hd += xj[mi] * sd;
           }
-          float we = 0.f, wed = 0.f, wdr = 0.f;
+          float we = 0.f, wed = 0.f, wdr = 0.f, wdd = 0.f;
 #pragma unroll
           for (int q = 0; q < NB; ++q) {
             we += e[R::kPhi + q] * wv[q];
             if constexpr (TAN) wed += e[R::kPhiDot + q] * wv[q];
             wdr += e[R::kDphi + q] * wv[q];
+            if constexpr (HESS) wdd += e[R::kDDphi + q] * wv[q];
           }
+          if constexpr (!HESS) {
 #pragma unroll
-          for (int mi = 0; mi < NI; ++mi) xb[mi] += TAN ? (wed * Q[mi] + we * Qd[mi]) : we * Q[mi];
+            for (int mi = 0; mi < NI; ++mi) xb[mi] += TAN ? (wed * Q[mi] + we * Qd[mi]) : we * Q[mi];
 #pragma unroll
-          for (int q = 0; q < NB; ++q)
-            wbar[q] += TAN ? (e[R::kPhiDot + q] * h + e[R::kPhi + q] * hd) : e[R::kPhi + q] * h;
+            for (int q = 0; q < NB; ++q)
+              wbar[q] += TAN ? (e[R::kPhiDot + q] * h + e[R::kPhi + q] * hd) : e[R::kPhi + q] * h;
+          }
           if (want_pos) {
             const float srad = wdr * h;
             float wy[NS];
@@ -441,18 +490,33 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
               for (int mi = 0; mi < NI; ++mi) s += xj[mi] * V[mi][my];
               wy[my] = s;
             }
-            float rb[3];
+            float rb[3], rbd[3];
 #pragma unroll
             for (int d = 0; d < 3; ++d) {
-              float s = 0.f;
+              float s = 0.f, sd = 0.f;
 #pragma unroll
-              for (int my = 0; my < NS; ++my) s += e[R::kDY + d * NS + my] * wy[my];
+              for (int my = 0; my < NS; ++my) {
+                s += e[R::kDY + d * NS + my] * wy[my];
+                if constexpr (HESS) sd += e[R::kDDY + d * NS + my] * wy[my];
+              }
               rb[d] = s;
+              rbd[d] = sd;
             }
             float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
 #pragma unroll
             for (int d = 0; d < 3; ++d) {
-              const float v = row_sum16(srad * e[R::kU + d] + we * rb[d]);
+              // r_bar = srad u + w_e dY^T Wy (srad = w_e' h); its tangent along r_dot:
+              // d srad u + srad du + d w_e dY^T Wy + w_e d(dY)^T Wy, with d w_e = rho_dot w_e',
+              // d srad = rho_dot w_e'' h + w_e' dh
+              float lanev;
+              if constexpr (HESS) {
+                const float rho_dot = e[R::kRhoDot];
+                const float sradd = rho_dot * wdd * h + wdr * hd;
+                lanev = sradd * e[R::kU + d] + srad * e[R::kUDot + d] + rho_dot * wdr * rb[d] + we * rbd[d];
+              } else {
+                lanev = srad * e[R::kU + d] + we * rb[d];
+              }
+              const float v = row_sum16(lanev);
               if (tvalid && row_leader) sr[d] = v;
             }
           }
@@ -507,40 +571,40 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
   }
 }
 
-template <int LI, int LS, int LO, bool NEED_P, bool POS, bool TAN>
+template <int LI, int LS, int LO, bool NEED_P, bool POS, bool TAN, bool HESS>
 hipError_t bwd_uvw_nb(const BwdUvwArgs& a, int nsend, int ntiles, hipStream_t s) {
   dim3 grid(nsend), block(64 * ntiles);
   const int rows = a.cp / 16;
   const size_t dyn = POS ? sizeof(float) * 64 * 3 * rows * ntiles : 0;
   if (a.g.nb <= 8)
-    hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 2, NEED_P, POS, TAN>), grid, block, dyn, s, a);
+    hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 2, NEED_P, POS, TAN, HESS>), grid, block, dyn, s, a);
   else
-    hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 4, NEED_P, POS, TAN>), grid, block, dyn, s, a);
+    hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 4, NEED_P, POS, TAN, HESS>), grid, block, dyn, s, a);
   return hipGetLastError();
 }
 
-template <int LI, int LS, int LO, bool TAN>
+template <int LI, int LS, int LO, bool TAN, bool HESS>
 hipError_t bwd_uvu_nb(const BwdUvuArgs& a, int nblocks, int ntiles, hipStream_t s) {
   dim3 grid(nblocks), block(64 * ntiles);
   const int rows = a.cp / 16;
   const size_t dyn = sizeof(float) * 64 * 3 * rows * ntiles;
   if (a.g.nb <= 8)
-    hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 2, TAN>), grid, block, dyn, s, a);
+    hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 2, TAN, HESS>), grid, block, dyn, s, a);
   else
-    hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 4, TAN>), grid, block, dyn, s, a);
+    hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 4, TAN, HESS>), grid, block, dyn, s, a);
   return hipGetLastError();
 }
 
-template <bool NEED_P, bool POS, bool TAN>
+template <bool NEED_P, bool POS, bool TAN, bool HESS>
 hipError_t launch_bwd_uvw_t(const BwdUvwArgs& a, int li, int lo, int nsend, int ntiles, hipStream_t s) {
-#define ETPC_CALL(LI, LS, LO) bwd_uvw_nb<LI, LS, LO, NEED_P, POS, TAN>(a, nsend, ntiles, s)
+#define ETPC_CALL(LI, LS, LO) bwd_uvw_nb<LI, LS, LO, NEED_P, POS, TAN, HESS>(a, nsend, ntiles, s)
   ETPC_TRIPLE_DISPATCH(li, a.ls, lo, ETPC_CALL)
 #undef ETPC_CALL
 }
 
-template <bool TAN>
+template <bool TAN, bool HESS>
 hipError_t launch_bwd_uvu_t(const BwdUvuArgs& a, int li, int lo, int nblocks, int ntiles, hipStream_t s) {
-#define ETPC_CALL(LI, LS, LO) bwd_uvu_nb<LI, LS, LO, TAN>(a, nblocks, ntiles, s)
+#define ETPC_CALL(LI, LS, LO) bwd_uvu_nb<LI, LS, LO, TAN, HESS>(a, nblocks, ntiles, s)
   ETPC_TRIPLE_DISPATCH(li, a.ls, lo, ETPC_CALL)
 #undef ETPC_CALL
 }

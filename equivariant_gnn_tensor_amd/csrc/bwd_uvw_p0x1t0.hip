@@ -3,6 +3,6 @@
 
 namespace etpc {
 namespace bwd_detail {
-template hipError_t launch_bwd_uvw_t<false, true, false>(const BwdUvwArgs&, int, int, int, int, hipStream_t);
+template hipError_t launch_bwd_uvw_t<false, true, false, false>(const BwdUvwArgs&, int, int, int, int, hipStream_t);
 }  // namespace bwd_detail
 }  // namespace etpc

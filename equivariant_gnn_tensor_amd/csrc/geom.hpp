@@ -102,9 +102,55 @@ __device__ inline void sh_grad_r(int l, float x, float y, float z, float inv_r, 
   }
 }
 
+// Hessian of the homogeneous polynomial P_l at u applied to v: h[m][d] = sum_e
+// d^2 P_l / du_d du_e (u) v_e (differentiating the gradients above once more).
+__device__ inline void sh_poly_hess_vec(int l, float x, float y, float z, float vx, float vy, float vz,
+                                        float (*__restrict__ h)[3]) {
+  if (l <= 1) {
+    for (int m = 0; m < 2 * l + 1; ++m) h[m][0] = h[m][1] = h[m][2] = 0.f;
+  } else if (l == 2) {
+    h[0][0] = kS15 * vy; h[0][1] = kS15 * vx; h[0][2] = 0.f;
+    h[1][0] = 0.f; h[1][1] = kS15 * vz; h[1][2] = kS15 * vy;
+    h[2][0] = -kS5 * vx; h[2][1] = -kS5 * vy; h[2][2] = 2.f * kS5 * vz;
+    h[3][0] = kS15 * vz; h[3][1] = 0.f; h[3][2] = kS15 * vx;
+    h[4][0] = kS15 * vx; h[4][1] = -kS15 * vy; h[4][2] = 0.f;
+  } else {
+    const float a70 = 0.25f * kS70, a42 = 0.25f * kS42, a7 = 0.5f * kS7, a105 = 0.5f * kS105;
+    const float xy = y * vx + x * vy, yz = z * vy + y * vz, xz = z * vx + x * vz;
+    h[0][0] = a70 * 6.f * xy; h[0][1] = a70 * 6.f * (x * vx - y * vy); h[0][2] = 0.f;
+    h[1][0] = kS105 * yz; h[1][1] = kS105 * xz; h[1][2] = kS105 * xy;
+    h[2][0] = -a42 * 2.f * xy; h[2][1] = a42 * (8.f * z * vz - 2.f * x * vx - 6.f * y * vy); h[2][2] = a42 * 8.f * yz;
+    h[3][0] = -a7 * 6.f * xz; h[3][1] = -a7 * 6.f * yz; h[3][2] = a7 * (12.f * z * vz - 6.f * x * vx - 6.f * y * vy);
+    h[4][0] = a42 * (8.f * z * vz - 6.f * x * vx - 2.f * y * vy); h[4][1] = -a42 * 2.f * xy; h[4][2] = a42 * 8.f * xz;
+    h[5][0] = a105 * 2.f * xz; h[5][1] = -a105 * 2.f * yz; h[5][2] = a105 * 2.f * (x * vx - y * vy);
+    h[6][0] = a70 * 6.f * (x * vx - y * vy); h[6][1] = -a70 * 6.f * xy; h[6][2] = 0.f;
+  }
+}
+
+// Directional derivative of dY_l/dr_e (above) along the edge-vector tangent rdot:
+//   with rho_dot = u . rdot and u_dot = (rdot - u rho_dot) / r,
+//   d(dY/dr) = (H_P(u) u_dot - l (grad P(u) . u_dot) u - l Y u_dot) / r - dY rho_dot / r.
+__device__ inline void sh_grad_r_dir(int l, float x, float y, float z, float inv_r, const float* __restrict__ yv,
+                                     const float (*__restrict__ dy)[3], float udx, float udy, float udz,
+                                     float rho_dot, float (*__restrict__ ddy)[3]) {
+  float gp[7][3], hv[7][3];
+  sh_poly_grad(l, x, y, z, gp);
+  sh_poly_hess_vec(l, x, y, z, udx, udy, udz, hv);
+  const float fl = static_cast<float>(l);
+  for (int m = 0; m < 2 * l + 1; ++m) {
+    const float gu = gp[m][0] * udx + gp[m][1] * udy + gp[m][2] * udz;
+    ddy[m][0] = (hv[m][0] - fl * gu * x - fl * yv[m] * udx) * inv_r - dy[m][0] * rho_dot * inv_r;
+    ddy[m][1] = (hv[m][1] - fl * gu * y - fl * yv[m] * udy) * inv_r - dy[m][1] * rho_dot * inv_r;
+    ddy[m][2] = (hv[m][2] - fl * gu * z - fl * yv[m] * udz) * inv_r - dy[m][2] * rho_dot * inv_r;
+  }
+}
+
 // phi[0..NB) (zero-padded beyond nb); if dphi != nullptr also d phi / d r.
+// If ddphi != nullptr also d^2 phi / d r^2 (Gaussian: (4 a^2 t^2 - 2 a) phi with
+// a = 1 / (2 D^2); Bessel: product rule on the bare sin(k r) / r and the envelope).
 template <int NB>
-__device__ inline void radial_eval(const GeomParams& g, float r, float* __restrict__ phi, float* __restrict__ dphi) {
+__device__ inline void radial_eval(const GeomParams& g, float r, float* __restrict__ phi, float* __restrict__ dphi,
+                                   float* __restrict__ ddphi = nullptr) {
   if (g.radial == ETPC_RADIAL_GAUSSIAN) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -113,23 +159,28 @@ __device__ inline void radial_eval(const GeomParams& g, float r, float* __restri
         const float e = __expf(-t * t * g.gauss_inv2d2);
         phi[b] = e;
         if (dphi) dphi[b] = -2.f * g.gauss_inv2d2 * t * e;
+        if (ddphi) ddphi[b] = (4.f * g.gauss_inv2d2 * g.gauss_inv2d2 * t * t - 2.f * g.gauss_inv2d2) * e;
       } else {
         phi[b] = 0.f;
         if (dphi) dphi[b] = 0.f;
+        if (ddphi) ddphi[b] = 0.f;
       }
     }
   } else {
     const float rc = g.r_hi;
     const float t = r / rc;
-    float f = 0.f, fp = 0.f;
+    float f = 0.f, fp = 0.f, fpp = 0.f;
     if (t < 1.f) {
       const int p = g.poly_p;
       const float pf = static_cast<float>(p);
-      const float tp1 = __powf(t, pf - 1.f);  // t^(p-1), t > 0
+      const float tp2 = __powf(t, pf - 2.f);  // t^(p-2), t > 0
+      const float tp1 = tp2 * t;
       const float tp = tp1 * t;
       const float a = 0.5f * (pf + 1.f) * (pf + 2.f), bb = pf * (pf + 2.f), c = 0.5f * pf * (pf + 1.f);
       f = 1.f - a * tp + bb * tp * t - c * tp * t * t;
       fp = (-a * pf * tp1 + bb * (pf + 1.f) * tp - c * (pf + 2.f) * tp * t) / rc;
+      fpp = (-a * pf * (pf - 1.f) * tp2 + bb * (pf + 1.f) * pf * tp1 - c * (pf + 2.f) * (pf + 1.f) * tp) /
+            (rc * rc);
     }
     const float amp = sqrtf(2.f / rc);
     const float inv_r = 1.f / r;
@@ -148,10 +199,15 @@ __device__ inline void radial_eval(const GeomParams& g, float r, float* __restri
         if (dphi) {
           const float dbare = amp * (k * cc - sc * inv_r) * inv_r;
           dphi[b] = dbare * f + bare * fp;
+          if (ddphi) {
+            const float ddbare = amp * (-k * k * sc - 2.f * k * cc * inv_r + 2.f * sc * inv_r * inv_r) * inv_r;
+            ddphi[b] = ddbare * f + 2.f * dbare * fp + bare * fpp;
+          }
         }
       } else {
         phi[b] = 0.f;
         if (dphi) dphi[b] = 0.f;
+        if (ddphi) ddphi[b] = 0.f;
       }
       const float sn = 2.f * c1 * sc - sp;
       const float cn = 2.f * c1 * cc - cpv;

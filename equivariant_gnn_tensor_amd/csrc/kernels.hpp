@@ -72,7 +72,9 @@ struct BwdUvwArgs {
   GeomParams g;
   CGTable cg;
 };
-hipError_t launch_bwd_uvw(const BwdUvwArgs& a, bool need_p, bool need_pos, bool tangent, int li, int lo,
+// hess: position-Hessian pass of double backward (need_pos only): rbar receives the
+// directional derivative of r_bar_e along r_dot_e = pos_dot_sender - pos_dot_receiver.
+hipError_t launch_bwd_uvw(const BwdUvwArgs& a, bool need_p, bool need_pos, bool tangent, bool hess, int li, int lo,
                           int nsend, int ntiles, hipStream_t s);
 
 // ---------------------------------------------------------------- backward, uvu
@@ -99,7 +101,8 @@ struct BwdUvuArgs {
   GeomParams g;
   CGTable cg;
 };
-hipError_t launch_bwd_uvu(const BwdUvuArgs& a, bool tangent, int li, int lo, int nblocks, int ntiles, hipStream_t s);
+hipError_t launch_bwd_uvu(const BwdUvuArgs& a, bool tangent, bool hess, int li, int lo, int nblocks, int ntiles,
+                          hipStream_t s);
 
 // ---------------------------------------------------------------- dense fp32 GEMM on MFMA
 // C(m, n) (+)= sum_k A(m, k) B(k, n)

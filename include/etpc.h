@@ -159,13 +159,15 @@ etpc_status etpc_backward(etpc_plan plan, const etpc_graph* graph, const float* 
 
 /* Double backward: vector-Jacobian product of backward (x, W, pos, z_bar) -> (x_bar, W_bar,
  * pos_bar) with cotangents (x_dot, w_dot, pos_dot) (directional second adjoints, Eq. 23-31,
- * channel identities Eq. 37-39).  Returns d/dz_bar, d/dx and d/dW; any cotangent may be NULL
- * (= zero) and any output may be NULL (skipped).  The d/dpos term (second derivatives of the
- * harmonics and radial basis) is not provided. */
+ * channel identities Eq. 37-39).  Returns d/dz_bar, d/dx, d/dW and d/dpos ([N][3]); any
+ * cotangent may be NULL (= zero) and any output may be NULL (skipped).  d/dpos holds the
+ * position Hessian of each edge's term applied to r_dot_e = pos_dot_sender - pos_dot_receiver
+ * (second derivatives of the harmonics and the radial basis, owned by the edge as the
+ * pages describe for second order), plus the position adjoint of the x_dot and w_dot terms. */
 etpc_status etpc_double_backward(etpc_plan plan, const etpc_graph* graph, const float* x,
                                  const float* pos, const float* w, const float* z_bar,
                                  const float* x_dot, const float* w_dot, const float* pos_dot,
-                                 float* z_bar_grad, float* x_grad, float* w_grad,
+                                 float* z_bar_grad, float* x_grad, float* w_grad, float* pos_grad,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Kernel timing (off by default).  While enabled, every kernel the library enqueues is

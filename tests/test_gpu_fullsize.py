@@ -1,7 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the bench uses.
 
 The oracle cannot evaluate whole graphs of 1e5-1e7 edges in seconds, so:
-- rows of z, x_bar, pos_bar, z_bar_grad and d/dx are checked for sampled nodes, the
+- rows of z, x_bar, pos_bar, z_bar_grad, d/dx and d/dpos are checked for sampled nodes, the
   oracle summing exactly the edges that reach those rows;
 - W-gradients are checked through linearity, which holds at any size: z is linear in
   W, so <W_bar, V> = <z_bar, z(W = V)>, and <dL/dW, V> = <pos_dot, pos_bar(W = V)>;
@@ -82,11 +82,14 @@ def test_full_size_sampled(name):
         return
     note(f"full size {cfg.name}: double backward")
     pos_dot = torch.from_numpy(-wl.force_c).cuda()
-    gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot)
+    gz, gx, gw, gp = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot)
     torch.cuda.synchronize()
-    rgz, rgx, _, _ = conv.double_backward(c.spec, wl.x, wl.pos, wl.w, wl.src, wl.dst, wl.z_bar,
-                                          pos_dot=-wl.force_c.astype(np.float64), edges=e_touch)
+    rgz, rgx, _, rgp = conv.double_backward(c.spec, wl.x, wl.pos, wl.w, wl.src, wl.dst, wl.z_bar,
+                                            pos_dot=-wl.force_c.astype(np.float64), edges=e_touch)
     ez = rel_err(_rows(gz, nodes), rgz[nodes])
+    ep = rel_err(_rows(gp, nodes), rgp[nodes])
+    note(f"  d/dpos rows {ep:.2e}")
+    assert ep <= 1e-3
     e_src = np.nonzero(np.isin(wl.src, nodes))[0]
     _, rgx2, _, _ = conv.double_backward(c.spec, wl.x, wl.pos, wl.w, wl.src, wl.dst, wl.z_bar,
                                          pos_dot=-wl.force_c.astype(np.float64), edges=e_src)

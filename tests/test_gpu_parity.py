@@ -133,12 +133,12 @@ def test_double_backward_force_loss(name, n):
     fc = c.wl.force_c if c.wl.force_c is not None else np.random.default_rng(9).standard_normal(
         (cfg.n_nodes, 3)).astype(np.float32)
     pos_dot = torch.from_numpy(-fc).cuda()
-    gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot)
+    gz, gx, gw, gp = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot)
     torch.cuda.synchronize()
-    rz, rx, rw, _ = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, c.wl.z_bar,
-                                         pos_dot=-fc.astype(np.float64))
-    errs = (rel_err(gz, rz), rel_err(gx, rx), rel_err(gw, rw))
-    note(f"double backward {cfg.name} rel err z_bar {errs[0]:.2e} x {errs[1]:.2e} w {errs[2]:.2e}")
+    rz, rx, rw, rp = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, c.wl.z_bar,
+                                          pos_dot=-fc.astype(np.float64))
+    errs = (rel_err(gz, rz), rel_err(gx, rx), rel_err(gw, rw), rel_err(gp, rp))
+    note(f"double backward {cfg.name} rel err z_bar {errs[0]:.2e} x {errs[1]:.2e} w {errs[2]:.2e} pos {errs[3]:.2e}")
     assert max(errs) <= TOL_DBL
 
 
@@ -154,19 +154,20 @@ def test_double_backward_all_cotangents(name, n):
     pd = rng.standard_normal(c.wl.pos.shape).astype(np.float32)
     zb = rng.standard_normal((cfg.n_nodes, c.spec.plan.z_dim)).astype(np.float32)
     T = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
-    gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, T(zb), x_dot=T(xd), w_dot=T(wd),
-                                           pos_dot=T(pd))
+    gz, gx, gw, gp = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, T(zb), x_dot=T(xd),
+                                               w_dot=T(wd), pos_dot=T(pd))
     torch.cuda.synchronize()
-    rz, rx, rw, _ = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, zb,
-                                         x_dot=xd, w_dot=wd, pos_dot=pd)
-    errs = (rel_err(gz, rz), rel_err(gx, rx), rel_err(gw, rw))
+    rz, rx, rw, rp = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, zb,
+                                          x_dot=xd, w_dot=wd, pos_dot=pd)
+    errs = (rel_err(gz, rz), rel_err(gx, rx), rel_err(gw, rw), rel_err(gp, rp))
     note(f"double backward all {cfg.name} rel err {errs}")
     assert max(errs) <= TOL_DBL
     # each cotangent alone
-    for kw, ref_kw in ((dict(x_dot=T(xd)), dict(x_dot=xd)), (dict(w_dot=T(wd)), dict(w_dot=wd))):
-        gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, T(zb), **kw)
-        rz, rx, rw, _ = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, zb, **ref_kw)
-        for got, ref in ((gz, rz), (gx, rx), (gw, rw)):
+    for kw, ref_kw in ((dict(x_dot=T(xd)), dict(x_dot=xd)), (dict(w_dot=T(wd)), dict(w_dot=wd)),
+                       (dict(pos_dot=T(pd)), dict(pos_dot=pd))):
+        gz, gx, gw, gp = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, T(zb), **kw)
+        rz, rx, rw, rp = conv.double_backward(c.spec, c.wl.x, c.wl.pos, c.wl.w, c.wl.src, c.wl.dst, zb, **ref_kw)
+        for got, ref in ((gz, rz), (gx, rx), (gw, rw), (gp, rp)):
             if np.abs(ref).max() == 0:
                 assert torch.count_nonzero(got) == 0
             else:
@@ -245,9 +246,10 @@ def test_ragged_channels(tag, base, kw):
     pd = rng.standard_normal(wl.pos.shape).astype(np.float32)
     xd = rng.standard_normal(wl.x.shape).astype(np.float32)
     T = lambda a: torch.from_numpy(a).cuda()  # noqa: E731
-    gz, gx, gw = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, x_dot=T(xd), pos_dot=T(pd))
+    gz, gx, gw, gp = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, x_dot=T(xd),
+                                               pos_dot=T(pd))
     torch.cuda.synchronize()
     r = conv.double_backward(c.spec, wl.x, wl.pos, wl.w, wl.src, wl.dst, wl.z_bar, x_dot=xd, pos_dot=pd)
-    derrs = [rel_err(gz, r[0]), rel_err(gx, r[1]), rel_err(gw, r[2])]
+    derrs = [rel_err(gz, r[0]), rel_err(gx, r[1]), rel_err(gw, r[2]), rel_err(gp, r[3])]
     note(f"  double backward rel err {['%.2e' % e for e in derrs]}")
     assert max(derrs) <= TOL_DBL
