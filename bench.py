@@ -247,30 +247,8 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
     print(json.dumps(out, indent=1))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="cfg2")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--workspace-mib", type=float, default=0.0,
-                    help="cap each pass's workspace (0 = the full size; smaller runs in node chunks)")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="after timing, run a plain device copy of this size (counter calibration)")
-    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
-                    help="summarize rocprofv3 output under DIR into profiles/ and exit (no GPU needed)")
-    args = ap.parse_args()
-    if args.summarize_profile:
-        summarize_profile(args.summarize_profile, args.workload, args.steps, args.warmup, args.copy_calibration_mib)
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on exactly one GPU (no multi-GPU path); "
-              f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported", file=sys.stderr)
-        sys.exit(2)
-
+def measure(args, name):
+    """Time one workload: (result dict without cpu_baseline, config, workload)."""
     import numpy as np
     import torch
     import equivariant_gnn_tensor_amd as etpc
@@ -278,7 +256,7 @@ def main():
     from workloads.generate import scalar_mask
 
     dev = torch.device("cuda:0")
-    cfg = CONFIGS[args.workload]
+    cfg = CONFIGS[name]
     plan = etpc.Plan(cfg.irreps_in, cfg.irreps_out, cfg.lmax_sh, cfg.mode, cfg.radial, cfg.n_basis, cfg.r_lo,
                      cfg.r_hi, cfg.poly_p, box=cfg.box, out_per_path=cfg.out_per_path)
     info = plan.info()
@@ -359,7 +337,7 @@ def main():
     dom_ms = kinds[dom]["ms_per_step"]
     achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
     bound = "mfma" if dom.endswith("gemm") else "alu"
-    traffic, traffic_step = traffic_from_profiles(dom, args.workload)
+    traffic, traffic_step = traffic_from_profiles(dom, name)
     total_tf = sum(flops.values()) / (ms * 1e-3) / 1e12
     log(f"whole step: {total_tf:.2f} TFLOP/s algorithmic ({total_tf / PEAK_FP32_TFLOPS:.1%} of fp32 peak)")
 
@@ -408,6 +386,67 @@ def main():
         "workspace_mib": (ws_f.numel() + ws_b.numel() + ws_d.numel()) / 2 ** 20,
         "resident_mib": resident / 2 ** 20,
     }
+    return result, cfg, wl
+
+
+def graph_count_sweep(args):
+    """Throughput of the block-diagonal batches of 128-atom cells (graph-count scaling):
+    prints one JSON line with every point and the endpoint's share of the peak."""
+    import gc
+    import torch
+    from workloads.configs import GRAPH_COUNTS
+    points = []
+    for b in GRAPH_COUNTS:
+        r, cfg, wl = measure(args, f"cfg6_b{b}")
+        points.append(dict(graphs=b, n_nodes=cfg.n_nodes, n_edges=wl.n_edges, ms_per_step=r["ms_per_step"],
+                           edges_per_s=r["value"], peak_mib=r["peak_mib"]))
+        log(f"graphs {b:4d}: E={wl.n_edges:9d}  {r['ms_per_step']:8.3f} ms  {r['value']:.4g} edges/s")
+        del r, cfg, wl
+        gc.collect()
+        torch.cuda.empty_cache()
+    peak = max(p["edges_per_s"] for p in points)
+    end = points[-1]
+    print(json.dumps({
+        "metric": "edges/s fwd+bwd, graph-count sweep (uvw, 64x0e+1o+2e, 128-atom periodic cells)",
+        "value": end["edges_per_s"], "unit": "edges/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": end["ms_per_step"], "higher_is_better": True, "scaling": "strong", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"graph_count: {len(points)} batch sizes of 128-atom cells, 0.1/A^3, radius 5 A"},
+        "retention_at_endpoint": end["edges_per_s"] / peak, "sweep": points}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="cfg2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--workspace-mib", type=float, default=0.0,
+                    help="cap each pass's workspace (0 = the full size; smaller runs in node chunks)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--graph-count-sweep", action="store_true",
+                    help="time the graph-count batches (1..511 cells) and report throughput retention")
+    ap.add_argument("--summarize-profile", metavar="DIR", default=None,
+                    help="summarize rocprofv3 output under DIR into profiles/ and exit (no GPU needed)")
+    args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile, args.workload, args.steps, args.warmup, args.copy_calibration_mib)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU (no multi-GPU path); "
+              f"--gpus {args.gpus} / WORLD_SIZE={world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    if args.graph_count_sweep:
+        graph_count_sweep(args)
+        return
+    result, cfg, wl = measure(args, args.workload)
     if args.copy_calibration_mib > 0:
         nel = args.copy_calibration_mib * 2 ** 20 // 4
         a_src = torch.ones(nel, device=dev)

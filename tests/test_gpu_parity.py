@@ -82,6 +82,7 @@ FWD_CASES = [
     ("cfg4_d16", 600, None),
     ("cfg4_d64", 300, None),
     ("cfg5", 256, None),
+    ("cfg6_b4", None, None),     # block-diagonal batch of four 128-atom cells
 ]
 
 

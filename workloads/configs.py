@@ -1,4 +1,4 @@
-"""The five synthetic workloads (sizes, irreps, radial basis, graph recipe).
+"""The synthetic workloads (sizes, irreps, radial basis, graph recipe).
 
 Each workload stands in for one of the scaling sweeps of the Sobek paper
 ("Sobek: Streaming Equivariant Tensor Product Convolutions", Sec. 5: memory and
@@ -37,6 +37,8 @@ class WorkloadConfig:
     cotangent: str                  # "normal" | "energy" (z_bar = 1 on 0e outputs)
     w_std: str                      # "fan_in" (1/sqrt(B * sum C_in of group)) | "uvu" (1/sqrt(B*C_sh))
     seed_k: int = 0
+    n_graphs: int = 1               # > 1: that many independent radius graphs of n_nodes / n_graphs
+                                    # atoms each (block-diagonal batch), all in the same box
 
     @property
     def seed(self) -> int:
@@ -96,6 +98,22 @@ def _cfg5(n: int = 8192) -> WorkloadConfig:
         passes=("fwd", "bwd", "dbl"), cotangent="energy", w_std="fan_in")
 
 
+GRAPH_COUNTS = (1, 4, 16, 64, 256, 511)
+
+
+def _cfg6(n_graphs: int, atoms: int = 128) -> WorkloadConfig:
+    """Graph-count scaling (Sobek Sec. 5): a batch of independent periodic cells of
+    `atoms` atoms at 0.1 / A^3 (side 10.86 A > 2 x cutoff), MACE-like features."""
+    L = _box(atoms)
+    return WorkloadConfig(
+        name=f"graph_count_uvw_b{n_graphs}", index=6, mode="uvw", n_nodes=atoms * n_graphs, graph="radius",
+        degree=0, cutoff=5.0, box=L, pos_extent=L,
+        irreps_in="64x0e+64x1o+64x2e", irreps_out="64x0e+64x1o+64x2e+64x3o", out_per_path=False,
+        lmax_sh=3, radial="bessel", n_basis=8, r_lo=0.0, r_hi=5.0, poly_p=6,
+        passes=("fwd", "bwd"), cotangent="normal", w_std="fan_in",
+        seed_k=GRAPH_COUNTS.index(n_graphs) if n_graphs in GRAPH_COUNTS else 9, n_graphs=n_graphs)
+
+
 CONFIGS = {
     "cfg1": _cfg1(),
     "cfg2": _cfg2(),
@@ -105,6 +123,7 @@ CONFIGS = {
     "cfg4_d256": _cfg4(256),
     "cfg4_d512": _cfg4(512),
     "cfg5": _cfg5(),
+    **{f"cfg6_b{b}": _cfg6(b) for b in GRAPH_COUNTS},
 }
 
 
@@ -120,6 +139,8 @@ def small_variant(name: str, n_nodes: int, degree: Optional[int] = None) -> Work
     """
     c = CONFIGS[name]
     kw = {"n_nodes": n_nodes}
+    if c.n_graphs > 1:
+        raise ValueError("graph-count batches scale through n_graphs, not n_nodes")
     if c.graph == "radius":
         L = _box(n_nodes)
         if L <= 2.0 * c.cutoff:

@@ -110,6 +110,14 @@ def make_workload(cfg: WorkloadConfig,
     pos = _positions(rng, cfg)
     if cfg.graph == "indegree":
         src, dst = _indegree_graph(rng, cfg.n_nodes, cfg.degree)
+    elif cfg.graph == "radius" and cfg.n_graphs > 1:
+        # block-diagonal batch: each cell's radius graph on its own atoms, indices offset
+        per = cfg.n_nodes // cfg.n_graphs
+        if per * cfg.n_graphs != cfg.n_nodes:
+            raise ValueError("n_nodes must be a multiple of n_graphs")
+        parts = [_radius_graph(pos[b * per:(b + 1) * per], cfg.cutoff, cfg.box) for b in range(cfg.n_graphs)]
+        src = np.concatenate([s + b * per for b, (s, _) in enumerate(parts)])
+        dst = np.concatenate([d + b * per for b, (_, d) in enumerate(parts)])
     elif cfg.graph == "radius":
         src, dst = _radius_graph(pos, cfg.cutoff, cfg.box)
     else:
