@@ -304,10 +304,25 @@ def measure(args, name):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # one step captured as a HIP graph (every launch of the library, no host work, no
+        # memset nodes: buffers are cleared by fill kernels) and replayed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        hg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(hg):
+            step()
+        hg.replay()
+        torch.cuda.synchronize()
+        run = hg.replay
     torch.cuda.reset_peak_memory_stats()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        run()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     peak = torch.cuda.max_memory_allocated()
@@ -365,6 +380,7 @@ def measure(args, name):
             "mode": cfg.mode,
             "pass": ("forward + backward (pos_bar) + double backward along pos_dot (d/dx, d/dW)" if force_step
                      else "forward + backward (x_bar, W_bar, pos_bar)"),
+            "launch": "hip graph replay" if args.graph else "eager",
         },
         "roofline": {
             "kernel": dom,
@@ -427,6 +443,8 @@ def main():
                     help="cap each pass's workspace (0 = the full size; smaller runs in node chunks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured as a HIP graph (launch-bound small workloads)")
     ap.add_argument("--graph-count-sweep", action="store_true",
                     help="time the graph-count batches (1..511 cells) and report throughput retention")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,

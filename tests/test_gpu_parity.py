@@ -254,3 +254,51 @@ def test_ragged_channels(tag, base, kw):
     derrs = [rel_err(gz, r[0]), rel_err(gx, r[1]), rel_err(gw, r[2]), rel_err(gp, r[3])]
     note(f"  double backward rel err {['%.2e' % e for e in derrs]}")
     assert max(derrs) <= TOL_DBL
+
+
+# ---------------------------------------------------------------- HIP graph capture
+@pytest.mark.parametrize("name,n", [("cfg1", None), ("cfg5", 128)])
+def test_graph_capture_replays_match_eager(name, n):
+    """A captured forward + backward (+ double backward) step replays bit-identically to the
+    eager step, several times, with eager work and synchronizations between replays."""
+    etpc = _etpc()
+    cfg = CONFIGS[name] if n is None else small_variant(name, n)
+    note(f"graph capture {cfg.name}")
+    c = make_case(cfg)
+    info = c.plan.info()
+    N = cfg.n_nodes
+    dev = c.x.device
+    ws = {p: torch.empty(etpc.etpc_workspace_size(c.plan, p, N, c.wl.n_edges), dtype=torch.uint8, device=dev)
+          for p in (etpc.PASS_FWD, etpc.PASS_BWD, etpc.PASS_DBL)}
+    z = torch.empty(N, info["z_dim"], device=dev)
+    outs = (torch.empty(N, info["x_dim"], device=dev), torch.empty(info["w_numel"], device=dev),
+            torch.empty(N, 3, device=dev))
+    pd = torch.from_numpy(np.random.default_rng(3).standard_normal((N, 3)).astype(np.float32)).to(dev)
+    douts = tuple(torch.empty_like(t) for t in (z, outs[0], outs[1], outs[2]))
+
+    def step():
+        etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, z=z, ws=ws[etpc.PASS_FWD])
+        etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, outs=outs, ws=ws[etpc.PASS_BWD])
+        etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pd, outs=douts,
+                                  ws=ws[etpc.PASS_DBL])
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (z, *outs, *douts)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (z, *outs, *douts):
+            t.fill_(float("nan"))          # eager work between replays; stale values would show
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((z, *outs, *douts), ref):
+            assert torch.equal(got, want), f"replay {rep} differs from the eager step"
+    note(f"graph capture {cfg.name}: 3 replays bit-identical")
