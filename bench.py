@@ -20,7 +20,10 @@ gives the scale factor):
         python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --copy-calibration-mib 256
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/fetch_cfg2 -o run -- python3 bench.py <same>
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write_cfg2 -o run -- python3 bench.py <same>
-    python bench.py --summarize-profile DIR --steps 3 --warmup 1 --workload cfg2 --copy-calibration-mib 256
+    python bench.py --summarize-profile DIR --steps 3 --warmup 1 --workload cfg2 --lanes 1 --copy-calibration-mib 256
+
+(--lanes 1 serializes the launches, as the event-timed pass does, so the trace's per-kernel
+durations are the kernels' own.)
 """
 from __future__ import annotations
 
@@ -192,7 +195,7 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
     f_scale = known_kib / max(fcopy) if fcopy else None
     w_scale = known_kib / max(wcopy) if wcopy else None
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    cmd_args = f"--steps {steps} --warmup {warmup} --no-cpu-baseline --workload {workload} " \
+    cmd_args = f"--steps {steps} --warmup {warmup} --no-cpu-baseline --workload {workload} --lanes 1 " \
                f"--copy-calibration-mib {copy_mib}"
     lines = [f"# rocprofv3 kernel trace, workload {workload}", "",
              "Commands (repo root, one MI355X):", "",
@@ -204,7 +207,7 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/write_{workload} -o run -- "
              f"python3 bench.py {cmd_args}",
              f"python bench.py --summarize-profile DIR --steps {steps} --warmup {warmup} --workload {workload} "
-             f"--copy-calibration-mib {copy_mib}",
+             f"--lanes 1 --copy-calibration-mib {copy_mib}",
              "```", "",
              f"Each run executes {execs} steps (warmup {warmup} + timed {steps} + event-profiled {steps}).", "",
              "| family | launches/step | ms/step (trace) | avg us/launch | HBM MB/step (calibrated) |",
@@ -241,7 +244,7 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
             rec = dict(out[fam], kind=kind, workload=workload, kernel_src_sha=kernel_source_hash(kind),
                        fetch_scale=f_scale, write_scale=w_scale, copy_calibration_mib=copy_mib,
                        command=f"python bench.py --summarize-profile DIR --steps {steps} --warmup {warmup} "
-                               f"--workload {workload} --copy-calibration-mib {copy_mib}")
+                               f"--workload {workload} --lanes 1 --copy-calibration-mib {copy_mib}")
             with open(os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.json"), "w") as fh:
                 json.dump(rec, fh, indent=1)
     print(json.dumps(out, indent=1))
@@ -256,6 +259,8 @@ def measure(args, name):
     from workloads.generate import scalar_mask
 
     dev = torch.device("cuda:0")
+    if args.lanes > 0:
+        etpc.etpc_set_lanes(args.lanes)
     cfg = CONFIGS[name]
     plan = etpc.Plan(cfg.irreps_in, cfg.irreps_out, cfg.lmax_sh, cfg.mode, cfg.radial, cfg.n_basis, cfg.r_lo,
                      cfg.r_hi, cfg.poly_p, box=cfg.box, out_per_path=cfg.out_per_path)
@@ -329,7 +334,11 @@ def measure(args, name):
     ms = dt / args.steps * 1e3
     value = E / (ms / 1e3)
 
-    # per-kind kernel time: event pairs recorded by the library on its launch stream
+    # per-kind kernel time: event pairs recorded by the library on its launch streams, with
+    # the lanes serialized so that each launch's duration is its own (concurrent launches
+    # share the chip and would each look slower)
+    timed_lanes = etpc.etpc_get_lanes()
+    etpc.etpc_set_lanes(1)
     etpc.etpc_profile_enable(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -342,6 +351,7 @@ def measure(args, name):
         tot, n = etpc.etpc_profile_read(k)
         kinds[k] = dict(ms_per_step=tot / args.steps, launches_per_step=n / args.steps)
     etpc.etpc_profile_enable(False)
+    etpc.etpc_set_lanes(timed_lanes)
     flops = flop_model(plan, N, E, cfg.n_basis, force_step)
     log(f"step {ms:.3f} ms (profiled pass {prof_ms:.3f} ms); csr build {csr_ms:.3f} ms")
     for k, v in kinds.items():
@@ -381,6 +391,7 @@ def measure(args, name):
             "pass": ("forward + backward (pos_bar) + double backward along pos_dot (d/dx, d/dW)" if force_step
                      else "forward + backward (x_bar, W_bar, pos_bar)"),
             "launch": "hip graph replay" if args.graph else "eager",
+            "lanes": timed_lanes,
         },
         "roofline": {
             "kernel": dom,
@@ -443,6 +454,8 @@ def main():
                     help="cap each pass's workspace (0 = the full size; smaller runs in node chunks)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (counter calibration)")
+    ap.add_argument("--lanes", type=int, default=0,
+                    help="concurrent launch lanes per pass for the timed steps (0 = library default)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured as a HIP graph (launch-bound small workloads)")
     ap.add_argument("--graph-count-sweep", action="store_true",

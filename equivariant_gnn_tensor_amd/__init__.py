@@ -9,5 +9,5 @@ from ._binding import (  # noqa: F401
     EtpcError, Graph, Plan,
     etpc_backward, etpc_csr_build, etpc_csr_workspace_size, etpc_double_backward, etpc_forward,
     etpc_graph_validate, etpc_plan_cg, etpc_plan_info, etpc_plan_out_irrep, etpc_plan_path,
-    etpc_profile_enable, etpc_profile_read, etpc_workspace_size, lib, parse_irreps,
+    etpc_get_lanes, etpc_profile_enable, etpc_profile_read, etpc_set_lanes, etpc_workspace_size, lib, parse_irreps,
 )

@@ -63,7 +63,8 @@ class etpc_graph(C.Structure):
 SYMBOLS = (
     "etpc_plan_create", "etpc_plan_destroy", "etpc_plan_info", "etpc_plan_path", "etpc_plan_out_irrep",
     "etpc_plan_cg", "etpc_workspace_size", "etpc_csr_workspace_size", "etpc_csr_build", "etpc_graph_validate",
-    "etpc_forward", "etpc_backward", "etpc_double_backward", "etpc_profile_enable", "etpc_profile_read",
+    "etpc_forward", "etpc_backward", "etpc_double_backward", "etpc_set_lanes", "etpc_get_lanes",
+    "etpc_profile_enable", "etpc_profile_read",
     "etpc_last_error",
 )
 KINDS = ("csr", "fwd_traverse", "channel_gemm", "bwd_traverse", "node_gemm", "aux")
@@ -91,6 +92,8 @@ def _load():
         "etpc_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_double_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_profile_enable": [i32],
+        "etpc_set_lanes": [i32],
+        "etpc_get_lanes": [],
         "etpc_profile_read": [i32, P(C.c_double), P(i64)],
     }
     for name, args in sig.items():
@@ -356,6 +359,15 @@ def etpc_double_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, x_dot=None,
                                     _ptr(x_dot), _ptr(w_dot), _ptr(pos_dot), _ptr(gz), _ptr(gx), _ptr(gw), _ptr(gp),
                                     wp, wn, _stream(stream)))
     return gz, gx, gw, gp
+
+
+def etpc_set_lanes(lanes: int) -> None:
+    """Concurrent launch lanes per pass (1 serializes; default 2)."""
+    _check(lib.etpc_set_lanes(int(lanes)))
+
+
+def etpc_get_lanes() -> int:
+    return int(lib.etpc_get_lanes())
 
 
 def etpc_profile_enable(enable: bool) -> None:

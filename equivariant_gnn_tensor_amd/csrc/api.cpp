@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "lanes.hpp"
 #include "plan.hpp"
 #include "profile.hpp"
 
@@ -60,6 +61,32 @@ int lane_width(int c, int* ntiles, int min_cp = 1) {
   while (cp < c) cp <<= 1;
   *ntiles = 1;
   return cp;
+}
+
+// Concurrent lanes of a pass (see lanes.hpp).  uvw: paths round-robin over the lanes;
+// uvu: one lane per input block (backward: x_bar accumulates per block) or per output
+// block (forward: z accumulates per block).  Each lane owns a copy of the edge adjoint:
+// the workspace holds rbar_slots copies; a call uses rbar_lanes of them, fixed once at
+// its start (the process-wide limit may change between calls).
+int count_blocks(const etpc_plan_s* p, bool by_in) {
+  const auto& groups = by_in ? p->by_in : p->by_out;
+  int used = 0;
+  for (const auto& gr : groups) used += gr.empty() ? 0 : 1;
+  return used;
+}
+int rbar_slots(const etpc_plan_s* p) {
+  const int units = p->mode == ETPC_UVW ? static_cast<int>(p->paths.size()) : count_blocks(p, true);
+  return std::max(1, std::min(kLanes, units));
+}
+int rbar_lanes(const etpc_plan_s* p) { return std::min(rbar_slots(p), lanes_limit()); }
+// lane of each block for n lanes (blocks without paths get lane 0, unused)
+std::vector<int> block_lanes(const etpc_plan_s* p, bool by_in, int n) {
+  const auto& groups = by_in ? p->by_in : p->by_out;
+  std::vector<int> lane(groups.size(), 0);
+  int used = 0;
+  for (size_t k = 0; k < groups.size(); ++k)
+    if (!groups[k].empty()) lane[k] = (used++) % n;
+  return lane;
 }
 
 // ---------------------------------------------------------------- per-plan derived sizes
@@ -129,13 +156,14 @@ struct BwdLayout {
   float *xt = nullptr, *P = nullptr, *Pd = nullptr;
   float* xpart = nullptr;
   int64_t xpart_cap = 0;
+  int64_t wpart_lane = 0;   // uvu: floats of W_bar partials per lane
 };
-// flags: pos = edge adjoint + Xt; p = plain P state; tan = tangent state; wbar = W_bar partials
+// flags: pos = edge adjoint (one copy per lane) + Xt; p = plain P state; tan = tangent state; wbar = W_bar partials
 // (two sets when wbar2); wt2 = second transposed weight (for w_dot)
 void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t chunk, bool pos, bool need_p,
                 bool tan, bool wbar, bool wbar2, bool xbar, bool wt2, Carver& c, BwdLayout& L) {
   if (p->mode == ETPC_UVW) {
-    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges));
+    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * rbar_slots(p)));
     if (pos) L.wcat = c.take<float>(static_cast<size_t>(d.max_wcat));
     if (xbar) L.wt = c.take<float>(static_cast<size_t>(d.max_wcat));
     if (wt2) L.wt2 = c.take<float>(static_cast<size_t>(d.max_wcat));
@@ -158,10 +186,11 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t
       L.xpart = c.take<float>(static_cast<size_t>(L.xpart_cap));
     }
   } else {
-    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges));
+    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * rbar_slots(p)));
     int64_t maxbc = 0;
     for (auto& q : p->paths) maxbc = std::max<int64_t>(maxbc, static_cast<int64_t>(p->n_basis) * q.c_in);
-    if (wbar) L.wpart = c.take<float>(static_cast<size_t>(chunk * maxbc));  // chunk = uvu grid size here
+    L.wpart_lane = chunk * maxbc;   // chunk = uvu grid size here; one partial set per lane
+    if (wbar) L.wpart = c.take<float>(static_cast<size_t>(L.wpart_lane * rbar_slots(p)));
   }
 }
 
@@ -306,8 +335,11 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     for (int64_t r0 = 0; r0 < N; r0 += chunk) {
       const int nrecv = static_cast<int>(std::min<int64_t>(chunk, N - r0));
       int32_t col0 = 0;
-      for (int qi : paths) {
-        const PathInfo& pi = p->paths[qi];
+      // the paths of a group fill disjoint column ranges of S: concurrent lanes
+      LaneGroup lanes(s, static_cast<int>(paths.size()));
+      ETPC_HIP(lanes.status());
+      for (size_t t = 0; t < paths.size(); ++t) {
+        const PathInfo& pi = p->paths[paths[t]];
         FwdUvwArgs a{};
         a.rowptr = g->rowptr;
         a.col = g->col;
@@ -326,9 +358,11 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.s_col0 = col0;
         a.g = geom;
         a.cg = pi.cgf;
-        ETPC_LAUNCH(ETPC_KIND_FWD_TRAVERSE, launch_fwd_uvw(a, tangent, pi.l_in, pi.l_out, nrecv, ntiles, s));
+        const hipStream_t ls = lanes.lane(static_cast<int>(t));
+        ETPC_LAUNCH_ON(ETPC_KIND_FWD_TRAVERSE, ls, launch_fwd_uvw(a, tangent, pi.l_in, pi.l_out, nrecv, ntiles, ls));
         col0 += p->n_basis * pi.c_in;
       }
+      ETPC_HIP(lanes.finish());
       GemmArgs ga{};
       ga.A = L.S;
       ga.amap = plain(D);
@@ -352,6 +386,10 @@ etpc_status fwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
                         const float* pos_dot, const float* win, float* z, bool beta, bool tangent, hipStream_t s) {
   const GeomParams geom = p->geom();
   std::vector<int> seen(p->out.size(), 0);
+  const int nl = std::max(1, std::min(lanes_limit(), count_blocks(p, false)));
+  const std::vector<int> lane_of = block_lanes(p, false, nl);   // z accumulates per output block
+  LaneGroup lanes(s, nl);
+  ETPC_HIP(lanes.status());
   for (const PathInfo& pi : p->paths) {
     FwdUvuArgs a{};
     a.rowptr = g->rowptr;
@@ -372,9 +410,11 @@ etpc_status fwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
     a.accumulate = (beta || seen[pi.out_block]) ? 1 : 0;
     a.g = geom;
     a.cg = pi.cgf;
-    ETPC_LAUNCH(ETPC_KIND_FWD_TRAVERSE, launch_fwd_uvu(a, tangent, pi.l_in, pi.l_out, g->n_nodes, ntiles, s));
+    const hipStream_t ls = lanes.lane(lane_of[pi.out_block]);
+    ETPC_LAUNCH_ON(ETPC_KIND_FWD_TRAVERSE, ls, launch_fwd_uvu(a, tangent, pi.l_in, pi.l_out, g->n_nodes, ntiles, ls));
     seen[pi.out_block] = 1;
   }
+  ETPC_HIP(lanes.finish());
   return ETPC_OK;
 }
 
@@ -392,6 +432,7 @@ struct UvwBwdReq {
   bool plain_needed;      // dbl: plain P needed for the x2 / w2 terms
   bool hess;              // dbl: rbar receives the position-Hessian term along pos_dot
   bool rbar_acc;          // add into rbar from the first path on (earlier passes wrote it)
+  int lanes;              // concurrent lanes = edge-adjoint copies in use (rbar_lanes)
 };
 
 void wprep_args(const etpc_plan_s* p, const Derived& d, int k, const float* w, float* wcat, float* wt, WPrepArgs& a) {
@@ -468,11 +509,15 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   const bool main_state = R.tangent || (R.x_out || R.w_out);        // P (plain) or dP (tangent)
   const bool need_plain = R.tangent ? R.plain_needed : main_state;   // plain P
   float* Pmain = R.tangent ? L.Pd : L.P;
-  bool rbar_started = false;
+  const int nl = std::max(1, R.lanes);
+  const int64_t rbar_stride = 3 * g->n_edges;
   if (R.x_out) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
   for (int64_t j0 = 0; j0 < N; j0 += chunk) {
     const int nsend = static_cast<int>(std::min<int64_t>(chunk, N - j0));
-    rbar_started = R.rbar_acc;  // the edges of this sender chunk are first written by its first path
+    // each lane's copy of the edge adjoint is first written by its first path of this chunk
+    bool rbar_started[kLanes];
+    for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc;
+    int t_glob = 0;
     for (size_t k = 0; k < p->in.size(); ++k) {
       const auto& paths = p->by_in[k];
       if (paths.empty()) continue;
@@ -505,8 +550,12 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         set_vec4(ga);
         ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, launch_gemm(ga, 1, s));
       }
-      for (size_t t = 0; t < paths.size(); ++t) {
+      // the block's paths write disjoint P columns and their own lane's edge adjoint copy
+      LaneGroup lanes(s, nl);
+      ETPC_HIP(lanes.status());
+      for (size_t t = 0; t < paths.size(); ++t, ++t_glob) {
         const PathInfo& pi = p->paths[paths[t]];
+        const int lane = t_glob % nl;
         BwdUvwArgs a{};
         a.s_rowptr = g->s_rowptr;
         a.s_col = g->s_col;
@@ -517,7 +566,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.xt = L.xt;
         a.P = L.P;
         a.Pdot = L.Pd;
-        a.rbar = R.rbar;
+        a.rbar = R.rbar ? R.rbar + lane * rbar_stride : nullptr;
         a.send0 = static_cast<int32_t>(j0);
         a.z_dim = static_cast<int32_t>(p->z_dim);
         a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
@@ -527,14 +576,17 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.ls = pi.l_sh;
         a.ld_state = ncols;
         a.state_col0 = d.block_col0[k][t];
-        a.rbar_accumulate = rbar_started ? 1 : 0;
+        a.rbar_accumulate = rbar_started[lane] ? 1 : 0;
         a.g = geom;
         a.cg = pi.cgf;
         const bool np = R.tangent ? need_plain : main_state;
-        ETPC_LAUNCH(ETPC_KIND_BWD_TRAVERSE,
-                    launch_bwd_uvw(a, R.hess ? false : np, want_pos, R.tangent, R.hess, pi.l_in, pi.l_out, nsend, ntiles, s));
-        if (want_pos) rbar_started = true;
+        const hipStream_t ls = lanes.lane(lane);
+        ETPC_LAUNCH_ON(ETPC_KIND_BWD_TRAVERSE, ls,
+                       launch_bwd_uvw(a, R.hess ? false : np, want_pos, R.tangent, R.hess, pi.l_in, pi.l_out, nsend,
+                                      ntiles, ls));
+        if (want_pos) rbar_started[lane] = true;
       }
+      ETPC_HIP(lanes.finish());
       if (R.x_out) {
         if (main_state) {
           etpc_status st = xbar_gemm(p, d, static_cast<int>(k), Pmain, L.wt, R.x_out, j0, nsend, false, L, s);
@@ -579,6 +631,7 @@ struct UvuBwdReq {
   bool w_acc;     // accumulate into w_out
   bool hess;      // rbar receives the position-Hessian term along pos_dot (no x_out / w_out)
   bool rbar_acc;  // add into rbar from the first path on
+  int lanes;      // concurrent lanes = edge-adjoint and W_bar partial copies in use
 };
 
 etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* pos, const float* z_bar,
@@ -588,8 +641,18 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
   const int grid = static_cast<int>(std::min<int64_t>(N, kUvuGrid));
   if (R.x_out && !R.x_acc) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
   std::vector<int> seen(p->in.size(), 0);
-  bool rbar_started = R.rbar_acc;
+  // one lane per input block (x_bar accumulates per block); per-lane edge adjoint and
+  // W_bar partial copies
+  const int nl = std::max(1, R.lanes);
+  const std::vector<int> lane_of = block_lanes(p, true, nl);
+  const int64_t rbar_stride = 3 * g->n_edges;
+  bool rbar_started[kLanes];
+  for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc;
+  LaneGroup lanes(s, nl);
+  ETPC_HIP(lanes.status());
   for (const PathInfo& pi : p->paths) {
+    const int lane = lane_of[pi.in_block];
+    float* wpart = R.w_out ? L.wpart + lane * L.wpart_lane : nullptr;
     BwdUvuArgs a{};
     a.s_rowptr = g->s_rowptr;
     a.s_col = g->s_col;
@@ -600,8 +663,8 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
     a.w = R.w + pi.w_off;
     a.z_bar = z_bar;
     a.x_bar = R.x_out;
-    a.wbar_part = R.w_out ? L.wpart : nullptr;
-    a.rbar = R.rbar;
+    a.wbar_part = wpart;
+    a.rbar = R.rbar ? R.rbar + lane * rbar_stride : nullptr;
     a.n_nodes = N;
     a.x_dim = static_cast<int32_t>(p->x_dim);
     a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
@@ -612,19 +675,23 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
     a.c = pi.c_in;
     a.ls = pi.l_sh;
     a.xbar_accumulate = (R.x_acc || seen[pi.in_block]) ? 1 : 0;
-    a.rbar_accumulate = rbar_started ? 1 : 0;
+    a.rbar_accumulate = rbar_started[lane] ? 1 : 0;
     a.g = geom;
     a.cg = pi.cgf;
-    ETPC_LAUNCH(ETPC_KIND_BWD_TRAVERSE, launch_bwd_uvu(a, R.tangent, R.hess, pi.l_in, pi.l_out, grid, ntiles, s));
+    const hipStream_t ls = lanes.lane(lane);
+    ETPC_LAUNCH_ON(ETPC_KIND_BWD_TRAVERSE, ls,
+                   launch_bwd_uvu(a, R.tangent, R.hess, pi.l_in, pi.l_out, grid, ntiles, ls));
     seen[pi.in_block] = 1;
-    if (R.rbar) rbar_started = true;
+    if (R.rbar) rbar_started[lane] = true;
     if (R.w_out) {
       int64_t poff[1] = {pi.w_off};
       int32_t col0[1] = {0}, cout[1] = {pi.c_in};
-      ETPC_LAUNCH(ETPC_KIND_AUX, launch_reduce_wbar(L.wpart, grid, 1, 1, p->n_basis, poff, col0, cout, p->n_basis * pi.c_in, R.w_out,
-                                  R.w_acc, s));
+      ETPC_LAUNCH_ON(ETPC_KIND_AUX, ls,
+                     launch_reduce_wbar(wpart, grid, 1, 1, p->n_basis, poff, col0, cout, p->n_basis * pi.c_in,
+                                        R.w_out, R.w_acc, ls));
     }
   }
+  ETPC_HIP(lanes.finish());
   return ETPC_OK;
 }
 
@@ -713,6 +780,7 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
   const Derived d = derive(p);
   const bool want_pos = pos_bar != nullptr;
   const bool need_p = x_bar || w_bar;
+  const int lanes = rbar_lanes(p);
   const int32_t N = g->n_nodes;
   if (N == 0) {
     if (w_bar) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_bar, p->w_numel, 0.f, s));
@@ -734,6 +802,7 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
              false, x_bar != nullptr, false, cv, L);
   if (p->mode == ETPC_UVW) {
     UvwBwdReq R{};
+    R.lanes = lanes;
     R.x = x;
     R.w = w;
     R.x_out = x_bar;
@@ -742,6 +811,7 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
     st = bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, s);
   } else {
     UvuBwdReq R{};
+    R.lanes = lanes;
     R.x = x;
     R.w = w;
     R.x_out = x_bar;
@@ -754,7 +824,8 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
     if (g->n_edges == 0 || p->paths.empty()) {
       ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(pos_bar, 3 * static_cast<int64_t>(N), 0.f, s));
     } else {
-      ETPC_LAUNCH(ETPC_KIND_AUX, launch_pos_bar(g->rowptr, g->s_rowptr, g->s_slot, L.rbar, pos_bar, N, s));
+      ETPC_LAUNCH(ETPC_KIND_AUX, launch_pos_bar(g->rowptr, g->s_rowptr, g->s_slot, L.rbar, lanes,
+                                                g->n_edges, pos_bar, N, s));
     }
   }
   if (w_bar && p->paths.empty()) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_bar, p->w_numel, 0.f, s));
@@ -777,6 +848,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     return ETPC_OK;
   }
   const bool want_pos = pos_grad != nullptr;
+  const int lanes = rbar_lanes(p);
   const Derived d = derive(p);
   const bool tan = pos_dot != nullptr;
   const bool plain = x_dot != nullptr || w_dot != nullptr;
@@ -841,6 +913,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     if (p->mode == ETPC_UVW) {
       // d/dx = W^T dP + w_dot^T P ;  d/dW = x^T dP + x_dot^T P
       UvwBwdReq R{};
+      R.lanes = lanes;
       R.pos_dot = pos_dot;
       if (tan) {
         R.x = x;
@@ -877,6 +950,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     bool xs = false, wsd = false;
     if (tan) {
       UvuBwdReq R{};
+      R.lanes = lanes;
       R.x = x;
       R.w = w;
       R.pos_dot = pos_dot;
@@ -890,6 +964,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     }
     if (x_grad && w_dot) {
       UvuBwdReq R{};
+      R.lanes = lanes;
       R.x = x;
       R.w = w_dot;
       R.x_out = x_grad;
@@ -900,6 +975,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     }
     if (w_grad && x_dot) {
       UvuBwdReq R{};
+      R.lanes = lanes;
       R.x = x_dot;
       R.w = w;
       R.w_out = w_grad;
@@ -944,6 +1020,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     }
     if (p->mode == ETPC_UVW) {
       UvwBwdReq R{};
+      R.lanes = lanes;
       R.x = xin;
       R.w = win;
       R.pos_dot = hess ? pos_dot : nullptr;
@@ -953,6 +1030,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
       st = bwd_uvw_run(p, d, g, pos, z_bar, R, Lp, chunk, s);
     } else {
       UvuBwdReq R{};
+      R.lanes = lanes;
       R.x = xin;
       R.w = win;
       R.pos_dot = hess ? pos_dot : nullptr;
@@ -964,7 +1042,8 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     if (st != ETPC_OK) return st;
     acc = true;
   }
-  ETPC_LAUNCH(ETPC_KIND_AUX, launch_pos_bar(g->rowptr, g->s_rowptr, g->s_slot, Lp.rbar, pos_grad, N, s));
+  ETPC_LAUNCH(ETPC_KIND_AUX, launch_pos_bar(g->rowptr, g->s_rowptr, g->s_slot, Lp.rbar, lanes, g->n_edges,
+                                            pos_grad, N, s));
   return ETPC_OK;
 }
 

@@ -74,26 +74,40 @@ __global__ void reduce_wbar_kernel(const ReduceWArgs a) {
 }
 
 // one wavefront per node: lanes stride over the node's sender and receiver slots; the lane
-// partials are combined by a fixed reduction tree (deterministic)
+// partials are combined by a fixed reduction tree (deterministic).  rbar holds `copies`
+// per-lane copies of the edge adjoint (stride floats apart), summed in copy order.
 __global__ __launch_bounds__(256) void pos_bar_kernel(const int32_t* __restrict__ rowptr,
                                                      const int32_t* __restrict__ s_rowptr,
                                                      const int32_t* __restrict__ s_slot,
-                                                     const float* __restrict__ rbar, float* __restrict__ pos_bar,
-                                                     int n) {
+                                                     const float* __restrict__ rbar, int copies, int64_t stride,
+                                                     float* __restrict__ pos_bar, int n) {
   const int v = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (v >= n) return;
   float sx = 0.f, sy = 0.f, sz = 0.f;
   for (int k = s_rowptr[v] + lane; k < s_rowptr[v + 1]; k += 64) {
-    const int64_t e = s_slot[k];
-    sx += rbar[3 * e + 0];
-    sy += rbar[3 * e + 1];
-    sz += rbar[3 * e + 2];
+    const float* r = rbar + 3 * static_cast<int64_t>(s_slot[k]);
+    float ex = 0.f, ey = 0.f, ez = 0.f;
+    for (int c = 0; c < copies; ++c) {
+      ex += r[c * stride + 0];
+      ey += r[c * stride + 1];
+      ez += r[c * stride + 2];
+    }
+    sx += ex;
+    sy += ey;
+    sz += ez;
   }
   for (int64_t e = rowptr[v] + lane; e < rowptr[v + 1]; e += 64) {
-    sx -= rbar[3 * e + 0];
-    sy -= rbar[3 * e + 1];
-    sz -= rbar[3 * e + 2];
+    const float* r = rbar + 3 * e;
+    float ex = 0.f, ey = 0.f, ez = 0.f;
+    for (int c = 0; c < copies; ++c) {
+      ex += r[c * stride + 0];
+      ey += r[c * stride + 1];
+      ez += r[c * stride + 2];
+    }
+    sx -= ex;
+    sy -= ey;
+    sz -= ez;
   }
   for (int off = 32; off > 0; off >>= 1) {
     sx += __shfl_xor(sx, off);
@@ -168,10 +182,10 @@ hipError_t launch_reduce_wbar(float* part, int splits, int c_in, int n_paths, in
 }
 
 hipError_t launch_pos_bar(const int32_t* rowptr, const int32_t* s_rowptr, const int32_t* s_slot, const float* rbar,
-                          float* pos_bar, int n_nodes, hipStream_t s) {
+                          int copies, int64_t n_edges, float* pos_bar, int n_nodes, hipStream_t s) {
   if (n_nodes <= 0) return hipSuccess;
   hipLaunchKernelGGL(pos_bar_kernel, dim3((n_nodes + 3) / 4), dim3(256), 0, s, rowptr, s_rowptr, s_slot, rbar,
-                     pos_bar, n_nodes);
+                     copies, 3 * n_edges, pos_bar, n_nodes);
   return hipGetLastError();
 }
 

@@ -137,9 +137,10 @@ hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 hipError_t launch_reduce_wbar(float* part, int splits, int c_in, int n_paths, int nb, const int64_t* path_off,
                               const int32_t* col0, const int32_t* cout, int ncols, float* out, bool accumulate,
                               hipStream_t s);
-// pos_bar[n] = sum_{sender slots of n} rbar[s_slot] - sum_{receiver slots of n} rbar[slot]
+// pos_bar[n] = sum_{sender slots of n} rbar[s_slot] - sum_{receiver slots of n} rbar[slot], where
+// rbar[e] is the sum of `copies` arrays of n_edges x 3 floats (one per concurrent lane)
 hipError_t launch_pos_bar(const int32_t* rowptr, const int32_t* s_rowptr, const int32_t* s_slot, const float* rbar,
-                          float* pos_bar, int n_nodes, hipStream_t s);
+                          int copies, int64_t n_edges, float* pos_bar, int n_nodes, hipStream_t s);
 // Reorder W blocks of one input block into the layouts the node GEMMs read.
 //   wcat[u][col0_t + q*cout_t + w]  = W_{pi_t}[q][u][w]   (t = position of the path within the input block)
 //   wt[col0_t + q*cout_t + w][u]    = W_{pi_t}[q][u][w]

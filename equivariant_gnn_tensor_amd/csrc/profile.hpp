@@ -26,3 +26,10 @@ class ProfScope {
     ::etpc::ProfScope _etpc_ps((kind), s);   \
     ETPC_HIP(call);                          \
   } while (0)
+
+// The same for a launch on another stream (a concurrent lane) than the call's `s`.
+#define ETPC_LAUNCH_ON(kind, stream, call)        \
+  do {                                            \
+    ::etpc::ProfScope _etpc_ps((kind), (stream)); \
+    ETPC_HIP(call);                               \
+  } while (0)

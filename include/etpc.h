@@ -39,7 +39,12 @@
  * kernel has been enqueued and etpc_last_error() describes the problem.
  * Compute calls are asynchronous on the given stream; results are
  * deterministic for a given workspace size (fixed reduction owners and orders,
- * no floating-point atomics).
+ * no floating-point atomics).  Inside a call, the independent per-path launches of a
+ * pass run on up to two side streams the library creates once per device (default
+ * priority), forked from and joined back into the given stream with events, so the
+ * call still behaves as one ordered unit of that stream (and can be captured into a HIP
+ * graph).  Calls from several host threads serialize their fork-to-join sections on a
+ * per-device lock; the first call on a device creates the side streams.
  */
 #ifndef ETPC_H
 #define ETPC_H
@@ -60,7 +65,7 @@ typedef enum {
   ETPC_ERR_UNSUPPORTED = 2,   /* l > 3, B > 16, more than 64 paths, ... */
   ETPC_ERR_INVALID_PATH = 3,  /* instruction violates the selection rule (Eq. 5) or uvu C_out != C_in */
   ETPC_ERR_WORKSPACE = 4,     /* workspace below the minimum of a pass (one node's state plus its
-                                 fixed parts; backward adds 12 B per edge); smaller than
+                                 fixed parts; backward adds 12 B per edge per lane); smaller than
                                  etpc_workspace_size() but above that minimum runs in node chunks */
   ETPC_ERR_OVERFLOW = 5,      /* N, E or an internal index would exceed int32 */
   ETPC_ERR_GRAPH = 6,         /* etpc_graph_validate found an inconsistent CSR */
@@ -125,9 +130,10 @@ etpc_status etpc_plan_out_irrep(etpc_plan plan, int32_t b, int32_t* n_out, etpc_
 etpc_status etpc_plan_cg(etpc_plan plan, int32_t p, double* out);
 
 /* Workspace bytes for a compute pass over a graph of n_nodes / n_edges with every node
- * in one chunk (the fastest schedule).  Grows with N (node-side states) and by 12 B per
- * edge for backward and double backward (the per-edge position adjoint); it never scales
- * with E times a channel width.  A compute call given less (down to one node's state)
+ * in one chunk (the fastest schedule).  Grows with N (node-side states) and, for backward
+ * and double backward, by 12 B per edge per concurrent launch lane (the per-edge position
+ * adjoint; up to two lanes, one per path or per uvu input block); it never scales with E
+ * times a channel width.  A compute call given less (down to one node's state)
  * runs the nodes in chunks that fit, with the same results up to summation order. */
 etpc_status etpc_workspace_size(etpc_plan plan, int32_t pass, int32_t n_nodes, int64_t n_edges,
                                 size_t* bytes);
@@ -169,6 +175,14 @@ etpc_status etpc_double_backward(etpc_plan plan, const etpc_graph* graph, const 
                                  const float* x_dot, const float* w_dot, const float* pos_dot,
                                  float* z_bar_grad, float* x_grad, float* w_grad, float* pos_grad,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Concurrent launch lanes (process-wide): the per-path launches of a pass run on up to
+ * `lanes` streams (1..2; default 2; out-of-range values are clamped).  1 serializes every
+ * launch on the caller's stream, which is how per-kernel durations are best timed.  Takes
+ * effect for calls that start afterwards; results do not depend on it beyond summation
+ * order of the per-lane position-adjoint copies.  etpc_get_lanes returns the setting. */
+etpc_status etpc_set_lanes(int32_t lanes);
+int32_t etpc_get_lanes(void);
 
 /* Kernel timing (off by default).  While enabled, every kernel the library enqueues is
  * bracketed by a pair of HIP events recorded on its launch stream, grouped by kind.

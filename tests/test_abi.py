@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "et
 
 def test_exports_every_declared_symbol():
     text = open(HEADER).read()
-    declared = set(re.findall(r"^\s*(?:etpc_status|void|const char\*)\s+(etpc_[a-z_]+)\s*\(", text, re.M))
+    declared = set(re.findall(r"^\s*(?:etpc_status|void|const char\*|int32_t)\s+(etpc_[a-z_]+)\s*\(", text, re.M))
     assert declared == set(etpc.SYMBOLS)
     for name in declared:
         assert hasattr(etpc.lib, name), name
@@ -71,22 +71,36 @@ def test_invalid_specs(kwargs, status):
 
 
 def test_workspace_is_node_sized():
-    """Workspace grows with N; with E only by the 12 B/edge position adjoint (backward, and
-    double backward with its d/dpos output)."""
+    """Workspace grows with N; with E only by the 12 B/edge position adjoint, one copy per
+    concurrent launch lane (backward, and double backward with its d/dpos output)."""
     plan = plan_from_config(CONFIGS["cfg4_d16"])
     n = 32768
     f = [etpc.etpc_workspace_size(plan, etpc.PASS_FWD, n, e) for e in (500000, 2000000, 16000000)]
     assert f[0] == f[1] == f[2]
+    lanes = min(2, plan.info()["n_paths"])   # one edge-adjoint copy per concurrent lane (two)
     b = [etpc.etpc_workspace_size(plan, etpc.PASS_BWD, n, int(e)) for e in (5e5, 2e6)]
-    assert abs((b[1] - b[0]) - 12 * 1.5e6) < 4096
+    assert abs((b[1] - b[0]) - 12 * lanes * 1.5e6) < 4096
     d = [etpc.etpc_workspace_size(plan, etpc.PASS_DBL, n, int(e)) for e in (5e5, 2e6)]
-    assert abs((d[1] - d[0]) - 12 * 1.5e6) < 4096
+    assert abs((d[1] - d[0]) - 12 * lanes * 1.5e6) < 4096
 
 
 def test_csr_workspace_size_and_argument_errors():
     assert etpc.etpc_csr_workspace_size(10, 100) > 0
     with pytest.raises(etpc.EtpcError):
         etpc.etpc_csr_workspace_size(-1, 10)
+
+
+def test_lane_setting_is_clamped():
+    old = etpc.etpc_get_lanes()
+    try:
+        etpc.etpc_set_lanes(1)
+        assert etpc.etpc_get_lanes() == 1
+        etpc.etpc_set_lanes(99)
+        assert 1 <= etpc.etpc_get_lanes() <= 4
+        etpc.etpc_set_lanes(0)
+        assert etpc.etpc_get_lanes() == 1
+    finally:
+        etpc.etpc_set_lanes(old)
 
 
 def test_missing_library_fails_loudly(tmp_path):
