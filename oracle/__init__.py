@@ -20,6 +20,8 @@ Modules:
   radial  -- Gaussian and Bessel-with-polynomial-envelope radial bases
   conv    -- forward / backward / double backward, materialized
   csr     -- receiver and sender CSR views (stable)
+  radius  -- radius graph of a point set by brute force (graph preparation)
+  layout  -- mul_ir <-> ir_mul feature layouts at the boundary
 
 Parity status: every function above is pinned by tests against something other
 than itself (closed forms, scipy/sympy routines, invariants, finite differences,
