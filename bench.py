@@ -442,6 +442,80 @@ def graph_count_sweep(args):
         "retention_at_endpoint": end["edges_per_s"] / peak, "sweep": points}), flush=True)
 
 
+def prep_bench(args):
+    """Graph preparation: radius-graph builds at the workloads' density and mul_ir -> ir_mul
+    conversions, each timed over --steps calls after --warmup; one JSON line."""
+    import ctypes as C
+
+    import numpy as np
+    import torch
+    import equivariant_gnn_tensor_amd as etpc
+    from workloads import CONFIGS
+
+    dev = torch.device("cuda:0")
+    rows = []
+    for n in (4096, 65536, 262144):
+        L = (n / 0.1) ** (1.0 / 3.0)
+        pos = torch.from_numpy(np.random.default_rng(n).uniform(0.0, L, size=(n, 3)).astype(np.float32)).to(dev)
+        cap = 64 * n
+        src = torch.empty(cap, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        ws = torch.empty(etpc.etpc_radius_graph_workspace_size(n, cap), dtype=torch.uint8, device=dev)
+        ne = C.c_int64()
+        box = (C.c_float * 3)(L, L, L)
+
+        def build():
+            st = etpc.lib.etpc_radius_graph(n, pos.data_ptr(), 5.0, box, cap, src.data_ptr(), dst.data_ptr(),
+                                            C.byref(ne), ws.data_ptr(), ws.numel(), None)
+            if st != 0:
+                raise RuntimeError(etpc.lib.etpc_last_error().decode())
+        for _ in range(args.warmup):
+            build()
+        torch.cuda.synchronize()
+        etpc.etpc_profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            build()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        kms, launches = etpc.etpc_profile_read("prep")
+        etpc.etpc_profile_enable(False)
+        rows.append(dict(n_nodes=n, box=round(L, 3), n_edges=int(ne.value), ms=ms, edges_per_s=ne.value / ms * 1e3,
+                         kernel_ms=kms / args.steps))
+        log(f"radius graph N={n}: E={ne.value} {ms:.3f} ms/build (kernels {kms / args.steps:.3f} ms) "
+            f"{ne.value / ms * 1e3:.3g} edges/s")
+        del pos, src, dst, ws
+    conv = []
+    cfg = CONFIGS["cfg2"]
+    plan = etpc.Plan(cfg.irreps_in, cfg.irreps_out, cfg.lmax_sh, cfg.mode, cfg.radial, cfg.n_basis, cfg.r_lo,
+                     cfg.r_hi, cfg.poly_p, box=cfg.box, out_per_path=cfg.out_per_path)
+    zdim = plan.info()["z_dim"]
+    for n in (4096, 262144):
+        x = torch.randn(n, zdim, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(args.warmup):
+            etpc.etpc_layout_convert(plan, "out", "to_ir_mul", x, out=y)
+        torch.cuda.synchronize()
+        etpc.etpc_profile_enable(True)
+        for _ in range(args.steps):
+            etpc.etpc_layout_convert(plan, "out", "to_ir_mul", x, out=y)
+        kms, _ = etpc.etpc_profile_read("prep")
+        etpc.etpc_profile_enable(False)
+        per = kms / args.steps
+        gbs = 2 * x.numel() * 4 / (per * 1e-3) / 1e9
+        conv.append(dict(rows=n, width=zdim, kernel_ms=per, gb_per_s=gbs, frac_hbm=gbs / 8000.0))
+        log(f"layout mul_ir->ir_mul {n}x{zdim}: {per * 1e3:.1f} us, {gbs:.0f} GB/s ({gbs / 8000:.3f} of 8 TB/s)")
+        del x, y
+    main_row = rows[1]
+    print(json.dumps({
+        "metric": "radius graph build, edges/s", "value": main_row["edges_per_s"], "unit": "edges/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_row["ms"], "higher_is_better": True,
+        "scaling": "strong", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "radius graph of uniform points at 0.1/A^3, cutoff 5 A, periodic cube",
+                   "n_nodes": main_row["n_nodes"]},
+        "radius_graph": rows, "layout_convert": conv}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +534,8 @@ def main():
                     help="time replays of one step captured as a HIP graph (launch-bound small workloads)")
     ap.add_argument("--graph-count-sweep", action="store_true",
                     help="time the graph-count batches (1..511 cells) and report throughput retention")
+    ap.add_argument("--prep", action="store_true",
+                    help="time the graph-preparation steps (radius graph, layout conversion)")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="summarize rocprofv3 output under DIR into profiles/ and exit (no GPU needed)")
     args = ap.parse_args()
@@ -476,6 +552,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.graph_count_sweep:
         graph_count_sweep(args)
+        return
+    if args.prep:
+        prep_bench(args)
         return
     result, cfg, wl = measure(args, args.workload)
     if args.copy_calibration_mib > 0:

@@ -23,7 +23,10 @@ UVW, UVU = 0, 1
 GAUSSIAN, BESSEL = 0, 1
 PASS_FWD, PASS_BWD, PASS_DBL = 0, 1, 2
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "INVALID_PATH", 4: "WORKSPACE", 5: "OVERFLOW",
-           6: "GRAPH", 7: "HIP"}
+           6: "GRAPH", 7: "HIP", 8: "CAPACITY"}
+ERR_CAPACITY = 8
+TO_IR_MUL, TO_MUL_IR = 0, 1
+FEATURES_IN, FEATURES_OUT = 0, 1
 
 
 class EtpcError(RuntimeError):
@@ -64,10 +67,10 @@ SYMBOLS = (
     "etpc_plan_create", "etpc_plan_destroy", "etpc_plan_info", "etpc_plan_path", "etpc_plan_out_irrep",
     "etpc_plan_cg", "etpc_workspace_size", "etpc_csr_workspace_size", "etpc_csr_build", "etpc_graph_validate",
     "etpc_forward", "etpc_backward", "etpc_double_backward", "etpc_set_lanes", "etpc_get_lanes",
-    "etpc_profile_enable", "etpc_profile_read",
-    "etpc_last_error",
+    "etpc_profile_enable", "etpc_profile_read", "etpc_radius_graph_workspace_size", "etpc_radius_graph",
+    "etpc_layout_convert", "etpc_last_error",
 )
-KINDS = ("csr", "fwd_traverse", "channel_gemm", "bwd_traverse", "node_gemm", "aux")
+KINDS = ("csr", "fwd_traverse", "channel_gemm", "bwd_traverse", "node_gemm", "aux", "prep")
 
 
 def _load():
@@ -95,6 +98,9 @@ def _load():
         "etpc_set_lanes": [i32],
         "etpc_get_lanes": [],
         "etpc_profile_read": [i32, P(C.c_double), P(i64)],
+        "etpc_radius_graph_workspace_size": [i32, i64, P(sz)],
+        "etpc_radius_graph": [i32, vp, C.c_float, P(C.c_float), i64, vp, vp, P(i64), vp, sz, vp],
+        "etpc_layout_convert": [vp, i32, i32, i32, vp, vp, vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -303,6 +309,51 @@ def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=No
 
 def etpc_graph_validate(graph: Graph, stream=None) -> None:
     _check(lib.etpc_graph_validate(C.byref(graph.c), _stream(stream)))
+
+
+def etpc_radius_graph_workspace_size(n_nodes: int, max_edges: int) -> int:
+    b = C.c_size_t()
+    _check(lib.etpc_radius_graph_workspace_size(n_nodes, max_edges, C.byref(b)))
+    return b.value
+
+
+def etpc_radius_graph(pos: torch.Tensor, cutoff: float, box=None, max_edges: Optional[int] = None,
+                      stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(src, dst) int32 device tensors of the radius graph, sorted by (receiver, sender).
+
+    Without max_edges the capacity starts at 64 edges per node; when the library reports
+    that it was too small, the buffers are re-allocated at the returned size and the call
+    is made once more."""
+    n = int(pos.shape[0])
+    dev = pos.device
+    cap = int(max_edges) if max_edges is not None else 64 * n
+    box_c = None if box is None else (C.c_float * 3)(*[float(b) for b in box])
+    for attempt in range(2):
+        src, dst = _empty_i32(cap, dev), _empty_i32(cap, dev)
+        ws, nb = _workspace(etpc_radius_graph_workspace_size(n, cap), dev)
+        ne = C.c_int64()
+        st = lib.etpc_radius_graph(n, _ptr(pos), float(cutoff), box_c, cap, _ptr(src, torch.int32),
+                                   _ptr(dst, torch.int32), C.byref(ne), None if ws is None else ws.data_ptr(), nb,
+                                   _stream(stream))
+        if st == ERR_CAPACITY and max_edges is None and attempt == 0:
+            cap = int(ne.value)
+            continue
+        _check(st)
+        e = int(ne.value)
+        return src[:e], dst[:e]
+    raise AssertionError("unreachable")
+
+
+def etpc_layout_convert(plan: Plan, features: str, direction: str, x: torch.Tensor, out=None,
+                        stream=None) -> torch.Tensor:
+    """features: "in" (x-like rows) or "out" (z-like rows); direction: "to_ir_mul" or "to_mul_ir"."""
+    f = {"in": FEATURES_IN, "out": FEATURES_OUT}[features]
+    d = {"to_ir_mul": TO_IR_MUL, "to_mul_ir": TO_MUL_IR}[direction]
+    if out is None:
+        out = torch.empty_like(x)
+    _check(lib.etpc_layout_convert(plan.handle, f, d, int(x.shape[0]) if x.dim() else 0, _ptr(x), _ptr(out),
+                                   _stream(stream)))
+    return out
 
 
 def _ws_for(plan, pass_, graph, ws):

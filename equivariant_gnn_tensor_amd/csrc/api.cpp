@@ -14,6 +14,7 @@
 //  double backward -- the directional program of Eq. 23-31 / 37-39 assembled from the
 //                  same traversals in tangent mode plus the same GEMMs.
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -28,6 +29,11 @@ etpc_status csr_build_impl(int32_t n_nodes, int64_t n_edges, const int32_t* src,
                            int32_t* col, int32_t* eid, int32_t* s_rowptr, int32_t* s_col, int32_t* s_slot, void* ws,
                            hipStream_t s);
 etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s);
+size_t radius_workspace_bytes(int32_t n_nodes, int64_t max_edges);
+etpc_status radius_graph_impl(int32_t n, const float* pos, float cutoff, const float* box, int64_t max_edges,
+                              int32_t* src, int32_t* dst, int64_t* n_edges, void* ws, hipStream_t s);
+etpc_status layout_convert_impl(const std::vector<etpc_irrep>& irreps, int direction, int32_t n_rows,
+                                const float* in, float* out, hipStream_t s);
 }  // namespace etpc
 
 namespace {
@@ -744,6 +750,54 @@ etpc_status etpc_graph_validate(const etpc_graph* g, hipStream_t stream) {
   if (g->n_edges > 0 && (g->col == nullptr || g->s_col == nullptr || g->s_slot == nullptr))
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null CSR index arrays");
   return graph_validate_impl(*g, stream);
+}
+
+etpc_status etpc_radius_graph_workspace_size(int32_t n_nodes, int64_t max_edges, size_t* bytes) {
+  if (bytes == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null output");
+  if (n_nodes < 0 || max_edges < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative size");
+  if (n_nodes >= (1 << 30)) ETPC_FAIL(ETPC_ERR_OVERFLOW, "n_nodes must be < 2^30");
+  *bytes = radius_workspace_bytes(n_nodes, max_edges);
+  return ETPC_OK;
+}
+
+etpc_status etpc_radius_graph(int32_t n_nodes, const float* pos, float cutoff, const float* box, int64_t max_edges,
+                              int32_t* src, int32_t* dst, int64_t* n_edges, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (n_edges == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null n_edges");
+  *n_edges = 0;
+  if (n_nodes < 0 || max_edges < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative size");
+  if (n_nodes >= (1 << 30)) ETPC_FAIL(ETPC_ERR_OVERFLOW, "n_nodes must be < 2^30");
+  if (!(cutoff > 0.f) || !std::isfinite(cutoff)) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "cutoff must be positive and finite");
+  if (box != nullptr)
+    for (int a = 0; a < 3; ++a) {
+      if (!(box[a] > 0.f) || !std::isfinite(box[a])) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "box lengths must be positive");
+      if (box[a] < 2.f * cutoff)
+        ETPC_FAIL(ETPC_ERR_INVALID_ARG, "cutoff exceeds half the box: the minimum image is not unique");
+    }
+  if (n_nodes == 0) return ETPC_OK;
+  if (pos == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null positions");
+  if (max_edges > 0 && (src == nullptr || dst == nullptr)) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null edge outputs");
+  etpc_status st = check_ws(ws, ws_bytes, radius_workspace_bytes(n_nodes, max_edges));
+  if (st != ETPC_OK) return st;
+  return radius_graph_impl(n_nodes, pos, cutoff, box, max_edges, src, dst, n_edges, ws, stream);
+}
+
+etpc_status etpc_layout_convert(etpc_plan p, int32_t features, int32_t direction, int32_t n_nodes, const float* in,
+                                float* out, hipStream_t stream) {
+  if (p == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null plan");
+  if (features != ETPC_FEATURES_IN && features != ETPC_FEATURES_OUT) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "bad features");
+  if (direction != ETPC_TO_IR_MUL && direction != ETPC_TO_MUL_IR) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "bad direction");
+  if (n_nodes < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative n_nodes");
+  if (n_nodes == 0) return ETPC_OK;
+  if (in == nullptr || out == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null in or out");
+  const std::vector<etpc_irrep>& ir = features == ETPC_FEATURES_IN ? p->in : p->out;
+  const int64_t width = features == ETPC_FEATURES_IN ? p->x_dim : p->z_dim;
+  if (static_cast<int64_t>(n_nodes) * width >= (int64_t(1) << 40)) ETPC_FAIL(ETPC_ERR_OVERFLOW, "too many elements");
+  const char* a = reinterpret_cast<const char*>(in);
+  const char* b = reinterpret_cast<const char*>(out);
+  const size_t bytes = static_cast<size_t>(n_nodes) * static_cast<size_t>(width) * sizeof(float);
+  if (a < b + bytes && b < a + bytes) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "in and out overlap");
+  return layout_convert_impl(ir, direction, n_nodes, in, out, stream);
 }
 
 etpc_status etpc_forward(etpc_plan p, const etpc_graph* g, const float* x, const float* pos, const float* w, float* z,

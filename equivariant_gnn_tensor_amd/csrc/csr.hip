@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "sort.hpp"
 
 namespace etpc {
 namespace {
@@ -156,6 +157,8 @@ __global__ void lower_bound_kernel(const int32_t* __restrict__ keys, int64_t n, 
   rowptr[v] = static_cast<int32_t>(lo);
 }
 
+}  // namespace
+
 int grid_for(int64_t n, int block) {
   int64_t g = (n + block - 1) / block;
   if (g > 65536) g = 65536;
@@ -192,11 +195,39 @@ int radix_passes(int32_t n_nodes) {
   return (bits + 7) / 8;
 }
 
-struct SortBufs {
-  int32_t *k0, *v0, *k1, *v1, *hist, *aux;
-};
+size_t sort_scratch_ints(int64_t n) {
+  const int64_t nblk = std::max<int64_t>((n + kSortTile - 1) / kSortTile, 1);
+  return static_cast<size_t>(256 * nblk) + scan_aux_ints(256 * nblk) + 64;
+}
 
-// Sorts (keys, vals) stably by key; result lands in (k0, v0).
+SortBufs make_sort_bufs(int32_t* k0, int32_t* v0, int32_t* k1, int32_t* v1, int32_t* scratch, int64_t n) {
+  const int64_t nblk = std::max<int64_t>((n + kSortTile - 1) / kSortTile, 1);
+  return SortBufs{k0, v0, k1, v1, scratch, scratch + 256 * nblk};
+}
+
+hipError_t launch_iota(int32_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(iota_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const int32_t* a, int32_t* b, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, a, b, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const int32_t* a, const int32_t* idx, int32_t* out, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, a, idx, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_lower_bound(const int32_t* keys, int64_t n, int32_t* rowptr, int32_t n_rows, hipStream_t s) {
+  hipLaunchKernelGGL(lower_bound_kernel, dim3((n_rows + 1 + 255) / 256), dim3(256), 0, s, keys, n, rowptr, n_rows);
+  return hipGetLastError();
+}
+
 hipError_t radix_sort(SortBufs& b, int64_t n, int passes, hipStream_t s) {
   const int nblk = static_cast<int>((n + kSortTile - 1) / kSortTile);
   for (int p = 0; p < passes; ++p) {
@@ -211,6 +242,8 @@ hipError_t radix_sort(SortBufs& b, int64_t n, int passes, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+namespace {
 
 __device__ int g_graph_error;
 

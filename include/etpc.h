@@ -69,7 +69,9 @@ typedef enum {
                                  etpc_workspace_size() but above that minimum runs in node chunks */
   ETPC_ERR_OVERFLOW = 5,      /* N, E or an internal index would exceed int32 */
   ETPC_ERR_GRAPH = 6,         /* etpc_graph_validate found an inconsistent CSR */
-  ETPC_ERR_HIP = 7            /* a HIP runtime call failed */
+  ETPC_ERR_HIP = 7,           /* a HIP runtime call failed */
+  ETPC_ERR_CAPACITY = 8       /* an output buffer is smaller than the result (the needed size is
+                                 returned where the call says) */
 } etpc_status;
 
 typedef enum { ETPC_UVW = 0, ETPC_UVU = 1 } etpc_mode;
@@ -151,6 +153,40 @@ etpc_status etpc_csr_build(int32_t n_nodes, int64_t n_edges, const int32_t* src,
 /* Debug check of the graph preconditions; synchronizes the stream.  Needs no workspace. */
 etpc_status etpc_graph_validate(const etpc_graph* graph, hipStream_t stream);
 
+/* Graph preparation: the radius graph of N points (the workloads of Sec. 3 are radius
+ * graphs, |E| growing as |V| rho r_c^3; the wrapper of Sec. 4 prepares the graph).
+ *   pos      [device] float [N][3]; finite.
+ *   cutoff   r_c > 0, finite.
+ *   box      [host] float[3] orthorhombic box edge lengths, each >= 2 r_c (minimum image,
+ *            at most one image within the cutoff), or NULL for open boundaries.
+ *   src, dst [device] int32 [max_edges] outputs: one edge j -> i for every ordered pair
+ *            (i != j) with 0 < |r|^2 < r_c^2, sorted by receiver, then sender.
+ *   n_edges  [host] out: the number of edges (also when it exceeds max_edges).
+ * The edge test is taken in float32 with every operation rounded on its own (no fused
+ * multiply-add): d_a = p_j,a - p_i,a, periodic d_a -= L_a rint(d_a (1/L_a)),
+ * |r|^2 = (d_x^2 + d_y^2) + d_z^2, compared with r_c * r_c; so the edge set depends on
+ * the positions only, never on the cell grid used to find it.  Bit-exact and
+ * deterministic.  Synchronizes the stream twice (to size the cell grid and to read the
+ * edge count), so it cannot be captured into a HIP graph.  Returns ETPC_ERR_CAPACITY,
+ * with *n_edges set and the outputs untouched, when max_edges is too small;
+ * ETPC_ERR_OVERFLOW for N >= 2^30 or 2^31 edges or more.  Workspace from
+ * etpc_radius_graph_workspace_size: about 36 B per node and 16 B per edge of capacity. */
+etpc_status etpc_radius_graph_workspace_size(int32_t n_nodes, int64_t max_edges, size_t* bytes);
+etpc_status etpc_radius_graph(int32_t n_nodes, const float* pos, float cutoff, const float* box,
+                              int64_t max_edges, int32_t* src, int32_t* dst, int64_t* n_edges,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Layout adapter (Sec. 4: kernels use ir_mul, the wrapper transposes the common mul_ir
+ * layout at the boundary).  Converts N feature rows of the plan's input irreps
+ * (features = ETPC_FEATURES_IN: x, x_bar, x_dot) or output irreps (ETPC_FEATURES_OUT: z,
+ * z_bar) between mul_ir (block k stored [C][2l+1]) and ir_mul ([2l+1][C]).  in and out
+ * are device [N][width] and must not overlap.  Asynchronous, allocates nothing, no
+ * workspace; bit-exact (pure data movement). */
+typedef enum { ETPC_TO_IR_MUL = 0, ETPC_TO_MUL_IR = 1 } etpc_layout_dir;
+typedef enum { ETPC_FEATURES_IN = 0, ETPC_FEATURES_OUT = 1 } etpc_features;
+etpc_status etpc_layout_convert(etpc_plan plan, int32_t features, int32_t direction, int32_t n_nodes,
+                                const float* in, float* out, hipStream_t stream);
+
 /* Forward: z = conv(x, pos, W) (Eq. 11-13), streaming order Eq. 32-35 (uvw: receiver
  * state S then a channel GEMM; uvu: edge-local weights, Eq. 17). */
 etpc_status etpc_forward(etpc_plan plan, const etpc_graph* graph, const float* x, const float* pos,
@@ -196,7 +232,8 @@ typedef enum {
   ETPC_KIND_BWD_TRAVERSE = 3, /* sender traversals (P state, edge position adjoint) */
   ETPC_KIND_NODE_GEMM = 4,    /* Xt = x W, x_bar = P W^T, W_bar = x^T P */
   ETPC_KIND_AUX = 5,          /* weight re-layout, fixed-order reductions, fills, pos_bar */
-  ETPC_KIND_COUNT = 6
+  ETPC_KIND_PREP = 6,         /* radius graph and layout conversion */
+  ETPC_KIND_COUNT = 7
 } etpc_kind;
 etpc_status etpc_profile_enable(int32_t enable);
 etpc_status etpc_profile_read(int32_t kind, double* total_ms, int64_t* launches);

@@ -113,3 +113,46 @@ def test_missing_library_fails_loudly(tmp_path):
         os.path.dirname(os.path.abspath(__file__))), env=env, capture_output=True, text=True)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "not built" in r.stderr
+
+
+def _radius_status(n, pos, cutoff, box, cap=0):
+    import ctypes as C
+    ne = C.c_int64(-1)
+    box_c = None if box is None else (C.c_float * 3)(*box)
+    st = etpc.lib.etpc_radius_graph(n, pos, cutoff, box_c, cap, None, None, C.byref(ne), None, 0, None)
+    return st, ne.value
+
+
+def test_radius_graph_argument_errors():
+    """Validated on the host before anything is enqueued."""
+    import ctypes as C
+    fake = 4096   # never dereferenced: every case below fails validation first
+    assert _radius_status(4, fake, 0.0, None)[0] == 1          # cutoff must be positive
+    assert _radius_status(4, fake, float("nan"), None)[0] == 1
+    assert _radius_status(4, fake, 3.0, (5.0, 8.0, 8.0))[0] == 1   # box below 2 r_c
+    assert _radius_status(4, fake, 1.0, (5.0, 0.0, 8.0))[0] == 1
+    assert _radius_status(-1, fake, 1.0, None)[0] == 1
+    assert _radius_status(1 << 30, fake, 1.0, None)[0] == 5
+    assert _radius_status(4, None, 1.0, None)[0] == 1          # null positions
+    assert _radius_status(0, None, 1.0, None) == (0, 0)       # empty point set: no edges
+    st = etpc.lib.etpc_radius_graph(4, fake, 1.0, None, 0, None, None, None, None, 0, None)
+    assert st == 1                                             # null n_edges
+    assert "n_edges" in etpc.lib.etpc_last_error().decode()
+    assert _radius_status(4, fake, 1.0, None, cap=8)[0] == 1   # null outputs with capacity
+
+
+def test_radius_graph_workspace_grows_with_capacity():
+    a = etpc.etpc_radius_graph_workspace_size(1000, 0)
+    b = etpc.etpc_radius_graph_workspace_size(1000, 100000)
+    assert a > 36 * 1000 and 16 * 100000 <= b - a <= 17 * 100000
+
+
+def test_layout_convert_argument_errors():
+    plan = plan_from_config(CONFIGS["cfg2"])
+    lib = etpc.lib
+    assert lib.etpc_layout_convert(None, 0, 0, 4, 4096, 8192, None) == 1
+    assert lib.etpc_layout_convert(plan.handle, 2, 0, 4, 4096, 8192, None) == 1
+    assert lib.etpc_layout_convert(plan.handle, 0, 5, 4, 4096, 8192, None) == 1
+    assert lib.etpc_layout_convert(plan.handle, 0, 0, 4, 4096, 4096 + 16, None) == 1   # overlap
+    assert "overlap" in lib.etpc_last_error().decode()
+    assert lib.etpc_layout_convert(plan.handle, 1, 1, 0, None, None, None) == 0       # no rows

@@ -1,0 +1,164 @@
+"""GPU parity of the graph-preparation steps against the oracle (bit-exact: integer output
+and pure data movement).
+
+Radius graph: the edge list (receiver-major, senders ascending) must equal the brute-force
+oracle's exactly.  Cases: the workloads' own densities (0.1 atoms / A^3, cutoff 5 A,
+periodic cubes of 4096 and 16384 atoms), open boundaries, ragged sizes, boxes with fewer
+than three cells per axis, atoms outside the box, coincident atoms and a pair exactly at
+the cutoff, far-apart clusters (the cell grid is widened to its cap), one and two atoms,
+and the capacity error.  At 65,536 atoms the oracle checks sampled receivers' rows, and
+the whole list is checked for order, symmetry and validity.
+
+Layout: mul_ir <-> ir_mul of the workloads' input and output irreps, ragged row counts,
+round trips.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import layout as olayout
+from oracle import radius as oradius
+from tests.gpu_helpers import note
+from tests.planner_helpers import plan_from_config
+from workloads import CONFIGS
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _etpc():
+    import equivariant_gnn_tensor_amd as etpc
+    return etpc
+
+
+def _uniform(n, L, seed):
+    return np.random.default_rng(seed).uniform(0.0, L, size=(n, 3)).astype(np.float32)
+
+
+def _run(pos, cutoff, box):
+    etpc = _etpc()
+    src, dst = etpc.etpc_radius_graph(torch.from_numpy(np.ascontiguousarray(pos)).cuda(), cutoff, box=box)
+    torch.cuda.synchronize()
+    return src.cpu().numpy(), dst.cpu().numpy()
+
+
+def _assert_same(pos, cutoff, box, what):
+    note(f"radius graph {what}: N={pos.shape[0]} cutoff={cutoff} box={box}")
+    gs, gd = _run(pos, cutoff, box)
+    rs, rd = oradius.radius_graph(pos, cutoff, box)
+    note(f"  edges gpu {gs.size} oracle {rs.size}")
+    assert gs.size == rs.size
+    assert np.array_equal(gd, rd) and np.array_equal(gs, rs)
+    return gs.size
+
+
+def _box_side(n, density=0.1):
+    return float((n / density) ** (1.0 / 3.0))
+
+
+@pytest.mark.parametrize("n", [4096, 16384])
+def test_radius_graph_workload_density(n):
+    L = _box_side(n)
+    pos = _uniform(n, L, 100 + n)
+    e = _assert_same(pos, 5.0, (L, L, L), f"periodic density 0.1, {n} atoms")
+    assert e > 40 * n   # about 52 neighbours per atom at this density
+
+
+def test_radius_graph_open_and_ragged():
+    pos = _uniform(1237, 30.0, 3)
+    _assert_same(pos, 4.0, None, "open, ragged")
+    pos = np.random.default_rng(4).normal(0.0, 3.0, size=(777, 3)).astype(np.float32)
+    _assert_same(pos, 2.5, None, "open, Gaussian cloud")
+
+
+def test_radius_graph_few_cells_and_wrapping():
+    # L = 2.4 r_c: two cells per axis, every cell visited once
+    pos = _uniform(300, 12.0, 5)
+    _assert_same(pos, 5.0, (12.0, 12.0, 12.0), "two cells per axis")
+    # L = 2 r_c exactly: one cell per axis
+    _assert_same(_uniform(120, 10.0, 6), 5.0, (10.0, 10.0, 10.0), "one cell per axis")
+    # atoms outside the box and non-cubic boxes
+    pos = (_uniform(500, 1.0, 7) * np.array([60.0, 20.0, 33.0], np.float32)
+           - np.array([25.0, 8.0, 40.0], np.float32)).astype(np.float32)
+    _assert_same(pos, 4.0, (20.0, 10.0, 11.0), "outside the box, orthorhombic")
+
+
+def test_radius_graph_degenerate_pairs():
+    pos = _uniform(200, 15.0, 8)
+    pos[10] = pos[11]                          # coincident atoms: no edge between them
+    pos[20] = pos[21] + np.array([3.0, 0.0, 0.0], np.float32)
+    pos = np.concatenate([pos, np.array([[0, 0, 0], [3, 0, 0], [0, 0, 0]], np.float32)])
+    _assert_same(pos, 3.0, None, "coincident and at-cutoff pairs")
+    lat = np.array(np.meshgrid(*[np.arange(6)] * 3, indexing="ij"), np.float32).reshape(3, -1).T
+    n = _assert_same(lat, 1.5, (6.0, 6.0, 6.0), "simple cubic lattice, 18 neighbours")
+    assert n == 18 * 216
+
+
+def test_radius_graph_far_clusters_and_tiny_sets():
+    a = _uniform(150, 8.0, 9)
+    b = _uniform(150, 8.0, 10) + np.float32(1e4)
+    _assert_same(np.concatenate([a, b]).astype(np.float32), 3.0, None, "far-apart clusters")
+    _assert_same(np.zeros((1, 3), np.float32), 2.0, None, "one atom")
+    _assert_same(np.array([[0, 0, 0], [1, 1, 1]], np.float32), 2.0, (5.0, 5.0, 5.0), "two atoms")
+    _assert_same(_uniform(64, 4.0, 11), 10.0, None, "all atoms in one cell")
+
+
+def test_radius_graph_capacity_error_reports_size():
+    etpc = _etpc()
+    pos = torch.from_numpy(_uniform(500, 12.0, 12)).cuda()
+    rs, _ = oradius.radius_graph(pos.cpu().numpy(), 3.0, None)
+    with pytest.raises(etpc.EtpcError) as ei:
+        etpc.etpc_radius_graph(pos, 3.0, max_edges=10)
+    assert ei.value.name == "CAPACITY" and str(rs.size) in str(ei.value)
+    src, dst = etpc.etpc_radius_graph(pos, 3.0, max_edges=rs.size)
+    assert src.numel() == rs.size
+
+
+def test_radius_graph_large_sampled():
+    etpc = _etpc()
+    n = 65536
+    L = _box_side(n)
+    pos = _uniform(n, L, 13)
+    note(f"radius graph large: N={n} box={L:.2f}")
+    src, dst = etpc.etpc_radius_graph(torch.from_numpy(pos).cuda(), 5.0, box=(L, L, L))
+    torch.cuda.synchronize()
+    s64, d64 = src.long(), dst.long()
+    e = s64.numel()
+    note(f"  edges {e}")
+    key = d64 * n + s64
+    assert bool((key[1:] > key[:-1]).all())                              # canonical order, no duplicates
+    assert bool((s64 != d64).all()) and int(s64.min()) >= 0 and int(s64.max()) < n
+    tkey, _ = torch.sort(s64 * n + d64)                                   # the transpose, sorted
+    assert torch.equal(tkey, key)                                         # symmetric
+    rowptr = torch.searchsorted(d64, torch.arange(n + 1, device=d64.device))
+    rng = np.random.default_rng(14)
+    recv = np.sort(rng.choice(n, 24, replace=False))
+    rs, rd = oradius.neighbours_of(pos, recv, 5.0, (L, L, L))
+    rp = rowptr.cpu().numpy()
+    gs = np.concatenate([src[rp[i]:rp[i + 1]].cpu().numpy() for i in recv])
+    assert np.array_equal(gs, rs)
+
+
+@pytest.mark.parametrize("name", ["cfg2", "cfg3", "cfg1"])
+@pytest.mark.parametrize("n_rows", [1, 37, 1000])
+def test_layout_convert_matches_oracle(name, n_rows):
+    etpc = _etpc()
+    cfg = CONFIGS[name]
+    plan = plan_from_config(cfg)
+    rng = np.random.default_rng(n_rows)
+    for features, irreps in (("in", etpc.parse_irreps(cfg.irreps_in)), ("out", plan.out_irreps())):
+        width = sum(m * (2 * l + 1) for m, l, _ in irreps)
+        x = rng.standard_normal((n_rows, width)).astype(np.float32)
+        xt = torch.from_numpy(x).cuda()
+        a = etpc.etpc_layout_convert(plan, features, "to_ir_mul", xt)
+        b = etpc.etpc_layout_convert(plan, features, "to_mul_ir", xt)
+        back = etpc.etpc_layout_convert(plan, features, "to_mul_ir", a)
+        torch.cuda.synchronize()
+        assert np.array_equal(a.cpu().numpy(), olayout.mul_ir_to_ir_mul(x, irreps))
+        assert np.array_equal(b.cpu().numpy(), olayout.ir_mul_to_mul_ir(x, irreps))
+        assert torch.equal(back, xt)
