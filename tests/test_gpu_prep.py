@@ -162,3 +162,27 @@ def test_layout_convert_matches_oracle(name, n_rows):
         assert np.array_equal(a.cpu().numpy(), olayout.mul_ir_to_ir_mul(x, irreps))
         assert np.array_equal(b.cpu().numpy(), olayout.ir_mul_to_mul_ir(x, irreps))
         assert torch.equal(back, xt)
+
+
+@pytest.mark.parametrize("irreps", ["3x0e+1x1o+5x2e", "2048x2e+3x0e+7x3o", "16x1o+1x0e+1x0o+2x3o"])
+def test_layout_convert_odd_widths_and_offsets(irreps):
+    """Widths that are not a multiple of 4 or exceed the LDS strip, and misaligned rows."""
+    etpc = _etpc()
+    plan = etpc.Plan(irreps, irreps, 1, "uvw", "gaussian", 4, 0.0, 5.0, 6)
+    ir = etpc.parse_irreps(irreps)
+    width = sum(m * (2 * l + 1) for m, l, _ in ir)
+    rng = np.random.default_rng(width)
+    for n_rows in (1, 29):
+        x = rng.standard_normal((n_rows, width)).astype(np.float32)
+        for shift in (0, 1):
+            buf_in = torch.zeros(n_rows * width + 1, device="cuda")
+            buf_out = torch.zeros(n_rows * width + 1, device="cuda")
+            xin = buf_in[shift:shift + n_rows * width].view(n_rows, width)
+            xin.copy_(torch.from_numpy(x))
+            xout = buf_out[shift:shift + n_rows * width].view(n_rows, width)
+            etpc.etpc_layout_convert(plan, "in", "to_ir_mul", xin, out=xout)
+            torch.cuda.synchronize()
+            assert np.array_equal(xout.cpu().numpy(), olayout.mul_ir_to_ir_mul(x, ir))
+            etpc.etpc_layout_convert(plan, "out", "to_mul_ir", xin, out=xout)
+            torch.cuda.synchronize()
+            assert np.array_equal(xout.cpu().numpy(), olayout.ir_mul_to_mul_ir(x, ir))
