@@ -263,7 +263,8 @@ def measure(args, name):
         etpc.etpc_set_lanes(args.lanes)
     cfg = CONFIGS[name]
     plan = etpc.Plan(cfg.irreps_in, cfg.irreps_out, cfg.lmax_sh, cfg.mode, cfg.radial, cfg.n_basis, cfg.r_lo,
-                     cfg.r_hi, cfg.poly_p, box=cfg.box, out_per_path=cfg.out_per_path)
+                     cfg.r_hi, cfg.poly_p, box=cfg.box, out_per_path=cfg.out_per_path,
+                     gemm_precision=args.gemm_precision)
     info = plan.info()
     mask = scalar_mask(cfg.irreps_out) if cfg.cotangent == "energy" else None
     wl = make_workload(cfg, w_blocks=plan.w_blocks(), z_dim=info["z_dim"], scalar_out_mask=mask)
@@ -378,7 +379,7 @@ def measure(args, name):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32" if args.gemm_precision == "fp32" else "f32, bf16 channel GEMMs",
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: N={N} atoms at 0.1/A^3 (periodic), radius graph 5 A, E={E}, "
@@ -530,6 +531,8 @@ def main():
                     help="after timing, run a plain device copy of this size (counter calibration)")
     ap.add_argument("--lanes", type=int, default=0,
                     help="concurrent launch lanes per pass for the timed steps (0 = library default)")
+    ap.add_argument("--gemm-precision", choices=("fp32", "bf16"), default="fp32",
+                    help="channel GEMM operands: fp32 (reference) or bf16 with fp32 accumulation")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured as a HIP graph (launch-bound small workloads)")
     ap.add_argument("--graph-count-sweep", action="store_true",

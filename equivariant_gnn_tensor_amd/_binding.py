@@ -27,6 +27,7 @@ _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "INVALID_PATH", 4: "W
 ERR_CAPACITY = 8
 TO_IR_MUL, TO_MUL_IR = 0, 1
 FEATURES_IN, FEATURES_OUT = 0, 1
+GEMM_FP32, GEMM_BF16 = 0, 1
 
 
 class EtpcError(RuntimeError):
@@ -51,7 +52,7 @@ class etpc_spec(C.Structure):
         ("out_per_path", C.c_int32), ("lmax_sh", C.c_int32), ("mode", C.c_int32),
         ("n_instr", C.c_int32), ("instr", C.POINTER(etpc_instr)),
         ("radial", C.c_int32), ("n_basis", C.c_int32), ("r_lo", C.c_float), ("r_hi", C.c_float),
-        ("poly_p", C.c_int32), ("box", C.c_float * 3),
+        ("poly_p", C.c_int32), ("box", C.c_float * 3), ("gemm_precision", C.c_int32),
     ]
 
 
@@ -158,7 +159,7 @@ class Plan:
     def __init__(self, irreps_in, irreps_out, lmax_sh: int, mode: str = "uvw", radial: str = "gaussian",
                  n_basis: int = 8, r_lo: float = 0.0, r_hi: float = 5.0, poly_p: int = 6,
                  box: Optional[Sequence[float]] = None, out_per_path: bool = False,
-                 instructions: Optional[Sequence[Tuple[int, int, int]]] = None):
+                 instructions: Optional[Sequence[Tuple[int, int, int]]] = None, gemm_precision: str = "fp32"):
         ins, outs = parse_irreps(irreps_in), parse_irreps(irreps_out)
         self.irreps_in = ins
         self._in = (etpc_irrep * len(ins))(*[etpc_irrep(*t) for t in ins])
@@ -177,6 +178,7 @@ class Plan:
         spec.n_basis, spec.r_lo, spec.r_hi, spec.poly_p = n_basis, r_lo, r_hi, poly_p
         b = (0.0, 0.0, 0.0) if box is None else (tuple(box) if hasattr(box, "__len__") else (box, box, box))
         spec.box = (C.c_float * 3)(*b)
+        spec.gemm_precision = {"fp32": GEMM_FP32, "bf16": GEMM_BF16}[gemm_precision]
         self.spec = spec
         self.handle = C.c_void_p()
         self.handle = etpc_plan_create(spec)

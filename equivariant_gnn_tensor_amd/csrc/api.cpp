@@ -370,6 +370,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       }
       ETPC_HIP(lanes.finish());
       GemmArgs ga{};
+      ga.bf16 = p->gemm_bf16 ? 1 : 0;
       ga.A = L.S;
       ga.amap = plain(D);
       ga.a_mcontig = 0;
@@ -469,6 +470,7 @@ hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float*
   int64_t ks = (K + sp - 1) / sp;
   ks = (ks + 31) / 32 * 32;
   GemmArgs ga{};
+  ga.bf16 = p->gemm_bf16 ? 1 : 0;
   ga.A = xa + j0 * p->x_dim + p->xoff[k];
   ga.amap = irmul(ni, p->x_dim, c_in);
   ga.a_mcontig = 1;
@@ -493,6 +495,7 @@ etpc_status xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float
   const int64_t ncols = d.block_ncols[k];
   const int c_in = p->in[k].mul;
   GemmArgs ga{};
+  ga.bf16 = p->gemm_bf16 ? 1 : 0;
   ga.A = state;
   ga.amap = plain(ncols);
   ga.a_mcontig = 0;
@@ -541,6 +544,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       }
       if (want_pos) {  // Xt = x W
         GemmArgs ga{};
+        ga.bf16 = p->gemm_bf16 ? 1 : 0;
         ga.A = R.x + j0 * p->x_dim + p->xoff[k];
         ga.amap = irmul(ni, p->x_dim, c_in);
         ga.a_mcontig = 0;

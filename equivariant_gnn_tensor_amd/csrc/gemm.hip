@@ -1,4 +1,5 @@
-// Dense fp32 GEMM on the gfx950 matrix cores (v_mfma_f32_32x32x2f32).
+// Dense GEMM on the gfx950 matrix cores: fp32 (v_mfma_f32_32x32x2f32), or with bf16
+// operands and fp32 accumulation (v_mfma_f32_32x32x16_bf16) when the plan asks for it.
 //
 // Used for the channel-space products of the Sobek paper (Sec. 4, Eq. 34-36):
 // m = S W (forward), and the node-side products of the sender-factorized
@@ -249,6 +250,137 @@ __global__ __launch_bounds__(256) void gemm_f32_narrow_kernel(const GemmArgs a) 
   }
 }
 
+// ---------------------------------------------------------------- bf16 operands
+// The reduced-precision option (the analogue of the TF32 channel GEMMs the Sobek paper
+// lists as optional in Sec. 4): A and B are read as fp32, rounded to bf16 (nearest, ties
+// to even) when staged in LDS, multiplied on v_mfma_f32_32x32x16_bf16 and accumulated in
+// fp32.  Tiles as in the fp32 kernels (WGM x WGN wavefronts of 32 x 32); LDS holds A as
+// [m][k] and B as [n][k] so each lane reads its eight consecutive k as one 16-byte load.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);   // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <int WGM, int WGN>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs a) {
+  constexpr int BM = 32 * WGM, BN = 32 * WGN;
+  constexpr int AG = BM / 32, BG = BN / 32;
+  constexpr int LK = BK + 8;   // padded k stride (elements): rows stay 16-byte aligned
+  __shared__ __attribute__((aligned(16))) uint16_t As[BM][LK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN][LK];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid % WGM, wn = wid / WGM;
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const int kz0 = blockIdx.z * a.k_split;
+  const int kz1 = min(a.K, kz0 + a.k_split);
+  float* C = a.C + static_cast<int64_t>(blockIdx.z) * a.c_split_stride;
+  const bool vec = a.vec4 != 0;
+
+  int64_t a_off[AG];
+  bool a_ok[AG];
+  if (!a.a_mcontig) {
+#pragma unroll
+    for (int h = 0; h < AG; ++h) {
+      const int m = m0 + ((tid + 256 * h) >> 3);
+      a_ok[h] = m < a.M;
+      a_off[h] = a_ok[h] ? rowoff(a.amap, m) : 0;
+    }
+  }
+  float ra[AG][4], rb[BG][4];
+  auto load4 = [&](const float* p, int valid, float* dst) {
+    if (valid == 4 && vec) {
+      const float4 v = *reinterpret_cast<const float4*>(p);
+      dst[0] = v.x;
+      dst[1] = v.y;
+      dst[2] = v.z;
+      dst[3] = v.w;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) dst[t] = t < valid ? p[t] : 0.f;
+    }
+  };
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int h = 0; h < AG; ++h) {
+      const int g = tid + 256 * h;
+      if (!a.a_mcontig) {
+        const int k = k0 + (g & 7) * 4;
+        load4(a.A + a_off[h] + k, a_ok[h] ? min(4, kz1 - k) : 0, ra[h]);
+      } else {
+        const int k = k0 + g / (BM / 4);
+        const int m = m0 + (g % (BM / 4)) * 4;
+        const int valid = k < kz1 ? min(4, a.M - m) : 0;
+        load4(a.A + (valid > 0 ? rowoff(a.amap, k) : 0) + m, valid, ra[h]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < BG; ++h) {
+      const int g = tid + 256 * h;
+      const int k = k0 + g / (BN / 4);
+      const int n = n0 + (g % (BN / 4)) * 4;
+      const int valid = k < kz1 ? min(4, a.N - n) : 0;
+      load4(a.B + static_cast<int64_t>(k < kz1 ? k : 0) * a.ldb + n, valid, rb[h]);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int h = 0; h < AG; ++h) {
+      const int g = tid + 256 * h;
+      if (!a.a_mcontig) {
+        const int row = g >> 3, k4 = (g & 7) * 4;
+        const uint32_t lo = bf16_rne(ra[h][0]) | (static_cast<uint32_t>(bf16_rne(ra[h][1])) << 16);
+        const uint32_t hi = bf16_rne(ra[h][2]) | (static_cast<uint32_t>(bf16_rne(ra[h][3])) << 16);
+        *reinterpret_cast<uint2*>(&As[row][k4]) = make_uint2(lo, hi);
+      } else {
+        const int k = g / (BM / 4), m4 = (g % (BM / 4)) * 4;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) As[m4 + t][k] = bf16_rne(ra[h][t]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < BG; ++h) {
+      const int g = tid + 256 * h;
+      const int k = g / (BN / 4), n4 = (g % (BN / 4)) * 4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Bs[n4 + t][k] = bf16_rne(rb[h][t]);
+    }
+  };
+
+  f16v acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  if (kz0 < kz1) load(kz0);
+  // lane l supplies row (or column) l % 32 and the eight k values 8 (l / 32) .. + 7
+  const int am = wm * 32 + (lane & 31), bn = wn * 32 + (lane & 31), k8 = 8 * (lane >> 5);
+  for (int k0 = kz0; k0 < kz1; k0 += BK) {
+    store();
+    __syncthreads();
+    if (k0 + BK < kz1) load(k0 + BK);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&As[am][kk + k8]);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bs[bn][kk + k8]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  const int n = n0 + wn * 32 + (lane & 31);
+  if (n < a.N) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (m < a.M) {
+        float* p = C + rowoff(a.cmap, m) + n;
+        *p = a.beta ? (*p + acc[r]) : acc[r];
+      }
+    }
+  }
+}
+
 // C(m, n) (+)= sum_s part[s][m][n], fixed order in s
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits, int M, int N, float* __restrict__ C,
                                      RowMap cmap, int beta) {
@@ -268,6 +400,19 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 
 hipError_t launch_gemm(const GemmArgs& a, int splits, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.bf16) {
+    if (a.N <= 32 && a.M > 32) {
+      dim3 grid((a.M + 127) / 128, (a.N + 31) / 32, splits);
+      hipLaunchKernelGGL((gemm_bf16_kernel<4, 1>), grid, dim3(256), 0, s, a);
+    } else if (a.M <= 32 && a.N > 32) {
+      dim3 grid((a.M + 31) / 32, (a.N + 127) / 128, splits);
+      hipLaunchKernelGGL((gemm_bf16_kernel<1, 4>), grid, dim3(256), 0, s, a);
+    } else {
+      dim3 grid((a.M + 63) / 64, (a.N + 63) / 64, splits);
+      hipLaunchKernelGGL((gemm_bf16_kernel<2, 2>), grid, dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   // a side of at most 32 (a 32-channel operand) gets a 32-wide tile, so no half tile of
   // MFMA work and loads is wasted on padding
   if (a.N <= 32 && a.M > 32) {

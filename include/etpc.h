@@ -77,6 +77,12 @@ typedef enum {
 typedef enum { ETPC_UVW = 0, ETPC_UVU = 1 } etpc_mode;
 typedef enum { ETPC_RADIAL_GAUSSIAN = 0, ETPC_RADIAL_BESSEL_POLY = 1 } etpc_radial;
 typedef enum { ETPC_PASS_FWD = 0, ETPC_PASS_BWD = 1, ETPC_PASS_DBL = 2 } etpc_pass;
+/* Arithmetic of the channel-space GEMMs (z = S W, Xt = x W, x_bar = P W^T, W_bar = x^T P).
+ * FP32 is the reference schedule.  BF16 rounds both operands to bf16 (nearest, ties to
+ * even) and accumulates in fp32 on the matrix cores: the analogue of the optional TF32
+ * channel GEMMs of Sec. 4, with about 2^-9 relative rounding per operand.  The traversals
+ * and every reduction stay fp32. */
+typedef enum { ETPC_GEMM_FP32 = 0, ETPC_GEMM_BF16 = 1 } etpc_gemm_precision;
 
 /* One irrep block: multiplicity, degree l (0..3) and parity (+1 'e', -1 'o'). */
 typedef struct { int32_t mul, l, parity; } etpc_irrep;
@@ -97,6 +103,7 @@ typedef struct {
   float r_lo, r_hi;                           /* Gaussian range; Bessel cutoff = r_hi */
   int32_t poly_p;                             /* Bessel envelope exponent p >= 1 */
   float box[3];                               /* all zero = open; else orthorhombic minimum image */
+  int32_t gemm_precision;                     /* etpc_gemm_precision; 0 (default) = fp32 */
 } etpc_spec;
 
 /* Receiver-sorted CSR plus the sender (source) view; all DEVICE pointers.

@@ -29,12 +29,12 @@ class Case:
     z_bar: torch.Tensor
 
 
-def make_case(cfg, dev="cuda:0"):
+def make_case(cfg, dev="cuda:0", gemm_precision="fp32"):
     import equivariant_gnn_tensor_amd as etpc
     spec = conv.spec_from_config(cfg)
     mask = scalar_mask(cfg.irreps_out) if cfg.cotangent == "energy" else None
     wl = make_workload(cfg, w_blocks=spec.plan.w_blocks(), z_dim=spec.plan.z_dim, scalar_out_mask=mask)
-    plan = plan_from_config(cfg)
+    plan = plan_from_config(cfg, gemm_precision)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     graph = etpc.etpc_csr_build(cfg.n_nodes, t(wl.src), t(wl.dst))
     return Case(cfg, spec, plan, wl, graph, t(wl.x), t(wl.pos), t(wl.w), t(wl.z_bar))
