@@ -508,13 +508,31 @@ def prep_bench(args):
         log(f"layout mul_ir->ir_mul {n}x{zdim}: {per * 1e3:.1f} us, {gbs:.0f} GB/s ({gbs / 8000:.3f} of 8 TB/s)")
         del x, y
     main_row = rows[1]
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle (brute force over all pairs) on a bounded sample of receivers of the 65,536-atom case
+        from oracle import radius as oradius
+        n = main_row["n_nodes"]
+        L = (n / 0.1) ** (1.0 / 3.0)
+        pos = np.random.default_rng(n).uniform(0.0, L, size=(n, 3)).astype(np.float32)
+        t0 = time.perf_counter()
+        done = edges = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0):
+            recv = np.arange(done, min(done + 256, n))
+            s_, _ = oradius.neighbours_of(pos, recv, 5.0, (L, L, L))
+            edges += s_.size
+            done += recv.size
+        dt = time.perf_counter() - t0
+        cpu = {"value": edges / dt, "unit": "edges/s", "cores": 1,   # numpy elementwise work: one thread
+               "kind": "oracle", "sample": f"brute-force rows of {done} of {n} receivers ({edges} edges) in {dt:.1f} s"}
+        log(f"oracle radius graph: {edges / dt:.3g} edges/s on {done} receivers")
     print(json.dumps({
         "metric": "radius graph build, edges/s", "value": main_row["edges_per_s"], "unit": "edges/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_row["ms"], "higher_is_better": True,
         "scaling": "strong", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "radius graph of uniform points at 0.1/A^3, cutoff 5 A, periodic cube",
                    "n_nodes": main_row["n_nodes"]},
-        "radius_graph": rows, "layout_convert": conv}), flush=True)
+        "radius_graph": rows, "layout_convert": conv, "cpu_baseline": cpu}), flush=True)
 
 
 def main():

@@ -84,7 +84,16 @@ int rbar_slots(const etpc_plan_s* p) {
   const int units = p->mode == ETPC_UVW ? static_cast<int>(p->paths.size()) : count_blocks(p, true);
   return std::max(1, std::min(kLanes, units));
 }
-int rbar_lanes(const etpc_plan_s* p) { return std::min(rbar_slots(p), lanes_limit()); }
+// Below about 2^16 edge-channels a pass's launches take a few microseconds each, less
+// than a fork and join of side streams costs, so such calls stay on one lane.
+constexpr int64_t kLaneMinWork = int64_t(1) << 16;
+int lane_cap(const etpc_plan_s* p, const etpc_graph* g) {
+  int64_t cmax = 1;
+  for (const auto& b : p->in) cmax = std::max<int64_t>(cmax, b.mul);
+  for (const auto& b : p->out) cmax = std::max<int64_t>(cmax, b.mul);
+  return g->n_edges * cmax < kLaneMinWork ? 1 : lanes_limit();
+}
+int rbar_lanes(const etpc_plan_s* p, const etpc_graph* g) { return std::min(rbar_slots(p), lane_cap(p, g)); }
 // lane of each block for n lanes (blocks without paths get lane 0, unused)
 std::vector<int> block_lanes(const etpc_plan_s* p, bool by_in, int n) {
   const auto& groups = by_in ? p->by_in : p->by_out;
@@ -342,7 +351,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       const int nrecv = static_cast<int>(std::min<int64_t>(chunk, N - r0));
       int32_t col0 = 0;
       // the paths of a group fill disjoint column ranges of S: concurrent lanes
-      LaneGroup lanes(s, static_cast<int>(paths.size()));
+      LaneGroup lanes(s, std::min(static_cast<int>(paths.size()), lane_cap(p, g)));
       ETPC_HIP(lanes.status());
       for (size_t t = 0; t < paths.size(); ++t) {
         const PathInfo& pi = p->paths[paths[t]];
@@ -393,7 +402,7 @@ etpc_status fwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
                         const float* pos_dot, const float* win, float* z, bool beta, bool tangent, hipStream_t s) {
   const GeomParams geom = p->geom();
   std::vector<int> seen(p->out.size(), 0);
-  const int nl = std::max(1, std::min(lanes_limit(), count_blocks(p, false)));
+  const int nl = std::max(1, std::min(lane_cap(p, g), count_blocks(p, false)));
   const std::vector<int> lane_of = block_lanes(p, false, nl);   // z accumulates per output block
   LaneGroup lanes(s, nl);
   ETPC_HIP(lanes.status());
@@ -838,7 +847,7 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
   const Derived d = derive(p);
   const bool want_pos = pos_bar != nullptr;
   const bool need_p = x_bar || w_bar;
-  const int lanes = rbar_lanes(p);
+  const int lanes = rbar_lanes(p, g);
   const int32_t N = g->n_nodes;
   if (N == 0) {
     if (w_bar) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_bar, p->w_numel, 0.f, s));
@@ -906,7 +915,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     return ETPC_OK;
   }
   const bool want_pos = pos_grad != nullptr;
-  const int lanes = rbar_lanes(p);
+  const int lanes = rbar_lanes(p, g);
   const Derived d = derive(p);
   const bool tan = pos_dot != nullptr;
   const bool plain = x_dot != nullptr || w_dot != nullptr;
