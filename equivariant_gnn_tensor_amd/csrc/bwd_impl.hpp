@@ -235,9 +235,13 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
         const int t = it * nslots + slot;
         const bool tvalid = t < ne;
         const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
+        // No mask on the gathered row: a padding trip reads real data (edge 0's record and a
+        // clamped row), so only its state update is masked (through phi below), its edge
+        // adjoint is never stored, and lanes past c_out hold Xt = 0, so they add zeros
+        // to every lane sum.
         float zb[NO];
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) zb[mo] = (tvalid && wvalid) ? zq[pf][mo] : 0.f;
+        for (int mo = 0; mo < NO; ++mo) zb[mo] = zq[pf][mo];
         float V[NI][NS];
         cg_contract_out<LI, LS, LO>(zb, V);
         // the row is consumed: its registers take the gather kPrefetch trips ahead (no
@@ -259,14 +263,14 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
         }
 #pragma unroll
         for (int qq = 0; qq < NBQ; ++qq) {
-          const float ph = e[R::kPhi + 4 * qq + q4];
+          const float ph = tvalid ? e[R::kPhi + 4 * qq + q4] : 0.f;
           if constexpr (NEED_P) {
 #pragma unroll
             for (int mi = 0; mi < NI; ++mi)
               P[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, Q[mi], P[mi][qq], 0, 0, 0);
           }
           if constexpr (TAN) {
-            const float phd = e[R::kPhiDot + 4 * qq + q4];
+            const float phd = tvalid ? e[R::kPhiDot + 4 * qq + q4] : 0.f;
 #pragma unroll
             for (int mi = 0; mi < NI; ++mi) {
               Pd[mi][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(phd, Q[mi], Pd[mi][qq], 0, 0, 0);
@@ -313,13 +317,17 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
             rb[d] = s;
           }
           float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+          float lanev[3];
 #pragma unroll
           for (int d = 0; d < 3; ++d) {
             // r_bar = srad u + dY^T Wy; its tangent = d srad u + srad du + d(dY)^T Wy + dY^T dWy
-            const float lanev = HESS ? sradd * e[R::kU + d] + srad * e[R::kUDot + d] + rb[d]
-                                     : srad * e[R::kU + d] + rb[d];
-            const float v = row_sum16(lanev);
-            if (tvalid && row_leader) sr[d] = v;
+            lanev[d] = HESS ? sradd * e[R::kU + d] + srad * e[R::kUDot + d] + rb[d] : srad * e[R::kU + d] + rb[d];
+          }
+          row_sum16x3(lanev[0], lanev[1], lanev[2]);
+          if (tvalid && row_leader) {
+            sr[0] = lanev[0];
+            sr[1] = lanev[1];
+            sr[2] = lanev[2];
           }
         }
       }
@@ -445,7 +453,7 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
           const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
           float zb[NO];
 #pragma unroll
-          for (int mo = 0; mo < NO; ++mo) zb[mo] = (tvalid && uvalid) ? zq[pf][mo] : 0.f;
+          for (int mo = 0; mo < NO; ++mo) zb[mo] = zq[pf][mo];   // masked below, through w_e and h
           gather(t + kPrefetch * nslots, zq[pf]);
           __builtin_amdgcn_sched_barrier(kSchedMask);
           float V[NI][NS];
@@ -474,11 +482,15 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
             if constexpr (HESS) wdd += e[R::kDDphi + q] * wv[q];
           }
           if constexpr (!HESS) {
+            // a padding trip (real but foreign data) adds nothing; lanes past c hold
+            // x = 0 and w = 0, so their h, w_e and lane-sum terms are zero already
+            const float wem = tvalid ? we : 0.f, wedm = tvalid ? wed : 0.f;
+            const float hm = tvalid ? h : 0.f, hdm = tvalid ? hd : 0.f;
 #pragma unroll
-            for (int mi = 0; mi < NI; ++mi) xb[mi] += TAN ? (wed * Q[mi] + we * Qd[mi]) : we * Q[mi];
+            for (int mi = 0; mi < NI; ++mi) xb[mi] += TAN ? (wedm * Q[mi] + wem * Qd[mi]) : wem * Q[mi];
 #pragma unroll
             for (int q = 0; q < NB; ++q)
-              wbar[q] += TAN ? (e[R::kPhiDot + q] * h + e[R::kPhi + q] * hd) : e[R::kPhi + q] * h;
+              wbar[q] += TAN ? (e[R::kPhiDot + q] * hm + e[R::kPhi + q] * hdm) : e[R::kPhi + q] * hm;
           }
           if (want_pos) {
             const float srad = wdr * h;
@@ -503,21 +515,25 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
               rbd[d] = sd;
             }
             float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+            float lanev[3];
 #pragma unroll
             for (int d = 0; d < 3; ++d) {
               // r_bar = srad u + w_e dY^T Wy (srad = w_e' h); its tangent along r_dot:
               // d srad u + srad du + d w_e dY^T Wy + w_e d(dY)^T Wy, with d w_e = rho_dot w_e',
               // d srad = rho_dot w_e'' h + w_e' dh
-              float lanev;
               if constexpr (HESS) {
                 const float rho_dot = e[R::kRhoDot];
                 const float sradd = rho_dot * wdd * h + wdr * hd;
-                lanev = sradd * e[R::kU + d] + srad * e[R::kUDot + d] + rho_dot * wdr * rb[d] + we * rbd[d];
+                lanev[d] = sradd * e[R::kU + d] + srad * e[R::kUDot + d] + rho_dot * wdr * rb[d] + we * rbd[d];
               } else {
-                lanev = srad * e[R::kU + d] + we * rb[d];
+                lanev[d] = srad * e[R::kU + d] + we * rb[d];
               }
-              const float v = row_sum16(lanev);
-              if (tvalid && row_leader) sr[d] = v;
+            }
+            row_sum16x3(lanev[0], lanev[1], lanev[2]);
+            if (tvalid && row_leader) {
+              sr[0] = lanev[0];
+              sr[1] = lanev[1];
+              sr[2] = lanev[2];
             }
           }
         }

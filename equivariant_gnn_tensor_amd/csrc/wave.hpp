@@ -19,4 +19,22 @@ __device__ inline float row_sum16(float v) {
   return v;
 }
 
+// Three row sums at once, their steps interleaved: each DPP step reads a value written
+// two instructions earlier, which covers the DPP read-after-write wait states without
+// s_nop.
+__device__ inline void row_sum16x3(float& a, float& b, float& c) {
+  a += dpp_f<0x128>(a);
+  b += dpp_f<0x128>(b);
+  c += dpp_f<0x128>(c);
+  a += dpp_f<0x124>(a);
+  b += dpp_f<0x124>(b);
+  c += dpp_f<0x124>(c);
+  a += dpp_f<0x122>(a);
+  b += dpp_f<0x122>(b);
+  c += dpp_f<0x122>(c);
+  a += dpp_f<0x121>(a);
+  b += dpp_f<0x121>(b);
+  c += dpp_f<0x121>(c);
+}
+
 }  // namespace etpc
