@@ -53,27 +53,34 @@ typedef float f4v __attribute__((ext_vector_type(4)));
 // d(dY/dr)[3][NS] along pos_dot (Hessian), u[3] (positions), du[3] and d|r| along
 // pos_dot (Hessian).  The coupling tensor is not stored per edge: its compile-time
 // sparse form is applied per lane (CgTab).
-template <int NB, int NS, bool POS, bool TAN, bool HESS = false>
+// Field offsets are rounded up to multiples of A floats.  A = 4 puts every field on a
+// 16-byte boundary, so its broadcast reads are ds_read_b128: the uvu traversal gains from
+// that (-2%), while the uvw traversals measured slower with the larger record (+4%), so
+// they keep the packed one (A = 1).
+template <int A>
+constexpr int rec_align(int n) { return (n + A - 1) / A * A; }
+template <int NB, int NS, bool POS, bool TAN, bool HESS = false, int A = 1>
 struct BwdRec {
+  static constexpr int kNSP = rec_align<A>(NS);   // row length of the dY/dr and d(dY/dr) rows
   static constexpr int kPhi = 0;
-  static constexpr int kDphi = NB;
-  static constexpr int kPhiDot = kDphi + (POS ? NB : 0);
-  static constexpr int kDDphi = kPhiDot + (TAN ? NB : 0);
-  static constexpr int kY = kDDphi + (HESS ? NB : 0);
-  static constexpr int kDY = kY + NS;
-  static constexpr int kYDot = kDY + (POS ? 3 * NS : 0);
-  static constexpr int kDDY = kYDot + ((TAN || HESS) ? NS : 0);
-  static constexpr int kU = kDDY + (HESS ? 3 * NS : 0);
+  static constexpr int kDphi = rec_align<A>(NB);
+  static constexpr int kPhiDot = rec_align<A>(kDphi + (POS ? NB : 0));
+  static constexpr int kDDphi = rec_align<A>(kPhiDot + (TAN ? NB : 0));
+  static constexpr int kY = rec_align<A>(kDDphi + (HESS ? NB : 0));
+  static constexpr int kDY = rec_align<A>(kY + NS);
+  static constexpr int kYDot = rec_align<A>(kDY + (POS ? 3 * kNSP : 0));
+  static constexpr int kDDY = rec_align<A>(kYDot + ((TAN || HESS) ? NS : 0));
+  static constexpr int kU = rec_align<A>(kDDY + (HESS ? 3 * kNSP : 0));
   static constexpr int kUDot = kU + (POS ? 3 : 0);
   static constexpr int kRhoDot = kUDot + (HESS ? 3 : 0);
-  static constexpr int kStride = kRhoDot + (HESS ? 1 : 0) + 1;
+  static constexpr int kStride = rec_align<A>(kRhoDot + (HESS ? 1 : 0) + 1);
 };
 
-template <int LS, int NB, bool POS, bool TAN, bool NEED_D, bool HESS = false>
+template <int LS, int NB, bool POS, bool TAN, bool NEED_D, bool HESS = false, int A = 1>
 __device__ inline void bwd_fill_rec(const GeomParams& g, const float* __restrict__ pos,
                                     const float* __restrict__ pos_dot, int j, int i, float* __restrict__ e) {
   constexpr int NS = 2 * LS + 1;
-  using R = BwdRec<NB, NS, POS, TAN, HESS>;
+  using R = BwdRec<NB, NS, POS, TAN, HESS, A>;
   float rx, ry, rz;
   edge_vector(g, pos, j, i, rx, ry, rz);
   const float r = sqrtf(rx * rx + ry * ry + rz * rz);
@@ -96,8 +103,8 @@ __device__ inline void bwd_fill_rec(const GeomParams& g, const float* __restrict
     e[R::kY + m] = y[m];
     if constexpr (POS) {
       e[R::kDY + m] = gy[m][0];
-      e[R::kDY + NS + m] = gy[m][1];
-      e[R::kDY + 2 * NS + m] = gy[m][2];
+      e[R::kDY + R::kNSP + m] = gy[m][1];
+      e[R::kDY + 2 * R::kNSP + m] = gy[m][2];
     }
   }
   if constexpr (TAN || HESS) {
@@ -119,8 +126,8 @@ __device__ inline void bwd_fill_rec(const GeomParams& g, const float* __restrict
 #pragma unroll
       for (int m = 0; m < NS; ++m) {
         e[R::kDDY + m] = ddy[m][0];
-        e[R::kDDY + NS + m] = ddy[m][1];
-        e[R::kDDY + 2 * NS + m] = ddy[m][2];
+        e[R::kDDY + R::kNSP + m] = ddy[m][1];
+        e[R::kDDY + 2 * R::kNSP + m] = ddy[m][2];
       }
       e[R::kUDot + 0] = udx;
       e[R::kUDot + 1] = udy;
@@ -160,7 +167,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
   static_assert(!HESS || (POS && !TAN && !NEED_P), "the Hessian pass is a position-only pass");
   using R = BwdRec<NB, NS, POS, TAN, HESS>;
-  __shared__ float s_edge[64 * R::kStride];
+  __shared__ __attribute__((aligned(16))) float s_edge[64 * R::kStride];
   __shared__ int s_i[64];
   __shared__ int s_sl[64];
   extern __shared__ float s_dyn[];   // [nwaves][64][rows][3] edge-adjoint partials
@@ -210,15 +217,20 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
     // Unconditional loads from a clamped in-bounds address (no branch per load); lanes
     // without an edge are zeroed when the row is consumed, not here, so nothing waits
     // on the load before its own trip.
-    auto gather = [&](int t, float* dst) {
-      const int i = s_i[t < ne ? t : 0];
-      const float* zr = a.z_bar + static_cast<int64_t>(t < ne ? i : 0) * a.z_dim + a.zoff + (wvalid ? w : 0);
+    // receiver of trip slot t (0 past the chunk: a clamped, harmless row)
+    auto recv_of = [&](int t) { return t < ne ? s_i[t] : 0; };
+    auto gather = [&](int i, float* dst) {
+      const float* zr = a.z_bar + static_cast<int64_t>(i) * a.z_dim + a.zoff + (wvalid ? w : 0);
 #pragma unroll
       for (int mo = 0; mo < NO; ++mo) dst[mo] = zr[mo * a.c_out];
     };
+    // the receiver index of each gather is read one round ahead, so forming the gather
+    // address never waits on an LDS read
+    int next_i[kPrefetch];
 #pragma unroll
     for (int pf = 0; pf < kPrefetch; ++pf) {
-      gather(pf * nslots + slot, zq[pf]);
+      gather(recv_of(pf * nslots + slot), zq[pf]);
+      next_i[pf] = recv_of((pf + kPrefetch) * nslots + slot);
       // Pass the first rows through an arithmetic op: when every value entering the
       // loop-carried registers is a plain load, the optimizer merges them into one load
       // at the top of the loop, which undoes the prefetch.
@@ -247,7 +259,8 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
         // the row is consumed: its registers take the gather kPrefetch trips ahead (no
         // register copy, so nothing waits for that load until its own trip); the
         // scheduling barrier keeps the loads here instead of sunk to the loop end
-        gather(t + kPrefetch * nslots, zq[pf]);
+        gather(next_i[pf], zq[pf]);
+        next_i[pf] = recv_of(t + 2 * kPrefetch * nslots);
         __builtin_amdgcn_sched_barrier(kSchedMask);
         float Q[NI], Qd[NI];
 #pragma unroll
@@ -310,9 +323,9 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
 #pragma unroll
             for (int my = 0; my < NS; ++my) {
               if constexpr (HESS)
-                s += e[R::kDDY + d * NS + my] * wy[my] + e[R::kRhoDot] * e[R::kDY + d * NS + my] * wg[my];
+                s += e[R::kDDY + d * R::kNSP + my] * wy[my] + e[R::kRhoDot] * e[R::kDY + d * R::kNSP + my] * wg[my];
               else
-                s += e[R::kDY + d * NS + my] * wy[my];
+                s += e[R::kDY + d * R::kNSP + my] * wy[my];
             }
             rb[d] = s;
           }
@@ -391,8 +404,9 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
   constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
   constexpr bool POS = !TAN;   // position adjoint only in the first-order and Hessian passes
   static_assert(!(HESS && TAN), "the Hessian pass has no tangent state");
-  using R = BwdRec<NB, NS, true, TAN, HESS>;
-  __shared__ float s_edge[64 * R::kStride];
+  constexpr int kRecAlign = 4;
+  using R = BwdRec<NB, NS, true, TAN, HESS, kRecAlign>;
+  __shared__ __attribute__((aligned(16))) float s_edge[64 * R::kStride];
   __shared__ int s_i[64];
   __shared__ int s_sl[64];
   extern __shared__ float s_dyn[];   // [nwaves][64][rows][3]
@@ -425,7 +439,8 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
       const int ne = min(kWave, k1 - base);
       if (tid < ne) {
         const int i = a.s_col[base + tid];
-        bwd_fill_rec<LS, NB, true, TAN, true, HESS>(a.g, a.pos, a.pos_dot, j, i, s_edge + tid * R::kStride);
+        bwd_fill_rec<LS, NB, true, TAN, true, HESS, kRecAlign>(a.g, a.pos, a.pos_dot, j, i,
+                                                                s_edge + tid * R::kStride);
         s_i[tid] = i;
         s_sl[tid] = a.s_slot[base + tid];
       }
@@ -433,6 +448,8 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
       const int trips = (ne + nslots - 1) / nslots;
       // same software pipeline as the uvw sender traversal
       float zq[kPrefetch][NO];
+      // (reading the receiver index one round ahead, as the uvw traversal does, measured
+      // 2% slower here)
       auto gather = [&](int t, float* dst) {
         const int i = s_i[t < ne ? t : 0];
         const float* zr = a.z_bar + static_cast<int64_t>(t < ne ? i : 0) * a.z_dim + a.zoff + (uvalid ? u : 0);
@@ -508,8 +525,8 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
               float s = 0.f, sd = 0.f;
 #pragma unroll
               for (int my = 0; my < NS; ++my) {
-                s += e[R::kDY + d * NS + my] * wy[my];
-                if constexpr (HESS) sd += e[R::kDDY + d * NS + my] * wy[my];
+                s += e[R::kDY + d * R::kNSP + my] * wy[my];
+                if constexpr (HESS) sd += e[R::kDDY + d * R::kNSP + my] * wy[my];
               }
               rb[d] = s;
               rbd[d] = sd;
