@@ -153,22 +153,28 @@ int pick_splits(int64_t M, int64_t N, int64_t K) {
 // ---------------------------------------------------------------- workspace layouts
 constexpr int kGemmSplits = 8;   // split-K partial sets kept for the long-K channel / x_bar GEMMs
 
+// Two sets of the buffers the node-side GEMMs read (S forward; Xt, P and the re-laid-out
+// weights backward): groups / blocks alternate between them, so one set's GEMMs can run
+// on the post stream while the next traversals fill the other set.
+constexpr int kSets = 2;
+
 struct FwdLayout {
-  float* S = nullptr;
+  float* S[kSets] = {};
   float* part = nullptr;
   int64_t part_cap = 0;
 };
 void fwd_layout(const etpc_plan_s* p, const Derived& d, int64_t chunk, Carver& c, FwdLayout& L) {
   if (p->mode == ETPC_UVW) {
-    L.S = c.take<float>(static_cast<size_t>(chunk * d.max_s));
+    for (int b = 0; b < kSets; ++b) L.S[b] = c.take<float>(static_cast<size_t>(chunk * d.max_s));
     L.part_cap = kGemmSplits * chunk * d.max_zrow;
     L.part = c.take<float>(static_cast<size_t>(L.part_cap));
   }
 }
 
 struct BwdLayout {
-  float *rbar = nullptr, *wcat = nullptr, *wt = nullptr, *wt2 = nullptr, *wpart = nullptr;
-  float *xt = nullptr, *P = nullptr, *Pd = nullptr;
+  float *rbar = nullptr, *wpart = nullptr;
+  float *wcat[kSets] = {}, *wt[kSets] = {}, *wt2[kSets] = {};
+  float *xt[kSets] = {}, *P[kSets] = {}, *Pd[kSets] = {};
   float* xpart = nullptr;
   int64_t xpart_cap = 0;
   int64_t wpart_lane = 0;   // uvu: floats of W_bar partials per lane
@@ -179,9 +185,11 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t
                 bool tan, bool wbar, bool wbar2, bool xbar, bool wt2, Carver& c, BwdLayout& L) {
   if (p->mode == ETPC_UVW) {
     if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * rbar_slots(p)));
-    if (pos) L.wcat = c.take<float>(static_cast<size_t>(d.max_wcat));
-    if (xbar) L.wt = c.take<float>(static_cast<size_t>(d.max_wcat));
-    if (wt2) L.wt2 = c.take<float>(static_cast<size_t>(d.max_wcat));
+    for (int b = 0; b < kSets; ++b) {
+      if (pos) L.wcat[b] = c.take<float>(static_cast<size_t>(d.max_wcat));
+      if (xbar) L.wt[b] = c.take<float>(static_cast<size_t>(d.max_wcat));
+      if (wt2) L.wt2[b] = c.take<float>(static_cast<size_t>(d.max_wcat));
+    }
     if (wbar) {
       // split-K partial tiles of W_bar: as many splits as wbar_gemm picks for this chunk
       int64_t need = 0;
@@ -193,9 +201,11 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t
       }
       L.wpart = c.take<float>(static_cast<size_t>((wbar2 ? 2 : 1) * need));
     }
-    if (pos) L.xt = c.take<float>(static_cast<size_t>(chunk * d.max_state));
-    if (need_p) L.P = c.take<float>(static_cast<size_t>(chunk * d.max_state));
-    if (tan) L.Pd = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+    for (int b = 0; b < kSets; ++b) {
+      if (pos) L.xt[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+      if (need_p) L.P[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+      if (tan) L.Pd[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+    }
     if (xbar) {
       L.xpart_cap = kGemmSplits * chunk * d.max_xrow;
       L.xpart = c.take<float>(static_cast<size_t>(L.xpart_cap));
@@ -334,6 +344,28 @@ hipError_t zero_unreached_in(const etpc_plan_s* p, float* x, int32_t n, hipStrea
   return launch_fill(x, static_cast<int64_t>(n) * p->x_dim, 0.f, s);
 }
 
+// Output groups with paths, by decreasing channel-GEMM work per node (o C_out D_g), ties
+// in plan order.
+std::vector<int> group_order(const etpc_plan_s* p, const Derived& d) {
+  std::vector<int> order;
+  for (size_t gi = 0; gi < p->out.size(); ++gi)
+    if (!p->by_out[gi].empty()) order.push_back(static_cast<int>(gi));
+  auto work = [&](int gi) { return int64_t(2 * p->out[gi].l + 1) * p->out[gi].mul * d.group_d[gi]; };
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) > work(b); });
+  return order;
+}
+
+// Input blocks with paths, by decreasing node-GEMM work per node ((2l+1) C_in ncols), ties
+// in plan order.
+std::vector<int> block_order(const etpc_plan_s* p, const Derived& d) {
+  std::vector<int> order;
+  for (size_t k = 0; k < p->in.size(); ++k)
+    if (!p->by_in[k].empty()) order.push_back(static_cast<int>(k));
+  auto work = [&](int k) { return int64_t(2 * p->in[k].l + 1) * p->in[k].mul * d.block_ncols[k]; };
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) > work(b); });
+  return order;
+}
+
 // One uvw forward evaluation into z (beta: accumulate into z).  With tangent, the
 // receiver traversal builds dS along pos_dot.  xin / win select the operands.
 etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* xin,
@@ -341,14 +373,19 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
                         const FwdLayout& L, int64_t chunk, hipStream_t s) {
   const GeomParams geom = p->geom();
   const int32_t N = g->n_nodes;
-  for (size_t gi = 0; gi < p->out.size(); ++gi) {
+  // the channel GEMM of one group runs on the post stream while the next group's
+  // traversals fill the other S set; the largest GEMMs go first, so they overlap most
+  PostStream post(s, lane_cap(p, g) > 1);
+  ETPC_HIP(post.status());
+  int set = 0;
+  for (const int gi : group_order(p, d)) {
     const auto& paths = p->by_out[gi];
-    if (paths.empty()) continue;
     const int no = 2 * p->out[gi].l + 1;
     const int64_t D = d.group_d[gi];
     const int c_out = p->out[gi].mul;
     for (int64_t r0 = 0; r0 < N; r0 += chunk) {
       const int nrecv = static_cast<int>(std::min<int64_t>(chunk, N - r0));
+      ETPC_HIP(post.wait_slot(set));
       int32_t col0 = 0;
       // the paths of a group fill disjoint column ranges of S: concurrent lanes
       LaneGroup lanes(s, std::min(static_cast<int>(paths.size()), lane_cap(p, g)));
@@ -361,7 +398,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.pos = pos;
         a.pos_dot = pos_dot;
         a.x = xin;
-        a.S = L.S;
+        a.S = L.S[set];
         a.recv0 = static_cast<int32_t>(r0);
         a.x_dim = static_cast<int32_t>(p->x_dim);
         a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
@@ -378,9 +415,10 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         col0 += p->n_basis * pi.c_in;
       }
       ETPC_HIP(lanes.finish());
+      ETPC_HIP(post.follow());
       GemmArgs ga{};
       ga.bf16 = p->gemm_bf16 ? 1 : 0;
-      ga.A = L.S;
+      ga.A = L.S[set];
       ga.amap = plain(D);
       ga.a_mcontig = 0;
       ga.B = win + p->paths[paths[0]].w_off;
@@ -391,10 +429,13 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       ga.M = nrecv * no;
       ga.N = c_out;
       ga.K = static_cast<int32_t>(D);
-      etpc_status st = gemm_auto(ga, L.part, L.part_cap, kGemmSplits, ETPC_KIND_CHANNEL_GEMM, s);
+      etpc_status st = gemm_auto(ga, L.part, L.part_cap, kGemmSplits, ETPC_KIND_CHANNEL_GEMM, post.stream());
       if (st != ETPC_OK) return st;
+      ETPC_HIP(post.mark(set));
+      set ^= 1;
     }
   }
+  ETPC_HIP(post.finish());
   return ETPC_OK;
 }
 
@@ -526,49 +567,93 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   const bool want_pos = R.rbar != nullptr;
   const bool main_state = R.tangent || (R.x_out || R.w_out);        // P (plain) or dP (tangent)
   const bool need_plain = R.tangent ? R.plain_needed : main_state;   // plain P
-  float* Pmain = R.tangent ? L.Pd : L.P;
   const int nl = std::max(1, R.lanes);
   const int64_t rbar_stride = 3 * g->n_edges;
   if (R.x_out) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
-  for (int64_t j0 = 0; j0 < N; j0 += chunk) {
+  // A software pipeline over (sender chunk, input block) items, alternating two buffer
+  // sets: while item i's traversals run on the caller's stream and its lanes, the post
+  // stream re-lays out the weights and forms Xt = x W for item i + 1 in the other set,
+  // then runs item i's x_bar / W_bar GEMMs once its traversals are done.
+  PostStream post(s, nl > 1);
+  ETPC_HIP(post.status());
+  const std::vector<int> order = block_order(p, d);
+  struct Item {
+    int64_t j0;
+    int k;
+  };
+  std::vector<Item> items;
+  for (int64_t j0 = 0; j0 < N; j0 += chunk)
+    for (const int k : order) items.push_back(Item{j0, k});
+  // weight re-layouts and Xt of one item into buffer set `b`, on stream `st`
+  auto prep = [&](const Item& it, int b, hipStream_t st) -> etpc_status {
+    const int k = it.k;
+    const int ni = 2 * p->in[k].l + 1;
+    const int64_t ncols = d.block_ncols[k];
+    const int c_in = p->in[k].mul;
+    const int nsend = static_cast<int>(std::min<int64_t>(chunk, N - it.j0));
+    WPrepArgs wa;
+    if (want_pos || R.x_out) {
+      wprep_args(p, d, k, R.w, want_pos ? L.wcat[b] : nullptr, R.x_out ? L.wt[b] : nullptr, wa);
+      ETPC_LAUNCH_ON(ETPC_KIND_AUX, st, launch_wprep(wa, st));
+    }
+    if (R.x_out && R.w2) {
+      wprep_args(p, d, k, R.w2, nullptr, L.wt2[b], wa);
+      ETPC_LAUNCH_ON(ETPC_KIND_AUX, st, launch_wprep(wa, st));
+    }
+    if (want_pos) {  // Xt = x W
+      GemmArgs ga{};
+      ga.bf16 = p->gemm_bf16 ? 1 : 0;
+      ga.A = R.x + it.j0 * p->x_dim + p->xoff[k];
+      ga.amap = irmul(ni, p->x_dim, c_in);
+      ga.a_mcontig = 0;
+      ga.B = L.wcat[b];
+      ga.ldb = ncols;
+      ga.C = L.xt[b];
+      ga.cmap = plain(ncols);
+      ga.beta = 0;
+      ga.M = nsend * ni;
+      ga.N = static_cast<int32_t>(ncols);
+      ga.K = c_in;
+      ga.k_split = c_in;
+      set_vec4(ga);
+      ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, st, launch_gemm(ga, 1, st));
+    }
+    return ETPC_OK;
+  };
+  if (!items.empty()) {
+    etpc_status st0 = prep(items[0], 0, s);
+    if (st0 != ETPC_OK) return st0;
+  }
+  // each lane's copy of the edge adjoint is first written by its first path of a chunk
+  bool rbar_started[kLanes];
+  int t_glob = 0;
+  for (size_t ii = 0; ii < items.size(); ++ii) {
+    const int64_t j0 = items[ii].j0;
+    const int k = items[ii].k;
+    const int set = static_cast<int>(ii & 1);
+    if (ii == 0 || j0 != items[ii - 1].j0) {
+      for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc;
+      t_glob = 0;
+    }
     const int nsend = static_cast<int>(std::min<int64_t>(chunk, N - j0));
-    // each lane's copy of the edge adjoint is first written by its first path of this chunk
-    bool rbar_started[kLanes];
-    for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc;
-    int t_glob = 0;
-    for (size_t k = 0; k < p->in.size(); ++k) {
+    {
       const auto& paths = p->by_in[k];
-      if (paths.empty()) continue;
-      const int ni = 2 * p->in[k].l + 1;
       const int64_t ncols = d.block_ncols[k];
       const int c_in = p->in[k].mul;
-      WPrepArgs wa;
-      if (want_pos || R.x_out) {
-        wprep_args(p, d, static_cast<int>(k), R.w, want_pos ? L.wcat : nullptr, R.x_out ? L.wt : nullptr, wa);
-        ETPC_LAUNCH(ETPC_KIND_AUX, launch_wprep(wa, s));
+      // the next item's weights and Xt go into the other set, behind the post work of
+      // the item that last used it
+      if (ii + 1 < items.size()) {
+        // the previous item's traversals (which read that set's Xt) are enqueued before
+        // this point: the post stream waits for them first
+        ETPC_HIP(post.follow());
+        etpc_status stp = prep(items[ii + 1], set ^ 1, post.stream());
+        if (stp != ETPC_OK) return stp;
+        ETPC_HIP(post.ready(set ^ 1));
       }
-      if (R.x_out && R.w2) {
-        wprep_args(p, d, static_cast<int>(k), R.w2, nullptr, L.wt2, wa);
-        ETPC_LAUNCH(ETPC_KIND_AUX, launch_wprep(wa, s));
-      }
-      if (want_pos) {  // Xt = x W
-        GemmArgs ga{};
-        ga.bf16 = p->gemm_bf16 ? 1 : 0;
-        ga.A = R.x + j0 * p->x_dim + p->xoff[k];
-        ga.amap = irmul(ni, p->x_dim, c_in);
-        ga.a_mcontig = 0;
-        ga.B = L.wcat;
-        ga.ldb = ncols;
-        ga.C = L.xt;
-        ga.cmap = plain(ncols);
-        ga.beta = 0;
-        ga.M = nsend * ni;
-        ga.N = static_cast<int32_t>(ncols);
-        ga.K = c_in;
-        ga.k_split = c_in;
-        set_vec4(ga);
-        ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, launch_gemm(ga, 1, s));
-      }
+      ETPC_HIP(post.wait_ready(set));   // this item's Xt (prefetched, or made above on s)
+      ETPC_HIP(post.wait_slot(set));    // its P set is no longer read by older post work
+      float* const Pset = L.P[set];
+      float* const Pmain = R.tangent ? L.Pd[set] : L.P[set];
       // the block's paths write disjoint P columns and their own lane's edge adjoint copy
       LaneGroup lanes(s, nl);
       ETPC_HIP(lanes.status());
@@ -582,9 +667,9 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.pos = pos;
         a.pos_dot = R.pos_dot;
         a.z_bar = z_bar;
-        a.xt = L.xt;
-        a.P = L.P;
-        a.Pdot = L.Pd;
+        a.xt = L.xt[set];
+        a.P = Pset;
+        a.Pdot = L.Pd[set];
         a.rbar = R.rbar ? R.rbar + lane * rbar_stride : nullptr;
         a.send0 = static_cast<int32_t>(j0);
         a.z_dim = static_cast<int32_t>(p->z_dim);
@@ -606,34 +691,42 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         if (want_pos) rbar_started[lane] = true;
       }
       ETPC_HIP(lanes.finish());
-      if (R.x_out) {
-        if (main_state) {
-          etpc_status st = xbar_gemm(p, d, static_cast<int>(k), Pmain, L.wt, R.x_out, j0, nsend, false, L, s);
-          if (st != ETPC_OK) return st;
+      if (R.x_out || R.w_out) {
+        ETPC_HIP(post.follow());
+        const hipStream_t ps = post.stream();
+        if (R.x_out) {
+          if (main_state) {
+            etpc_status st = xbar_gemm(p, d, k, Pmain, L.wt[set], R.x_out, j0, nsend, false, L, ps);
+            if (st != ETPC_OK) return st;
+          }
+          if (R.tangent && R.w2) {
+            etpc_status st = xbar_gemm(p, d, k, Pset, L.wt2[set], R.x_out, j0, nsend, true, L, ps);
+            if (st != ETPC_OK) return st;
+          }
         }
-        if (R.tangent && R.w2) {
-          etpc_status st = xbar_gemm(p, d, static_cast<int>(k), L.P, L.wt2, R.x_out, j0, nsend, true, L, s);
-          if (st != ETPC_OK) return st;
+        if (R.w_out) {
+          int sp1 = 0, sp2 = 0;
+          ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, ps, wbar_gemm(p, d, k, R.x, j0, nsend, Pmain, L.wpart, &sp1, ps));
+          if (R.tangent && R.x2)
+            ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, ps,
+                           wbar_gemm(p, d, k, R.x2, j0, nsend, Pset, L.wpart + static_cast<int64_t>(sp1) * c_in * ncols,
+                                     &sp2, ps));
+          int64_t poff[kMaxPaths];
+          int32_t col0[kMaxPaths], cout[kMaxPaths];
+          for (size_t t = 0; t < paths.size(); ++t) {
+            poff[t] = p->paths[paths[t]].w_off;
+            col0[t] = d.block_col0[k][t];
+            cout[t] = p->paths[paths[t]].c_out;
+          }
+          ETPC_LAUNCH_ON(ETPC_KIND_AUX, ps,
+                         launch_reduce_wbar(L.wpart, sp1 + sp2, c_in, static_cast<int>(paths.size()), p->n_basis, poff,
+                                            col0, cout, static_cast<int>(ncols), R.w_out, j0 > 0, ps));
         }
-      }
-      if (R.w_out) {
-        int sp1 = 0, sp2 = 0;
-        ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, wbar_gemm(p, d, static_cast<int>(k), R.x, j0, nsend, Pmain, L.wpart, &sp1, s));
-        if (R.tangent && R.x2)
-          ETPC_LAUNCH(ETPC_KIND_NODE_GEMM, wbar_gemm(p, d, static_cast<int>(k), R.x2, j0, nsend, L.P,
-                             L.wpart + static_cast<int64_t>(sp1) * c_in * ncols, &sp2, s));
-        int64_t poff[kMaxPaths];
-        int32_t col0[kMaxPaths], cout[kMaxPaths];
-        for (size_t t = 0; t < paths.size(); ++t) {
-          poff[t] = p->paths[paths[t]].w_off;
-          col0[t] = d.block_col0[k][t];
-          cout[t] = p->paths[paths[t]].c_out;
-        }
-        ETPC_LAUNCH(ETPC_KIND_AUX, launch_reduce_wbar(L.wpart, sp1 + sp2, c_in, static_cast<int>(paths.size()), p->n_basis, poff, col0,
-                                    cout, static_cast<int>(ncols), R.w_out, j0 > 0, s));
+        ETPC_HIP(post.mark(set));
       }
     }
   }
+  ETPC_HIP(post.finish());
   return ETPC_OK;
 }
 

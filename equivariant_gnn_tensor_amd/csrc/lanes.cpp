@@ -17,6 +17,15 @@ struct DeviceLanes {
   hipStream_t side[kLanes] = {};
   hipEvent_t fork = nullptr;
   hipEvent_t join[kLanes] = {};
+  // post stream (its own lock, held for a whole pass)
+  std::mutex post_mu;
+  bool post_tried = false;
+  bool post_ok = false;
+  hipStream_t post = nullptr;
+  hipEvent_t post_follow = nullptr;
+  hipEvent_t post_slot[2] = {};
+  hipEvent_t post_ready[2] = {};
+  hipEvent_t post_join = nullptr;
 };
 
 DeviceLanes g_dev[kMaxDevices];
@@ -31,6 +40,20 @@ bool ensure(DeviceLanes& dl) {
          hipEventCreateWithFlags(&dl.join[i], hipEventDisableTiming) == hipSuccess;
   }
   dl.ok = ok;
+  return ok;
+}
+
+// Lazily creates the post stream and its events; holds dl.post_mu.
+bool ensure_post(DeviceLanes& dl) {
+  if (dl.post_tried) return dl.post_ok;
+  dl.post_tried = true;
+  bool ok = hipStreamCreateWithFlags(&dl.post, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&dl.post_follow, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&dl.post_join, hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; ok && i < 2; ++i)
+    ok = hipEventCreateWithFlags(&dl.post_slot[i], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&dl.post_ready[i], hipEventDisableTiming) == hipSuccess;
+  dl.post_ok = ok;
   return ok;
 }
 
@@ -80,6 +103,73 @@ hipError_t LaneGroup::finish() {
 }
 
 LaneGroup::~LaneGroup() { (void)finish(); }
+
+PostStream::PostStream(hipStream_t main, bool enable) : main_(main) {
+  if (!enable || lanes_limit() < 2) return;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
+  DeviceLanes& dl = g_dev[dev];
+  lock_ = std::unique_lock<std::mutex>(dl.post_mu);
+  if (!ensure_post(dl)) {
+    lock_.unlock();
+    return;
+  }
+  post_ = dl.post;
+  follow_ev_ = dl.post_follow;
+  slot_ev_[0] = dl.post_slot[0];
+  slot_ev_[1] = dl.post_slot[1];
+  ready_ev_[0] = dl.post_ready[0];
+  ready_ev_[1] = dl.post_ready[1];
+  join_ev_ = dl.post_join;
+  on_ = true;
+}
+
+hipError_t PostStream::follow() {
+  if (!on_ || err_ != hipSuccess) return err_;
+  err_ = hipEventRecord(follow_ev_, main_);
+  if (err_ == hipSuccess) err_ = hipStreamWaitEvent(post_, follow_ev_, 0);
+  return err_;
+}
+
+hipError_t PostStream::mark(int slot) {
+  if (!on_ || err_ != hipSuccess) return err_;
+  err_ = hipEventRecord(slot_ev_[slot & 1], post_);
+  if (err_ == hipSuccess) marked_[slot & 1] = true;
+  return err_;
+}
+
+hipError_t PostStream::wait_slot(int slot) {
+  if (!on_ || err_ != hipSuccess || !marked_[slot & 1]) return err_;
+  err_ = hipStreamWaitEvent(main_, slot_ev_[slot & 1], 0);
+  return err_;
+}
+
+hipError_t PostStream::ready(int slot) {
+  if (!on_ || err_ != hipSuccess) return err_;
+  err_ = hipEventRecord(ready_ev_[slot & 1], post_);
+  if (err_ == hipSuccess) readied_[slot & 1] = true;
+  return err_;
+}
+
+hipError_t PostStream::wait_ready(int slot) {
+  if (!on_ || err_ != hipSuccess || !readied_[slot & 1]) return err_;
+  err_ = hipStreamWaitEvent(main_, ready_ev_[slot & 1], 0);
+  return err_;
+}
+
+hipError_t PostStream::finish() {
+  if (done_) return err_;
+  done_ = true;
+  if (on_) {
+    hipError_t e = hipEventRecord(join_ev_, post_);
+    if (e == hipSuccess) e = hipStreamWaitEvent(main_, join_ev_, 0);
+    if (e != hipSuccess && err_ == hipSuccess) err_ = e;
+  }
+  if (lock_.owns_lock()) lock_.unlock();
+  return err_;
+}
+
+PostStream::~PostStream() { (void)finish(); }
 
 }  // namespace etpc
 

@@ -54,4 +54,49 @@ class LaneGroup {
   std::unique_lock<std::mutex> lock_;
 };
 
+// A side stream for the node-side GEMMs of a pass (the channel GEMM of a forward output
+// group, the x_bar and W_bar GEMMs of a backward input block), so they run while the
+// next group's or block's traversals do.  The pass keeps two sets of the buffers those
+// GEMMs read and alternates between them; before its traversals write set b again, the
+// caller's stream waits for the post work that last read set b (wait_slot).  Disabled
+// (every call a no-op, stream() the caller's stream) when the lane limit is 1 or when
+// `enable` is false.  Holds a per-device lock from construction to finish; it is taken
+// before any LaneGroup lock of the same call, never after.
+class PostStream {
+ public:
+  PostStream(hipStream_t main, bool enable);
+  ~PostStream();
+  PostStream(const PostStream&) = delete;
+  PostStream& operator=(const PostStream&) = delete;
+
+  hipStream_t stream() const { return on_ ? post_ : main_; }
+  // The post stream waits for everything enqueued on the caller's stream so far.
+  hipError_t follow();
+  // Buffer set `slot` is free again once the post work enqueued so far has run.
+  hipError_t mark(int slot);
+  // The caller's stream waits until buffer set `slot` is free.
+  hipError_t wait_slot(int slot);
+  // Buffer set `slot` has been filled by the post work enqueued so far...
+  hipError_t ready(int slot);
+  // ...and the caller's stream waits for that before reading it.
+  hipError_t wait_ready(int slot);
+  // The caller's stream waits for all post work (idempotent).
+  hipError_t finish();
+  hipError_t status() const { return err_; }
+
+ private:
+  hipStream_t main_;
+  hipStream_t post_ = nullptr;
+  bool on_ = false;
+  bool done_ = false;
+  bool marked_[2] = {false, false};
+  bool readied_[2] = {false, false};
+  hipEvent_t follow_ev_ = nullptr;
+  hipEvent_t slot_ev_[2] = {nullptr, nullptr};
+  hipEvent_t ready_ev_[2] = {nullptr, nullptr};
+  hipEvent_t join_ev_ = nullptr;
+  hipError_t err_ = hipSuccess;
+  std::unique_lock<std::mutex> lock_;
+};
+
 }  // namespace etpc
