@@ -40,11 +40,13 @@
  * Compute calls are asynchronous on the given stream; results are
  * deterministic for a given workspace size (fixed reduction owners and orders,
  * no floating-point atomics).  Inside a call, the independent per-path launches of a
- * pass run on up to two side streams the library creates once per device (default
- * priority), forked from and joined back into the given stream with events, so the
- * call still behaves as one ordered unit of that stream (and can be captured into a HIP
- * graph).  Calls from several host threads serialize their fork-to-join sections on a
- * per-device lock; the first call on a device creates the side streams.
+ * pass run on up to two side streams, and the node-side GEMMs of a pass on a third
+ * ("post") stream that overlaps them with the next group's or block's traversals; the
+ * library creates these streams once per device (default priority) and forks them from
+ * and joins them back into the given stream with events, so the call still behaves as
+ * one ordered unit of that stream (and can be captured into a HIP graph).  Calls from
+ * several host threads serialize their fork-to-join sections on per-device locks; the
+ * first call on a device creates the side streams.
  */
 #ifndef ETPC_H
 #define ETPC_H
@@ -139,7 +141,8 @@ etpc_status etpc_plan_out_irrep(etpc_plan plan, int32_t b, int32_t* n_out, etpc_
 etpc_status etpc_plan_cg(etpc_plan plan, int32_t p, double* out);
 
 /* Workspace bytes for a compute pass over a graph of n_nodes / n_edges with every node
- * in one chunk (the fastest schedule).  Grows with N (node-side states) and, for backward
+ * in one chunk (the fastest schedule).  Grows with N (node-side states, two sets of them
+ * so the GEMMs of one group or block overlap the traversals of the next) and, for backward
  * and double backward, by 12 B per edge per concurrent launch lane (the per-edge position
  * adjoint; up to two lanes, one per path or per uvu input block); it never scales with E
  * times a channel width.  A compute call given less (down to one node's state)
