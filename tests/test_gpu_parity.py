@@ -302,3 +302,45 @@ def test_graph_capture_replays_match_eager(name, n):
         for got, want in zip((z, *outs, *douts), ref):
             assert torch.equal(got, want), f"replay {rep} differs from the eager step"
     note(f"graph capture {cfg.name}: 3 replays bit-identical")
+
+
+def test_concurrent_schedules_are_deterministic_and_agree():
+    """Lanes and the post stream change only where work runs, not what it computes:
+    repeated calls are bit-identical, forward / x_bar / W_bar equal the serialized
+    schedule bit for bit, pos_bar (per-lane edge-adjoint copies summed in a fixed order)
+    to 1e-6; calls issued on a non-default stream give the same results."""
+    etpc = _etpc()
+    cfg = small_variant("cfg5", 256)
+    c = make_case(cfg)
+    note(f"schedules {cfg.name}")
+    pos_dot = torch.from_numpy(-c.wl.force_c).cuda()
+    old = etpc.etpc_get_lanes()
+
+    def run(stream=None):
+        z = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, stream=stream)
+        b = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, stream=stream)
+        d = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot, stream=stream)
+        return [z, *b, *d]
+
+    try:
+        etpc.etpc_set_lanes(2)
+        first = run()
+        for _ in range(3):
+            again = run()
+            assert all(torch.equal(a, b) for a, b in zip(first, again))
+        side = torch.cuda.Stream()
+        with torch.cuda.stream(side):
+            on_side = run(stream=side)
+        side.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(first, on_side))
+        etpc.etpc_set_lanes(1)
+        serial = run()
+        torch.cuda.synchronize()
+    finally:
+        etpc.etpc_set_lanes(old)
+    z, xb, wb, pb = first[:4]
+    assert torch.equal(z, serial[0]) and torch.equal(xb, serial[1]) and torch.equal(wb, serial[2])
+    assert rel_err(pb, serial[3].double().cpu().numpy()) < 1e-6
+    for a, b in zip(first[4:], serial[4:]):
+        if a is not None:
+            assert rel_err(a, b.double().cpu().numpy()) < 1e-5
