@@ -205,21 +205,9 @@ SortBufs make_sort_bufs(int32_t* k0, int32_t* v0, int32_t* k1, int32_t* v1, int3
   return SortBufs{k0, v0, k1, v1, scratch, scratch + 256 * nblk};
 }
 
-hipError_t launch_iota(int32_t* p, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(iota_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
-
 hipError_t launch_copy(const int32_t* a, int32_t* b, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, a, b, n);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather(const int32_t* a, const int32_t* idx, int32_t* out, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, a, idx, out, n);
   return hipGetLastError();
 }
 

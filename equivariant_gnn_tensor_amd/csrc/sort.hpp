@@ -1,6 +1,6 @@
 // Integer building blocks of the graph preparation steps (internal, defined in csr.hip):
 // a stable least-significant-digit radix sort of (key, value) int32 pairs with 8-bit
-// digits, an exclusive scan, and small copy/gather/lower-bound launches.  All of them are
+// digits, an exclusive scan, and small copy and lower-bound launches.  All of them are
 // deterministic and bit-exact (LDS atomics only count).
 #pragma once
 
@@ -27,10 +27,7 @@ int radix_passes(int32_t n_keys);
 hipError_t radix_sort(SortBufs& b, int64_t n, int passes, hipStream_t s);
 // In-place exclusive scan of n ints; aux holds scan_aux_ints(n) ints.
 hipError_t exclusive_scan(int32_t* data, int64_t n, int32_t* aux, hipStream_t s);
-hipError_t launch_iota(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_copy(const int32_t* a, int32_t* b, int64_t n, hipStream_t s);
-// out[i] = a[idx[i]]
-hipError_t launch_gather(const int32_t* a, const int32_t* idx, int32_t* out, int64_t n, hipStream_t s);
 // rowptr[v] = first index whose key is >= v, v = 0..n_rows (keys sorted ascending)
 hipError_t launch_lower_bound(const int32_t* keys, int64_t n, int32_t* rowptr, int32_t n_rows, hipStream_t s);
 

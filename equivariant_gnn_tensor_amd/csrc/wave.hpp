@@ -10,18 +10,10 @@ __device__ inline float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Every lane of each 16-lane row receives the sum over that row (row_ror rotations).
-__device__ inline float row_sum16(float v) {
-  v += dpp_f<0x128>(v);  // row_ror:8
-  v += dpp_f<0x124>(v);  // row_ror:4
-  v += dpp_f<0x122>(v);  // row_ror:2
-  v += dpp_f<0x121>(v);  // row_ror:1
-  return v;
-}
-
-// Three row sums at once, their steps interleaved: each DPP step reads a value written
-// two instructions earlier, which covers the DPP read-after-write wait states without
-// s_nop.
+// Three row sums at once: every lane of each 16-lane row receives the sum over that row
+// of each value (row_ror rotations by 8, 4, 2, 1).  The three chains are interleaved, so
+// each DPP step reads a value written two instructions earlier, which covers the DPP
+// read-after-write wait states without s_nop.
 __device__ inline void row_sum16x3(float& a, float& b, float& c) {
   a += dpp_f<0x128>(a);
   b += dpp_f<0x128>(b);
