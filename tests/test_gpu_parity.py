@@ -344,3 +344,12 @@ def test_concurrent_schedules_are_deterministic_and_agree():
     for a, b in zip(first[4:], serial[4:]):
         if a is not None:
             assert rel_err(a, b.double().cpu().numpy()) < 1e-5
+    # a third of the full workspace: the double backward runs the block pipeline over
+    # several sender chunks
+    full = etpc.etpc_workspace_size(c.plan, etpc.PASS_DBL, cfg.n_nodes, c.graph.n_edges)
+    ws = torch.empty(full // 3, dtype=torch.uint8, device="cuda")
+    chunked = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot, ws=ws)
+    torch.cuda.synchronize()
+    for a, b in zip(chunked, first[4:]):
+        if a is not None:
+            assert rel_err(a, b.double().cpu().numpy()) < 1e-5
