@@ -250,6 +250,27 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
     print(json.dumps(out, indent=1))
 
 
+def morton_relabel(wl):
+    """Renumber the workload's nodes in Morton (Z-curve) order of their positions: the same
+    graph and values, with neighbours close in index.  Returns a new Workload."""
+    import dataclasses
+
+    import numpy as np
+    pos = wl.pos.astype(np.float64)
+    lo, hi = pos.min(axis=0), pos.max(axis=0)
+    q = np.clip(((pos - lo) / np.maximum(hi - lo, 1e-12) * 1023).astype(np.int64), 0, 1023)
+    code = np.zeros(len(pos), np.int64)
+    for bit in range(10):
+        for a in range(3):
+            code |= ((q[:, a] >> bit) & 1) << (3 * bit + a)
+    order = np.argsort(code, kind="stable")          # new index -> old index
+    new_of_old = np.empty_like(order)
+    new_of_old[order] = np.arange(len(order))
+    perm = lambda a: None if a is None else np.ascontiguousarray(a[order])  # noqa: E731
+    return dataclasses.replace(wl, pos=perm(wl.pos), x=perm(wl.x), z_bar=perm(wl.z_bar), force_c=perm(wl.force_c),
+                               src=new_of_old[wl.src].astype(np.int32), dst=new_of_old[wl.dst].astype(np.int32))
+
+
 def measure(args, name):
     """Time one workload: (result dict without cpu_baseline, config, workload)."""
     import numpy as np
@@ -268,6 +289,8 @@ def measure(args, name):
     info = plan.info()
     mask = scalar_mask(cfg.irreps_out) if cfg.cotangent == "energy" else None
     wl = make_workload(cfg, w_blocks=plan.w_blocks(), z_dim=info["z_dim"], scalar_out_mask=mask)
+    if args.node_order == "morton":
+        wl = morton_relabel(wl)
     N, E = wl.n_nodes, wl.n_edges
     log(f"workload {cfg.name}: N={N} E={E} paths={info['n_paths']} x_dim={info['x_dim']} z_dim={info['z_dim']}")
     T = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
@@ -392,6 +415,7 @@ def measure(args, name):
             "pass": ("forward + backward (pos_bar) + double backward along pos_dot (d/dx, d/dW)" if force_step
                      else "forward + backward (x_bar, W_bar, pos_bar)"),
             "launch": "hip graph replay" if args.graph else "eager",
+            "node_order": args.node_order,
             "lanes": timed_lanes,
         },
         "roofline": {
@@ -549,6 +573,8 @@ def main():
                     help="after timing, run a plain device copy of this size (counter calibration)")
     ap.add_argument("--lanes", type=int, default=0,
                     help="concurrent launch lanes per pass for the timed steps (0 = library default)")
+    ap.add_argument("--node-order", choices=("given", "morton"), default="given",
+                    help="node numbering: as generated (random in space) or Morton order of the positions")
     ap.add_argument("--gemm-precision", choices=("fp32", "bf16"), default="fp32",
                     help="channel GEMM operands: fp32 (reference) or bf16 with fp32 accumulation")
     ap.add_argument("--graph", action="store_true",

@@ -36,6 +36,18 @@ inline RowMap make_rowmap(int64_t s1, int64_t s2, int32_t div) {
   return RowMap{s1, s2, div, static_cast<uint32_t>(magic), l};
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  The
+// receiver traversals take node slot node_block(b, g) for workgroup b of a grid of g, so
+// the workgroups of one XCD cover one contiguous range of receivers: with a spatially
+// ordered numbering, receivers that share senders then share an L2 (uvu forward -4.5%
+// on a Morton-ordered graph, neutral on a random numbering).  The sender traversals
+// measured slower with it and keep the plain order.  A bijection on [0, g).
+constexpr int kXcds = 8;
+__device__ inline int node_block(int b, int g) {
+  const int x = b % kXcds, q = g / kXcds, r = g % kXcds;
+  return x * q + min(x, r) + b / kXcds;
+}
+
 // Edge geometry parameters shared by every traversal kernel.
 struct GeomParams {
   int32_t radial;     // etpc_radial

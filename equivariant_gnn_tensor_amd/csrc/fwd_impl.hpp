@@ -95,7 +95,8 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
   __shared__ float s_edge[64 * L::kStride];
   __shared__ int s_j[64];
   const int lane = threadIdx.x;
-  const int i = a.recv0 + blockIdx.x;
+  const int bx = node_block(blockIdx.x, gridDim.x);
+  const int i = a.recv0 + bx;
   const int cp = a.cp;
   const int nslots = kWave / cp;
   const int slot = lane / cp;
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
 #pragma unroll
       for (int m = 0; m < NO; ++m) acc[q][m] += __shfl_xor(acc[q][m], off);
   if (slot == 0 && uvalid) {
-    float* srow = a.S + static_cast<int64_t>(blockIdx.x) * NO * a.s_row_stride + a.s_col0 + u;
+    float* srow = a.S + static_cast<int64_t>(bx) * NO * a.s_row_stride + a.s_col0 + u;
 #pragma unroll
     for (int q = 0; q < NB; ++q)
       if (q < a.g.nb)
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(64) void fwd_uvu_kernel(const FwdUvuArgs a) {
   __shared__ float s_edge[64 * L::kStride];
   __shared__ int s_j[64];
   const int lane = threadIdx.x;
-  const int i = blockIdx.x;
+  const int i = node_block(blockIdx.x, gridDim.x);
   const int cp = a.cp;
   const int nslots = kWave / cp;
   const int slot = lane / cp;
