@@ -344,6 +344,22 @@ hipError_t zero_unreached_in(const etpc_plan_s* p, float* x, int32_t n, hipStrea
   return launch_fill(x, static_cast<int64_t>(n) * p->x_dim, 0.f, s);
 }
 
+// Waves that split one node's edges inside a traversal workgroup (1, 2 or 4).  A launch
+// over few nodes has one workgroup per node and at most one wave per SIMD, each walking
+// its whole edge list in series (latency bound: a 128-atom cell); splitting the edges over
+// more waves shortens that walk.  Used while the launch stays under 1024 waves, the mean
+// degree gives each wave at least 12 edges, and the state the waves exchange at the end
+// (`states` accumulators of (2 l + 1) x B floats per lane and channel tile) fits 48 KB of LDS.
+int edge_parts(int nodes, int ntiles, const etpc_graph* g, int l, int nb, int states) {
+  const int64_t deg = g->n_nodes > 0 ? g->n_edges / g->n_nodes : 0;
+  const int64_t nbp = nb <= 8 ? 8 : 16;
+  int np = 1;
+  while (np < 4 && ntiles * np * 2 <= 4 && static_cast<int64_t>(nodes) * ntiles * np * 2 <= 1024 &&
+         deg >= 12 * np * 2 && int64_t(ntiles) * 64 * (2 * l + 1) * nbp * states * 4 <= 48 * 1024)
+    np *= 2;
+  return np;
+}
+
 // Output groups with paths, by decreasing channel-GEMM work per node (o C_out D_g), ties
 // in plan order.
 std::vector<int> group_order(const etpc_plan_s* p, const Derived& d) {
@@ -408,6 +424,8 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.ls = pi.l_sh;
         a.s_row_stride = D;
         a.s_col0 = col0;
+        // one workgroup per (receiver, channel tile): the tiles are separate workgroups
+        a.nparts = edge_parts(nrecv * ntiles, 1, g, pi.l_out, p->n_basis, 1);
         a.g = geom;
         a.cg = pi.cgf;
         const hipStream_t ls = lanes.lane(static_cast<int>(t));
@@ -677,6 +695,8 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         int ntiles = 1;
         a.cp = lane_width(pi.c_out, &ntiles, 16);
         a.c_out = pi.c_out;
+        a.nparts = edge_parts(nsend, ntiles, g, pi.l_in, p->n_basis,
+                              (R.hess ? 0 : (R.tangent ? need_plain : main_state) ? 1 : 0) + (R.tangent ? 1 : 0));
         a.ls = pi.l_sh;
         a.ld_state = ncols;
         a.state_col0 = d.block_col0[k][t];

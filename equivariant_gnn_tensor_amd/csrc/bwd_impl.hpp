@@ -162,7 +162,9 @@ __device__ inline void cg_contract_out(const float* __restrict__ zb, float (*__r
 // POS) the per-edge output is not r_bar_e but its directional derivative along
 // r_dot_e = pos_dot_sender - pos_dot_receiver, i.e. H_e r_dot_e with H_e the Hessian of the
 // edge's term of <z_bar, z> in the edge vector: the position term of double backward.
-template <int LI, int LS, int LO, int NBQ, bool NEED_P, bool POS, bool TAN, bool HESS = false>
+// SPLIT: a.nparts waves per channel tile share the sender's edges (small launches);
+// without it the part count is the constant 1 and that code folds away.
+template <int LI, int LS, int LO, int NBQ, bool NEED_P, bool POS, bool TAN, bool HESS = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
   static_assert(!HESS || (POS && !TAN && !NEED_P), "the Hessian pass is a position-only pass");
@@ -170,13 +172,20 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   __shared__ __attribute__((aligned(16))) float s_edge[64 * R::kStride];
   __shared__ int s_i[64];
   __shared__ int s_sl[64];
-  extern __shared__ float s_dyn[];   // [nwaves][64][rows][3] edge-adjoint partials
+  // [nwaves][64][rows][3] edge-adjoint partials, then (nparts > 1) the state exchange
+  extern __shared__ float s_dyn[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int j = a.send0 + blockIdx.x;
   const int cp = a.cp;
   const int nslots = kWave / cp;
   const int slot = lane / cp;
-  const int w = wave * cp + (lane - slot * cp);
+  // waves are (part, tile): tile = channel range, part = share of the sender's edges
+  const int nparts = SPLIT ? a.nparts : 1;
+  const int ntiles = nwaves / nparts;
+  const int tile = SPLIT ? wave % ntiles : wave, part = SPLIT ? wave / ntiles : 0;
+  const int tslots = nslots * nparts;     // edge slots of the workgroup per trip
+  const int gslot = part * nslots + slot;
+  const int w = tile * cp + (lane - slot * cp);
   const bool wvalid = w < a.c_out;
   const int rows = rows_per_slot(cp);
   const int row_in_slot = (lane - slot * cp) >> 4;
@@ -211,7 +220,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
       s_sl[tid] = a.s_slot[base + tid];
     }
     __syncthreads();
-    const int trips = (ne + nslots - 1) / nslots;
+    const int trips = (ne + tslots - 1) / tslots;
     // z_bar rows of the next kPrefetch edges of this slot are in flight while one is used
     float zq[kPrefetch][NO];
     // Unconditional loads from a clamped in-bounds address (no branch per load); lanes
@@ -229,8 +238,8 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
     int next_i[kPrefetch];
 #pragma unroll
     for (int pf = 0; pf < kPrefetch; ++pf) {
-      gather(recv_of(pf * nslots + slot), zq[pf]);
-      next_i[pf] = recv_of((pf + kPrefetch) * nslots + slot);
+      gather(recv_of(pf * tslots + gslot), zq[pf]);
+      next_i[pf] = recv_of((pf + kPrefetch) * tslots + gslot);
       // Pass the first rows through an arithmetic op: when every value entering the
       // loop-carried registers is a plain load, the optimizer merges them into one load
       // at the top of the loop, which undoes the prefetch.
@@ -244,7 +253,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
         // would make the compiler copy the loop-carried registers and wait on the loads);
         // a padding trip has t >= ne, gathers zeros and adds exact zeros
         const int it = it0 + pf;
-        const int t = it * nslots + slot;
+        const int t = it * tslots + gslot;
         const bool tvalid = t < ne;
         const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
         // No mask on the gathered row: a padding trip reads real data (edge 0's record and a
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
         // register copy, so nothing waits for that load until its own trip); the
         // scheduling barrier keeps the loads here instead of sunk to the loop end
         gather(next_i[pf], zq[pf]);
-        next_i[pf] = recv_of(t + 2 * kPrefetch * nslots);
+        next_i[pf] = recv_of(t + 2 * kPrefetch * tslots);
         __builtin_amdgcn_sched_barrier(kSchedMask);
         float Q[NI], Qd[NI];
 #pragma unroll
@@ -348,9 +357,12 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
     __syncthreads();
     if constexpr (POS) {
       if (tid < ne) {
+        // the waves of every channel tile of the part that took this edge
+        const int pe = (tid % tslots) / nslots;
         float r0 = 0.f, r1 = 0.f, r2 = 0.f;
-        for (int w2 = 0; w2 < nwaves; ++w2)
+        for (int tl = 0; tl < ntiles; ++tl)
           for (int r = 0; r < rows; ++r) {
+            const int w2 = pe * ntiles + tl;
             const float* src = s_dyn + ((w2 * 64 + tid) * rows + r) * 3;
             r0 += src[0];
             r1 += src[1];
@@ -381,7 +393,40 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
           if constexpr (NEED_P) P[mi][qq][r] += __shfl_xor(P[mi][qq][r], off);
           if constexpr (TAN) Pd[mi][qq][r] += __shfl_xor(Pd[mi][qq][r], off);
         }
-  if (slot == 0 && wvalid) {
+  if constexpr (NEED_P || TAN) {
+    // parts 1.. hand their state to part 0 through LDS, one part at a time (fixed order)
+    constexpr int kState = NI * NB * ((NEED_P ? 1 : 0) + (TAN ? 1 : 0));
+    float* s_x = s_dyn + (POS ? nwaves * 64 * rows * 3 : 0) + (tile * 64 + lane) * kState;
+    for (int pp = 1; pp < nparts; ++pp) {
+      __syncthreads();
+      if (part == pp && slot == 0) {
+        int o = 0;
+#pragma unroll
+        for (int mi = 0; mi < NI; ++mi)
+#pragma unroll
+          for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if constexpr (NEED_P) s_x[o++] = P[mi][qq][r];
+              if constexpr (TAN) s_x[o++] = Pd[mi][qq][r];
+            }
+      }
+      __syncthreads();
+      if (part == 0 && slot == 0) {
+        int o = 0;
+#pragma unroll
+        for (int mi = 0; mi < NI; ++mi)
+#pragma unroll
+          for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if constexpr (NEED_P) P[mi][qq][r] += s_x[o++];
+              if constexpr (TAN) Pd[mi][qq][r] += s_x[o++];
+            }
+      }
+    }
+  }
+  if (part == 0 && slot == 0 && wvalid) {
 #pragma unroll
     for (int qq = 0; qq < NBQ; ++qq)
 #pragma unroll
@@ -606,13 +651,24 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
 
 template <int LI, int LS, int LO, bool NEED_P, bool POS, bool TAN, bool HESS>
 hipError_t bwd_uvw_nb(const BwdUvwArgs& a, int nsend, int ntiles, hipStream_t s) {
-  dim3 grid(nsend), block(64 * ntiles);
+  const int nwaves = ntiles * a.nparts;
+  dim3 grid(nsend), block(64 * nwaves);
   const int rows = a.cp / 16;
-  const size_t dyn = POS ? sizeof(float) * 64 * 3 * rows * ntiles : 0;
-  if (a.g.nb <= 8)
-    hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 2, NEED_P, POS, TAN, HESS>), grid, block, dyn, s, a);
-  else
-    hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 4, NEED_P, POS, TAN, HESS>), grid, block, dyn, s, a);
+  const int ni = 2 * LI + 1, nb = a.g.nb <= 8 ? 8 : 16;
+  const size_t state = a.nparts > 1 ? static_cast<size_t>(ntiles) * 64 * ni * nb * ((NEED_P ? 1 : 0) + (TAN ? 1 : 0)) : 0;
+  const size_t dyn = sizeof(float) * ((POS ? 64 * 3 * rows * nwaves : 0) + state);
+  const bool split = a.nparts > 1;
+  if (a.g.nb <= 8) {
+    if (split)
+      hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 2, NEED_P, POS, TAN, HESS, true>), grid, block, dyn, s, a);
+    else
+      hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 2, NEED_P, POS, TAN, HESS, false>), grid, block, dyn, s, a);
+  } else {
+    if (split)
+      hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 4, NEED_P, POS, TAN, HESS, true>), grid, block, dyn, s, a);
+    else
+      hipLaunchKernelGGL((bwd_uvw_kernel<LI, LS, LO, 4, NEED_P, POS, TAN, HESS, false>), grid, block, dyn, s, a);
+  }
   return hipGetLastError();
 }
 

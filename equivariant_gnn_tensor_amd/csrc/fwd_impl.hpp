@@ -88,18 +88,25 @@ __device__ inline void fill_edge(const GeomParams& g, const float* __restrict__ 
     }
 }
 
-template <int LI, int LS, int LO, int NBQ, bool TANGENT>
-__global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
+// SPLIT: a.nparts waves share the receiver's edges (small launches); without it the
+// part count is the constant 1 and that code folds away.
+template <int LI, int LS, int LO, int NBQ, bool TANGENT, bool SPLIT = false>
+__global__ __launch_bounds__(SPLIT ? 256 : 64) void fwd_uvw_kernel(const FwdUvwArgs a) {
   constexpr int NI = 2 * LI + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
   using L = EdgeLds<NB, NI * NO, TANGENT>;
   __shared__ float s_edge[64 * L::kStride];
   __shared__ int s_j[64];
-  const int lane = threadIdx.x;
+  extern __shared__ float s_part[];   // nparts > 1: accumulators handed to part 0
+  const int lane = threadIdx.x & 63;
+  const int part = SPLIT ? threadIdx.x >> 6 : 0;   // the wave's share of the receiver's edges
+  const int nparts = SPLIT ? a.nparts : 1;
   const int bx = node_block(blockIdx.x, gridDim.x);
   const int i = a.recv0 + bx;
   const int cp = a.cp;
   const int nslots = kWave / cp;
   const int slot = lane / cp;
+  const int tslots = nslots * nparts;
+  const int gslot = part * nslots + slot;
   const int u = blockIdx.y * cp + (lane - slot * cp);
   const bool uvalid = u < a.c_in;
   float acc[NB][NO];
@@ -110,13 +117,13 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
   const int e0 = a.rowptr[i], e1 = a.rowptr[i + 1];
   for (int base = e0; base < e1; base += kWave) {
     const int ne = min(kWave, e1 - base);
-    if (lane < ne) {
+    if (threadIdx.x < ne) {
       const int j = a.col[base + lane];
       fill_edge<LI, LS, LO, NB, TANGENT>(a.g, a.pos, a.pos_dot, j, i, s_edge + lane * L::kStride);
       s_j[lane] = j;
     }
     __syncthreads();
-    const int trips = (ne + nslots - 1) / nslots;
+    const int trips = (ne + tslots - 1) / tslots;
     // sender rows of the next kPrefetch edges of this slot are in flight while one is used
     float xq[kPrefetch][NI];
     // Unconditional loads from a clamped in-bounds address (no branch per load); lanes
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
     };
 #pragma unroll
     for (int pf = 0; pf < kPrefetch; ++pf) {
-      gather(pf * nslots + slot, xq[pf]);
+      gather(pf * tslots + gslot, xq[pf]);
       // Pass the first rows through an arithmetic op: when every value entering the
       // loop-carried registers is a plain load, the optimizer merges them into one load
       // at the top of the loop, which undoes the prefetch.
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
         // would make the compiler copy the loop-carried registers and wait on the loads);
         // a padding trip has t >= ne, gathers zeros and adds exact zeros
         const int it = it0 + pf;
-        const int t = it * nslots + slot;
+        const int t = it * tslots + gslot;
         const float* e = s_edge + (t < ne ? t : 0) * L::kStride;
         const bool tv = t < ne && uvalid;
         float xv[NI];
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
         // the row is consumed: its registers take the gather kPrefetch trips ahead (no
         // register copy, so nothing waits for that load until its own trip); the
         // scheduling barrier keeps the loads here instead of sunk to the loop end
-        gather(t + kPrefetch * nslots, xq[pf]);
+        gather(t + kPrefetch * tslots, xq[pf]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
@@ -188,7 +195,23 @@ __global__ __launch_bounds__(64) void fwd_uvw_kernel(const FwdUvwArgs a) {
     for (int q = 0; q < NB; ++q)
 #pragma unroll
       for (int m = 0; m < NO; ++m) acc[q][m] += __shfl_xor(acc[q][m], off);
-  if (slot == 0 && uvalid) {
+  for (int pp = 1; pp < nparts; ++pp) {
+    // parts 1.. hand their sums to part 0 through LDS, one part at a time (fixed order)
+    float* sx = s_part + lane * NB * NO;
+    __syncthreads();
+    if (part == pp && slot == 0)
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int m = 0; m < NO; ++m) sx[q * NO + m] = acc[q][m];
+    __syncthreads();
+    if (part == 0 && slot == 0)
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int m = 0; m < NO; ++m) acc[q][m] += sx[q * NO + m];
+  }
+  if (part == 0 && slot == 0 && uvalid) {
     float* srow = a.S + static_cast<int64_t>(bx) * NO * a.s_row_stride + a.s_col0 + u;
 #pragma unroll
     for (int q = 0; q < NB; ++q)
@@ -293,11 +316,20 @@ __global__ __launch_bounds__(64) void fwd_uvu_kernel(const FwdUvuArgs a) {
 
 template <int LI, int LS, int LO, bool T>
 hipError_t fwd_uvw_nb(const FwdUvwArgs& a, int nrecv, int ntiles, hipStream_t s) {
-  dim3 grid(nrecv, ntiles), block(64);
-  if (a.g.nb <= 8)
-    hipLaunchKernelGGL((fwd_uvw_kernel<LI, LS, LO, 2, T>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((fwd_uvw_kernel<LI, LS, LO, 4, T>), grid, block, 0, s, a);
+  dim3 grid(nrecv, ntiles), block(64 * a.nparts);
+  const size_t dyn = a.nparts > 1 ? sizeof(float) * 64 * (2 * LO + 1) * (a.g.nb <= 8 ? 8 : 16) : 0;
+  const bool split = a.nparts > 1;
+  if (a.g.nb <= 8) {
+    if (split)
+      hipLaunchKernelGGL((fwd_uvw_kernel<LI, LS, LO, 2, T, true>), grid, block, dyn, s, a);
+    else
+      hipLaunchKernelGGL((fwd_uvw_kernel<LI, LS, LO, 2, T, false>), grid, block, dyn, s, a);
+  } else {
+    if (split)
+      hipLaunchKernelGGL((fwd_uvw_kernel<LI, LS, LO, 4, T, true>), grid, block, dyn, s, a);
+    else
+      hipLaunchKernelGGL((fwd_uvw_kernel<LI, LS, LO, 4, T, false>), grid, block, dyn, s, a);
+  }
   return hipGetLastError();
 }
 

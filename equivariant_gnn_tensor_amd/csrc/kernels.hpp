@@ -22,6 +22,7 @@ struct FwdUvwArgs {
   int32_t ls;
   int64_t s_row_stride;   // D_g (floats per S row)
   int32_t s_col0;         // column offset of this path inside the group
+  int32_t nparts;         // waves that split a receiver's edges (1..4)
   GeomParams g;
   CGTable cg;
 };
@@ -69,6 +70,7 @@ struct BwdUvwArgs {
   int64_t ld_state;       // floats per state row
   int32_t state_col0;     // column of (q = 0, w = 0) for this path
   int32_t rbar_accumulate;
+  int32_t nparts;         // waves per channel tile that split a sender's edges (1..4)
   GeomParams g;
   CGTable cg;
 };
