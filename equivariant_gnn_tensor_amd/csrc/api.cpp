@@ -349,14 +349,17 @@ hipError_t zero_unreached_in(const etpc_plan_s* p, float* x, int32_t n, hipStrea
 // its whole edge list in series (latency bound: a 128-atom cell); splitting the edges over
 // more waves shortens that walk.  Used while the launch stays under 1024 waves, the mean
 // degree gives each wave at least 12 edges, and the state the waves exchange at the end
-// (`states` accumulators of (2 l + 1) x B floats per lane and channel tile) fits 48 KB of LDS.
+// (`states` accumulators of (2 l + 1) x B floats per lane and channel tile) fits kSplitMaxLds.
 constexpr int64_t kSplitMaxWaves = 1024;   // 4096 measured slower on 2048-node launches
+// The exchange buffer stays at 24 KB so that, with the edge record (up to ~20 KB) and the
+// edge-adjoint partials (up to 12 KB), a workgroup stays inside the default 64 KB of LDS.
+constexpr int64_t kSplitMaxLds = 24 * 1024;
 int edge_parts(int nodes, int ntiles, const etpc_graph* g, int l, int nb, int states) {
   const int64_t deg = g->n_nodes > 0 ? g->n_edges / g->n_nodes : 0;
   const int64_t nbp = nb <= 8 ? 8 : 16;
   int np = 1;
   while (np < 4 && ntiles * np * 2 <= 4 && static_cast<int64_t>(nodes) * ntiles * np * 2 <= kSplitMaxWaves &&
-         deg >= 12 * np * 2 && int64_t(ntiles) * 64 * (2 * l + 1) * nbp * states * 4 <= 48 * 1024)
+         deg >= 12 * np * 2 && int64_t(ntiles) * 64 * (2 * l + 1) * nbp * states * 4 <= kSplitMaxLds)
     np *= 2;
   return np;
 }
