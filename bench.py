@@ -83,11 +83,12 @@ def flop_model(plan, n_nodes, n_edges, radial_b, force_step=False):
 
 
 def kernel_source_hash(kind):
+    shared = ["common.hpp", "kernels.hpp", "wave.hpp", "triples.hpp", "cg_tables.inc"]
     files = {
-        "fwd_traverse": ["fwd_impl.hpp", "geom.hpp"],
-        "bwd_traverse": ["bwd_impl.hpp", "geom.hpp"],
-        "channel_gemm": ["gemm.hip"],
-        "node_gemm": ["gemm.hip"],
+        "fwd_traverse": ["fwd_impl.hpp", "geom.hpp"] + shared,
+        "bwd_traverse": ["bwd_impl.hpp", "geom.hpp"] + shared,
+        "channel_gemm": ["gemm.hip", "common.hpp", "kernels.hpp"],
+        "node_gemm": ["gemm.hip", "common.hpp", "kernels.hpp"],
     }.get(kind, [])
     h = hashlib.sha256()
     for f in files:
