@@ -38,8 +38,8 @@
  * Every call validates its arguments on the host first; on a non-OK status no
  * kernel has been enqueued and etpc_last_error() describes the problem.
  * Compute calls are asynchronous on the given stream; results are
- * deterministic for a given workspace size (fixed reduction owners and orders,
- * no floating-point atomics).  Inside a call, the independent per-path launches of a
+ * deterministic for a given workspace size and lane setting (fixed reduction owners
+ * and orders, no floating-point atomics; timing never changes a result).  Inside a call, the independent per-path launches of a
  * pass run on up to two side streams, and the node-side GEMMs of a pass on a third
  * ("post") stream that overlaps them with the next group's or block's traversals; the
  * library creates these streams once per device (default priority) and forks them from
