@@ -10,11 +10,13 @@
 //   edge j -> i  iff  0 < (d_x^2 + d_y^2) + d_z^2 < r_c^2   (i != j).
 // Steps: bounding box (open boundary), cell keys, stable radix sort of atoms by cell,
 // cell row pointers, per-atom neighbour counts over the 27 surrounding cells, a scan,
-// the fill, then two stable radix sorts (by sender, then by receiver) that put the edge
-// list in canonical (receiver, sender) order.  Cells are at least r_c (1 + 2^-10) wide,
+// the fill, then the canonical (receiver, sender) order: rows come out in receiver order,
+// so when no row exceeds 256 edges one wavefront per row sorts its senders; otherwise two
+// stable radix sorts (by sender, then by receiver) order the whole list.  Cells are at least r_c (1 + 2^-10) wide,
 // so every pair inside the cutoff lies in adjacent cells whatever the rounding of the
 // cell index.
 #include <algorithm>
+#include <cstdint>
 #include <cmath>
 #include <string>
 
@@ -144,7 +146,7 @@ __device__ inline int axis_cells(int c, int a, const CellGrid& g, int* out) {
 }
 
 // One thread per atom (in cell order).  FILL = false: counts[i] = number of neighbours,
-// counts[n] = 0, *total += sum.  FILL = true: writes the neighbours of i at
+// counts[n] = 0, total[0] += sum, total[1] = max(total[1], count).  FILL = true: writes the neighbours of i at
 // rowptr[i]..rowptr[i+1] as (src = j, dst = i).
 template <bool FILL>
 __global__ __launch_bounds__(kThreads) void neighbour_kernel(const float4* __restrict__ spos,
@@ -188,13 +190,66 @@ __global__ __launch_bounds__(kThreads) void neighbour_kernel(const float4* __res
   }
   if (!FILL) {
     // one integer atomic per wavefront; the sum does not depend on their order
-    unsigned long long v = static_cast<unsigned long long>(cnt);
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, 64);
-    if ((threadIdx.x & 63) == 0 && v) atomicAdd(total, v);
+    unsigned long long v = static_cast<unsigned long long>(cnt), m = v;
+    for (int off = 32; off > 0; off >>= 1) {
+      v += __shfl_down(v, off, 64);
+      m = max(m, __shfl_down(m, off, 64));
+    }
+    if ((threadIdx.x & 63) == 0 && v) {
+      atomicAdd(total, v);
+      atomicMax(total + 1, m);
+    }
   }
 }
 
-__global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
+__global__ void zero_u64_kernel(unsigned long long* p) {
+  p[0] = 0ull;
+  p[1] = 0ull;
+}
+
+// Sorts each row of at most 64 K senders ascending in place: one wavefront per row, each
+// lane holding K values (element r * 64 + lane in register r), a bitonic network whose
+// partners at distance j < 64 are other lanes (shuffles) and at j >= 64 other registers
+// of the same lane.  Padding holds INT32_MAX and sorts to the end.
+constexpr int kRowSortRows = 4;   // rows (wavefronts) per 256-thread workgroup
+template <int K>
+__global__ __launch_bounds__(256) void row_sort_kernel(const int32_t* __restrict__ rowptr, int32_t n,
+                                                      int32_t* __restrict__ src) {
+  constexpr int M = 64 * K;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowSortRows + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n) return;   // whole wavefronts only
+  const int32_t b = rowptr[row], len = rowptr[row + 1] - b;
+  int32_t v[K];
+#pragma unroll
+  for (int r = 0; r < K; ++r) v[r] = r * 64 + lane < len ? src[b + r * 64 + lane] : INT32_MAX;
+#pragma unroll
+  for (int k = 2; k <= M; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int rj = j >> 6;
+#pragma unroll
+        for (int r = 0; r < K; ++r)
+          if ((r & rj) == 0) {
+            const bool ascending = ((r * 64 + lane) & k) == 0;
+            const int32_t lo = min(v[r], v[r | rj]), hi = max(v[r], v[r | rj]);
+            v[r] = ascending ? lo : hi;
+            v[r | rj] = ascending ? hi : lo;
+          }
+      } else {
+#pragma unroll
+        for (int r = 0; r < K; ++r) {
+          const int32_t other = __shfl_xor(v[r], j, 64);
+          const bool lower = (lane & j) == 0, ascending = ((r * 64 + lane) & k) == 0;
+          v[r] = (lower == ascending) ? min(v[r], other) : max(v[r], other);
+        }
+      }
+    }
+#pragma unroll
+  for (int r = 0; r < K; ++r)
+    if (r * 64 + lane < len) src[b + r * 64 + lane] = v[r];
+}
 
 struct RadiusLayout {
   float* partial;
@@ -221,7 +276,7 @@ RadiusLayout carve(void* base, int32_t n, int64_t max_edges) {
   };
   const size_t N = static_cast<size_t>(n), E = static_cast<size_t>(max_edges);
   L.partial = static_cast<float*>(take(sizeof(float) * 8 * kBoxBlocks));
-  L.total = static_cast<unsigned long long*>(take(sizeof(unsigned long long)));
+  L.total = static_cast<unsigned long long*>(take(2 * sizeof(unsigned long long)));   // edges, max degree
   L.ak0 = static_cast<int32_t*>(take(4 * N));
   L.av0 = static_cast<int32_t*>(take(4 * N));
   L.ak1 = static_cast<int32_t*>(take(4 * N));
@@ -327,9 +382,10 @@ etpc_status radius_graph_impl(int32_t n, const float* pos, float cutoff, const f
                        W.counts, W.total, static_cast<int32_t*>(nullptr), static_cast<int32_t*>(nullptr));
     ETPC_HIP(hipGetLastError());
   }
-  unsigned long long total = 0;
-  ETPC_HIP(hipMemcpyAsync(&total, W.total, sizeof(total), hipMemcpyDeviceToHost, s));
+  unsigned long long counters[2] = {0ull, 0ull};
+  ETPC_HIP(hipMemcpyAsync(counters, W.total, sizeof(counters), hipMemcpyDeviceToHost, s));
   ETPC_HIP(hipStreamSynchronize(s));
+  const unsigned long long total = counters[0], max_degree = counters[1];
   *n_edges = static_cast<int64_t>(total);
   if (total >= (1ull << 31)) ETPC_FAIL(ETPC_ERR_OVERFLOW, "the radius graph has 2^31 edges or more");
   if (static_cast<int64_t>(total) > max_edges)
@@ -341,6 +397,23 @@ etpc_status radius_graph_impl(int32_t n, const float* pos, float cutoff, const f
   {
     ::etpc::ProfScope ps(ETPC_KIND_PREP, s);
     ETPC_HIP(exclusive_scan(W.counts, static_cast<int64_t>(n) + 1, W.scan_aux, s));
+    if (max_degree <= 256) {
+      // rows already in receiver order: fill the outputs and sort each row's senders
+      hipLaunchKernelGGL(neighbour_kernel<true>, dim3(nb), dim3(kThreads), 0, s, W.spos, ab.k0, W.cellptr, n, g,
+                         W.counts, W.total, src, dst);
+      ETPC_HIP(hipGetLastError());
+      const unsigned rb = static_cast<unsigned>((static_cast<int64_t>(n) + kRowSortRows - 1) / kRowSortRows);
+      if (E > 0) {
+        if (max_degree <= 64)
+          hipLaunchKernelGGL(row_sort_kernel<1>, dim3(rb), dim3(256), 0, s, W.counts, n, src);
+        else if (max_degree <= 128)
+          hipLaunchKernelGGL(row_sort_kernel<2>, dim3(rb), dim3(256), 0, s, W.counts, n, src);
+        else
+          hipLaunchKernelGGL(row_sort_kernel<4>, dim3(rb), dim3(256), 0, s, W.counts, n, src);
+      }
+      ETPC_HIP(hipGetLastError());
+      return ETPC_OK;
+    }
     hipLaunchKernelGGL(neighbour_kernel<true>, dim3(nb), dim3(kThreads), 0, s, W.spos, ab.k0, W.cellptr, n, g,
                        W.counts, W.total, eb.k0, eb.v0);
     ETPC_HIP(hipGetLastError());

@@ -6,7 +6,7 @@ oracle's exactly.  Cases: the workloads' own densities (0.1 atoms / A^3, cutoff 
 periodic cubes of 4096 and 16384 atoms), open boundaries, ragged sizes, boxes with fewer
 than three cells per axis, atoms outside the box, coincident atoms and a pair exactly at
 the cutoff, far-apart clusters (the cell grid is widened to its cap), one and two atoms,
-and the capacity error.  At 65,536 atoms the oracle checks sampled receivers' rows, and
+rows longer than one wavefront (the global-sort path), and the capacity error.  At 65,536 atoms the oracle checks sampled receivers' rows, and
 the whole list is checked for order, symmetry and validity.
 
 Layout: mul_ir <-> ir_mul of the workloads' input and output irreps, ragged row counts,
@@ -106,6 +106,15 @@ def test_radius_graph_far_clusters_and_tiny_sets():
     _assert_same(np.zeros((1, 3), np.float32), 2.0, None, "one atom")
     _assert_same(np.array([[0, 0, 0], [1, 1, 1]], np.float32), 2.0, (5.0, 5.0, 5.0), "two atoms")
     _assert_same(_uniform(64, 4.0, 11), 10.0, None, "all atoms in one cell")
+
+
+def test_radius_graph_rows_longer_than_a_wavefront():
+    """Rows of more than 64 edges take the global-sort path, shorter ones the per-row sort."""
+    dense = _uniform(300, 6.0, 15)                     # ~299 neighbours each
+    n = _assert_same(dense, 5.0, None, "dense cluster, rows > 64")
+    assert n > 64 * 300
+    mixed = np.concatenate([_uniform(150, 4.0, 16), _uniform(400, 60.0, 17) + np.float32(20)]).astype(np.float32)
+    _assert_same(mixed, 3.0, None, "dense core and sparse halo")
 
 
 def test_radius_graph_capacity_error_reports_size():
