@@ -1,15 +1,21 @@
 // C ABI: argument validation, workspace carving, chunk scheduling and launches.
 //
-// Schedules (all on the caller's stream, all deterministic for a given workspace):
-//  forward uvw  -- per output group g, per receiver chunk: one receiver traversal per
-//                  path of g builds the receiver state S_g (Sobek paper, Sec. 4, Eq. 33),
-//                  then one MFMA GEMM m_g = S_g W_g writes the output rows (Eq. 34-35).
+// Schedules (one ordered unit of the caller's stream, deterministic for a given workspace
+// and lane setting; the per-path launches of a pass fork onto up to two lanes and the
+// node-side GEMMs onto the post stream, see lanes.hpp):
+//  forward uvw  -- per output group g (largest first), per receiver chunk: one receiver
+//                  traversal per path of g builds the receiver state S_g (Sobek paper,
+//                  Sec. 4, Eq. 33) in one of two S sets, then one MFMA GEMM m_g = S_g W_g
+//                  writes the output rows (Eq. 34-35) on the post stream while the next
+//                  group's traversals fill the other set.
 //  forward uvu  -- one receiver traversal per path writes the output block (Eq. 7, 17).
-//  backward uvw -- per sender chunk, per input block k: Xt = x W (GEMM, if positions
-//                  are wanted), one sender traversal per path of k (P state and the
-//                  edge position adjoint), x_bar = P W^T and W_bar = x^T P (GEMMs,
-//                  split-K with a fixed-order reduction); finally pos_bar from the
-//                  edge adjoints by a segment sum over both CSR views (Eq. 18-22).
+//  backward uvw -- a pipeline over (sender chunk, input block) items, two buffer sets:
+//                  Xt = x W (GEMM, if positions are wanted; for the next item on the post
+//                  stream), one sender traversal per path of the block (P state and the
+//                  edge position adjoint), then x_bar = P W^T and W_bar = x^T P (GEMMs,
+//                  split-K with a fixed-order reduction) on the post stream; finally
+//                  pos_bar from the edge adjoints by a segment sum over both CSR views
+//                  (Eq. 18-22).
 //  backward uvu -- one sender traversal per path (x_bar, W_bar partials, edge adjoint).
 //  double backward -- the directional program of Eq. 23-31 / 37-39 assembled from the
 //                  same traversals in tangent mode plus the same GEMMs.
