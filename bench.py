@@ -403,7 +403,7 @@ def measure(args, name):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if args.gemm_precision == "fp32" else "f32, bf16 channel GEMMs",
+        "dtype": "f32" if args.gemm_precision == "fp32" else f"f32, {args.gemm_precision} channel GEMMs",
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: N={N} atoms at 0.1/A^3 (periodic), radius graph 5 A, E={E}, "
@@ -576,8 +576,8 @@ def main():
                     help="concurrent launch lanes per pass for the timed steps (0 = library default)")
     ap.add_argument("--node-order", choices=("given", "morton"), default="given",
                     help="node numbering: as generated (random in space) or Morton order of the positions")
-    ap.add_argument("--gemm-precision", choices=("fp32", "bf16"), default="fp32",
-                    help="channel GEMM operands: fp32 (reference) or bf16 with fp32 accumulation")
+    ap.add_argument("--gemm-precision", choices=("fp32", "bf16", "fp16"), default="fp32",
+                    help="channel GEMM operands: fp32 (reference), or bf16 / fp16 with fp32 accumulation")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured as a HIP graph (launch-bound small workloads)")
     ap.add_argument("--graph-count-sweep", action="store_true",

@@ -27,7 +27,7 @@ _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "INVALID_PATH", 4: "W
 ERR_CAPACITY = 8
 TO_IR_MUL, TO_MUL_IR = 0, 1
 FEATURES_IN, FEATURES_OUT = 0, 1
-GEMM_FP32, GEMM_BF16 = 0, 1
+GEMM_FP32, GEMM_BF16, GEMM_FP16 = 0, 1, 2
 
 
 class EtpcError(RuntimeError):
@@ -178,7 +178,7 @@ class Plan:
         spec.n_basis, spec.r_lo, spec.r_hi, spec.poly_p = n_basis, r_lo, r_hi, poly_p
         b = (0.0, 0.0, 0.0) if box is None else (tuple(box) if hasattr(box, "__len__") else (box, box, box))
         spec.box = (C.c_float * 3)(*b)
-        spec.gemm_precision = {"fp32": GEMM_FP32, "bf16": GEMM_BF16}[gemm_precision]
+        spec.gemm_precision = {"fp32": GEMM_FP32, "bf16": GEMM_BF16, "fp16": GEMM_FP16}[gemm_precision]
         self.spec = spec
         self.handle = C.c_void_p()
         self.handle = etpc_plan_create(spec)

@@ -445,7 +445,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       ETPC_HIP(lanes.finish());
       ETPC_HIP(post.follow());
       GemmArgs ga{};
-      ga.bf16 = p->gemm_bf16 ? 1 : 0;
+      ga.lowp = p->gemm_precision;
       ga.A = L.S[set];
       ga.amap = plain(D);
       ga.a_mcontig = 0;
@@ -548,7 +548,7 @@ hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float*
   int64_t ks = (K + sp - 1) / sp;
   ks = (ks + 31) / 32 * 32;
   GemmArgs ga{};
-  ga.bf16 = p->gemm_bf16 ? 1 : 0;
+  ga.lowp = p->gemm_precision;
   ga.A = xa + j0 * p->x_dim + p->xoff[k];
   ga.amap = irmul(ni, p->x_dim, c_in);
   ga.a_mcontig = 1;
@@ -573,7 +573,7 @@ etpc_status xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float
   const int64_t ncols = d.block_ncols[k];
   const int c_in = p->in[k].mul;
   GemmArgs ga{};
-  ga.bf16 = p->gemm_bf16 ? 1 : 0;
+  ga.lowp = p->gemm_precision;
   ga.A = state;
   ga.amap = plain(ncols);
   ga.a_mcontig = 0;
@@ -630,7 +630,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     }
     if (want_pos) {  // Xt = x W
       GemmArgs ga{};
-      ga.bf16 = p->gemm_bf16 ? 1 : 0;
+      ga.lowp = p->gemm_precision;
       ga.A = R.x + it.j0 * p->x_dim + p->xoff[k];
       ga.amap = irmul(ni, p->x_dim, c_in);
       ga.a_mcontig = 0;

@@ -1,5 +1,5 @@
-// Dense GEMM on the gfx950 matrix cores: fp32 (v_mfma_f32_32x32x2f32), or with bf16
-// operands and fp32 accumulation (v_mfma_f32_32x32x16_bf16) when the plan asks for it.
+// Dense GEMM on the gfx950 matrix cores: fp32 (v_mfma_f32_32x32x2f32), or with bf16 or
+// fp16 operands and fp32 accumulation (v_mfma_f32_32x32x16_bf16 / _f16) when the plan asks.
 //
 // Used for the channel-space products of the Sobek paper (Sec. 4, Eq. 34-36):
 // m = S W (forward), and the node-side products of the sender-factorized
@@ -250,13 +250,15 @@ __global__ __launch_bounds__(256) void gemm_f32_narrow_kernel(const GemmArgs a) 
   }
 }
 
-// ---------------------------------------------------------------- bf16 operands
+// ---------------------------------------------------------------- bf16 / fp16 operands
 // The reduced-precision option (the analogue of the TF32 channel GEMMs the Sobek paper
-// lists as optional in Sec. 4): A and B are read as fp32, rounded to bf16 (nearest, ties
-// to even) when staged in LDS, multiplied on v_mfma_f32_32x32x16_bf16 and accumulated in
-// fp32.  Tiles as in the fp32 kernels (WGM x WGN wavefronts of 32 x 32); LDS holds A as
-// [m][k] and B as [n][k] so each lane reads its eight consecutive k as one 16-byte load.
+// lists as optional in Sec. 4): A and B are read as fp32, rounded to bf16 or fp16
+// (nearest, ties to even) when staged in LDS, multiplied on v_mfma_f32_32x32x16_bf16 or
+// _f16 and accumulated in fp32.  Tiles as in the fp32 kernels (WGM x WGN wavefronts of
+// 32 x 32); LDS holds A as [m][k] and B as [n][k] so each lane reads its eight
+// consecutive k as one 16-byte load.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ inline uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -265,8 +267,27 @@ __device__ inline uint16_t bf16_rne(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-template <int WGM, int WGN>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs a) {
+// F16: fp16 operands (the hardware conversion rounds to nearest, ties to even), else bf16.
+template <bool F16>
+__device__ inline uint16_t to_low(float f) {
+  if constexpr (F16)
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  else
+    return bf16_rne(f);
+}
+
+template <bool F16>
+__device__ inline f16v mfma_low(const uint16_t* a, const uint16_t* b, const f16v& acc) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const f16x8*>(a),
+                                                  *reinterpret_cast<const f16x8*>(b), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(a),
+                                                   *reinterpret_cast<const bf16x8*>(b), acc, 0, 0, 0);
+}
+
+template <int WGM, int WGN, bool F16>
+__global__ __launch_bounds__(256) void gemm_low_kernel(const GemmArgs a) {
   constexpr int BM = 32 * WGM, BN = 32 * WGN;
   constexpr int AG = BM / 32, BG = BN / 32;
   constexpr int LK = BK + 8;   // padded k stride (elements): rows stay 16-byte aligned
@@ -332,13 +353,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs a) {
       const int g = tid + 256 * h;
       if (!a.a_mcontig) {
         const int row = g >> 3, k4 = (g & 7) * 4;
-        const uint32_t lo = bf16_rne(ra[h][0]) | (static_cast<uint32_t>(bf16_rne(ra[h][1])) << 16);
-        const uint32_t hi = bf16_rne(ra[h][2]) | (static_cast<uint32_t>(bf16_rne(ra[h][3])) << 16);
+        const uint32_t lo = to_low<F16>(ra[h][0]) | (static_cast<uint32_t>(to_low<F16>(ra[h][1])) << 16);
+        const uint32_t hi = to_low<F16>(ra[h][2]) | (static_cast<uint32_t>(to_low<F16>(ra[h][3])) << 16);
         *reinterpret_cast<uint2*>(&As[row][k4]) = make_uint2(lo, hi);
       } else {
         const int k = g / (BM / 4), m4 = (g % (BM / 4)) * 4;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) As[m4 + t][k] = bf16_rne(ra[h][t]);
+        for (int t = 0; t < 4; ++t) As[m4 + t][k] = to_low<F16>(ra[h][t]);
       }
     }
 #pragma unroll
@@ -346,7 +367,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs a) {
       const int g = tid + 256 * h;
       const int k = g / (BN / 4), n4 = (g % (BN / 4)) * 4;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) Bs[n4 + t][k] = bf16_rne(rb[h][t]);
+      for (int t = 0; t < 4; ++t) Bs[n4 + t][k] = to_low<F16>(rb[h][t]);
     }
   };
 
@@ -362,9 +383,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs a) {
     if (k0 + BK < kz1) load(k0 + BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&As[am][kk + k8]);
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bs[bn][kk + k8]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      acc = mfma_low<F16>(&As[am][kk + k8], &Bs[bn][kk + k8], acc);
     }
     __syncthreads();
   }
@@ -400,16 +419,27 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int splits,
 
 hipError_t launch_gemm(const GemmArgs& a, int splits, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.bf16) {
+  if (a.lowp) {
+    const bool f16 = a.lowp == 2;
+    dim3 grid;
     if (a.N <= 32 && a.M > 32) {
-      dim3 grid((a.M + 127) / 128, (a.N + 31) / 32, splits);
-      hipLaunchKernelGGL((gemm_bf16_kernel<4, 1>), grid, dim3(256), 0, s, a);
+      grid = dim3((a.M + 127) / 128, (a.N + 31) / 32, splits);
+      if (f16)
+        hipLaunchKernelGGL((gemm_low_kernel<4, 1, true>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_low_kernel<4, 1, false>), grid, dim3(256), 0, s, a);
     } else if (a.M <= 32 && a.N > 32) {
-      dim3 grid((a.M + 31) / 32, (a.N + 127) / 128, splits);
-      hipLaunchKernelGGL((gemm_bf16_kernel<1, 4>), grid, dim3(256), 0, s, a);
+      grid = dim3((a.M + 31) / 32, (a.N + 127) / 128, splits);
+      if (f16)
+        hipLaunchKernelGGL((gemm_low_kernel<1, 4, true>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_low_kernel<1, 4, false>), grid, dim3(256), 0, s, a);
     } else {
-      dim3 grid((a.M + 63) / 64, (a.N + 63) / 64, splits);
-      hipLaunchKernelGGL((gemm_bf16_kernel<2, 2>), grid, dim3(256), 0, s, a);
+      grid = dim3((a.M + 63) / 64, (a.N + 63) / 64, splits);
+      if (f16)
+        hipLaunchKernelGGL((gemm_low_kernel<2, 2, true>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_low_kernel<2, 2, false>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
   }

@@ -125,7 +125,7 @@ struct GemmArgs {
   int32_t k_split;
   int64_t c_split_stride;
   int32_t vec4;           // 1: every A row / B row start is 16-byte aligned (float4 loads allowed)
-  int32_t bf16;           // 1: operands rounded to bf16, fp32 accumulation
+  int32_t lowp;           // operands rounded to 1: bf16, 2: fp16 (fp32 accumulation); 0: fp32
 };
 hipError_t launch_gemm(const GemmArgs& a, int splits, hipStream_t s);
 // C(m, n) (+)= sum_{s < splits} part[s][m][n] (fixed order), C rows through cmap

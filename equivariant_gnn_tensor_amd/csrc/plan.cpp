@@ -204,7 +204,8 @@ etpc_status etpc_plan_create(const etpc_spec* s, etpc_plan* out) {
   const bool any_box = s->box[0] != 0.f || s->box[1] != 0.f || s->box[2] != 0.f;
   if (any_box && !(s->box[0] > 0.f && s->box[1] > 0.f && s->box[2] > 0.f))
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "box must be all zero (open) or all positive");
-  if (s->gemm_precision != ETPC_GEMM_FP32 && s->gemm_precision != ETPC_GEMM_BF16)
+  if (s->gemm_precision != ETPC_GEMM_FP32 && s->gemm_precision != ETPC_GEMM_BF16 &&
+      s->gemm_precision != ETPC_GEMM_FP16)
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "unknown gemm_precision");
 
   auto p = new etpc_plan_s();
@@ -218,7 +219,7 @@ etpc_status etpc_plan_create(const etpc_spec* s, etpc_plan* out) {
   p->r_hi = s->r_hi;
   p->periodic = any_box;
   for (int d = 0; d < 3; ++d) p->box[d] = s->box[d];
-  p->gemm_bf16 = s->gemm_precision == ETPC_GEMM_BF16;
+  p->gemm_precision = s->gemm_precision;
 
   std::vector<std::tuple<int, int, int>> instr;
   if (s->out_per_path) {

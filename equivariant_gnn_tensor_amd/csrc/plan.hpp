@@ -28,7 +28,7 @@ struct etpc_plan_s {
   float r_lo = 0.f, r_hi = 0.f;
   float box[3] = {0.f, 0.f, 0.f};
   bool periodic = false;
-  bool gemm_bf16 = false;   // channel GEMMs with bf16 operands (fp32 accumulation)
+  int32_t gemm_precision = 0;   // etpc_gemm_precision of the channel GEMMs
   int64_t x_dim = 0, z_dim = 0, w_numel = 0;
   std::vector<etpc::PathInfo> paths;
   // paths grouped by output block / input block (indices into `paths`, plan order)

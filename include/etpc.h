@@ -82,9 +82,10 @@ typedef enum { ETPC_PASS_FWD = 0, ETPC_PASS_BWD = 1, ETPC_PASS_DBL = 2 } etpc_pa
 /* Arithmetic of the channel-space GEMMs (z = S W, Xt = x W, x_bar = P W^T, W_bar = x^T P).
  * FP32 is the reference schedule.  BF16 rounds both operands to bf16 (nearest, ties to
  * even) and accumulates in fp32 on the matrix cores: the analogue of the optional TF32
- * channel GEMMs of Sec. 4, with about 2^-9 relative rounding per operand.  The traversals
- * and every reduction stay fp32. */
-typedef enum { ETPC_GEMM_FP32 = 0, ETPC_GEMM_BF16 = 1 } etpc_gemm_precision;
+ * channel GEMMs of Sec. 4, with about 2^-9 relative rounding per operand.  FP16 does the
+ * same in fp16 (2^-11 relative rounding; magnitudes above 65504 overflow to infinity).
+ * The traversals and every reduction stay fp32. */
+typedef enum { ETPC_GEMM_FP32 = 0, ETPC_GEMM_BF16 = 1, ETPC_GEMM_FP16 = 2 } etpc_gemm_precision;
 
 /* One irrep block: multiplicity, degree l (0..3) and parity (+1 'e', -1 'o'). */
 typedef struct { int32_t mul, l, parity; } etpc_irrep;

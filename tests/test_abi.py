@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import equivariant_gnn_tensor_amd as etpc
+from equivariant_gnn_tensor_amd import _binding
 from oracle import irreps as oir
 from oracle.cg import real_cg
 from tests.planner_helpers import plan_from_config
@@ -68,6 +69,18 @@ def test_invalid_specs(kwargs, status):
     with pytest.raises(etpc.EtpcError) as ei:
         etpc.Plan(**base)
     assert ei.value.name == status
+
+
+def test_gemm_precision_codes():
+    """fp32, bf16 and fp16 channel GEMMs are accepted; any other code is an argument error."""
+    base = dict(irreps_in="4x0e+4x1o", irreps_out="4x0e+4x1o", lmax_sh=2)
+    for prec in ("fp32", "bf16", "fp16"):
+        etpc.Plan(**base, gemm_precision=prec)
+    spec = etpc.Plan(**base).spec
+    spec.gemm_precision = 3
+    with pytest.raises(etpc.EtpcError) as ei:
+        _binding.etpc_plan_create(spec)
+    assert ei.value.name == "INVALID_ARG"
 
 
 def test_workspace_is_node_sized():
