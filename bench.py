@@ -300,11 +300,11 @@ def measure(args, name):
     torch.cuda.synchronize()
 
     # CSR build, timed on its own (not part of a step)
-    graph = etpc.etpc_csr_build(N, src, dst)
+    graph = etpc.etpc_csr_build(N, src, dst, order=args.sender_order == "degree")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(3):
-        graph = etpc.etpc_csr_build(N, src, dst)
+        graph = etpc.etpc_csr_build(N, src, dst, order=args.sender_order == "degree")
     torch.cuda.synchronize()
     csr_ms = (time.perf_counter() - t0) / 3 * 1e3
 
@@ -417,6 +417,7 @@ def measure(args, name):
                      else "forward + backward (x_bar, W_bar, pos_bar)"),
             "launch": "hip graph replay" if args.graph else "eager",
             "node_order": args.node_order,
+            "sender_order": args.sender_order,
             "lanes": timed_lanes,
         },
         "roofline": {
@@ -576,6 +577,8 @@ def main():
                     help="concurrent launch lanes per pass for the timed steps (0 = library default)")
     ap.add_argument("--node-order", choices=("given", "morton"), default="given",
                     help="node numbering: as generated (random in space) or Morton order of the positions")
+    ap.add_argument("--sender-order", choices=("degree", "index"), default="degree",
+                    help="sender traversal dispatch: decreasing degree (the graph's s_order) or index order")
     ap.add_argument("--gemm-precision", choices=("fp32", "bf16", "fp16"), default="fp32",
                     help="channel GEMM operands: fp32 (reference), or bf16 / fp16 with fp32 accumulation")
     ap.add_argument("--graph", action="store_true",

@@ -60,7 +60,7 @@ class etpc_graph(C.Structure):
     _fields_ = [
         ("n_nodes", C.c_int32), ("n_edges", C.c_int64),
         ("rowptr", C.c_void_p), ("col", C.c_void_p),
-        ("s_rowptr", C.c_void_p), ("s_col", C.c_void_p), ("s_slot", C.c_void_p),
+        ("s_rowptr", C.c_void_p), ("s_col", C.c_void_p), ("s_slot", C.c_void_p), ("s_order", C.c_void_p),
     ]
 
 
@@ -69,7 +69,7 @@ SYMBOLS = (
     "etpc_plan_cg", "etpc_workspace_size", "etpc_csr_workspace_size", "etpc_csr_build", "etpc_graph_validate",
     "etpc_forward", "etpc_backward", "etpc_double_backward", "etpc_set_lanes", "etpc_get_lanes",
     "etpc_profile_enable", "etpc_profile_read", "etpc_radius_graph_workspace_size", "etpc_radius_graph",
-    "etpc_layout_convert", "etpc_last_error",
+    "etpc_layout_convert", "etpc_last_error", "etpc_degree_order_workspace_size", "etpc_degree_order",
 )
 KINDS = ("csr", "fwd_traverse", "channel_gemm", "bwd_traverse", "node_gemm", "aux", "prep")
 
@@ -92,6 +92,8 @@ def _load():
         "etpc_csr_workspace_size": [i32, i64, P(sz)],
         "etpc_csr_build": [i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_graph_validate": [P(etpc_graph), vp],
+        "etpc_degree_order_workspace_size": [i32, P(sz)],
+        "etpc_degree_order": [i32, vp, vp, vp, sz, vp],
         "etpc_forward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, sz, vp],
         "etpc_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_double_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -270,10 +272,11 @@ def etpc_csr_workspace_size(n_nodes: int, n_edges: int) -> int:
 class Graph:
     """Device CSR views (receiver and sender) of one graph."""
 
-    def __init__(self, n_nodes: int, rowptr, col, s_rowptr, s_col, s_slot, eid=None):
+    def __init__(self, n_nodes: int, rowptr, col, s_rowptr, s_col, s_slot, eid=None, s_order=None):
         self.n_nodes = int(n_nodes)
         self.rowptr, self.col, self.eid = rowptr, col, eid
         self.s_rowptr, self.s_col, self.s_slot = s_rowptr, s_col, s_slot
+        self.s_order = s_order
         self.n_edges = int(col.shape[0])
         g = etpc_graph()
         g.n_nodes, g.n_edges = self.n_nodes, self.n_edges
@@ -282,7 +285,12 @@ class Graph:
         g.s_rowptr = _ptr(s_rowptr, torch.int32)
         g.s_col = _ptr(s_col, torch.int32) if self.n_edges else None
         g.s_slot = _ptr(s_slot, torch.int32) if self.n_edges else None
+        g.s_order = _ptr(s_order, torch.int32) if s_order is not None and self.n_nodes else None
         self.c = g
+
+    def without_order(self) -> "Graph":
+        """The same views with s_order unset (senders dispatched in index order)."""
+        return Graph(self.n_nodes, self.rowptr, self.col, self.s_rowptr, self.s_col, self.s_slot, eid=self.eid)
 
 
 def _empty_i32(n, device):
@@ -296,7 +304,9 @@ def _workspace(nbytes: int, device) -> Tuple[Optional[torch.Tensor], int]:
     return t, nbytes
 
 
-def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=None) -> Graph:
+def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=None, order: bool = True) -> Graph:
+    """Both CSR views of the COO list; with `order`, also the sender dispatch order
+    (etpc_degree_order of s_rowptr)."""
     dev = src.device
     e = int(src.shape[0])
     rowptr, s_rowptr = _empty_i32(n_nodes + 1, dev), _empty_i32(n_nodes + 1, dev)
@@ -306,7 +316,24 @@ def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=No
                               _ptr(col, torch.int32), _ptr(eid, torch.int32), _ptr(s_rowptr, torch.int32),
                               _ptr(s_col, torch.int32), _ptr(s_slot, torch.int32),
                               None if ws is None else ws.data_ptr(), nb, _stream(stream)))
-    return Graph(n_nodes, rowptr, col, s_rowptr, s_col, s_slot, eid=eid)
+    s_order = etpc_degree_order(s_rowptr, stream=stream) if order else None
+    return Graph(n_nodes, rowptr, col, s_rowptr, s_col, s_slot, eid=eid, s_order=s_order)
+
+
+def etpc_degree_order_workspace_size(n_nodes: int) -> int:
+    b = C.c_size_t()
+    _check(lib.etpc_degree_order_workspace_size(n_nodes, C.byref(b)))
+    return b.value
+
+
+def etpc_degree_order(rowptr: torch.Tensor, stream=None) -> torch.Tensor:
+    """Nodes by decreasing row length rowptr[v+1] - rowptr[v], ties by index (int32 [N])."""
+    n = int(rowptr.shape[0]) - 1
+    order = _empty_i32(n, rowptr.device)
+    ws, nb = _workspace(etpc_degree_order_workspace_size(n), rowptr.device)
+    _check(lib.etpc_degree_order(n, _ptr(rowptr, torch.int32), _ptr(order, torch.int32) if n > 0 else None,
+                                 None if ws is None else ws.data_ptr(), nb, _stream(stream)))
+    return order
 
 
 def etpc_graph_validate(graph: Graph, stream=None) -> None:

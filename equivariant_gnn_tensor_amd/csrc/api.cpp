@@ -35,6 +35,8 @@ etpc_status csr_build_impl(int32_t n_nodes, int64_t n_edges, const int32_t* src,
                            int32_t* col, int32_t* eid, int32_t* s_rowptr, int32_t* s_col, int32_t* s_slot, void* ws,
                            hipStream_t s);
 etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s);
+size_t degree_order_bytes(int32_t n);
+etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t* order, void* ws, hipStream_t s);
 size_t radius_workspace_bytes(int32_t n_nodes, int64_t max_edges);
 etpc_status radius_graph_impl(int32_t n, const float* pos, float cutoff, const float* box, int64_t max_edges,
                               int32_t* src, int32_t* dst, int64_t* n_edges, void* ws, hipStream_t s);
@@ -700,6 +702,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.Pdot = L.Pd[set];
         a.rbar = R.rbar ? R.rbar + lane * rbar_stride : nullptr;
         a.send0 = static_cast<int32_t>(j0);
+        a.order = (g->s_order != nullptr && j0 == 0 && nsend == g->n_nodes) ? g->s_order : nullptr;
         a.z_dim = static_cast<int32_t>(p->z_dim);
         a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
         int ntiles = 1;
@@ -876,6 +879,24 @@ etpc_status etpc_csr_build(int32_t n_nodes, int64_t n_edges, const int32_t* src,
   if (st != ETPC_OK) return st;
   ::etpc::ProfScope ps(ETPC_KIND_CSR, stream);
   return csr_build_impl(n_nodes, n_edges, src, dst, rowptr, col, eid, s_rowptr, s_col, s_slot, ws, stream);
+}
+
+etpc_status etpc_degree_order_workspace_size(int32_t n_nodes, size_t* bytes) {
+  if (bytes == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null output");
+  if (n_nodes < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative node count");
+  *bytes = degree_order_bytes(n_nodes);
+  return ETPC_OK;
+}
+
+etpc_status etpc_degree_order(int32_t n_nodes, const int32_t* rowptr, int32_t* order, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
+  if (n_nodes < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative node count");
+  if (n_nodes == 0) return ETPC_OK;
+  if (rowptr == nullptr || order == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null arrays");
+  etpc_status st = check_ws(ws, ws_bytes, degree_order_bytes(n_nodes));
+  if (st != ETPC_OK) return st;
+  ::etpc::ProfScope ps(ETPC_KIND_CSR, stream);
+  return degree_order_impl(n_nodes, rowptr, order, ws, stream);
 }
 
 etpc_status etpc_graph_validate(const etpc_graph* g, hipStream_t stream) {

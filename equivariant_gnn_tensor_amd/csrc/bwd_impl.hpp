@@ -36,6 +36,14 @@ constexpr int kMaxTiles = 4;
 #define ETPC_BWD_PREFETCH 2
 #endif
 constexpr int kPrefetch = ETPC_BWD_PREFETCH;
+// The radial contractions of the position adjoint, T = sum_q phi_q Xt[q] and
+// G = sum_q phi'_q Xt[q], on the matrix cores (1) or on the VALU (0).
+#ifndef ETPC_BWD_XT_MFMA
+#define ETPC_BWD_XT_MFMA 1
+#endif
+constexpr bool kXtMfma = ETPC_BWD_XT_MFMA != 0;
+static_assert(!kXtMfma || kPrefetch == 2, "the matrix-core radial contraction covers two trips");
+
 // What may cross the scheduling barrier placed after each pipelined gather: LDS reads and
 // writes (0x80 | 0x100 | 0x200), so record reads can be hoisted; global loads never.
 constexpr int kSchedMask = 0x380;
@@ -175,7 +183,11 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   // [nwaves][64][rows][3] edge-adjoint partials, then (nparts > 1) the state exchange
   extern __shared__ float s_dyn[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
-  const int j = a.send0 + blockIdx.x;
+  // Senders in decreasing degree when an order is given: the hardware hands out
+  // workgroups in index order, so the last ones to start are the short ones and the
+  // launch ends with a short tail.  Each sender keeps its own state rows, so the
+  // results do not depend on the order.
+  const int j = a.order ? a.order[blockIdx.x] : a.send0 + static_cast<int>(blockIdx.x);
   const int cp = a.cp;
   const int nslots = kWave / cp;
   const int slot = lane / cp;
@@ -191,7 +203,7 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
   const int row_in_slot = (lane - slot * cp) >> 4;
   const bool row_leader = (lane & 15) == 0;
   const int q4 = lane & 3;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * NI;
+  const int64_t row0 = static_cast<int64_t>(j - a.send0) * NI;
   float xt[NB][NI];
   if constexpr (POS) {
 #pragma unroll
@@ -247,6 +259,26 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
       for (int mo = 0; mo < NO; ++mo) zq[pf][mo] += 0.f;
     }
     for (int it0 = 0; it0 < trips; it0 += kPrefetch) {
+      // Position adjoint, radial contractions of both trips of the group at once: with
+      // 4x4x1 matrix-core blocks of four lanes, row r of a block takes phi (r = 0, 1) or
+      // phi' (r = 2, 3) of the edge of trip it0 + (r & 1), and each lane's column is its own
+      // Xt[q][m_in]; so after the NB accumulations register r of a lane holds T (r < 2) or
+      // G (r >= 2) of that edge for the lane's channel.  A padding trip reads edge 0's
+      // record; its results feed only the edge adjoint that is never stored.
+      f4v TG[NI];
+      if constexpr (POS && kXtMfma) {
+        const int r4 = lane & 3;
+        const int tt = (it0 + (r4 & 1)) * tslots + gslot;
+        const float* er = s_edge + (tt < ne ? tt : 0) * R::kStride + (r4 < 2 ? R::kPhi : R::kDphi);
+#pragma unroll
+        for (int mi = 0; mi < NI; ++mi) TG[mi] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const float aq = er[q];
+#pragma unroll
+          for (int mi = 0; mi < NI; ++mi) TG[mi] = __builtin_amdgcn_mfma_f32_4x4x1f32(aq, xt[q][mi], TG[mi], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int pf = 0; pf < kPrefetch; ++pf) {
         // trips run in whole groups of kPrefetch (no exit inside the unrolled body, which
@@ -310,11 +342,19 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
 #pragma unroll
           for (int mi = 0; mi < NI; ++mi) {
             float tq = 0.f, gq = 0.f, g2 = 0.f;
+            if constexpr (kXtMfma) {
+              tq = TG[mi][pf];
+              gq = TG[mi][2 + pf];
+            } else {
 #pragma unroll
-            for (int q = 0; q < NB; ++q) {
-              tq += e[R::kPhi + q] * xt[q][mi];
-              gq += e[R::kDphi + q] * xt[q][mi];
-              if constexpr (HESS) g2 += e[R::kDDphi + q] * xt[q][mi];
+              for (int q = 0; q < NB; ++q) {
+                tq += e[R::kPhi + q] * xt[q][mi];
+                gq += e[R::kDphi + q] * xt[q][mi];
+              }
+            }
+            if constexpr (HESS) {
+#pragma unroll
+              for (int q = 0; q < NB; ++q) g2 += e[R::kDDphi + q] * xt[q][mi];
             }
             srad += gq * Q[mi];
             // Hessian pass: d srad = sum (rho_dot G2 Q + G dQ), dQ = dY . V

@@ -233,6 +233,36 @@ hipError_t radix_sort(SortBufs& b, int64_t n, int passes, hipStream_t s) {
 
 namespace {
 
+// key = INT32_MAX - degree, so ascending keys are descending degrees; value = node
+__global__ void degree_key_kernel(const int32_t* __restrict__ rowptr, int32_t n, int32_t* __restrict__ key,
+                                  int32_t* __restrict__ val) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= n) return;
+  key[v] = 0x7fffffff - (rowptr[v + 1] - rowptr[v]);
+  val[v] = v;
+}
+
+}  // namespace
+
+size_t degree_order_bytes(int32_t n) {
+  const size_t a = (static_cast<size_t>(n) + 63) & ~size_t(63);
+  return sizeof(int32_t) * (4 * a + sort_scratch_ints(n));
+}
+
+etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t* order, void* ws, hipStream_t s) {
+  if (n == 0) return ETPC_OK;
+  const size_t a = (static_cast<size_t>(n) + 63) & ~size_t(63);
+  int32_t* base = static_cast<int32_t*>(ws);
+  SortBufs b = make_sort_bufs(base, base + a, base + 2 * a, base + 3 * a, base + 4 * a, n);
+  hipLaunchKernelGGL(degree_key_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, rowptr, n, b.k0, b.v0);
+  // a stable LSD sort over all four key bytes: ties keep increasing node index
+  ETPC_HIP(radix_sort(b, n, 4, s));
+  ETPC_HIP(launch_copy(b.v0, order, n, s));
+  return ETPC_OK;
+}
+
+namespace {
+
 __device__ int g_graph_error;
 
 __global__ void validate_rowptr_kernel(const int32_t* __restrict__ rp, int n, int64_t e, int code) {
@@ -275,6 +305,24 @@ __global__ void validate_slots_kernel(const etpc_graph g) {
 }
 
 // sender rows: strictly increasing slots in range
+// s_order: every entry in range and each adjacent pair in (decreasing degree, increasing
+// index) order; a strictly ordered sequence of N values in [0, N) is a permutation
+__global__ void validate_order_kernel(const etpc_graph g) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= g.n_nodes) return;
+  const int v = g.s_order[k];
+  if (v < 0 || v >= g.n_nodes) {
+    atomicMax(&g_graph_error, 7);
+    return;
+  }
+  if (k + 1 < g.n_nodes) {
+    const int u = g.s_order[k + 1];
+    if (u < 0 || u >= g.n_nodes) return;   // reported by thread k + 1
+    const int dv = g.s_rowptr[v + 1] - g.s_rowptr[v], du = g.s_rowptr[u + 1] - g.s_rowptr[u];
+    if (!(dv > du || (dv == du && v < u))) atomicMax(&g_graph_error, 7);
+  }
+}
+
 __global__ void validate_sender_rows_kernel(const etpc_graph g) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   if (j >= g.n_nodes) return;
@@ -355,6 +403,8 @@ etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s) {
   if (err == 0) {
     hipLaunchKernelGGL(validate_sender_rows_kernel, dim3(blocks), dim3(threads), 0, s, g);
     hipLaunchKernelGGL(validate_slots_kernel, dim3(blocks), dim3(threads), 0, s, g);
+    if (g.s_order != nullptr && g.n_nodes > 0)
+      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g);
     ETPC_HIP(hipGetLastError());
     ETPC_HIP(hipMemcpyFromSymbolAsync(&err, HIP_SYMBOL(g_graph_error), sizeof(int), 0, hipMemcpyDeviceToHost, s));
     ETPC_HIP(hipStreamSynchronize(s));
@@ -365,7 +415,8 @@ etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s) {
                                "receiver col out of range",
                                "self loop (sender == receiver)",
                                "sender view does not hold a receiver slot (or s_col mismatch)",
-                               "sender row slots out of range or not strictly increasing"};
+                               "sender row slots out of range or not strictly increasing",
+                               "s_order is not the decreasing-degree order of s_rowptr"};
   if (err != 0) ETPC_FAIL(ETPC_ERR_GRAPH, what[err]);
   return ETPC_OK;
 }

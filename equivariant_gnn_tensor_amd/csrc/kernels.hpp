@@ -64,6 +64,7 @@ struct BwdUvwArgs {
   float* P;               // [N*NI rows][ld_state] (needs_p)
   float* Pdot;            // tangent only
   float* rbar;            // [E][3] edge position adjoint, receiver-slot order (needs_pos)
+  const int32_t* order;   // workgroup b takes sender order[b] (whole-graph launches), or null: send0 + b
   int32_t send0;          // first sender of this chunk (state rows are chunk-relative)
   int32_t z_dim, zoff, c_out, cp;
   int32_t ls;

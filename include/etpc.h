@@ -112,8 +112,13 @@ typedef struct {
 /* Receiver-sorted CSR plus the sender (source) view; all DEVICE pointers.
  * rowptr[N+1], col[E] = sender of each receiver slot;
  * s_rowptr[N+1], s_col[E] = receiver of each sender slot, s_slot[E] = the receiver slot.
+ * s_order[N] (optional, NULL = index order): the senders by decreasing out-degree, ties
+ * in index order, as etpc_degree_order writes it for s_rowptr.  The uvw sender
+ * traversals then start the longest senders first, which shortens the tail of each
+ * launch; results are bit-identical either way.
  * Preconditions (checked only by etpc_graph_validate): indices in range, both views
- * describe the same edge multiset, no self loops, |r_e| > 0 on every edge. */
+ * describe the same edge multiset, no self loops, |r_e| > 0 on every edge, s_order (when
+ * given) equal to etpc_degree_order of s_rowptr. */
 typedef struct {
   int32_t n_nodes;
   int64_t n_edges;
@@ -122,6 +127,7 @@ typedef struct {
   const int32_t* s_rowptr;
   const int32_t* s_col;
   const int32_t* s_slot;
+  const int32_t* s_order;
 } etpc_graph;
 
 /* Planner (host only).  Parses the spec, enumerates the valid paths (selection
@@ -161,6 +167,17 @@ etpc_status etpc_csr_build(int32_t n_nodes, int64_t n_edges, const int32_t* src,
                            int32_t* rowptr, int32_t* col, int32_t* eid,
                            int32_t* s_rowptr, int32_t* s_col, int32_t* s_slot,
                            void* ws, size_t ws_bytes, hipStream_t stream);
+/* Node dispatch order: order[k] = the node with the k-th largest row length
+ * rowptr[v+1] - rowptr[v], ties in increasing node index (a stable sort by decreasing
+ * degree).  For s_rowptr this is the graph's s_order.  The sender traversals own a node's
+ * whole adjoint (Sec. 4, source-contiguous traversal), so their per-workgroup work is
+ * the node's degree; running the heavy nodes first is the longest-first rule of list
+ * scheduling.  rowptr [device] int32 [N+1] (non-decreasing); order [device] int32 [N]
+ * out.  Bit-exact and deterministic.  Workspace from etpc_degree_order_workspace_size;
+ * ETPC_ERR_INVALID_ARG for N < 0, null pointers with N > 0, or a workspace too small. */
+etpc_status etpc_degree_order_workspace_size(int32_t n_nodes, size_t* bytes);
+etpc_status etpc_degree_order(int32_t n_nodes, const int32_t* rowptr, int32_t* order, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
 /* Debug check of the graph preconditions; synchronizes the stream.  Needs no workspace. */
 etpc_status etpc_graph_validate(const etpc_graph* graph, hipStream_t stream);
 

@@ -8,6 +8,9 @@ receiver view: edges sorted by receiver, ties by original COO index;
   rowptr[N+1], col = sender of each slot, eid = COO index of each slot.
 sender view: receiver-view slots sorted by sender, ties by slot;
   s_rowptr[N+1], s_col = receiver of each sender slot, s_slot = receiver slot.
+degree order: the nodes by decreasing row length of a CSR view, ties by increasing
+  index (the dispatch order of the source-major traversal; no arithmetic, a stable
+  sort of the degrees).
 
 Pinned by tests/test_oracle_csr.py against a brute-force construction.
 """
@@ -30,3 +33,9 @@ def csr_build(n_nodes: int, src, dst):
     i32 = lambda a: a.astype(np.int32)  # noqa: E731
     return dict(rowptr=i32(rowptr), col=i32(col), eid=i32(perm),
                 s_rowptr=i32(s_rowptr), s_col=i32(s_col), s_slot=i32(sperm))
+
+
+def degree_order(rowptr):
+    """Nodes by decreasing rowptr[v+1] - rowptr[v], ties by increasing v."""
+    deg = np.diff(np.asarray(rowptr, np.int64))
+    return np.argsort(-deg, kind="stable").astype(np.int32)

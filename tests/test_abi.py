@@ -169,3 +169,18 @@ def test_layout_convert_argument_errors():
     assert lib.etpc_layout_convert(plan.handle, 0, 0, 4, 4096, 4096 + 16, None) == 1   # overlap
     assert "overlap" in lib.etpc_last_error().decode()
     assert lib.etpc_layout_convert(plan.handle, 1, 1, 0, None, None, None) == 0       # no rows
+
+
+def test_degree_order_argument_errors():
+    assert etpc.etpc_degree_order_workspace_size(4096) > 0
+    with pytest.raises(etpc.EtpcError):
+        etpc.etpc_degree_order_workspace_size(-1)
+    lib = _binding.lib
+    assert lib.etpc_degree_order(0, None, None, None, 0, None) == 0      # empty: nothing to do
+    st = lib.etpc_degree_order(-1, None, None, None, 0, None)
+    assert st != 0
+    st = lib.etpc_degree_order(8, None, None, None, 0, None)              # null arrays
+    assert st != 0
+    # a workspace too small is refused before anything is launched
+    st = lib.etpc_degree_order(8, 16, 16, 16, 8, None)
+    assert st != 0 and "workspace" in etpc.lib.etpc_last_error().decode().lower()

@@ -181,6 +181,34 @@ def test_double_backward_all_cotangents(name, n):
     assert max(errs) <= TOL_DBL
 
 
+@pytest.mark.parametrize("n", [256, None])
+def test_sender_order_is_bit_identical(n):
+    """Dispatching senders in decreasing degree (the graph's s_order) changes only which
+    workgroup takes which sender: backward and double backward are bit-identical to the
+    index-order dispatch (the small graph takes the edge-split launches, the full one the
+    plain ones)."""
+    etpc = _etpc()
+    cfg = CONFIGS["cfg2"] if n is None else small_variant("cfg2", n)
+    c = make_case(cfg)
+    assert c.graph.s_order is not None
+    g0 = c.graph.without_order()
+    note(f"sender order {cfg.name}")
+    a = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar)
+    b = etpc.etpc_backward(c.plan, g0, c.x, c.pos, c.w, c.z_bar)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    if n is not None:
+        rng = np.random.default_rng(5)
+        kw = dict(x_dot=torch.from_numpy(rng.standard_normal(c.wl.x.shape).astype(np.float32)).cuda(),
+                  pos_dot=torch.from_numpy(rng.standard_normal(c.wl.pos.shape).astype(np.float32)).cuda())
+        a = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, **kw)
+        b = etpc.etpc_double_backward(c.plan, g0, c.x, c.pos, c.w, c.z_bar, **kw)
+        torch.cuda.synchronize()
+        for u, v in zip(a, b):
+            assert torch.equal(u, v)
+
+
 def test_determinism_and_chunked_workspace():
     etpc = _etpc()
     cfg = small_variant("cfg2", 256)

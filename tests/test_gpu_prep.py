@@ -9,6 +9,9 @@ the cutoff, far-apart clusters (the cell grid is widened to its cap), one and tw
 rows longer than one wavefront (the global-sort path), and the capacity error.  At 65,536 atoms the oracle checks sampled receivers' rows, and
 the whole list is checked for order, symmetry and validity.
 
+Degree order: the sender dispatch order (decreasing degree, ties by index) equals the
+oracle's stable sort bit for bit; etpc_graph_validate accepts it and rejects a wrong one.
+
 Layout: mul_ir <-> ir_mul of the workloads' input and output irreps, ragged row counts,
 round trips.
 """
@@ -16,6 +19,7 @@ import numpy as np
 import pytest
 import torch
 
+from oracle import csr as ocsr
 from oracle import layout as olayout
 from oracle import radius as oradius
 from tests.gpu_helpers import note
@@ -195,3 +199,31 @@ def test_layout_convert_odd_widths_and_offsets(irreps):
             etpc.etpc_layout_convert(plan, "out", "to_mul_ir", xin, out=xout)
             torch.cuda.synchronize()
             assert np.array_equal(xout.cpu().numpy(), olayout.ir_mul_to_mul_ir(x, ir))
+
+
+@pytest.mark.parametrize("n,e", [(1, 0), (7, 0), (500, 4000), (4096, 200000), (70000, 300000)])
+def test_degree_order_matches_oracle(n, e):
+    etpc = _etpc()
+    rng = np.random.default_rng(n + e)
+    src = rng.integers(0, n, e).astype(np.int32)
+    dst = rng.integers(0, n, e).astype(np.int32)
+    keep = src != dst
+    src, dst = src[keep], dst[keep]
+    note(f"degree order N={n} E={src.size}")
+    g = etpc.etpc_csr_build(n, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    r_order = etpc.etpc_degree_order(g.rowptr)
+    torch.cuda.synchronize()
+    ref = ocsr.csr_build(n, src, dst)
+    assert np.array_equal(g.s_order.cpu().numpy(), ocsr.degree_order(ref["s_rowptr"]))
+    assert np.array_equal(r_order.cpu().numpy(), ocsr.degree_order(ref["rowptr"]))
+    etpc.etpc_graph_validate(g)
+    if n > 1:
+        bad = g.s_order.clone()
+        bad[[0, -1]] = bad[[-1, 0]]
+        with pytest.raises(etpc.EtpcError) as ei:
+            etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot, s_order=bad))
+        assert ei.value.name == "GRAPH"
+        bad = g.s_order.clone()
+        bad[1] = n
+        with pytest.raises(etpc.EtpcError):
+            etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot, s_order=bad))

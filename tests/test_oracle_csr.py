@@ -1,7 +1,7 @@
 """Pins for oracle/csr.py against a brute-force construction."""
 import numpy as np
 
-from oracle.csr import csr_build
+from oracle.csr import csr_build, degree_order
 
 
 def _brute(n, src, dst):
@@ -42,3 +42,22 @@ def test_all_into_one_and_duplicates():
     want = _brute(4, src, dst)
     for k in want:
         assert list(got[k]) == list(want[k])
+
+
+def test_degree_order_brute_force(rng):
+    """Selection of the remaining node with the largest degree, smallest index first."""
+    for n, e in [(1, 0), (6, 0), (9, 40), (40, 300), (64, 2000)]:
+        src = rng.integers(0, n, e) if e else np.zeros(0, np.int64)
+        dst = rng.integers(0, n, e) if e else np.zeros(0, np.int64)
+        g = csr_build(n, src, dst)
+        deg = [int(g["s_rowptr"][v + 1] - g["s_rowptr"][v]) for v in range(n)]
+        left, want = list(range(n)), []
+        while left:
+            best = left[0]
+            for v in left[1:]:
+                if deg[v] > deg[best]:
+                    best = v
+            want.append(best)
+            left.remove(best)
+        assert list(degree_order(g["s_rowptr"])) == want
+    assert list(degree_order(np.array([0, 2, 4, 4, 7]))) == [3, 0, 1, 2]
