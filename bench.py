@@ -578,7 +578,8 @@ def main():
     ap.add_argument("--node-order", choices=("given", "morton"), default="given",
                     help="node numbering: as generated (random in space) or Morton order of the positions")
     ap.add_argument("--sender-order", choices=("degree", "index"), default="degree",
-                    help="sender traversal dispatch: decreasing degree (the graph's s_order) or index order")
+                    help="traversal dispatch: nodes by decreasing degree (the graph's s_order and r_order) "
+                         "or in index order")
     ap.add_argument("--gemm-precision", choices=("fp32", "bf16", "fp16"), default="fp32",
                     help="channel GEMM operands: fp32 (reference), or bf16 / fp16 with fp32 accumulation")
     ap.add_argument("--graph", action="store_true",

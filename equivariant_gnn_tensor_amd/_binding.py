@@ -61,6 +61,7 @@ class etpc_graph(C.Structure):
         ("n_nodes", C.c_int32), ("n_edges", C.c_int64),
         ("rowptr", C.c_void_p), ("col", C.c_void_p),
         ("s_rowptr", C.c_void_p), ("s_col", C.c_void_p), ("s_slot", C.c_void_p), ("s_order", C.c_void_p),
+        ("r_order", C.c_void_p),
     ]
 
 
@@ -272,11 +273,11 @@ def etpc_csr_workspace_size(n_nodes: int, n_edges: int) -> int:
 class Graph:
     """Device CSR views (receiver and sender) of one graph."""
 
-    def __init__(self, n_nodes: int, rowptr, col, s_rowptr, s_col, s_slot, eid=None, s_order=None):
+    def __init__(self, n_nodes: int, rowptr, col, s_rowptr, s_col, s_slot, eid=None, s_order=None, r_order=None):
         self.n_nodes = int(n_nodes)
         self.rowptr, self.col, self.eid = rowptr, col, eid
         self.s_rowptr, self.s_col, self.s_slot = s_rowptr, s_col, s_slot
-        self.s_order = s_order
+        self.s_order, self.r_order = s_order, r_order
         self.n_edges = int(col.shape[0])
         g = etpc_graph()
         g.n_nodes, g.n_edges = self.n_nodes, self.n_edges
@@ -286,10 +287,11 @@ class Graph:
         g.s_col = _ptr(s_col, torch.int32) if self.n_edges else None
         g.s_slot = _ptr(s_slot, torch.int32) if self.n_edges else None
         g.s_order = _ptr(s_order, torch.int32) if s_order is not None and self.n_nodes else None
+        g.r_order = _ptr(r_order, torch.int32) if r_order is not None and self.n_nodes else None
         self.c = g
 
     def without_order(self) -> "Graph":
-        """The same views with s_order unset (senders dispatched in index order)."""
+        """The same views with s_order and r_order unset (nodes dispatched in index order)."""
         return Graph(self.n_nodes, self.rowptr, self.col, self.s_rowptr, self.s_col, self.s_slot, eid=self.eid)
 
 
@@ -305,8 +307,8 @@ def _workspace(nbytes: int, device) -> Tuple[Optional[torch.Tensor], int]:
 
 
 def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=None, order: bool = True) -> Graph:
-    """Both CSR views of the COO list; with `order`, also the sender dispatch order
-    (etpc_degree_order of s_rowptr)."""
+    """Both CSR views of the COO list; with `order`, also the sender and receiver
+    dispatch orders (etpc_degree_order of s_rowptr and rowptr)."""
     dev = src.device
     e = int(src.shape[0])
     rowptr, s_rowptr = _empty_i32(n_nodes + 1, dev), _empty_i32(n_nodes + 1, dev)
@@ -317,7 +319,8 @@ def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=No
                               _ptr(s_col, torch.int32), _ptr(s_slot, torch.int32),
                               None if ws is None else ws.data_ptr(), nb, _stream(stream)))
     s_order = etpc_degree_order(s_rowptr, stream=stream) if order else None
-    return Graph(n_nodes, rowptr, col, s_rowptr, s_col, s_slot, eid=eid, s_order=s_order)
+    r_order = etpc_degree_order(rowptr, stream=stream) if order else None
+    return Graph(n_nodes, rowptr, col, s_rowptr, s_col, s_slot, eid=eid, s_order=s_order, r_order=r_order)
 
 
 def etpc_degree_order_workspace_size(n_nodes: int) -> int:

@@ -428,6 +428,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.x = xin;
         a.S = L.S[set];
         a.recv0 = static_cast<int32_t>(r0);
+        a.order = (g->r_order != nullptr && r0 == 0 && nrecv == g->n_nodes) ? g->r_order : nullptr;
         a.x_dim = static_cast<int32_t>(p->x_dim);
         a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
         int ntiles = 1;

@@ -305,20 +305,20 @@ __global__ void validate_slots_kernel(const etpc_graph g) {
 }
 
 // sender rows: strictly increasing slots in range
-// s_order: every entry in range and each adjacent pair in (decreasing degree, increasing
+// order: every entry in range and each adjacent pair in (decreasing degree, increasing
 // index) order; a strictly ordered sequence of N values in [0, N) is a permutation
-__global__ void validate_order_kernel(const etpc_graph g) {
+__global__ void validate_order_kernel(const int32_t* __restrict__ order, const int32_t* __restrict__ rp, int n) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= g.n_nodes) return;
-  const int v = g.s_order[k];
-  if (v < 0 || v >= g.n_nodes) {
+  if (k >= n) return;
+  const int v = order[k];
+  if (v < 0 || v >= n) {
     atomicMax(&g_graph_error, 7);
     return;
   }
-  if (k + 1 < g.n_nodes) {
-    const int u = g.s_order[k + 1];
-    if (u < 0 || u >= g.n_nodes) return;   // reported by thread k + 1
-    const int dv = g.s_rowptr[v + 1] - g.s_rowptr[v], du = g.s_rowptr[u + 1] - g.s_rowptr[u];
+  if (k + 1 < n) {
+    const int u = order[k + 1];
+    if (u < 0 || u >= n) return;   // reported by thread k + 1
+    const int dv = rp[v + 1] - rp[v], du = rp[u + 1] - rp[u];
     if (!(dv > du || (dv == du && v < u))) atomicMax(&g_graph_error, 7);
   }
 }
@@ -404,7 +404,9 @@ etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s) {
     hipLaunchKernelGGL(validate_sender_rows_kernel, dim3(blocks), dim3(threads), 0, s, g);
     hipLaunchKernelGGL(validate_slots_kernel, dim3(blocks), dim3(threads), 0, s, g);
     if (g.s_order != nullptr && g.n_nodes > 0)
-      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g);
+      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g.s_order, g.s_rowptr, g.n_nodes);
+    if (g.r_order != nullptr && g.n_nodes > 0)
+      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g.r_order, g.rowptr, g.n_nodes);
     ETPC_HIP(hipGetLastError());
     ETPC_HIP(hipMemcpyFromSymbolAsync(&err, HIP_SYMBOL(g_graph_error), sizeof(int), 0, hipMemcpyDeviceToHost, s));
     ETPC_HIP(hipStreamSynchronize(s));
@@ -416,7 +418,7 @@ etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s) {
                                "self loop (sender == receiver)",
                                "sender view does not hold a receiver slot (or s_col mismatch)",
                                "sender row slots out of range or not strictly increasing",
-                               "s_order is not the decreasing-degree order of s_rowptr"};
+                               "s_order or r_order is not the decreasing-degree order of its row pointers"};
   if (err != 0) ETPC_FAIL(ETPC_ERR_GRAPH, what[err]);
   return ETPC_OK;
 }

@@ -113,12 +113,13 @@ typedef struct {
  * rowptr[N+1], col[E] = sender of each receiver slot;
  * s_rowptr[N+1], s_col[E] = receiver of each sender slot, s_slot[E] = the receiver slot.
  * s_order[N] (optional, NULL = index order): the senders by decreasing out-degree, ties
- * in index order, as etpc_degree_order writes it for s_rowptr.  The uvw sender
- * traversals then start the longest senders first, which shortens the tail of each
- * launch; results are bit-identical either way.
+ * in index order, as etpc_degree_order writes it for s_rowptr; r_order[N] (optional)
+ * likewise the receivers for rowptr.  The uvw sender and receiver traversals then start
+ * the longest rows first, which shortens the tail of each launch; results are
+ * bit-identical either way.
  * Preconditions (checked only by etpc_graph_validate): indices in range, both views
- * describe the same edge multiset, no self loops, |r_e| > 0 on every edge, s_order (when
- * given) equal to etpc_degree_order of s_rowptr. */
+ * describe the same edge multiset, no self loops, |r_e| > 0 on every edge, s_order and
+ * r_order (when given) equal to etpc_degree_order of s_rowptr and rowptr. */
 typedef struct {
   int32_t n_nodes;
   int64_t n_edges;
@@ -128,6 +129,7 @@ typedef struct {
   const int32_t* s_col;
   const int32_t* s_slot;
   const int32_t* s_order;
+  const int32_t* r_order;
 } etpc_graph;
 
 /* Planner (host only).  Parses the spec, enumerates the valid paths (selection

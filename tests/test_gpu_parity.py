@@ -182,20 +182,23 @@ def test_double_backward_all_cotangents(name, n):
 
 
 @pytest.mark.parametrize("n", [256, None])
-def test_sender_order_is_bit_identical(n):
-    """Dispatching senders in decreasing degree (the graph's s_order) changes only which
-    workgroup takes which sender: backward and double backward are bit-identical to the
-    index-order dispatch (the small graph takes the edge-split launches, the full one the
-    plain ones)."""
+def test_dispatch_order_is_bit_identical(n):
+    """Dispatching nodes in decreasing degree (the graph's s_order and r_order) changes only
+    which workgroup takes which node: forward, backward and double backward are
+    bit-identical to the index-order dispatch (the small graph takes the edge-split
+    launches, the full one the plain ones)."""
     etpc = _etpc()
     cfg = CONFIGS["cfg2"] if n is None else small_variant("cfg2", n)
     c = make_case(cfg)
-    assert c.graph.s_order is not None
+    assert c.graph.s_order is not None and c.graph.r_order is not None
     g0 = c.graph.without_order()
-    note(f"sender order {cfg.name}")
+    note(f"dispatch order {cfg.name}")
+    za = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w)
+    zb = etpc.etpc_forward(c.plan, g0, c.x, c.pos, c.w)
     a = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar)
     b = etpc.etpc_backward(c.plan, g0, c.x, c.pos, c.w, c.z_bar)
     torch.cuda.synchronize()
+    assert torch.equal(za, zb)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
     if n is not None:

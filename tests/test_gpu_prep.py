@@ -215,7 +215,8 @@ def test_degree_order_matches_oracle(n, e):
     torch.cuda.synchronize()
     ref = ocsr.csr_build(n, src, dst)
     assert np.array_equal(g.s_order.cpu().numpy(), ocsr.degree_order(ref["s_rowptr"]))
-    assert np.array_equal(r_order.cpu().numpy(), ocsr.degree_order(ref["rowptr"]))
+    assert np.array_equal(g.r_order.cpu().numpy(), ocsr.degree_order(ref["rowptr"]))
+    assert torch.equal(r_order, g.r_order)
     etpc.etpc_graph_validate(g)
     if n > 1:
         bad = g.s_order.clone()
@@ -227,3 +228,8 @@ def test_degree_order_matches_oracle(n, e):
         bad[1] = n
         with pytest.raises(etpc.EtpcError):
             etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot, s_order=bad))
+        if not torch.equal(g.r_order, g.s_order):
+            # each order is checked against its own view
+            with pytest.raises(etpc.EtpcError):
+                etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot,
+                                                    s_order=g.s_order, r_order=g.s_order))
