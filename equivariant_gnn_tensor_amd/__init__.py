@@ -11,5 +11,5 @@ from ._binding import (  # noqa: F401
     etpc_graph_validate, etpc_plan_cg, etpc_plan_info, etpc_plan_out_irrep, etpc_plan_path,
     etpc_get_lanes, etpc_profile_enable, etpc_profile_read, etpc_set_lanes, etpc_workspace_size, lib, parse_irreps,
     etpc_layout_convert, etpc_radius_graph, etpc_radius_graph_workspace_size,
-    etpc_degree_order, etpc_degree_order_workspace_size,
+    etpc_degree_order, etpc_degree_order_workspace_size, RECV_ORDER_WINDOW, SEND_ORDER_WINDOW,
 )

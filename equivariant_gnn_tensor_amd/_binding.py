@@ -28,6 +28,7 @@ ERR_CAPACITY = 8
 TO_IR_MUL, TO_MUL_IR = 0, 1
 FEATURES_IN, FEATURES_OUT = 0, 1
 GEMM_FP32, GEMM_BF16, GEMM_FP16 = 0, 1, 2
+SEND_ORDER_WINDOW, RECV_ORDER_WINDOW = 4096, 512   # ETPC_SEND_ORDER_WINDOW, ETPC_RECV_ORDER_WINDOW
 
 
 class EtpcError(RuntimeError):
@@ -94,7 +95,7 @@ def _load():
         "etpc_csr_build": [i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_graph_validate": [P(etpc_graph), vp],
         "etpc_degree_order_workspace_size": [i32, P(sz)],
-        "etpc_degree_order": [i32, vp, vp, vp, sz, vp],
+        "etpc_degree_order": [i32, vp, i32, vp, vp, sz, vp],
         "etpc_forward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, sz, vp],
         "etpc_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_double_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -318,8 +319,8 @@ def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=No
                               _ptr(col, torch.int32), _ptr(eid, torch.int32), _ptr(s_rowptr, torch.int32),
                               _ptr(s_col, torch.int32), _ptr(s_slot, torch.int32),
                               None if ws is None else ws.data_ptr(), nb, _stream(stream)))
-    s_order = etpc_degree_order(s_rowptr, stream=stream) if order else None
-    r_order = etpc_degree_order(rowptr, stream=stream) if order else None
+    s_order = etpc_degree_order(s_rowptr, window=SEND_ORDER_WINDOW, stream=stream) if order else None
+    r_order = etpc_degree_order(rowptr, window=RECV_ORDER_WINDOW, stream=stream) if order else None
     return Graph(n_nodes, rowptr, col, s_rowptr, s_col, s_slot, eid=eid, s_order=s_order, r_order=r_order)
 
 
@@ -329,12 +330,13 @@ def etpc_degree_order_workspace_size(n_nodes: int) -> int:
     return b.value
 
 
-def etpc_degree_order(rowptr: torch.Tensor, stream=None) -> torch.Tensor:
-    """Nodes by decreasing row length rowptr[v+1] - rowptr[v], ties by index (int32 [N])."""
+def etpc_degree_order(rowptr: torch.Tensor, window: int = 0, stream=None) -> torch.Tensor:
+    """Nodes by decreasing row length rowptr[v+1] - rowptr[v], ties by index (int32 [N]);
+    with window > 0, within each aligned window of that many nodes."""
     n = int(rowptr.shape[0]) - 1
     order = _empty_i32(n, rowptr.device)
     ws, nb = _workspace(etpc_degree_order_workspace_size(n), rowptr.device)
-    _check(lib.etpc_degree_order(n, _ptr(rowptr, torch.int32), _ptr(order, torch.int32) if n > 0 else None,
+    _check(lib.etpc_degree_order(n, _ptr(rowptr, torch.int32), window, _ptr(order, torch.int32) if n > 0 else None,
                                  None if ws is None else ws.data_ptr(), nb, _stream(stream)))
     return order
 

@@ -242,6 +242,13 @@ __global__ void degree_key_kernel(const int32_t* __restrict__ rowptr, int32_t n,
   val[v] = v;
 }
 
+// second key: the window of the node each entry now holds
+__global__ void window_key_kernel(const int32_t* __restrict__ val, int32_t n, int32_t window,
+                                  int32_t* __restrict__ key) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n) key[t] = val[t] / window;
+}
+
 }  // namespace
 
 size_t degree_order_bytes(int32_t n) {
@@ -249,7 +256,8 @@ size_t degree_order_bytes(int32_t n) {
   return sizeof(int32_t) * (4 * a + sort_scratch_ints(n));
 }
 
-etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t* order, void* ws, hipStream_t s) {
+etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t window, int32_t* order, void* ws,
+                              hipStream_t s) {
   if (n == 0) return ETPC_OK;
   const size_t a = (static_cast<size_t>(n) + 63) & ~size_t(63);
   int32_t* base = static_cast<int32_t*>(ws);
@@ -257,6 +265,12 @@ etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t* order, 
   hipLaunchKernelGGL(degree_key_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, rowptr, n, b.k0, b.v0);
   // a stable LSD sort over all four key bytes: ties keep increasing node index
   ETPC_HIP(radix_sort(b, n, 4, s));
+  if (window > 0 && window < n) {
+    // then stably by window (radix sort keys must be non-negative: v / window is):
+    // window-major, heaviest first inside each window
+    hipLaunchKernelGGL(window_key_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, b.v0, n, window, b.k0);
+    ETPC_HIP(radix_sort(b, n, radix_passes((n + window - 1) / window), s));
+  }
   ETPC_HIP(launch_copy(b.v0, order, n, s));
   return ETPC_OK;
 }
@@ -305,17 +319,20 @@ __global__ void validate_slots_kernel(const etpc_graph g) {
 }
 
 // sender rows: strictly increasing slots in range
-// order: every entry in range and each adjacent pair in (decreasing degree, increasing
-// index) order; a strictly ordered sequence of N values in [0, N) is a permutation
-__global__ void validate_order_kernel(const int32_t* __restrict__ order, const int32_t* __restrict__ rp, int n) {
+// order with windows of w nodes: every entry in range and in the
+// window of its position, and each adjacent pair of a window in (decreasing degree,
+// increasing index) order; a window's strictly ordered entries, all from that window
+// and as many as its positions, are a permutation of it
+__global__ void validate_order_kernel(const int32_t* __restrict__ order, const int32_t* __restrict__ rp, int n,
+                                      int w) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= n) return;
   const int v = order[k];
-  if (v < 0 || v >= n) {
+  if (v < 0 || v >= n || v / w != k / w) {
     atomicMax(&g_graph_error, 7);
     return;
   }
-  if (k + 1 < n) {
+  if (k + 1 < n && (k + 1) / w == k / w) {
     const int u = order[k + 1];
     if (u < 0 || u >= n) return;   // reported by thread k + 1
     const int dv = rp[v + 1] - rp[v], du = rp[u + 1] - rp[u];
@@ -404,9 +421,11 @@ etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s) {
     hipLaunchKernelGGL(validate_sender_rows_kernel, dim3(blocks), dim3(threads), 0, s, g);
     hipLaunchKernelGGL(validate_slots_kernel, dim3(blocks), dim3(threads), 0, s, g);
     if (g.s_order != nullptr && g.n_nodes > 0)
-      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g.s_order, g.s_rowptr, g.n_nodes);
+      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g.s_order, g.s_rowptr, g.n_nodes,
+                         static_cast<int>(ETPC_SEND_ORDER_WINDOW));
     if (g.r_order != nullptr && g.n_nodes > 0)
-      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g.r_order, g.rowptr, g.n_nodes);
+      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g.r_order, g.rowptr, g.n_nodes,
+                         static_cast<int>(ETPC_RECV_ORDER_WINDOW));
     ETPC_HIP(hipGetLastError());
     ETPC_HIP(hipMemcpyFromSymbolAsync(&err, HIP_SYMBOL(g_graph_error), sizeof(int), 0, hipMemcpyDeviceToHost, s));
     ETPC_HIP(hipStreamSynchronize(s));

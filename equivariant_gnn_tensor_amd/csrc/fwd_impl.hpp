@@ -100,10 +100,11 @@ __global__ __launch_bounds__(SPLIT ? 256 : 64) void fwd_uvw_kernel(const FwdUvwA
   const int lane = threadIdx.x & 63;
   const int part = SPLIT ? threadIdx.x >> 6 : 0;   // the wave's share of the receiver's edges
   const int nparts = SPLIT ? a.nparts : 1;
-  // receivers by decreasing degree when an order is given (the launch then ends on short
-  // rows; a receiver's S row does not depend on which workgroup takes it), else the
-  // XCD-aware mapping of contiguous receiver ranges
-  const int bx = a.order ? a.order[blockIdx.x] - a.recv0 : node_block(blockIdx.x, gridDim.x);
+  // XCD-aware mapping of contiguous receiver ranges; with an order (heaviest first within
+  // small aligned windows) each XCD still sweeps its own range, but every window ends on
+  // short rows.  A receiver's S row does not depend on which workgroup takes it.
+  const int nb = node_block(blockIdx.x, gridDim.x);
+  const int bx = a.order ? a.order[nb] - a.recv0 : nb;
   const int i = a.recv0 + bx;
   const int cp = a.cp;
   const int nslots = kWave / cp;

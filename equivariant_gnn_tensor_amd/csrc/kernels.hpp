@@ -17,7 +17,7 @@ struct FwdUvwArgs {
   const float* pos_dot;   // tangent only
   const float* x;
   float* S;
-  const int32_t* order;   // workgroup b takes receiver order[b] (whole-graph launches), or null
+  const int32_t* order;   // node slot b takes receiver order[b] (whole-graph launches), or null
   int32_t recv0;          // first receiver of this chunk
   int32_t x_dim, xoff, c_in, cp;
   int32_t ls;

@@ -113,13 +113,20 @@ typedef struct {
  * rowptr[N+1], col[E] = sender of each receiver slot;
  * s_rowptr[N+1], s_col[E] = receiver of each sender slot, s_slot[E] = the receiver slot.
  * s_order[N] (optional, NULL = index order): the senders by decreasing out-degree, ties
- * in index order, as etpc_degree_order writes it for s_rowptr; r_order[N] (optional)
- * likewise the receivers for rowptr.  The uvw sender and receiver traversals then start
- * the longest rows first, which shortens the tail of each launch; results are
- * bit-identical either way.
+ * in index order, within aligned windows of ETPC_SEND_ORDER_WINDOW senders:
+ * etpc_degree_order(s_rowptr, ETPC_SEND_ORDER_WINDOW).  r_order[N] (optional): likewise
+ * the receivers by in-degree within windows of ETPC_RECV_ORDER_WINDOW:
+ * etpc_degree_order(rowptr, ETPC_RECV_ORDER_WINDOW).  The uvw traversals then start the
+ * longest rows first, which shortens the tail of each launch.  The orders stay
+ * window-local so that nodes numbered close together (cells of a batch, a
+ * space-filling-curve numbering) still run close together in time and share cache; the
+ * sender window is about the number of waves resident on the chip at once, the receiver
+ * window a fraction of one XCD's share (the receiver traversals also give each XCD a
+ * contiguous range of node slots).  Results are bit-identical either way.
  * Preconditions (checked only by etpc_graph_validate): indices in range, both views
  * describe the same edge multiset, no self loops, |r_e| > 0 on every edge, s_order and
- * r_order (when given) equal to etpc_degree_order of s_rowptr and rowptr. */
+ * r_order (when given) equal to the etpc_degree_order results named above. */
+enum { ETPC_SEND_ORDER_WINDOW = 4096, ETPC_RECV_ORDER_WINDOW = 512 };
 typedef struct {
   int32_t n_nodes;
   int64_t n_edges;
@@ -169,17 +176,19 @@ etpc_status etpc_csr_build(int32_t n_nodes, int64_t n_edges, const int32_t* src,
                            int32_t* rowptr, int32_t* col, int32_t* eid,
                            int32_t* s_rowptr, int32_t* s_col, int32_t* s_slot,
                            void* ws, size_t ws_bytes, hipStream_t stream);
-/* Node dispatch order: order[k] = the node with the k-th largest row length
- * rowptr[v+1] - rowptr[v], ties in increasing node index (a stable sort by decreasing
- * degree).  For s_rowptr this is the graph's s_order.  The sender traversals own a node's
- * whole adjoint (Sec. 4, source-contiguous traversal), so their per-workgroup work is
- * the node's degree; running the heavy nodes first is the longest-first rule of list
- * scheduling.  rowptr [device] int32 [N+1] (non-decreasing); order [device] int32 [N]
- * out.  Bit-exact and deterministic.  Workspace from etpc_degree_order_workspace_size;
- * ETPC_ERR_INVALID_ARG for N < 0, null pointers with N > 0, or a workspace too small. */
+/* Node dispatch order.  window = 0: order[k] = the node with the k-th largest row
+ * length rowptr[v+1] - rowptr[v], ties in increasing node index (a stable sort by
+ * decreasing degree).  window > 0: the same within each aligned window of `window`
+ * nodes: positions [k w, (k+1) w) hold the nodes [k w, (k+1) w), heaviest first.  The
+ * traversals own whole CSR rows (Sec. 4: receiver rows forward, source-contiguous rows
+ * backward), so a workgroup's work is its node's degree; starting the heavy nodes first is
+ * the longest-first rule of list scheduling.  rowptr [device] int32 [N+1]
+ * (non-decreasing); order [device] int32 [N] out.  Bit-exact and deterministic.
+ * Workspace from etpc_degree_order_workspace_size; ETPC_ERR_INVALID_ARG for N < 0,
+ * window < 0, null pointers with N > 0, or a workspace too small. */
 etpc_status etpc_degree_order_workspace_size(int32_t n_nodes, size_t* bytes);
-etpc_status etpc_degree_order(int32_t n_nodes, const int32_t* rowptr, int32_t* order, void* ws, size_t ws_bytes,
-                              hipStream_t stream);
+etpc_status etpc_degree_order(int32_t n_nodes, const int32_t* rowptr, int32_t window, int32_t* order, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 /* Debug check of the graph preconditions; synchronizes the stream.  Needs no workspace. */
 etpc_status etpc_graph_validate(const etpc_graph* graph, hipStream_t stream);
 

@@ -9,8 +9,8 @@ receiver view: edges sorted by receiver, ties by original COO index;
 sender view: receiver-view slots sorted by sender, ties by slot;
   s_rowptr[N+1], s_col = receiver of each sender slot, s_slot = receiver slot.
 degree order: the nodes by decreasing row length of a CSR view, ties by increasing
-  index (the dispatch order of the source-major traversal; no arithmetic, a stable
-  sort of the degrees).
+  index, over all nodes or inside aligned windows (the dispatch order of the
+  traversals; no arithmetic, a stable sort of the degrees).
 
 Pinned by tests/test_oracle_csr.py against a brute-force construction.
 """
@@ -35,7 +35,13 @@ def csr_build(n_nodes: int, src, dst):
                 s_rowptr=i32(s_rowptr), s_col=i32(s_col), s_slot=i32(sperm))
 
 
-def degree_order(rowptr):
-    """Nodes by decreasing rowptr[v+1] - rowptr[v], ties by increasing v."""
+def degree_order(rowptr, window: int = 0):
+    """Nodes by decreasing rowptr[v+1] - rowptr[v], ties by increasing v; with
+    window > 0, the same inside each aligned window of `window` nodes."""
     deg = np.diff(np.asarray(rowptr, np.int64))
-    return np.argsort(-deg, kind="stable").astype(np.int32)
+    if window <= 0:
+        return np.argsort(-deg, kind="stable").astype(np.int32)
+    out = []
+    for w0 in range(0, deg.size, window):
+        out.append(w0 + np.argsort(-deg[w0:w0 + window], kind="stable"))
+    return np.concatenate(out).astype(np.int32) if out else np.zeros(0, np.int32)

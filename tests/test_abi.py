@@ -176,11 +176,11 @@ def test_degree_order_argument_errors():
     with pytest.raises(etpc.EtpcError):
         etpc.etpc_degree_order_workspace_size(-1)
     lib = _binding.lib
-    assert lib.etpc_degree_order(0, None, None, None, 0, None) == 0      # empty: nothing to do
-    st = lib.etpc_degree_order(-1, None, None, None, 0, None)
-    assert st != 0
-    st = lib.etpc_degree_order(8, None, None, None, 0, None)              # null arrays
-    assert st != 0
+    assert lib.etpc_degree_order(0, None, 0, None, None, 0, None) == 0      # empty: nothing to do
+    assert lib.etpc_degree_order(-1, None, 0, None, None, 0, None) != 0
+    assert lib.etpc_degree_order(8, None, 0, None, None, 0, None) != 0      # null arrays
+    assert lib.etpc_degree_order(8, 16, -1, 16, 16, 1 << 20, None) != 0    # negative window
+    assert "window" in etpc.lib.etpc_last_error().decode().lower()
     # a workspace too small is refused before anything is launched
-    st = lib.etpc_degree_order(8, 16, 16, 16, 8, None)
+    st = lib.etpc_degree_order(8, 16, 0, 16, 16, 8, None)
     assert st != 0 and "workspace" in etpc.lib.etpc_last_error().decode().lower()

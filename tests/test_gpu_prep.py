@@ -9,8 +9,9 @@ the cutoff, far-apart clusters (the cell grid is widened to its cap), one and tw
 rows longer than one wavefront (the global-sort path), and the capacity error.  At 65,536 atoms the oracle checks sampled receivers' rows, and
 the whole list is checked for order, symmetry and validity.
 
-Degree order: the sender dispatch order (decreasing degree, ties by index) equals the
-oracle's stable sort bit for bit; etpc_graph_validate accepts it and rejects a wrong one.
+Degree order: the dispatch orders (decreasing degree, ties by index; over all nodes or
+in aligned windows) equal the oracle's stable sorts bit for bit; etpc_graph_validate
+accepts the graph's orders and rejects wrong ones.
 
 Layout: mul_ir <-> ir_mul of the workloads' input and output irreps, ragged row counts,
 round trips.
@@ -211,12 +212,15 @@ def test_degree_order_matches_oracle(n, e):
     src, dst = src[keep], dst[keep]
     note(f"degree order N={n} E={src.size}")
     g = etpc.etpc_csr_build(n, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
-    r_order = etpc.etpc_degree_order(g.rowptr)
+    r_all = etpc.etpc_degree_order(g.rowptr)
+    s_win = {w: etpc.etpc_degree_order(g.s_rowptr, window=w) for w in (1, 3, 512, 70000, 10 ** 6)}
     torch.cuda.synchronize()
     ref = ocsr.csr_build(n, src, dst)
-    assert np.array_equal(g.s_order.cpu().numpy(), ocsr.degree_order(ref["s_rowptr"]))
-    assert np.array_equal(g.r_order.cpu().numpy(), ocsr.degree_order(ref["rowptr"]))
-    assert torch.equal(r_order, g.r_order)
+    assert np.array_equal(g.s_order.cpu().numpy(), ocsr.degree_order(ref["s_rowptr"], window=etpc.SEND_ORDER_WINDOW))
+    assert np.array_equal(g.r_order.cpu().numpy(), ocsr.degree_order(ref["rowptr"], window=etpc.RECV_ORDER_WINDOW))
+    assert np.array_equal(r_all.cpu().numpy(), ocsr.degree_order(ref["rowptr"]))
+    for w, o in s_win.items():
+        assert np.array_equal(o.cpu().numpy(), ocsr.degree_order(ref["s_rowptr"], window=w)), w
     etpc.etpc_graph_validate(g)
     if n > 1:
         bad = g.s_order.clone()
@@ -228,8 +232,13 @@ def test_degree_order_matches_oracle(n, e):
         bad[1] = n
         with pytest.raises(etpc.EtpcError):
             etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot, s_order=bad))
-        if not torch.equal(g.r_order, g.s_order):
-            # each order is checked against its own view
+        if n > etpc.RECV_ORDER_WINDOW and not torch.equal(r_all, g.r_order):
+            # the receiver order is the windowed one
             with pytest.raises(etpc.EtpcError):
                 etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot,
-                                                    s_order=g.s_order, r_order=g.s_order))
+                                                    s_order=g.s_order, r_order=r_all))
+        s_all = s_win[10 ** 6]
+        if n > etpc.SEND_ORDER_WINDOW and not torch.equal(s_all, g.s_order):
+            with pytest.raises(etpc.EtpcError):
+                etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot,
+                                                    s_order=s_all, r_order=g.r_order))

@@ -60,4 +60,18 @@ def test_degree_order_brute_force(rng):
             want.append(best)
             left.remove(best)
         assert list(degree_order(g["s_rowptr"])) == want
+        for w in (1, 4, 7, n, n + 3):
+            # each aligned window alone: the same selection restricted to its nodes
+            want_w = []
+            for w0 in range(0, n, w):
+                left = list(range(w0, min(n, w0 + w)))
+                while left:
+                    best = left[0]
+                    for v in left[1:]:
+                        if deg[v] > deg[best]:
+                            best = v
+                    want_w.append(best)
+                    left.remove(best)
+            assert list(degree_order(g["s_rowptr"], window=w)) == want_w
     assert list(degree_order(np.array([0, 2, 4, 4, 7]))) == [3, 0, 1, 2]
+    assert list(degree_order(np.array([0, 2, 4, 4, 7]), window=2)) == [0, 1, 3, 2]
