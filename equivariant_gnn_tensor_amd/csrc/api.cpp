@@ -488,6 +488,7 @@ etpc_status fwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
     a.x = xin;
     a.w = win + pi.w_off;
     a.z = z;
+    a.order = g->r_order;
     a.x_dim = static_cast<int32_t>(p->x_dim);
     a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
     a.z_dim = static_cast<int32_t>(p->z_dim);

@@ -232,7 +232,9 @@ __global__ __launch_bounds__(64) void fwd_uvu_kernel(const FwdUvuArgs a) {
   __shared__ float s_edge[64 * L::kStride];
   __shared__ int s_j[64];
   const int lane = threadIdx.x;
-  const int i = node_block(blockIdx.x, gridDim.x);
+  // XCD-aware slots, then the receiver order within small windows (as in the uvw traversal)
+  const int nb = node_block(blockIdx.x, gridDim.x);
+  const int i = a.order ? a.order[nb] : nb;
   const int cp = a.cp;
   const int nslots = kWave / cp;
   const int slot = lane / cp;

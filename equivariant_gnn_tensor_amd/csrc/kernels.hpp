@@ -40,6 +40,7 @@ struct FwdUvuArgs {
   const float* x;
   const float* w;         // path block [B][C]
   float* z;
+  const int32_t* order;   // node slot b takes receiver order[b], or null
   int32_t x_dim, xoff, z_dim, zoff, c, cp;
   int32_t ls;
   int32_t accumulate;

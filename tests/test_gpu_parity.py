@@ -181,14 +181,14 @@ def test_double_backward_all_cotangents(name, n):
     assert max(errs) <= TOL_DBL
 
 
-@pytest.mark.parametrize("n", [256, None])
-def test_dispatch_order_is_bit_identical(n):
+@pytest.mark.parametrize("name,n", [("cfg2", 256), ("cfg2", None), ("cfg3", 128)])
+def test_dispatch_order_is_bit_identical(name, n):
     """Dispatching nodes in decreasing degree (the graph's s_order and r_order) changes only
     which workgroup takes which node: forward, backward and double backward are
     bit-identical to the index-order dispatch (the small graph takes the edge-split
-    launches, the full one the plain ones)."""
+    launches, the full one the plain ones; workload 3 is the channelwise forward)."""
     etpc = _etpc()
-    cfg = CONFIGS["cfg2"] if n is None else small_variant("cfg2", n)
+    cfg = CONFIGS[name] if n is None else small_variant(name, n)
     c = make_case(cfg)
     assert c.graph.s_order is not None and c.graph.r_order is not None
     g0 = c.graph.without_order()
@@ -201,7 +201,7 @@ def test_dispatch_order_is_bit_identical(n):
     assert torch.equal(za, zb)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
-    if n is not None:
+    if n is not None and name == "cfg2":
         rng = np.random.default_rng(5)
         kw = dict(x_dot=torch.from_numpy(rng.standard_normal(c.wl.x.shape).astype(np.float32)).cuda(),
                   pos_dot=torch.from_numpy(rng.standard_normal(c.wl.pos.shape).astype(np.float32)).cuda())
