@@ -433,7 +433,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
         a.x_dim = static_cast<int32_t>(p->x_dim);
         a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
         int ntiles = 1;
-        a.cp = lane_width(pi.c_in, &ntiles);
+        a.cp = lane_width(pi.c_in, &ntiles, 4);   // 4-lane matrix-core blocks never mix edges
         a.c_in = pi.c_in;
         a.ls = pi.l_sh;
         a.s_row_stride = D;

@@ -29,6 +29,16 @@ namespace fwd_detail {
 #endif
 constexpr int kPrefetch = ETPC_FWD_PREFETCH;
 
+// The state update S[q][m_out] += phi_q cm[m_out] on the matrix cores (1) or the VALU (0).
+// As 4x4x1 blocks of four lanes: lane 4g + r supplies phi_{4qq+r}, every lane its own
+// cm[m_out], so accumulator register r of a lane holds q = 4qq + r for its channel.
+// Needs edge slots of at least four lanes (the host rounds the channel count up).
+#ifndef ETPC_FWD_MFMA
+#define ETPC_FWD_MFMA 1
+#endif
+constexpr bool kFwdMfma = ETPC_FWD_MFMA != 0;
+typedef float f4v __attribute__((ext_vector_type(4)));
+
 // LDS per edge: phi[NB], (dphi[NB]), cY[NI*NO], (dcY[NI*NO]), padded by one float.
 template <int NB, int CY, bool TANGENT>
 struct EdgeLds {
@@ -113,11 +123,13 @@ __global__ __launch_bounds__(SPLIT ? 256 : 64) void fwd_uvw_kernel(const FwdUvwA
   const int gslot = part * nslots + slot;
   const int u = blockIdx.y * cp + (lane - slot * cp);
   const bool uvalid = u < a.c_in;
-  float acc[NB][NO];
+  const int q4 = lane & 3;
+  // acc[m_out][qq][r] = S[q = 4 qq + r][m_out] of the lane's channel
+  f4v acc[NO][NBQ];
 #pragma unroll
-  for (int q = 0; q < NB; ++q)
+  for (int m = 0; m < NO; ++m)
 #pragma unroll
-    for (int m = 0; m < NO; ++m) acc[q][m] = 0.f;
+    for (int qq = 0; qq < NBQ; ++qq) acc[m][qq] = f4v{0.f, 0.f, 0.f, 0.f};
   const int e0 = a.rowptr[i], e1 = a.rowptr[i + 1];
   for (int base = e0; base < e1; base += kWave) {
     const int ne = min(kWave, e1 - base);
@@ -179,15 +191,32 @@ __global__ __launch_bounds__(SPLIT ? 256 : 64) void fwd_uvw_kernel(const FwdUvwA
         gather(t + kPrefetch * tslots, xq[pf]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-          const float ph = e[L::kPhi + q];
-          if constexpr (TANGENT) {
-            const float phd = e[L::kPhiDot + q];
+        for (int qq = 0; qq < NBQ; ++qq) {
+          if constexpr (kFwdMfma) {
+            const float ph = e[L::kPhi + 4 * qq + q4];
+            const float phd = TANGENT ? e[L::kPhiDot + 4 * qq + q4] : 0.f;
 #pragma unroll
-            for (int mo = 0; mo < NO; ++mo) acc[q][mo] += phd * cm[mo] + ph * cmd[mo];
+            for (int mo = 0; mo < NO; ++mo) {
+              if constexpr (TANGENT) {
+                acc[mo][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(phd, cm[mo], acc[mo][qq], 0, 0, 0);
+                acc[mo][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, cmd[mo], acc[mo][qq], 0, 0, 0);
+              } else {
+                acc[mo][qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(ph, cm[mo], acc[mo][qq], 0, 0, 0);
+              }
+            }
           } else {
 #pragma unroll
-            for (int mo = 0; mo < NO; ++mo) acc[q][mo] += ph * cm[mo];
+            for (int r = 0; r < 4; ++r) {
+              const float ph = e[L::kPhi + 4 * qq + r];
+              if constexpr (TANGENT) {
+                const float phd = e[L::kPhiDot + 4 * qq + r];
+#pragma unroll
+                for (int mo = 0; mo < NO; ++mo) acc[mo][qq][r] += phd * cm[mo] + ph * cmd[mo];
+              } else {
+#pragma unroll
+                for (int mo = 0; mo < NO; ++mo) acc[mo][qq][r] += ph * cm[mo];
+              }
+            }
           }
         }
       }
@@ -196,32 +225,40 @@ __global__ __launch_bounds__(SPLIT ? 256 : 64) void fwd_uvw_kernel(const FwdUvwA
   }
   for (int off = cp; off < kWave; off <<= 1)
 #pragma unroll
-    for (int q = 0; q < NB; ++q)
+    for (int m = 0; m < NO; ++m)
 #pragma unroll
-      for (int m = 0; m < NO; ++m) acc[q][m] += __shfl_xor(acc[q][m], off);
+      for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[m][qq][r] += __shfl_xor(acc[m][qq][r], off);
   for (int pp = 1; pp < nparts; ++pp) {
     // parts 1.. hand their sums to part 0 through LDS, one part at a time (fixed order)
     float* sx = s_part + lane * NB * NO;
     __syncthreads();
     if (part == pp && slot == 0)
 #pragma unroll
-      for (int q = 0; q < NB; ++q)
+      for (int m = 0; m < NO; ++m)
 #pragma unroll
-        for (int m = 0; m < NO; ++m) sx[q * NO + m] = acc[q][m];
+        for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sx[(4 * qq + r) * NO + m] = acc[m][qq][r];
     __syncthreads();
     if (part == 0 && slot == 0)
 #pragma unroll
-      for (int q = 0; q < NB; ++q)
+      for (int m = 0; m < NO; ++m)
 #pragma unroll
-        for (int m = 0; m < NO; ++m) acc[q][m] += sx[q * NO + m];
+        for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[m][qq][r] += sx[(4 * qq + r) * NO + m];
   }
   if (part == 0 && slot == 0 && uvalid) {
     float* srow = a.S + static_cast<int64_t>(bx) * NO * a.s_row_stride + a.s_col0 + u;
 #pragma unroll
-    for (int q = 0; q < NB; ++q)
-      if (q < a.g.nb)
+    for (int qq = 0; qq < NBQ; ++qq)
 #pragma unroll
-        for (int mo = 0; mo < NO; ++mo) srow[mo * a.s_row_stride + q * a.c_in] = acc[q][mo];
+      for (int r = 0; r < 4; ++r)
+        if (4 * qq + r < a.g.nb)
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo) srow[mo * a.s_row_stride + (4 * qq + r) * a.c_in] = acc[mo][qq][r];
   }
 }
 
