@@ -134,14 +134,34 @@ def cpu_baseline(cfg, wl, seconds):
     dt = time.perf_counter() - t0
     return dict(value=done / dt, unit="edges/s", cores=torch.get_num_threads(), kind="oracle",
                 sample=f"float64 materialized forward+backward of {done} randomly chosen edges "
-                       f"({done / wl.n_edges:.1%} of the graph) in {dt:.1f} s")
+                       f"({done / wl.n_edges:.1%} of the graph) in {dt:.1f} s",
+                cpu=_cpu_model(), blas=_blas_name())
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_name():
+    import re
+    import torch
+    m = re.search(r"BLAS_INFO=([^,\s]+)", torch.__config__.show())
+    return m.group(1) if m else "unknown"
 
 
 KERNEL_FAMILIES = (
     ("fwd_traverse", ("fwd_uvw_kernel", "fwd_uvu_kernel")),
     ("bwd_traverse", ("bwd_uvw_kernel", "bwd_uvu_kernel")),
-    ("gemm", ("gemm_f32_kernel",)),
-    ("csr", ("radix_", "scan_", "lower_bound", "validate_", "iota_", "gather_", "copy_kernel")),
+    ("gemm", ("gemm_f32_kernel", "gemm_low_kernel")),
+    ("csr", ("radix_", "scan_", "lower_bound", "validate_", "iota_", "gather_", "copy_kernel", "degree_key_kernel",
+             "window_key_kernel")),
     ("aux", ("fill_kernel", "wprep_kernel", "reduce_wbar_kernel", "segment_sum_kernel", "pos_bar_kernel",
              "splitk_reduce_kernel")),
 )

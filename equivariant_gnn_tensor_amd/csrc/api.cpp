@@ -292,7 +292,7 @@ etpc_status gemm_auto(GemmArgs ga, float* part, int64_t part_cap, int max_splits
     return ETPC_OK;
   }
   int64_t ks = (ga.K + sp - 1) / sp;
-  ks = (ks + 31) / 32 * 32;
+  ks = (ks + kGemmBK - 1) / kGemmBK * kGemmBK;
   sp = static_cast<int>((ga.K + ks - 1) / ks);
   float* C = ga.C;
   const RowMap cmap = ga.cmap;
@@ -551,7 +551,7 @@ hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float*
   const int64_t K = static_cast<int64_t>(nsend) * ni;
   const int sp = pick_splits(c_in, ncols, K);
   int64_t ks = (K + sp - 1) / sp;
-  ks = (ks + 31) / 32 * 32;
+  ks = (ks + kGemmBK - 1) / kGemmBK * kGemmBK;
   GemmArgs ga{};
   ga.lowp = p->gemm_precision;
   ga.A = xa + j0 * p->x_dim + p->xoff[k];

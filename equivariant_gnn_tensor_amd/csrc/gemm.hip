@@ -24,12 +24,17 @@ __device__ inline int64_t rowoff(const RowMap& m, int r) {
   return static_cast<int64_t>(q) * m.s1 + static_cast<int64_t>(r - q * m.div) * m.s2;
 }
 
-// A(m, k) and B(k, n) tiles: each of the 256 threads moves 8 elements of A and 8 of B
-// per K slice, as two groups of 4 consecutive elements (float4 when aligned).
+// A(m, k) and B(k, n) tiles: each of the 256 threads moves KB / 4 elements of A and of B
+// per K slice, in groups of 4 consecutive elements (float4 when aligned).
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
-  constexpr int BM = 64, BN = 64;
-  __shared__ float As[BK][BM + 4];
-  __shared__ float Bs[BK][BN + 4];
+  constexpr int BM = 64, BN = 64, KB = kGemmBK;
+  static_assert(KB == 32 || KB == 64, "K slice of 32 or 64");
+  constexpr int TPR = KB / 4;          // threads per A row (K-contiguous A), 4 k each
+  constexpr int RP = 256 / TPR;        // A rows per pass
+  constexpr int HA = BM / RP;          // passes (groups of 4) per thread, K-contiguous A
+  constexpr int HK = KB / 16;          // passes per thread for k-major tiles (16 k rows each)
+  __shared__ float As[KB][BM + 4];
+  __shared__ float Bs[KB][BN + 4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid & 1, wn = wid >> 1;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
@@ -37,23 +42,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
   const int kz1 = min(a.K, kz0 + a.k_split);
   float* C = a.C + static_cast<int64_t>(blockIdx.z) * a.c_split_stride;
 
-  // K-contiguous A: rows a_row and a_row + 32, k offset a_k4 (4 consecutive k)
-  const int a_row = tid >> 3, a_k4 = (tid & 7) * 4;
-  // k-major tiles: k rows t_k and t_k + 16, 4 consecutive columns at t_c4
+  // K-contiguous A: rows a_row + RP h, k offset a_k4 (4 consecutive k; TPR threads span
+  // the slice, so a row's slice is one contiguous KB * 4-byte segment)
+  const int a_row = tid / TPR, a_k4 = (tid % TPR) * 4;
+  // k-major tiles: k rows t_k + 16 h, 4 consecutive columns at t_c4
   const int t_k = tid >> 4, t_c4 = (tid & 15) * 4;
-  int64_t a_off[2] = {0, 0};
-  bool a_ok[2] = {false, false};
+  constexpr int HAM = HA > HK ? HA : HK;
+  int64_t a_off[HAM];
+  bool a_ok[HAM];
+#pragma unroll
+  for (int h = 0; h < HAM; ++h) {
+    a_off[h] = 0;
+    a_ok[h] = false;
+  }
   if (!a.a_mcontig) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int m = m0 + a_row + 32 * h;
+    for (int h = 0; h < HA; ++h) {
+      const int m = m0 + a_row + RP * h;
       a_ok[h] = m < a.M;
       if (a_ok[h]) a_off[h] = rowoff(a.amap, m);
     }
   }
   const bool vec = a.vec4 != 0;
 
-  float ra[8], rb[8];
+  float ra[4 * HAM], rb[4 * HK];
   auto load4 = [&](const float* p, bool full, int valid, float* dst) {
     if (full && vec) {
       const float4 v = *reinterpret_cast<const float4*>(p);
@@ -69,14 +81,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
   auto load = [&](int k0) {
     if (!a.a_mcontig) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < HA; ++h) {
         const int k = k0 + a_k4;
         const int valid = a_ok[h] ? min(4, kz1 - k) : 0;
         load4(a.A + a_off[h] + k, valid == 4, valid, ra + 4 * h);
       }
     } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < HK; ++h) {
         const int k = k0 + t_k + 16 * h;
         const int m = m0 + t_c4;
         const int valid = k < kz1 ? min(4, a.M - m) : 0;
@@ -84,7 +96,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
       }
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < HK; ++h) {
       const int k = k0 + t_k + 16 * h;
       const int n = n0 + t_c4;
       const int valid = k < kz1 ? min(4, a.N - n) : 0;
@@ -94,17 +106,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
   auto store = [&]() {
     if (!a.a_mcontig) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < HA; ++h)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) As[a_k4 + t][a_row + 32 * h] = ra[4 * h + t];
+        for (int t = 0; t < 4; ++t) As[a_k4 + t][a_row + RP * h] = ra[4 * h + t];
     } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < HK; ++h)
 #pragma unroll
         for (int t = 0; t < 4; ++t) As[t_k + 16 * h][t_c4 + t] = ra[4 * h + t];
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < HK; ++h)
 #pragma unroll
       for (int t = 0; t < 4; ++t) Bs[t_k + 16 * h][t_c4 + t] = rb[4 * h + t];
   };
@@ -114,12 +126,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   if (kz0 < kz1) load(kz0);
   const int am = wm * 32 + (lane & 31), bn = wn * 32 + (lane & 31), kh = lane >> 5;
-  for (int k0 = kz0; k0 < kz1; k0 += BK) {
+  for (int k0 = kz0; k0 < kz1; k0 += KB) {
     store();
     __syncthreads();
-    if (k0 + BK < kz1) load(k0 + BK);
+    if (k0 + KB < kz1) load(k0 + KB);
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2)
+    for (int kk = 0; kk < KB; kk += 2)
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + kh][am], Bs[kk + kh][bn], acc, 0, 0, 0);
     __syncthreads();
   }

@@ -110,6 +110,13 @@ hipError_t launch_bwd_uvu(const BwdUvuArgs& a, bool tangent, bool hess, int li, 
                           hipStream_t s);
 
 // ---------------------------------------------------------------- dense fp32 GEMM on MFMA
+// K slice of the 64 x 64 fp32 GEMM tiles (32 or 64; 64 measured 12-16% slower on the
+// channel and node GEMMs: more LDS and registers per workgroup, fewer workgroups per
+// CU); split-K ranges are multiples of it.
+#ifndef ETPC_GEMM_BK
+#define ETPC_GEMM_BK 32
+#endif
+constexpr int kGemmBK = ETPC_GEMM_BK;
 // C(m, n) (+)= sum_k A(m, k) B(k, n)
 //   a_mcontig = 0: A(m, k) = A[amap(m) + k];  1: A(m, k) = A[amap(k) + m]
 //   B(k, n) = B[k * ldb + n];  C(m, n) = C[cmap(m) + n]
