@@ -82,6 +82,52 @@ def flop_model(plan, n_nodes, n_edges, radial_b, force_step=False):
     return {key: 2.0 * v for key, v in f.items()}
 
 
+def algorithmic_bytes(plan, n_nodes, n_edges, radial_b, force_step=False):
+    """Compulsory HBM bytes per step by kernel kind: every operand a launch reads or writes,
+    touched once (fp32 data, int32 indices); re-reads through the caches are not counted.
+
+    Per uvw path pi (i = 2l_in+1, o = 2l_out+1):
+      fwd traversal   read x block (N i C_in), CSR (rowptr, col: 4 N + 4 E), pos (12 N);
+                      write S columns (N B C_in o)
+      channel GEMM    read S (N B sum_g C_in o), W; write z
+      bwd traversal   read z_bar block (N o C_out), Xt and write P (N B C_out i each), sender
+                      CSR (s_rowptr, s_col, s_slot: 4 N + 8 E), pos (12 N); edge adjoint
+                      read-modify-write (24 E; 12 E for the first path of a lane)
+      node GEMMs      Xt = x W, x_bar = P W^T, W_bar = x^T P: each operand once
+    uvu (per path): forward reads x block, W block, CSR, pos and read-modify-writes its z
+    block; backward reads z_bar and x blocks, read-modify-writes x_bar, edge adjoint as uvw.
+    The force step counts the backward's kinds twice (backward and double backward)."""
+    ins = plan.irreps_in
+    outs = plan.out_irreps()
+    B = radial_b
+    f = dict(fwd_traverse=0.0, channel_gemm=0.0, bwd_traverse=0.0, node_gemm=0.0)
+    graph_r = 4.0 * n_nodes + 4.0 * n_edges
+    graph_s = 4.0 * n_nodes + 8.0 * n_edges
+    lanes_seen = 0
+    for q in plan.paths():
+        ci, li, _ = ins[q["in_block"]]
+        co, lo, _ = outs[q["out_block"]]
+        i, o = 2 * li + 1, 2 * lo + 1
+        rbar = 12.0 * n_edges if lanes_seen < 2 else 24.0 * n_edges
+        lanes_seen += 1
+        if plan.mode == "uvw":
+            f["fwd_traverse"] += 4.0 * (n_nodes * i * ci + n_nodes * B * ci * o) + graph_r + 12.0 * n_nodes
+            f["channel_gemm"] += 4.0 * (n_nodes * B * ci * o + B * ci * co)
+            f["bwd_traverse"] += 4.0 * (n_nodes * o * co + 2 * n_nodes * B * co * i) + graph_s + 12.0 * n_nodes + rbar
+            f["node_gemm"] += 4.0 * 3 * (n_nodes * i * ci + B * ci * co + n_nodes * B * co * i)
+        else:
+            f["fwd_traverse"] += 4.0 * (n_nodes * i * ci + B * ci + 2 * n_nodes * o * ci) + graph_r + 12.0 * n_nodes
+            f["bwd_traverse"] += 4.0 * (n_nodes * o * ci + 3 * n_nodes * i * ci + B * ci) + graph_s + \
+                12.0 * n_nodes + rbar
+    if plan.mode == "uvw":
+        zrow = sum(4.0 * n_nodes * m * (2 * l + 1) for m, l, _ in outs)
+        f["channel_gemm"] += zrow
+    if force_step:
+        f["bwd_traverse"] *= 2
+        f["node_gemm"] *= 2
+    return f
+
+
 def kernel_source_hash(kind):
     shared = ["common.hpp", "kernels.hpp", "wave.hpp", "triples.hpp", "cg_tables.inc"]
     files = {
@@ -301,12 +347,15 @@ def measure(args, name):
     from workloads.generate import scalar_mask
 
     dev = torch.device("cuda:0")
-    if args.lanes > 0:
-        etpc.etpc_set_lanes(args.lanes)
     cfg = CONFIGS[name]
-    plan = etpc.Plan(cfg.irreps_in, cfg.irreps_out, cfg.lmax_sh, cfg.mode, cfg.radial, cfg.n_basis, cfg.r_lo,
-                     cfg.r_hi, cfg.poly_p, box=cfg.box, out_per_path=cfg.out_per_path,
-                     gemm_precision=args.gemm_precision)
+
+    def make_plan(lanes):
+        return etpc.Plan(cfg.irreps_in, cfg.irreps_out, cfg.lmax_sh, cfg.mode, cfg.radial, cfg.n_basis, cfg.r_lo,
+                         cfg.r_hi, cfg.poly_p, box=cfg.box, out_per_path=cfg.out_per_path,
+                         gemm_precision=args.gemm_precision, lanes=lanes)
+    plan = make_plan(args.lanes)
+    # the same plan with every launch in order on one stream, for the per-kernel timing pass
+    plan_serial = make_plan(1)
     info = plan.info()
     mask = scalar_mask(cfg.irreps_out) if cfg.cotangent == "energy" else None
     wl = make_workload(cfg, w_blocks=plan.w_blocks(), z_dim=info["z_dim"], scalar_out_mask=mask)
@@ -329,13 +378,13 @@ def measure(args, name):
     csr_ms = (time.perf_counter() - t0) / 3 * 1e3
 
     force_step = "dbl" in cfg.passes
-    def ws_bytes(pass_):
-        full = etpc.etpc_workspace_size(plan, pass_, N, E)
-        return min(full, int(args.workspace_mib * 2 ** 20)) if args.workspace_mib > 0 else full
-    ws_f = torch.empty(ws_bytes(etpc.PASS_FWD), dtype=torch.uint8, device=dev)
-    ws_b = torch.empty(ws_bytes(etpc.PASS_BWD), dtype=torch.uint8, device=dev)
-    ws_d = (torch.empty(ws_bytes(etpc.PASS_DBL), dtype=torch.uint8, device=dev)
-            if force_step else torch.empty(0, dtype=torch.uint8, device=dev))
+    budget = int(args.workspace_mib * 2 ** 20) if args.workspace_mib > 0 else 0
+    # the passes of a step run one after another on one stream: one workspace, sized to the
+    # largest pass, serves them all
+    passes = (etpc.PASS_FWD, etpc.PASS_BWD) + ((etpc.PASS_DBL,) if force_step else ())
+    ws_all = torch.empty(max(etpc.etpc_workspace_size(plan, p_, N, E, budget) for p_ in passes),
+                         dtype=torch.uint8, device=dev)
+    ws_f = ws_b = ws_d = ws_all
     z = torch.empty(N, info["z_dim"], device=dev)
     outs = (torch.empty(N, info["x_dim"], device=dev), torch.empty(info["w_numel"], device=dev),
             torch.empty(N, 3, device=dev))
@@ -345,7 +394,7 @@ def measure(args, name):
         douts = (None, torch.empty(N, info["x_dim"], device=dev), torch.empty(info["w_numel"], device=dev))
     resident = torch.cuda.memory_allocated()
 
-    def step():
+    def step(plan=plan):
         etpc.etpc_forward(plan, graph, x, pos, w, z=z, ws=ws_f)
         etpc.etpc_backward(plan, graph, x, pos, w, zb, outs=outs, ws=ws_b)
         if force_step:
@@ -382,13 +431,12 @@ def measure(args, name):
     # per-kind kernel time: event pairs recorded by the library on its launch streams, with
     # the lanes serialized so that each launch's duration is its own (concurrent launches
     # share the chip and would each look slower)
-    timed_lanes = etpc.etpc_get_lanes()
-    etpc.etpc_set_lanes(1)
+    timed_lanes = plan.spec.lanes or 2
     etpc.etpc_profile_enable(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(plan_serial)
     torch.cuda.synchronize()
     prof_ms = (time.perf_counter() - t1) / args.steps * 1e3
     kinds = {}
@@ -396,7 +444,6 @@ def measure(args, name):
         tot, n = etpc.etpc_profile_read(k)
         kinds[k] = dict(ms_per_step=tot / args.steps, launches_per_step=n / args.steps)
     etpc.etpc_profile_enable(False)
-    etpc.etpc_set_lanes(timed_lanes)
     flops = flop_model(plan, N, E, cfg.n_basis, force_step)
     log(f"step {ms:.3f} ms (profiled pass {prof_ms:.3f} ms); csr build {csr_ms:.3f} ms")
     for k, v in kinds.items():
@@ -408,6 +455,8 @@ def measure(args, name):
     achieved = flops[dom] / (dom_ms * 1e-3) / 1e12
     bound = "mfma" if dom.endswith("gemm") else "alu"
     traffic, traffic_step = traffic_from_profiles(dom, name)
+    alg_bytes = algorithmic_bytes(plan, N, E, cfg.n_basis, force_step).get(dom)
+    hbm_achieved = None if traffic_step is None else traffic_step / (dom_ms * 1e-3) / 1e9
     total_tf = sum(flops.values()) / (ms * 1e-3) / 1e12
     log(f"whole step: {total_tf:.2f} TFLOP/s algorithmic ({total_tf / PEAK_FP32_TFLOPS:.1%} of fp32 peak)")
 
@@ -449,6 +498,10 @@ def measure(args, name):
             "frac": achieved / PEAK_FP32_TFLOPS,
             "traffic": traffic,
             "traffic_per_step": traffic_step,
+            "hbm_gbs": hbm_achieved,
+            "hbm_frac": None if hbm_achieved is None else hbm_achieved / PEAK_HBM_GBS,
+            "algorithmic_bytes_per_step": alg_bytes,
+            "algorithmic_gbs": None if alg_bytes is None else alg_bytes / (dom_ms * 1e-3) / 1e9,
             "launches_per_step": kinds[dom]["launches_per_step"],
             "kernel_ms_per_step": dom_ms,
         },
@@ -457,7 +510,8 @@ def measure(args, name):
         "kernels_ms_per_step": {k: round(v["ms_per_step"], 4) for k, v in kinds.items()},
         "csr_build_ms": csr_ms,
         "peak_mib": peak / 2 ** 20,
-        "workspace_mib": (ws_f.numel() + ws_b.numel() + ws_d.numel()) / 2 ** 20,
+        "workspace_mib": ws_all.numel() / 2 ** 20,
+        "workspace_budget_mib": budget / 2 ** 20 if budget else None,
         "resident_mib": resident / 2 ** 20,
     }
     return result, cfg, wl

@@ -53,7 +53,7 @@ class etpc_spec(C.Structure):
         ("out_per_path", C.c_int32), ("lmax_sh", C.c_int32), ("mode", C.c_int32),
         ("n_instr", C.c_int32), ("instr", C.POINTER(etpc_instr)),
         ("radial", C.c_int32), ("n_basis", C.c_int32), ("r_lo", C.c_float), ("r_hi", C.c_float),
-        ("poly_p", C.c_int32), ("box", C.c_float * 3), ("gemm_precision", C.c_int32),
+        ("poly_p", C.c_int32), ("box", C.c_float * 3), ("gemm_precision", C.c_int32), ("lanes", C.c_int32),
     ]
 
 
@@ -69,7 +69,7 @@ class etpc_graph(C.Structure):
 SYMBOLS = (
     "etpc_plan_create", "etpc_plan_destroy", "etpc_plan_info", "etpc_plan_path", "etpc_plan_out_irrep",
     "etpc_plan_cg", "etpc_workspace_size", "etpc_csr_workspace_size", "etpc_csr_build", "etpc_graph_validate",
-    "etpc_forward", "etpc_backward", "etpc_double_backward", "etpc_set_lanes", "etpc_get_lanes",
+    "etpc_forward", "etpc_backward", "etpc_double_backward",
     "etpc_profile_enable", "etpc_profile_read", "etpc_radius_graph_workspace_size", "etpc_radius_graph",
     "etpc_layout_convert", "etpc_last_error", "etpc_degree_order_workspace_size", "etpc_degree_order",
 )
@@ -87,10 +87,11 @@ def _load():
     sig = {
         "etpc_plan_create": [P(etpc_spec), P(vp)],
         "etpc_plan_info": [vp, P(i64), P(i64), P(i64), P(i32)],
-        "etpc_plan_path": [vp, i32, P(i32), P(i32), P(i32), P(i64), P(i64), P(i32)],
+        "etpc_plan_path": [vp, i32, P(i32), P(i32), P(i32), P(i32), P(i32), P(i64), P(i64), P(i64), P(i64),
+                           P(i32)],
         "etpc_plan_out_irrep": [vp, i32, P(i32), P(etpc_irrep)],
         "etpc_plan_cg": [vp, i32, P(C.c_double)],
-        "etpc_workspace_size": [vp, i32, i32, i64, P(sz)],
+        "etpc_workspace_size": [vp, i32, i32, i64, sz, P(sz)],
         "etpc_csr_workspace_size": [i32, i64, P(sz)],
         "etpc_csr_build": [i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_graph_validate": [P(etpc_graph), vp],
@@ -100,8 +101,6 @@ def _load():
         "etpc_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_double_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_profile_enable": [i32],
-        "etpc_set_lanes": [i32],
-        "etpc_get_lanes": [],
         "etpc_profile_read": [i32, P(C.c_double), P(i64)],
         "etpc_radius_graph_workspace_size": [i32, i64, P(sz)],
         "etpc_radius_graph": [i32, vp, C.c_float, P(C.c_float), i64, vp, vp, P(i64), vp, sz, vp],
@@ -157,13 +156,34 @@ def _stream(stream) -> int:
     return getattr(stream, "cuda_stream", stream)
 
 
+def _torch_stream(stream, device):
+    """The torch stream object of a call's stream (current stream, a torch stream, or a raw
+    HIP stream handle)."""
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def _check_shape(name: str, t: Optional[torch.Tensor], shape: Tuple[int, ...], device=None):
+    """Raise ValueError unless t is None or has exactly `shape` (and lives on `device`)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
 class Plan:
     """Owns an etpc_plan handle (host tables only)."""
 
     def __init__(self, irreps_in, irreps_out, lmax_sh: int, mode: str = "uvw", radial: str = "gaussian",
                  n_basis: int = 8, r_lo: float = 0.0, r_hi: float = 5.0, poly_p: int = 6,
                  box: Optional[Sequence[float]] = None, out_per_path: bool = False,
-                 instructions: Optional[Sequence[Tuple[int, int, int]]] = None, gemm_precision: str = "fp32"):
+                 instructions: Optional[Sequence[Tuple[int, int, int]]] = None, gemm_precision: str = "fp32",
+                 lanes: int = 0):
         ins, outs = parse_irreps(irreps_in), parse_irreps(irreps_out)
         self.irreps_in = ins
         self._in = (etpc_irrep * len(ins))(*[etpc_irrep(*t) for t in ins])
@@ -183,6 +203,7 @@ class Plan:
         b = (0.0, 0.0, 0.0) if box is None else (tuple(box) if hasattr(box, "__len__") else (box, box, box))
         spec.box = (C.c_float * 3)(*b)
         spec.gemm_precision = {"fp32": GEMM_FP32, "bf16": GEMM_BF16, "fp16": GEMM_FP16}[gemm_precision]
+        spec.lanes = int(lanes)
         self.spec = spec
         self.handle = C.c_void_p()
         self.handle = etpc_plan_create(spec)
@@ -224,12 +245,12 @@ def etpc_plan_info(plan: Plan) -> Dict[str, int]:
 
 
 def etpc_plan_path(plan: Plan, p: int) -> Dict[str, int]:
-    ib, ls, ob, fi = C.c_int32(), C.c_int32(), C.c_int32(), C.c_int32()
-    wo, wn = C.c_int64(), C.c_int64()
-    _check(lib.etpc_plan_path(plan.handle, p, C.byref(ib), C.byref(ls), C.byref(ob), C.byref(wo), C.byref(wn),
-                              C.byref(fi)))
-    return dict(in_block=ib.value, l_sh=ls.value, out_block=ob.value, w_off=wo.value, w_numel=wn.value,
-                fan_in=fi.value)
+    ib, ls, ob, li, lo, fi = (C.c_int32() for _ in range(6))
+    xo, zo, wo, wn = (C.c_int64() for _ in range(4))
+    _check(lib.etpc_plan_path(plan.handle, p, C.byref(ib), C.byref(ls), C.byref(ob), C.byref(li), C.byref(lo),
+                              C.byref(xo), C.byref(zo), C.byref(wo), C.byref(wn), C.byref(fi)))
+    return dict(in_block=ib.value, l_sh=ls.value, out_block=ob.value, l_in=li.value, l_out=lo.value,
+                x_off=xo.value, z_off=zo.value, w_off=wo.value, w_numel=wn.value, fan_in=fi.value)
 
 
 def etpc_plan_out_irrep(plan: Plan) -> List[Tuple[int, int, int]]:
@@ -246,9 +267,7 @@ def etpc_plan_out_irrep(plan: Plan) -> List[Tuple[int, int, int]]:
 def etpc_plan_cg(plan: Plan, p: int):
     import numpy as np
     q = etpc_plan_path(plan, p)
-    li = parse_irreps_of(plan, "in")[q["in_block"]][1]
-    lo = etpc_plan_out_irrep(plan)[q["out_block"]][1]
-    ls = q["l_sh"]
+    li, ls, lo = q["l_in"], q["l_sh"], q["l_out"]
     buf = (C.c_double * ((2 * li + 1) * (2 * ls + 1) * (2 * lo + 1)))()
     _check(lib.etpc_plan_cg(plan.handle, p, buf))
     return np.array(buf[:], dtype=np.float64).reshape(2 * li + 1, 2 * ls + 1, 2 * lo + 1)
@@ -259,9 +278,10 @@ def parse_irreps_of(plan: Plan, which: str) -> List[Tuple[int, int, int]]:
     return [(arr[i].mul, arr[i].l, arr[i].parity) for i in range(n)]
 
 
-def etpc_workspace_size(plan: Plan, pass_: int, n_nodes: int, n_edges: int) -> int:
+def etpc_workspace_size(plan: Plan, pass_: int, n_nodes: int, n_edges: int, budget: int = 0) -> int:
+    """Workspace bytes of a pass; budget > 0 caps the node-state scratch (node chunks)."""
     b = C.c_size_t()
-    _check(lib.etpc_workspace_size(plan.handle, pass_, n_nodes, n_edges, C.byref(b)))
+    _check(lib.etpc_workspace_size(plan.handle, pass_, n_nodes, n_edges, int(budget), C.byref(b)))
     return b.value
 
 
@@ -300,10 +320,14 @@ def _empty_i32(n, device):
     return torch.empty(max(n, 0), dtype=torch.int32, device=device)
 
 
-def _workspace(nbytes: int, device) -> Tuple[Optional[torch.Tensor], int]:
+def _workspace(nbytes: int, device, stream=None) -> Tuple[Optional[torch.Tensor], int]:
+    """A library-call scratch buffer, allocated on the call's stream so that the caching
+    allocator does not hand its memory out again before that stream's kernels are done
+    with it (it is dropped as soon as the call has been enqueued)."""
     if nbytes <= 0:
         return None, 0
-    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(_torch_stream(stream, device)):
+        t = torch.empty(nbytes, dtype=torch.uint8, device=device)
     return t, nbytes
 
 
@@ -312,9 +336,10 @@ def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=No
     dispatch orders (etpc_degree_order of s_rowptr and rowptr)."""
     dev = src.device
     e = int(src.shape[0])
+    _check_shape("dst", dst, (e,), dev)
     rowptr, s_rowptr = _empty_i32(n_nodes + 1, dev), _empty_i32(n_nodes + 1, dev)
     col, eid, s_col, s_slot = (_empty_i32(e, dev) for _ in range(4))
-    ws, nb = _workspace(etpc_csr_workspace_size(n_nodes, e), dev)
+    ws, nb = _workspace(etpc_csr_workspace_size(n_nodes, e), dev, stream)
     _check(lib.etpc_csr_build(n_nodes, e, _ptr(src, torch.int32), _ptr(dst, torch.int32), _ptr(rowptr, torch.int32),
                               _ptr(col, torch.int32), _ptr(eid, torch.int32), _ptr(s_rowptr, torch.int32),
                               _ptr(s_col, torch.int32), _ptr(s_slot, torch.int32),
@@ -335,7 +360,7 @@ def etpc_degree_order(rowptr: torch.Tensor, window: int = 0, stream=None) -> tor
     with window > 0, within each aligned window of that many nodes."""
     n = int(rowptr.shape[0]) - 1
     order = _empty_i32(n, rowptr.device)
-    ws, nb = _workspace(etpc_degree_order_workspace_size(n), rowptr.device)
+    ws, nb = _workspace(etpc_degree_order_workspace_size(n), rowptr.device, stream)
     _check(lib.etpc_degree_order(n, _ptr(rowptr, torch.int32), window, _ptr(order, torch.int32) if n > 0 else None,
                                  None if ws is None else ws.data_ptr(), nb, _stream(stream)))
     return order
@@ -364,7 +389,7 @@ def etpc_radius_graph(pos: torch.Tensor, cutoff: float, box=None, max_edges: Opt
     box_c = None if box is None else (C.c_float * 3)(*[float(b) for b in box])
     for attempt in range(2):
         src, dst = _empty_i32(cap, dev), _empty_i32(cap, dev)
-        ws, nb = _workspace(etpc_radius_graph_workspace_size(n, cap), dev)
+        ws, nb = _workspace(etpc_radius_graph_workspace_size(n, cap), dev, stream)
         ne = C.c_int64()
         st = lib.etpc_radius_graph(n, _ptr(pos), float(cutoff), box_c, cap, _ptr(src, torch.int32),
                                    _ptr(dst, torch.int32), C.byref(ne), None if ws is None else ws.data_ptr(), nb,
@@ -385,23 +410,41 @@ def etpc_layout_convert(plan: Plan, features: str, direction: str, x: torch.Tens
     d = {"to_ir_mul": TO_IR_MUL, "to_mul_ir": TO_MUL_IR}[direction]
     if out is None:
         out = torch.empty_like(x)
+    _check_shape("out", out, tuple(x.shape), x.device)
     _check(lib.etpc_layout_convert(plan.handle, f, d, int(x.shape[0]) if x.dim() else 0, _ptr(x), _ptr(out),
                                    _stream(stream)))
     return out
 
 
-def _ws_for(plan, pass_, graph, ws):
+def _ws_for(plan, pass_, graph, ws, stream):
     if isinstance(ws, torch.Tensor):
         return ws.data_ptr(), ws.numel() * ws.element_size(), ws
     n = etpc_workspace_size(plan, pass_, graph.n_nodes, graph.n_edges)
-    t, nb = _workspace(n, graph.rowptr.device)
+    t, nb = _workspace(n, graph.rowptr.device, stream)
     return (None if t is None else t.data_ptr()), nb, t
 
 
+def _check_inputs(plan: Plan, graph: Graph, x, pos, w, z_bar=None, **extra):
+    """Shapes of the dense operands against the plan and the graph (the library reads and
+    writes exactly these extents, so a wrong size would be an out-of-bounds access)."""
+    info = plan.info()
+    N, dev = graph.n_nodes, graph.rowptr.device
+    shapes = dict(x=(N, info["x_dim"]), pos=(N, 3), w=(info["w_numel"],), z_bar=(N, info["z_dim"]),
+                  z=(N, info["z_dim"]), x_bar=(N, info["x_dim"]), w_bar=(info["w_numel"],), pos_bar=(N, 3),
+                  x_dot=(N, info["x_dim"]), w_dot=(info["w_numel"],), pos_dot=(N, 3),
+                  z_bar_grad=(N, info["z_dim"]), x_grad=(N, info["x_dim"]), w_grad=(info["w_numel"],),
+                  pos_grad=(N, 3))
+    for name, t in dict(x=x, pos=pos, w=w, z_bar=z_bar, **extra).items():
+        _check_shape(name, t, shapes[name], dev)
+    return info
+
+
 def etpc_forward(plan: Plan, graph: Graph, x, pos, w, z=None, ws=None, stream=None):
+    _check_inputs(plan, graph, x, pos, w, z=z)
     if z is None:
-        z = torch.empty(graph.n_nodes, plan.info()["z_dim"], dtype=torch.float32, device=x.device)
-    wp, wn, _keep = _ws_for(plan, PASS_FWD, graph, ws)
+        with torch.cuda.stream(_torch_stream(stream, x.device)):
+            z = torch.empty(graph.n_nodes, plan.info()["z_dim"], dtype=torch.float32, device=x.device)
+    wp, wn, _keep = _ws_for(plan, PASS_FWD, graph, ws, stream)
     _check(lib.etpc_forward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z), wp, wn,
                             _stream(stream)))
     return z
@@ -409,16 +452,18 @@ def etpc_forward(plan: Plan, graph: Graph, x, pos, w, z=None, ws=None, stream=No
 
 def etpc_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, want=("x", "w", "pos"), outs=None, ws=None,
                   stream=None):
-    info = plan.info()
+    info = _check_inputs(plan, graph, x, pos, w, z_bar)
     dev = x.device
     if outs is None:
-        outs = (
-            torch.empty(graph.n_nodes, info["x_dim"], dtype=torch.float32, device=dev) if "x" in want else None,
-            torch.empty(info["w_numel"], dtype=torch.float32, device=dev) if "w" in want else None,
-            torch.empty(graph.n_nodes, 3, dtype=torch.float32, device=dev) if "pos" in want else None,
-        )
+        with torch.cuda.stream(_torch_stream(stream, dev)):
+            outs = (
+                torch.empty(graph.n_nodes, info["x_dim"], dtype=torch.float32, device=dev) if "x" in want else None,
+                torch.empty(info["w_numel"], dtype=torch.float32, device=dev) if "w" in want else None,
+                torch.empty(graph.n_nodes, 3, dtype=torch.float32, device=dev) if "pos" in want else None,
+            )
     xb, wb, pb = outs
-    wp, wn, _keep = _ws_for(plan, PASS_BWD, graph, ws)
+    _check_inputs(plan, graph, x, pos, w, z_bar, x_bar=xb, w_bar=wb, pos_bar=pb)
+    wp, wn, _keep = _ws_for(plan, PASS_BWD, graph, ws, stream)
     _check(lib.etpc_backward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z_bar), _ptr(xb),
                              _ptr(wb), _ptr(pb), wp, wn, _stream(stream)))
     return xb, wb, pb
@@ -427,32 +472,26 @@ def etpc_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, want=("x", "w", "p
 def etpc_double_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, x_dot=None, w_dot=None, pos_dot=None,
                          want=("z_bar", "x", "w", "pos"), outs=None, ws=None, stream=None):
     """Returns (d/dz_bar, d/dx, d/dW, d/dpos); outputs not in ``want`` are None."""
-    info = plan.info()
+    info = _check_inputs(plan, graph, x, pos, w, z_bar, x_dot=x_dot, w_dot=w_dot, pos_dot=pos_dot)
     dev = x.device
     if outs is None:
-        outs = (
-            torch.empty(graph.n_nodes, info["z_dim"], dtype=torch.float32, device=dev) if "z_bar" in want else None,
-            torch.empty(graph.n_nodes, info["x_dim"], dtype=torch.float32, device=dev) if "x" in want else None,
-            torch.empty(info["w_numel"], dtype=torch.float32, device=dev) if "w" in want else None,
-            torch.empty(graph.n_nodes, 3, dtype=torch.float32, device=dev) if "pos" in want else None,
-        )
+        with torch.cuda.stream(_torch_stream(stream, dev)):
+            outs = (
+                torch.empty(graph.n_nodes, info["z_dim"], dtype=torch.float32, device=dev)
+                if "z_bar" in want else None,
+                torch.empty(graph.n_nodes, info["x_dim"], dtype=torch.float32, device=dev) if "x" in want else None,
+                torch.empty(info["w_numel"], dtype=torch.float32, device=dev) if "w" in want else None,
+                torch.empty(graph.n_nodes, 3, dtype=torch.float32, device=dev) if "pos" in want else None,
+            )
     if len(outs) == 3:
         outs = tuple(outs) + (None,)
     gz, gx, gw, gp = outs
-    wp, wn, _keep = _ws_for(plan, PASS_DBL, graph, ws)
+    _check_inputs(plan, graph, x, pos, w, z_bar, z_bar_grad=gz, x_grad=gx, w_grad=gw, pos_grad=gp)
+    wp, wn, _keep = _ws_for(plan, PASS_DBL, graph, ws, stream)
     _check(lib.etpc_double_backward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z_bar),
                                     _ptr(x_dot), _ptr(w_dot), _ptr(pos_dot), _ptr(gz), _ptr(gx), _ptr(gw), _ptr(gp),
                                     wp, wn, _stream(stream)))
     return gz, gx, gw, gp
-
-
-def etpc_set_lanes(lanes: int) -> None:
-    """Concurrent launch lanes per pass (1 serializes; default 2)."""
-    _check(lib.etpc_set_lanes(int(lanes)))
-
-
-def etpc_get_lanes() -> int:
-    return int(lib.etpc_get_lanes())
 
 
 def etpc_profile_enable(enable: bool) -> None:

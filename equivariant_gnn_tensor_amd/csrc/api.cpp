@@ -81,8 +81,8 @@ int lane_width(int c, int* ntiles, int min_cp = 1) {
 // Concurrent lanes of a pass (see lanes.hpp).  uvw: paths round-robin over the lanes;
 // uvu: one lane per input block (backward: x_bar accumulates per block) or per output
 // block (forward: z accumulates per block).  Each lane owns a copy of the edge adjoint:
-// the workspace holds rbar_slots copies; a call uses rbar_lanes of them, fixed once at
-// its start (the process-wide limit may change between calls).
+// the workspace holds rbar_slots copies (one per lane the plan allows); a call uses
+// rbar_lanes of them (one when the call is too small to gain from lanes).
 int count_blocks(const etpc_plan_s* p, bool by_in) {
   const auto& groups = by_in ? p->by_in : p->by_out;
   int used = 0;
@@ -91,7 +91,7 @@ int count_blocks(const etpc_plan_s* p, bool by_in) {
 }
 int rbar_slots(const etpc_plan_s* p) {
   const int units = p->mode == ETPC_UVW ? static_cast<int>(p->paths.size()) : count_blocks(p, true);
-  return std::max(1, std::min(kLanes, units));
+  return std::max(1, std::min(std::min(p->lanes, kLanes), units));
 }
 // Below about 2^16 edge-channels a pass's launches take a few microseconds each, less
 // than a fork and join of side streams costs, so such calls stay on one lane.
@@ -100,7 +100,7 @@ int lane_cap(const etpc_plan_s* p, const etpc_graph* g) {
   int64_t cmax = 1;
   for (const auto& b : p->in) cmax = std::max<int64_t>(cmax, b.mul);
   for (const auto& b : p->out) cmax = std::max<int64_t>(cmax, b.mul);
-  return g->n_edges * cmax < kLaneMinWork ? 1 : lanes_limit();
+  return g->n_edges * cmax < kLaneMinWork ? 1 : std::max(1, std::min(p->lanes, kLanes));
 }
 int rbar_lanes(const etpc_plan_s* p, const etpc_graph* g) { return std::min(rbar_slots(p), lane_cap(p, g)); }
 // lane of each block for n lanes (blocks without paths get lane 0, unused)
@@ -397,14 +397,15 @@ std::vector<int> block_order(const etpc_plan_s* p, const Derived& d) {
 
 // One uvw forward evaluation into z (beta: accumulate into z).  With tangent, the
 // receiver traversal builds dS along pos_dot.  xin / win select the operands.
+// nl: concurrent lanes the call may use (lane_cap, or 1 to stay on the caller's stream).
 etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* xin,
                         const float* pos, const float* pos_dot, const float* win, float* z, bool beta, bool tangent,
-                        const FwdLayout& L, int64_t chunk, hipStream_t s) {
+                        const FwdLayout& L, int64_t chunk, int nl, hipStream_t s) {
   const GeomParams geom = p->geom();
   const int32_t N = g->n_nodes;
   // the channel GEMM of one group runs on the post stream while the next group's
   // traversals fill the other S set; the largest GEMMs go first, so they overlap most
-  PostStream post(s, lane_cap(p, g) > 1);
+  PostStream post(s, nl > 1);
   ETPC_HIP(post.status());
   int set = 0;
   for (const int gi : group_order(p, d)) {
@@ -417,7 +418,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       ETPC_HIP(post.wait_slot(set));
       int32_t col0 = 0;
       // the paths of a group fill disjoint column ranges of S: concurrent lanes
-      LaneGroup lanes(s, std::min(static_cast<int>(paths.size()), lane_cap(p, g)));
+      LaneGroup lanes(s, std::min(static_cast<int>(paths.size()), nl));
       ETPC_HIP(lanes.status());
       for (size_t t = 0; t < paths.size(); ++t) {
         const PathInfo& pi = p->paths[paths[t]];
@@ -472,10 +473,11 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
 }
 
 etpc_status fwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* xin, const float* pos,
-                        const float* pos_dot, const float* win, float* z, bool beta, bool tangent, hipStream_t s) {
+                        const float* pos_dot, const float* win, float* z, bool beta, bool tangent, int nlanes,
+                        hipStream_t s) {
   const GeomParams geom = p->geom();
   std::vector<int> seen(p->out.size(), 0);
-  const int nl = std::max(1, std::min(lane_cap(p, g), count_blocks(p, false)));
+  const int nl = std::max(1, std::min(nlanes, count_blocks(p, false)));
   const std::vector<int> lane_of = block_lanes(p, false, nl);   // z accumulates per output block
   LaneGroup lanes(s, nl);
   ETPC_HIP(lanes.status());
@@ -843,21 +845,52 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
   return ETPC_OK;
 }
 
+// Forward on a caller-given workspace (uvw: node chunks that fit; uvu needs none).
+etpc_status forward_impl(const etpc_plan_s* p, const etpc_graph* g, const float* x, const float* pos, const float* w,
+                         float* z, void* ws, size_t ws_bytes, int nl, hipStream_t s) {
+  const Derived d = derive(p);
+  const int64_t chunk = pick_chunk(g->n_nodes, ws_bytes, [&](int64_t c) { return fwd_bytes(p, d, c); });
+  if (p->mode == ETPC_UVW) {
+    etpc_status st = check_ws(ws, ws_bytes, fwd_bytes(p, d, 1));
+    if (st != ETPC_OK) return st;
+  }
+  Carver c{static_cast<char*>(ws), 0};
+  FwdLayout L;
+  fwd_layout(p, d, std::max<int64_t>(chunk, 0), c, L);
+  ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached(p, z, g->n_nodes, s));
+  if (p->mode == ETPC_UVW) return fwd_uvw_run(p, d, g, x, pos, nullptr, w, z, false, false, L, chunk, nl, s);
+  return fwd_uvu_run(p, g, x, pos, nullptr, w, z, false, false, nl, s);
+}
+
 }  // namespace
 
 extern "C" {
 
-etpc_status etpc_workspace_size(etpc_plan p, int32_t pass, int32_t n_nodes, int64_t n_edges, size_t* bytes) {
+etpc_status etpc_workspace_size(etpc_plan p, int32_t pass, int32_t n_nodes, int64_t n_edges, size_t budget,
+                                size_t* bytes) {
   if (p == nullptr || bytes == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null plan or output");
   if (n_nodes < 0 || n_edges < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative graph size");
+  if (pass != ETPC_PASS_FWD && pass != ETPC_PASS_BWD && pass != ETPC_PASS_DBL)
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "unknown pass");
   const Derived d = derive(p);
-  const int64_t chunk = p->mode == ETPC_UVW ? n_nodes : kUvuGrid;
-  switch (pass) {
-    case ETPC_PASS_FWD: *bytes = fwd_bytes(p, d, chunk); break;
-    case ETPC_PASS_BWD: *bytes = bwd_bytes(p, d, n_edges, chunk); break;
-    case ETPC_PASS_DBL: *bytes = dbl_bytes(p, d, n_edges, chunk); break;
-    default: ETPC_FAIL(ETPC_ERR_INVALID_ARG, "unknown pass");
+  // uvu keeps no node state: its layout depends on the persistent grid, not on a chunk
+  auto bytes_of = [&](int64_t c) -> size_t {
+    const int64_t chunk = p->mode == ETPC_UVW ? c : kUvuGrid;
+    if (pass == ETPC_PASS_FWD) return fwd_bytes(p, d, chunk);
+    if (pass == ETPC_PASS_BWD) return bwd_bytes(p, d, n_edges, chunk);
+    return dbl_bytes(p, d, n_edges, chunk);
+  };
+  const size_t full = bytes_of(n_nodes);
+  if (budget == 0 || full <= budget || n_nodes == 0) {
+    *bytes = full;
+    return ETPC_OK;
   }
+  const int64_t chunk = pick_chunk(n_nodes, budget, bytes_of);
+  if (chunk < 1) {
+    *bytes = bytes_of(1);
+    ETPC_FAIL(ETPC_ERR_WORKSPACE, "budget below the pass's minimum of " + std::to_string(*bytes) + " bytes");
+  }
+  *bytes = bytes_of(chunk);
   return ETPC_OK;
 }
 
@@ -968,18 +1001,7 @@ etpc_status etpc_forward(etpc_plan p, const etpc_graph* g, const float* x, const
   if (g->n_nodes == 0) return ETPC_OK;
   if (x == nullptr || pos == nullptr || w == nullptr || z == nullptr)
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null x, pos, w or z");
-  const Derived d = derive(p);
-  const int64_t chunk = pick_chunk(g->n_nodes, ws_bytes, [&](int64_t c) { return fwd_bytes(p, d, c); });
-  if (p->mode == ETPC_UVW) {
-    st = check_ws(ws, ws_bytes, fwd_bytes(p, d, 1));
-    if (st != ETPC_OK) return st;
-  }
-  Carver c{static_cast<char*>(ws), 0};
-  FwdLayout L;
-  fwd_layout(p, d, std::max<int64_t>(chunk, 0), c, L);
-  ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached(p, z, g->n_nodes, s));
-  if (p->mode == ETPC_UVW) return fwd_uvw_run(p, d, g, x, pos, nullptr, w, z, false, false, L, chunk, s);
-  return fwd_uvu_run(p, g, x, pos, nullptr, w, z, false, false, s);
+  return forward_impl(p, g, x, pos, w, z, ws, ws_bytes, lane_cap(p, g), s);
 }
 
 etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, const float* pos, const float* w,
@@ -1104,9 +1126,9 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
           win = w_dot;
         }
         if (p->mode == ETPC_UVW)
-          st = fwd_uvw_run(p, d, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, L, chunk, s);
+          st = fwd_uvw_run(p, d, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, L, chunk, lane_cap(p, g), s);
         else
-          st = fwd_uvu_run(p, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, s);
+          st = fwd_uvu_run(p, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, lane_cap(p, g), s);
         if (st != ETPC_OK) return st;
         beta = true;
       }

@@ -14,6 +14,14 @@ constexpr int kMaxBasis = 16;
 constexpr int kMaxPaths = 64;
 constexpr int kWave = 64;
 
+// Concurrent launch lanes of a pass (side streams per device).  Two measured best on
+// MI355X: one launch's tail filled by the next; more lanes contend for the four hardware
+// queues of a process.  A plan selects 1..kLanes (etpc_spec.lanes).
+#ifndef ETPC_LANES
+#define ETPC_LANES 2
+#endif
+constexpr int kLanes = ETPC_LANES;
+
 // Row offset map: row r of a logical matrix lives at (r / div) * s1 + (r % div) * s2.
 // Covers plain row-major matrices (div = 1) and ir_mul blocks, whose rows are
 // (node, m) pairs: node stride = feature width, m stride = multiplicity.

@@ -1,12 +1,8 @@
 // Concurrent launch lanes: per-device side streams and fork/join events.
 #include "lanes.hpp"
 
-#include <atomic>
-
 namespace etpc {
 namespace {
-
-std::atomic<int> g_limit{kLanes};
 
 constexpr int kMaxDevices = 64;
 
@@ -59,13 +55,8 @@ bool ensure_post(DeviceLanes& dl) {
 
 }  // namespace
 
-int lanes_limit() { return g_limit.load(); }
-
-void set_lanes_limit(int n) { g_limit.store(n < 1 ? 1 : (n > kLanes ? kLanes : n)); }
-
 LaneGroup::LaneGroup(hipStream_t main, int n) : main_(main) {
-  const int lim = lanes_limit();
-  n_ = n < 1 ? 1 : (n > lim ? lim : n);
+  n_ = n < 1 ? 1 : (n > kLanes ? kLanes : n);
   if (n_ == 1) return;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
@@ -105,7 +96,7 @@ hipError_t LaneGroup::finish() {
 LaneGroup::~LaneGroup() { (void)finish(); }
 
 PostStream::PostStream(hipStream_t main, bool enable) : main_(main) {
-  if (!enable || lanes_limit() < 2) return;
+  if (!enable) return;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
   DeviceLanes& dl = g_dev[dev];
@@ -172,14 +163,3 @@ hipError_t PostStream::finish() {
 PostStream::~PostStream() { (void)finish(); }
 
 }  // namespace etpc
-
-extern "C" {
-
-etpc_status etpc_set_lanes(int32_t lanes) {
-  etpc::set_lanes_limit(lanes);
-  return ETPC_OK;
-}
-
-int32_t etpc_get_lanes(void) { return etpc::lanes_limit(); }
-
-}  // extern "C"

@@ -16,22 +16,10 @@
 
 namespace etpc {
 
-// Two lanes measured best on MI355X (one launch's tail filled by the next; more lanes
-// contend for the four hardware queues of the process).
-#ifndef ETPC_LANES
-#define ETPC_LANES 2
-#endif
-constexpr int kLanes = ETPC_LANES;
-
-// Process-wide lane limit in [1, kLanes] (etpc_set_lanes); 1 serializes every launch on
-// the caller's stream, e.g. to time kernels one at a time.
-int lanes_limit();
-void set_lanes_limit(int n);
-
 class LaneGroup {
  public:
-  // n lanes (clamped to [1, lanes_limit()]); with n == 1, or if the side streams cannot
-  // be created, every lane is the caller's stream itself.
+  // n lanes (clamped to [1, kLanes]; callers pass at most their plan's lane count); with
+  // n == 1, or if the side streams cannot be created, every lane is the caller's stream.
   LaneGroup(hipStream_t main, int n);
   ~LaneGroup();
   LaneGroup(const LaneGroup&) = delete;
@@ -59,8 +47,8 @@ class LaneGroup {
 // next group's or block's traversals do.  The pass keeps two sets of the buffers those
 // GEMMs read and alternates between them; before its traversals write set b again, the
 // caller's stream waits for the post work that last read set b (wait_slot).  Disabled
-// (every call a no-op, stream() the caller's stream) when the lane limit is 1 or when
-// `enable` is false.  Holds a per-device lock from construction to finish; it is taken
+// (every call a no-op, stream() the caller's stream) when `enable` is false (the plan has
+// one lane, or the call is too small to gain from it).  Holds a per-device lock from construction to finish; it is taken
 // before any LaneGroup lock of the same call, never after.
 class PostStream {
  public:

@@ -207,6 +207,8 @@ etpc_status etpc_plan_create(const etpc_spec* s, etpc_plan* out) {
   if (s->gemm_precision != ETPC_GEMM_FP32 && s->gemm_precision != ETPC_GEMM_BF16 &&
       s->gemm_precision != ETPC_GEMM_FP16)
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "unknown gemm_precision");
+  if (s->lanes < 0 || s->lanes > etpc::kLanes)
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "lanes must be 0 (default) or 1.." + std::to_string(etpc::kLanes));
 
   auto p = new etpc_plan_s();
   p->in.assign(s->in, s->in + s->n_in);
@@ -220,6 +222,7 @@ etpc_status etpc_plan_create(const etpc_spec* s, etpc_plan* out) {
   p->periodic = any_box;
   for (int d = 0; d < 3; ++d) p->box[d] = s->box[d];
   p->gemm_precision = s->gemm_precision;
+  p->lanes = s->lanes == 0 ? etpc::kLanes : s->lanes;
 
   std::vector<std::tuple<int, int, int>> instr;
   if (s->out_per_path) {
@@ -359,13 +362,18 @@ etpc_status etpc_plan_info(etpc_plan p, int64_t* x_dim, int64_t* z_dim, int64_t*
 }
 
 etpc_status etpc_plan_path(etpc_plan p, int32_t i, int32_t* in_block, int32_t* l_sh, int32_t* out_block,
-                           int64_t* w_off, int64_t* w_numel, int32_t* fan_in) {
+                           int32_t* l_in, int32_t* l_out, int64_t* x_off, int64_t* z_off, int64_t* w_off,
+                           int64_t* w_numel, int32_t* fan_in) {
   if (p == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null plan");
   if (i < 0 || i >= static_cast<int32_t>(p->paths.size())) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "path index out of range");
   const auto& q = p->paths[i];
   if (in_block) *in_block = q.in_block;
   if (l_sh) *l_sh = q.l_sh;
   if (out_block) *out_block = q.out_block;
+  if (l_in) *l_in = q.l_in;
+  if (l_out) *l_out = q.l_out;
+  if (x_off) *x_off = p->xoff[q.in_block];
+  if (z_off) *z_off = p->zoff[q.out_block];
   if (w_off) *w_off = q.w_off;
   if (w_numel) *w_numel = q.w_numel;
   if (fan_in) *fan_in = q.fan_in;

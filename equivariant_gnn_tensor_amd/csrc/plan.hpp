@@ -29,6 +29,7 @@ struct etpc_plan_s {
   float box[3] = {0.f, 0.f, 0.f};
   bool periodic = false;
   int32_t gemm_precision = 0;   // etpc_gemm_precision of the channel GEMMs
+  int32_t lanes = 2;            // concurrent launch lanes of a pass (1 = serialized)
   int64_t x_dim = 0, z_dim = 0, w_numel = 0;
   std::vector<etpc::PathInfo> paths;
   // paths grouped by output block / input block (indices into `paths`, plan order)

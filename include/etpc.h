@@ -38,9 +38,9 @@
  * Every call validates its arguments on the host first; on a non-OK status no
  * kernel has been enqueued and etpc_last_error() describes the problem.
  * Compute calls are asynchronous on the given stream; results are
- * deterministic for a given workspace size and lane setting (fixed reduction owners
- * and orders, no floating-point atomics; timing never changes a result).  Inside a call, the independent per-path launches of a
- * pass run on up to two side streams, and the node-side GEMMs of a pass on a third
+ * deterministic for a given workspace size and plan (fixed reduction owners and orders,
+ * no floating-point atomics; timing never changes a result).  Inside a call, the
+ * independent per-path launches of a pass run on up to two side streams (etpc_spec.lanes), and the node-side GEMMs of a pass on a third
  * ("post") stream that overlaps them with the next group's or block's traversals; the
  * library creates these streams once per device (default priority) and forks them from
  * and joins them back into the given stream with events, so the call still behaves as
@@ -107,6 +107,11 @@ typedef struct {
   int32_t poly_p;                             /* Bessel envelope exponent p >= 1 */
   float box[3];                               /* all zero = open; else orthorhombic minimum image */
   int32_t gemm_precision;                     /* etpc_gemm_precision; 0 (default) = fp32 */
+  int32_t lanes;     /* concurrent launch lanes of a pass: 0 = default (2), 1 = every launch in
+                        order on the caller's stream (e.g. to time kernels one at a time), 2 =
+                        independent per-path launches on two library side streams plus the
+                        node-side GEMMs on a third.  Results do not depend on it beyond the
+                        summation order of the per-lane position-adjoint copies (pos_bar). */
 } etpc_spec;
 
 /* Receiver-sorted CSR plus the sender (source) view; all DEVICE pointers.
@@ -148,23 +153,41 @@ void etpc_plan_destroy(etpc_plan plan);
 /* Widths: x_dim = sum C(2l+1) (Eq. 4), z_dim likewise, w_numel = B * sum n_pi (Eq. 9-10). */
 etpc_status etpc_plan_info(etpc_plan plan, int64_t* x_dim, int64_t* z_dim, int64_t* w_numel,
                            int32_t* n_paths);
-/* Path p in plan order.  fan_in = B * (sum of C_in over the output group) for uvw, B for uvu. */
+/* [host] Path p (0 <= p < n_paths) in plan order: one instruction (in_block, l_sh, out_block)
+ * that passes the selection rule (Eq. 5), its degrees l_in, l_out, and where its operands
+ * live (Eq. 9-10: each path owns one radial-weight block W_pi[b]):
+ *   x_off  offset (floats) of the input block within an x row ([2l_in+1][C_in], ir_mul);
+ *   z_off  offset (floats) of the output block within a z row ([2l_out+1][C_out]);
+ *   w_off, w_numel  the path's block of w: uvw [B][C_in][C_out], uvu [B][C_in];
+ *   fan_in = B * (sum of C_in over the paths of the output block) for uvw (the D_g of the
+ *            channel GEMM, Eq. 34), B for uvu.
+ * Every output pointer may be NULL.  ETPC_ERR_INVALID_ARG for a null plan or p out of range. */
 etpc_status etpc_plan_path(etpc_plan plan, int32_t p, int32_t* in_block, int32_t* l_sh, int32_t* out_block,
-                           int64_t* w_off, int64_t* w_numel, int32_t* fan_in);
+                           int32_t* l_in, int32_t* l_out, int64_t* x_off, int64_t* z_off, int64_t* w_off,
+                           int64_t* w_numel, int32_t* fan_in);
 /* Output block b (useful when out_per_path built the output list). */
 etpc_status etpc_plan_out_irrep(etpc_plan plan, int32_t b, int32_t* n_out, etpc_irrep* irrep);
 /* [host] dense coupling tensor of path p, [2l_in+1][2l_sh+1][2l_out+1] doubles (Eq. 32). */
 etpc_status etpc_plan_cg(etpc_plan plan, int32_t p, double* out);
 
-/* Workspace bytes for a compute pass over a graph of n_nodes / n_edges with every node
- * in one chunk (the fastest schedule).  Grows with N (node-side states, two sets of them
- * so the GEMMs of one group or block overlap the traversals of the next) and, for backward
- * and double backward, by 12 B per edge per concurrent launch lane (the per-edge position
- * adjoint; up to two lanes, one per path or per uvu input block); it never scales with E
- * times a channel width.  A compute call given less (down to one node's state)
- * runs the nodes in chunks that fit, with the same results up to summation order. */
+/* [host] Workspace bytes of a compute pass (etpc_pass) over a graph of n_nodes / n_edges.
+ * Sec. 4 keeps the tensor-product scratch within a fixed budget (Sec. 5: 128 MiB) by
+ * running bounded receiver ranges; here the node-side states (the uvw receiver state S of
+ * Eq. 33, the sender state P and Xt of the backward, two sets of each so the GEMMs of one
+ * output group or input block overlap the traversals of the next) are sized by a node
+ * chunk:
+ *   budget == 0: every node in one chunk, the fastest schedule;
+ *   budget  > 0: the largest node chunk whose workspace fits in `budget` bytes (the full
+ *                size when that already fits).
+ * Backward and double backward add 12 B per edge per concurrent lane of the plan (the
+ * per-edge position adjoint, in receiver-slot order); nothing scales with E times a
+ * channel width.  A compute call given any workspace of at least this many bytes runs
+ * with a chunk at least this large; results differ between chunk sizes only in summation
+ * order.  ETPC_ERR_WORKSPACE (with *bytes set to the minimum, one node per chunk) when the
+ * budget is below that minimum; ETPC_ERR_INVALID_ARG for a null plan or output, negative
+ * sizes or an unknown pass. */
 etpc_status etpc_workspace_size(etpc_plan plan, int32_t pass, int32_t n_nodes, int64_t n_edges,
-                                size_t* bytes);
+                                size_t budget, size_t* bytes);
 
 /* Build both CSR views from a COO list (src[e] -> dst[e]), stable: receiver view sorted
  * by receiver with ties in COO order; sender view sorted by sender with ties in
@@ -189,7 +212,17 @@ etpc_status etpc_csr_build(int32_t n_nodes, int64_t n_edges, const int32_t* src,
 etpc_status etpc_degree_order_workspace_size(int32_t n_nodes, size_t* bytes);
 etpc_status etpc_degree_order(int32_t n_nodes, const int32_t* rowptr, int32_t window, int32_t* order, void* ws,
                               size_t ws_bytes, hipStream_t stream);
-/* Debug check of the graph preconditions; synchronizes the stream.  Needs no workspace. */
+/* Debug check of the graph preconditions listed with etpc_graph (Sec. 4: the traversals
+ * own whole rows of cached, stable receiver and source CSR views, so both views must
+ * describe one edge multiset in the stable orders etpc_csr_build produces; Eq. 8 needs
+ * |r_e| > 0).  Checks on the device: rowptr / s_rowptr start at 0, are non-decreasing
+ * and end at n_edges; col / s_col in [0, N); no self loops; s_slot a permutation of the
+ * receiver slots with s_col[k] = receiver of slot s_slot[k] and col[s_slot[k]] = the
+ * sender of row k; each sender row in increasing slot order; s_order / r_order (when
+ * given) equal to their etpc_degree_order results.  Positions are not read, so |r_e| > 0
+ * stays the caller's precondition.  Synchronizes the stream and needs no workspace.
+ * ETPC_ERR_GRAPH with a description of the first violation found; ETPC_ERR_INVALID_ARG
+ * for null arrays or negative sizes. */
 etpc_status etpc_graph_validate(const etpc_graph* graph, hipStream_t stream);
 
 /* Graph preparation: the radius graph of N points (the workloads of Sec. 3 are radius
@@ -251,19 +284,13 @@ etpc_status etpc_double_backward(etpc_plan plan, const etpc_graph* graph, const 
                                  float* z_bar_grad, float* x_grad, float* w_grad, float* pos_grad,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Concurrent launch lanes (process-wide): the per-path launches of a pass run on up to
- * `lanes` streams (1..2; default 2; out-of-range values are clamped).  1 serializes every
- * launch on the caller's stream, which is how per-kernel durations are best timed.  Takes
- * effect for calls that start afterwards; results do not depend on it beyond summation
- * order of the per-lane position-adjoint copies.  etpc_get_lanes returns the setting. */
-etpc_status etpc_set_lanes(int32_t lanes);
-int32_t etpc_get_lanes(void);
-
-/* Kernel timing (off by default).  While enabled, every kernel the library enqueues is
- * bracketed by a pair of HIP events recorded on its launch stream, grouped by kind.
- * etpc_profile_read synchronizes on the recorded events and returns the summed
- * durations (milliseconds) and launch count of one kind since the last enable.
- * Process-wide; not meant for concurrent use from several threads. */
+/* Kernel timing (off by default), a measurement aid outside the compute path.  While
+ * enabled, every kernel the library enqueues is bracketed by a pair of HIP events recorded
+ * on its launch stream, grouped by kind.  etpc_profile_read synchronizes on the recorded
+ * events and returns the summed durations (milliseconds) and launch count of one kind
+ * since the last enable.  Process-wide (a timer of the whole library, as a profiler is);
+ * it never changes what a call computes.  Not meant for concurrent use from several
+ * threads. */
 typedef enum {
   ETPC_KIND_CSR = 0,          /* CSR build kernels */
   ETPC_KIND_FWD_TRAVERSE = 1, /* receiver traversals (uvw state S, uvu outputs) */

@@ -33,9 +33,12 @@ def test_planner_matches_oracle_plan(name):
     assert (info["x_dim"], info["z_dim"], info["w_numel"], info["n_paths"]) == \
         (oplan.x_dim, oplan.z_dim, oplan.w_numel, len(oplan.paths))
     assert plan.out_irreps() == [tuple(t) for t in oplan.irreps_out]
+    xoff, zoff = oir.offsets(oplan.irreps_in), oir.offsets(oplan.irreps_out)
     for p, (q, o) in enumerate(zip(plan.paths(), oplan.paths)):
         assert (q["in_block"], q["l_sh"], q["out_block"], q["w_off"], q["w_numel"]) == \
             (o.in_block, o.l_sh, o.out_block, o.w_off, o.w_numel)
+        assert (q["l_in"], q["l_out"], q["x_off"], q["z_off"]) == \
+            (o.l_in, o.l_out, xoff[o.in_block], zoff[o.out_block])
         assert q["fan_in"] == oplan.fan_in(o)
         np.testing.assert_allclose(plan.cg(p), real_cg(o.l_in, o.l_sh, o.l_out), atol=1e-12)
 
@@ -103,17 +106,57 @@ def test_csr_workspace_size_and_argument_errors():
         etpc.etpc_csr_workspace_size(-1, 10)
 
 
-def test_lane_setting_is_clamped():
-    old = etpc.etpc_get_lanes()
-    try:
-        etpc.etpc_set_lanes(1)
-        assert etpc.etpc_get_lanes() == 1
-        etpc.etpc_set_lanes(99)
-        assert 1 <= etpc.etpc_get_lanes() <= 4
-        etpc.etpc_set_lanes(0)
-        assert etpc.etpc_get_lanes() == 1
-    finally:
-        etpc.etpc_set_lanes(old)
+def test_workspace_budget():
+    """budget = 0 gives the full (one chunk) size; a budget caps the node-state scratch at the
+    largest chunk that fits; below one node's state (plus the per-edge adjoint) the call is
+    refused with the minimum reported."""
+    plan = plan_from_config(CONFIGS["cfg2"])
+    n, e = 4096, 214980
+    for pass_ in (etpc.PASS_FWD, etpc.PASS_BWD, etpc.PASS_DBL):
+        full = etpc.etpc_workspace_size(plan, pass_, n, e)
+        assert etpc.etpc_workspace_size(plan, pass_, n, e, budget=full) == full
+        assert etpc.etpc_workspace_size(plan, pass_, n, e, budget=4 * full) == full
+        for mib in (512, 256, 128):
+            b = etpc.etpc_workspace_size(plan, pass_, n, e, budget=mib << 20)
+            assert b <= min(full, mib << 20)
+            # monotone: a larger budget never gives a smaller workspace
+            assert etpc.etpc_workspace_size(plan, pass_, n, e, budget=2 * (mib << 20)) >= b
+        with pytest.raises(etpc.EtpcError) as ei:
+            etpc.etpc_workspace_size(plan, pass_, n, e, budget=1024)
+        assert ei.value.name == "WORKSPACE" and "minimum" in str(ei.value)
+    # an empty graph needs no chunking
+    assert etpc.etpc_workspace_size(plan, etpc.PASS_FWD, 0, 0, budget=1) >= 0
+
+
+def test_lanes_belong_to_the_plan():
+    """Concurrent launch lanes are a plan field (no process-wide setting): 0 = default (2),
+    1 serializes, anything else is refused; a one-lane plan keeps one edge-adjoint copy."""
+    base = dict(irreps_in="4x0e+4x1o", irreps_out="4x0e+4x1o", lmax_sh=2)
+    for lanes in (0, 1, 2):
+        etpc.Plan(**base, lanes=lanes)
+    for bad in (-1, 3, 99):
+        with pytest.raises(etpc.EtpcError) as ei:
+            etpc.Plan(**base, lanes=bad)
+        assert ei.value.name == "INVALID_ARG"
+    cfg = CONFIGS["cfg4_d16"]
+    two = plan_from_config(cfg)
+    one = etpc.Plan(cfg.irreps_in, cfg.irreps_out, cfg.lmax_sh, cfg.mode, cfg.radial, cfg.n_basis, cfg.r_lo,
+                    cfg.r_hi, cfg.poly_p, box=cfg.box, lanes=1)
+    n = 32768
+    b2 = [etpc.etpc_workspace_size(two, etpc.PASS_BWD, n, int(e)) for e in (5e5, 2e6)]
+    b1 = [etpc.etpc_workspace_size(one, etpc.PASS_BWD, n, int(e)) for e in (5e5, 2e6)]
+    assert abs((b2[1] - b2[0]) - 24 * 1.5e6) < 4096 and abs((b1[1] - b1[0]) - 12 * 1.5e6) < 4096
+    assert not hasattr(etpc.lib, "etpc_set_lanes")
+
+
+def test_plan_path_argument_errors():
+    plan = plan_from_config(CONFIGS["cfg1"])
+    n = plan.info()["n_paths"]
+    lib = etpc.lib
+    assert lib.etpc_plan_path(plan.handle, n, None, None, None, None, None, None, None, None, None, None) == 1
+    assert lib.etpc_plan_path(plan.handle, -1, None, None, None, None, None, None, None, None, None, None) == 1
+    assert lib.etpc_plan_path(None, 0, None, None, None, None, None, None, None, None, None, None) == 1
+    assert lib.etpc_plan_path(plan.handle, 0, None, None, None, None, None, None, None, None, None, None) == 0
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -12,6 +12,7 @@ import torch
 from oracle import conv
 from oracle.csr import csr_build
 from tests.gpu_helpers import make_case, note, rel_err
+from tests.planner_helpers import plan_from_config
 from workloads import CONFIGS, small_variant
 
 pytestmark = pytest.mark.gpu
@@ -351,30 +352,25 @@ def test_concurrent_schedules_are_deterministic_and_agree():
     c = make_case(cfg)
     note(f"schedules {cfg.name}")
     pos_dot = torch.from_numpy(-c.wl.force_c).cuda()
-    old = etpc.etpc_get_lanes()
+    serial_plan = plan_from_config(cfg, lanes=1)
 
-    def run(stream=None):
-        z = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, stream=stream)
-        b = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, stream=stream)
-        d = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot, stream=stream)
+    def run(stream=None, plan=c.plan):
+        z = etpc.etpc_forward(plan, c.graph, c.x, c.pos, c.w, stream=stream)
+        b = etpc.etpc_backward(plan, c.graph, c.x, c.pos, c.w, c.z_bar, stream=stream)
+        d = etpc.etpc_double_backward(plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot, stream=stream)
         return [z, *b, *d]
 
-    try:
-        etpc.etpc_set_lanes(2)
-        first = run()
-        for _ in range(3):
-            again = run()
-            assert all(torch.equal(a, b) for a, b in zip(first, again))
-        side = torch.cuda.Stream()
-        with torch.cuda.stream(side):
-            on_side = run(stream=side)
-        side.synchronize()
-        assert all(torch.equal(a, b) for a, b in zip(first, on_side))
-        etpc.etpc_set_lanes(1)
-        serial = run()
-        torch.cuda.synchronize()
-    finally:
-        etpc.etpc_set_lanes(old)
+    first = run()
+    for _ in range(3):
+        again = run()
+        assert all(torch.equal(a, b) for a, b in zip(first, again))
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        on_side = run(stream=side)
+    side.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(first, on_side))
+    serial = run(plan=serial_plan)
+    torch.cuda.synchronize()
     z, xb, wb, pb = first[:4]
     assert torch.equal(z, serial[0]) and torch.equal(xb, serial[1]) and torch.equal(wb, serial[2])
     assert rel_err(pb, serial[3].double().cpu().numpy()) < 1e-6
@@ -390,3 +386,45 @@ def test_concurrent_schedules_are_deterministic_and_agree():
     for a, b in zip(chunked, first[4:]):
         if a is not None:
             assert rel_err(a, b.double().cpu().numpy()) < 1e-5
+
+
+def test_binding_rejects_wrong_shapes_before_launch():
+    """The binding compares every dense operand with the plan and the graph before calling
+    the library, so a wrong-sized tensor is an argument error, not an out-of-bounds access."""
+    etpc = _etpc()
+    cfg = CONFIGS["cfg1"]
+    c = make_case(cfg)
+    N = cfg.n_nodes
+    info = c.plan.info()
+    bad = [
+        dict(x=c.x[:-1]), dict(pos=c.pos[:, :2]), dict(w=c.w[:-3]),
+    ]
+    for kw in bad:
+        args = dict(x=c.x, pos=c.pos, w=c.w)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            etpc.etpc_forward(c.plan, c.graph, args["x"], args["pos"], args["w"])
+    with pytest.raises(ValueError):
+        etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, z=torch.empty(N, info["z_dim"] - 1, device="cuda"))
+    zb = torch.randn(N, info["z_dim"], device="cuda")
+    with pytest.raises(ValueError):
+        etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, zb[:, 1:])
+    with pytest.raises(ValueError):
+        etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, zb,
+                           outs=(torch.empty(N, info["x_dim"], device="cuda"), torch.empty(5, device="cuda"), None))
+    with pytest.raises(ValueError):
+        etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, zb, pos_dot=torch.zeros(N + 1, 3, device="cuda"))
+    with pytest.raises(ValueError):
+        etpc.etpc_layout_convert(c.plan, "in", "to_mul_ir", c.x, out=torch.empty(N, info["x_dim"] + 1, device="cuda"))
+    with pytest.raises(ValueError):
+        etpc.etpc_csr_build(N, torch.zeros(4, dtype=torch.int32, device="cuda"),
+                            torch.zeros(3, dtype=torch.int32, device="cuda"))
+    # the correct shapes still run, also on a non-default stream with library-allocated
+    # outputs and workspace (allocated on that stream)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        z = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, stream=side)
+    side.synchronize()
+    z0 = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w)
+    torch.cuda.synchronize()
+    assert torch.equal(z, z0)
