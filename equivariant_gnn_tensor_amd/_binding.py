@@ -69,7 +69,7 @@ class etpc_graph(C.Structure):
 SYMBOLS = (
     "etpc_plan_create", "etpc_plan_destroy", "etpc_plan_info", "etpc_plan_path", "etpc_plan_out_irrep",
     "etpc_plan_cg", "etpc_workspace_size", "etpc_csr_workspace_size", "etpc_csr_build", "etpc_graph_validate",
-    "etpc_forward", "etpc_backward", "etpc_double_backward",
+    "etpc_forward", "etpc_forward_noalloc", "etpc_backward", "etpc_double_backward",
     "etpc_profile_enable", "etpc_profile_read", "etpc_radius_graph_workspace_size", "etpc_radius_graph",
     "etpc_layout_convert", "etpc_last_error", "etpc_degree_order_workspace_size", "etpc_degree_order",
 )
@@ -98,6 +98,7 @@ def _load():
         "etpc_degree_order_workspace_size": [i32, P(sz)],
         "etpc_degree_order": [i32, vp, i32, vp, vp, sz, vp],
         "etpc_forward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, sz, vp],
+        "etpc_forward_noalloc": [vp, P(etpc_graph), vp, vp, vp, vp, vp],
         "etpc_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_double_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "etpc_profile_enable": [i32],
@@ -447,6 +448,17 @@ def etpc_forward(plan: Plan, graph: Graph, x, pos, w, z=None, ws=None, stream=No
     wp, wn, _keep = _ws_for(plan, PASS_FWD, graph, ws, stream)
     _check(lib.etpc_forward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z), wp, wn,
                             _stream(stream)))
+    return z
+
+
+def etpc_forward_noalloc(plan: Plan, graph: Graph, x, pos, w, z, stream=None):
+    """Forward into a caller-given z using the library's fixed device scratch: allocates
+    nothing (not even here: z must be given).  Calls that overlap on one GPU race."""
+    _check_inputs(plan, graph, x, pos, w, z=z)
+    if z is None:
+        raise ValueError("etpc_forward_noalloc writes into a caller-given z")
+    _check(lib.etpc_forward_noalloc(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z),
+                                    _stream(stream)))
     return z
 
 

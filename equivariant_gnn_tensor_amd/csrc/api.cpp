@@ -22,6 +22,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.hpp"
@@ -862,6 +863,35 @@ etpc_status forward_impl(const etpc_plan_s* p, const etpc_graph* g, const float*
   return fwd_uvu_run(p, g, x, pos, nullptr, w, z, false, false, nl, s);
 }
 
+// ---------------------------------------------------------------- fixed scratch
+// Device scratch of etpc_forward_noalloc, for callers that cannot allocate: a file-scope
+// device array (one copy per GPU, resident until the process ends), 128 MiB, the
+// tensor-product scratch cap the Sobek paper's measurements use (Sec. 5).  In host code
+// the array's name only stands in for the symbol: its device address (one per device) is
+// taken once per device with hipGetSymbolAddress and only that address is passed on.
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call on that device.
+etpc_status static_scratch(void** out) {
+  int dev = 0;
+  ETPC_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices) ETPC_FAIL(ETPC_ERR_UNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    ETPC_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (ptr == nullptr) ETPC_FAIL(ETPC_ERR_HIP, "hipGetSymbolAddress returned no address for the fixed scratch");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ETPC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1002,6 +1032,26 @@ etpc_status etpc_forward(etpc_plan p, const etpc_graph* g, const float* x, const
   if (x == nullptr || pos == nullptr || w == nullptr || z == nullptr)
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null x, pos, w or z");
   return forward_impl(p, g, x, pos, w, z, ws, ws_bytes, lane_cap(p, g), s);
+}
+
+etpc_status etpc_forward_noalloc(etpc_plan p, const etpc_graph* g, const float* x, const float* pos, const float* w,
+                                 float* z, hipStream_t s) {
+  etpc_status st = check_common(p, g);
+  if (st != ETPC_OK) return st;
+  if (g->n_nodes == 0) return ETPC_OK;
+  if (x == nullptr || pos == nullptr || w == nullptr || z == nullptr)
+    ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null x, pos, w or z");
+  if (p->mode == ETPC_UVU) return forward_impl(p, g, x, pos, w, z, nullptr, 0, 1, s);   // no scratch
+  const Derived d = derive(p);
+  if (fwd_bytes(p, d, 1) > kStaticScratchBytes)
+    ETPC_FAIL(ETPC_ERR_WORKSPACE, "one receiver's state (" + std::to_string(fwd_bytes(p, d, 1)) +
+                                      " bytes) exceeds the fixed scratch of " +
+                                      std::to_string(kStaticScratchBytes) + " bytes");
+  void* ptr = nullptr;
+  st = static_scratch(&ptr);
+  if (st != ETPC_OK) return st;
+  // one lane: the side streams would be created on first use, which this entry point avoids
+  return forward_impl(p, g, x, pos, w, z, ptr, kStaticScratchBytes, 1, s);
 }
 
 etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, const float* pos, const float* w,

@@ -264,6 +264,20 @@ etpc_status etpc_layout_convert(etpc_plan plan, int32_t features, int32_t direct
 etpc_status etpc_forward(etpc_plan plan, const etpc_graph* graph, const float* x, const float* pos,
                          const float* w, float* z, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same result as etpc_forward
+ * (up to the summation order of node chunks), with no workspace argument.  Its scratch is
+ * a fixed 128 MiB device array inside the library (one per GPU, held until the process
+ * ends); graphs whose receiver state needs more are run in node chunks that fit.  It
+ * calls no hipMalloc, hipFree or other allocating routine and runs every launch in order
+ * on `stream` (no side streams).  Every call on one GPU shares that GPU's array and
+ * leaves its last contents there: calls that overlap in time on one GPU (two streams, or
+ * two host threads) race and give undefined results; calls ordered on one stream do not.
+ * ETPC_ERR_WORKSPACE when one receiver's state alone exceeds the 128 MiB (a clear message
+ * names both sizes); other errors as etpc_forward. */
+etpc_status etpc_forward_noalloc(etpc_plan plan, const etpc_graph* graph, const float* x, const float* pos,
+                                 const float* w, float* z, hipStream_t stream);
+
 /* Backward: gradients of <z_bar, z> with respect to x, W and positions (Eq. 18-22 and
  * the chain rule through Eq. 8).  Each output pointer may be NULL to skip it. */
 etpc_status etpc_backward(etpc_plan plan, const etpc_graph* graph, const float* x, const float* pos,

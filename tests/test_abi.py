@@ -227,3 +227,19 @@ def test_degree_order_argument_errors():
     # a workspace too small is refused before anything is launched
     st = lib.etpc_degree_order(8, 16, 0, 16, 16, 8, None)
     assert st != 0 and "workspace" in etpc.lib.etpc_last_error().decode().lower()
+
+
+def test_noalloc_forward_refuses_oversized_state():
+    """The allocation-free forward refuses, on the host and before any HIP call, a plan whose
+    single-receiver state exceeds its fixed 128 MiB scratch.  The size is confirmed through
+    the workspace query first, so the call below can only take the refusal path (its
+    pointers are placeholders that nothing dereferences)."""
+    import ctypes as C
+    huge = etpc.Plan("300000x0e+300000x1o", "4x0e+4x1o", 1, "uvw", "gaussian", 16, 0.0, 5.0)
+    one_receiver = etpc.etpc_workspace_size(huge, etpc.PASS_FWD, 1, 0)
+    assert one_receiver > (128 << 20)
+    g = _binding.etpc_graph()
+    g.n_nodes, g.n_edges = 1, 0
+    g.rowptr = g.s_rowptr = 4096
+    st = etpc.lib.etpc_forward_noalloc(huge.handle, C.byref(g), 4096, 4096, 4096, 4096, None)
+    assert st == 4 and "fixed scratch" in etpc.lib.etpc_last_error().decode()
