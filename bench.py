@@ -305,7 +305,7 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
         lines.append(f"| {tot / 1e6:.3f} | {calls} | {avg / 1e3:.1f} | {fam} | `{short}` |")
     with open(os.path.join(ROOT, "profiles", f"trace_{workload}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
-    kind_of = {"fwd_traverse": "fwd_traverse", "bwd_traverse": "bwd_traverse"}
+    kind_of = {"fwd_traverse": "fwd_traverse", "bwd_traverse": "bwd_traverse", "gemm": "gemm"}
     for fam, kind in kind_of.items():
         if fam in out and out[fam]["hbm_bytes_per_step"] is not None:
             rec = dict(out[fam], kind=kind, workload=workload, kernel_src_sha=kernel_source_hash(kind),
@@ -314,7 +314,71 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
                                f"--workload {workload} --lanes 1 --copy-calibration-mib {copy_mib}")
             with open(os.path.join(ROOT, "profiles", f"pmc_{kind}_{workload}.json"), "w") as fh:
                 json.dump(rec, fh, indent=1)
+    summarize_counters(d, workload, steps, warmup, {f: v[0] for f, v in fam_t.items()}, execs, cmd_args)
     print(json.dumps(out, indent=1))
+
+
+SQ_RUNS = {
+    # one rocprofv3 --pmc pass each (at most 8 SQ counters per pass)
+    "sq1": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAVES "
+           "SQ_INSTS_LDS SQ_ACTIVE_INST_VALU",
+    "sq2": "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_LDS "
+           "SQ_LDS_BANK_CONFLICT SQ_WAVES SQ_INSTS_VALU",
+}
+
+
+def summarize_counters(d, workload, steps, warmup, fam_ns, execs, cmd_args):
+    """Issue rates, matrix-core use, occupancy and LDS bank conflicts per kernel family from
+    the two SQ counter passes (DIR/sq1_<workload>, DIR/sq2_<workload>) and the kernel trace,
+    into profiles/counters_<workload>.md.  Skipped when the passes are absent."""
+    import csv
+    import glob
+    import collections
+    runs = {}
+    for tag in SQ_RUNS:
+        files = glob.glob(os.path.join(d, f"{tag}_{workload}", "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            return
+        agg = collections.defaultdict(lambda: collections.defaultdict(float))
+        for fn in files:
+            for r in csv.DictReader(open(fn)):
+                agg[kernel_family(r.get("Kernel_Name", ""))][r["Counter_Name"]] += float(r["Counter_Value"])
+        runs[tag] = agg
+    simd_cycles = lambda ns: ns * 1e-9 * 2.4e9 * 1024          # noqa: E731  (256 CUs x 4 SIMDs)
+    lines = [f"# Issue rates, matrix cores, occupancy and LDS bank conflicts, workload {workload}", "",
+             "Commands (repo root, one MI355X; each run executes "
+             f"{execs} steps: warmup {warmup}, timed {steps}, event-profiled {steps}):", "", "```"]
+    for tag, ctrs in SQ_RUNS.items():
+        lines.append(f"rocprofv3 --pmc {ctrs} --output-format csv -d DIR/{tag}_{workload} -o run -- "
+                     f"python3 bench.py {cmd_args}")
+    lines += [f"python bench.py --summarize-profile DIR --steps {steps} --warmup {warmup} --workload {workload} "
+              f"--lanes 1 --copy-calibration-mib 256", "```", "",
+              "Counters are summed over all dispatches of a family; durations come from the kernel trace "
+              "(trace_" + workload + ".md) of the same command.",
+              "- VALU issue = SQ_INSTS_VALU x 4 cycles / (duration x 2.4 GHz x 1024 SIMDs): a wave64 fp32 VALU "
+              "operation holds a 16-lane SIMD for four cycles (SQ_INSTS_VALU includes the MFMA instructions).",
+              "- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (duration x 2.4 GHz x 1024).",
+              "- waves / SIMD = 4 x SQ_WAVE_CYCLES (quad-cycles) / (duration x 2.4 GHz x 1024).",
+              "- active / wait / wait-issue: SQ_ACTIVE_INST_ANY, SQ_WAIT_ANY, SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES.",
+              "- LDS bank conflict rate = SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (conflict cycles per LDS-active "
+              "cycle).", "",
+              "| family | ms (all steps) | VALU issue | MFMA busy | waves / SIMD | active / wait / wait-issue | "
+              "LDS instr / wave | LDS bank conflict rate |", "|---|---|---|---|---|---|---|---|"]
+    for fam in ("fwd_traverse", "bwd_traverse", "gemm", "aux", "csr"):
+        if fam not in fam_ns or fam not in runs["sq1"]:
+            continue
+        ns = fam_ns[fam]
+        a, b = runs["sq1"][fam], runs["sq2"].get(fam, {})
+        cyc = simd_cycles(ns)
+        wc = b.get("SQ_WAVE_CYCLES", 0.0) or 1.0
+        lines.append(
+            f"| {fam} | {ns / 1e6:.3f} | {a['SQ_INSTS_VALU'] * 4 / cyc:.3f} | "
+            f"{a['SQ_VALU_MFMA_BUSY_CYCLES'] / cyc:.3f} | {4 * a['SQ_WAVE_CYCLES'] / cyc:.2f} | "
+            f"{b.get('SQ_ACTIVE_INST_ANY', 0) / wc:.2f} / {b.get('SQ_WAIT_ANY', 0) / wc:.2f} / "
+            f"{b.get('SQ_WAIT_INST_ANY', 0) / wc:.2f} | {a['SQ_INSTS_LDS'] / max(a['SQ_WAVES'], 1):.0f} | "
+            f"{b.get('SQ_LDS_BANK_CONFLICT', 0) / max(b.get('SQ_ACTIVE_INST_LDS', 0), 1):.3f} |")
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def morton_relabel(wl):

@@ -163,20 +163,70 @@ int pick_splits(int64_t M, int64_t N, int64_t K) {
 // ---------------------------------------------------------------- workspace layouts
 constexpr int kGemmSplits = 8;   // split-K partial sets kept for the long-K channel / x_bar GEMMs
 
-// Two sets of the buffers the node-side GEMMs read (S forward; Xt, P and the re-laid-out
-// weights backward): groups / blocks alternate between them, so one set's GEMMs can run
-// on the post stream while the next traversals fill the other set.
+// Up to two sets of the buffers the node-side GEMMs read (S forward; Xt, P and the
+// re-laid-out weights backward): groups / blocks alternate between them, so one set's
+// GEMMs can run on the post stream while the next traversals fill the other set.
 constexpr int kSets = 2;
+
+// How a pass uses its workspace.
+//  fast (the workspace holds every node's state): one chunk of all nodes, two buffer sets,
+//    one edge-adjoint copy per concurrent lane, kGemmSplits split-K partial slots.
+//  bounded (less workspace than that, e.g. a scratch budget): one buffer set, node chunks
+//    sized separately for each output group (forward) or input block (backward) so that
+//    each fills the state buffer, two split-K partial slots, and one edge-adjoint copy per
+//    lane only while those copies take at most an eighth of the workspace (else one).
+//    The chunk passed to the layouts is the chunk of the largest group or block; a smaller
+//    one runs bigger chunks in the same buffer (group_chunk / block_chunk).
+struct Sched {
+  bool bounded = false;
+  int nsets = kSets;
+  int rbar_copies = 1;
+  int part_slots = kGemmSplits;
+};
+
+Sched fast_sched(const etpc_plan_s* p) {
+  Sched s;
+  s.rbar_copies = rbar_slots(p);
+  return s;
+}
+
+Sched bounded_sched(const etpc_plan_s* p, int64_t n_edges, size_t ws_bytes) {
+  Sched s;
+  s.bounded = true;
+  s.nsets = 1;
+  s.part_slots = 2;
+  const int slots = rbar_slots(p);
+  const size_t all = static_cast<size_t>(3 * sizeof(float)) * static_cast<size_t>(n_edges) * slots;
+  s.rbar_copies = (slots > 1 && all <= ws_bytes / 8) ? slots : 1;
+  return s;
+}
+
+// receivers per launch of output group g when the S buffer holds `chunk` receivers of the
+// largest group (bounded schedules; the fast schedule runs every node at once)
+int64_t group_chunk(const etpc_plan_s* p, const Derived& d, int g, int64_t chunk, int64_t n, const Sched& sch) {
+  if (!sch.bounded) return chunk;
+  const int64_t per = d.group_d[g] * (2 * p->out[g].l + 1);
+  return std::max<int64_t>(1, std::min<int64_t>(n, per > 0 ? chunk * d.max_s / per : n));
+}
+
+// senders per launch of input block k (likewise for the Xt / P buffers)
+int64_t block_chunk(const etpc_plan_s* p, const Derived& d, int k, int64_t chunk, int64_t n, const Sched& sch) {
+  if (!sch.bounded) return chunk;
+  const int64_t per = d.block_ncols[k] * (2 * p->in[k].l + 1);
+  return std::max<int64_t>(1, std::min<int64_t>(n, per > 0 ? chunk * d.max_state / per : n));
+}
 
 struct FwdLayout {
   float* S[kSets] = {};
   float* part = nullptr;
   int64_t part_cap = 0;
+  int nsets = kSets;
 };
-void fwd_layout(const etpc_plan_s* p, const Derived& d, int64_t chunk, Carver& c, FwdLayout& L) {
+void fwd_layout(const etpc_plan_s* p, const Derived& d, int64_t chunk, const Sched& sch, Carver& c, FwdLayout& L) {
+  L.nsets = sch.nsets;
   if (p->mode == ETPC_UVW) {
-    for (int b = 0; b < kSets; ++b) L.S[b] = c.take<float>(static_cast<size_t>(chunk * d.max_s));
-    L.part_cap = kGemmSplits * chunk * d.max_zrow;
+    for (int b = 0; b < sch.nsets; ++b) L.S[b] = c.take<float>(static_cast<size_t>(chunk * d.max_s));
+    L.part_cap = sch.part_slots * chunk * d.max_zrow;
     L.part = c.take<float>(static_cast<size_t>(L.part_cap));
   }
 }
@@ -187,41 +237,51 @@ struct BwdLayout {
   float *xt[kSets] = {}, *P[kSets] = {}, *Pd[kSets] = {};
   float* xpart = nullptr;
   int64_t xpart_cap = 0;
+  int64_t wpart_cap = 0;    // uvw: floats of W_bar split-K partials (one or two operand sets)
   int64_t wpart_lane = 0;   // uvu: floats of W_bar partials per lane
+  int nsets = kSets;
+  int rbar_copies = 1;
 };
-// flags: pos = edge adjoint (one copy per lane) + Xt; p = plain P state; tan = tangent state; wbar = W_bar partials
-// (two sets when wbar2); wt2 = second transposed weight (for w_dot)
-void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t chunk, bool pos, bool need_p,
-                bool tan, bool wbar, bool wbar2, bool xbar, bool wt2, Carver& c, BwdLayout& L) {
+// flags: pos = edge adjoint (sch.rbar_copies copies) + Xt; p = plain P state; tan = tangent state; wbar = W_bar
+// partials (two sets when wbar2); wt2 = second transposed weight (for w_dot).  n_nodes bounds the per-block
+// chunks of a bounded schedule (the W_bar split count follows each block's chunk).
+void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t chunk,
+                const Sched& sch, bool pos, bool need_p, bool tan, bool wbar, bool wbar2, bool xbar, bool wt2,
+                Carver& c, BwdLayout& L) {
+  L.nsets = sch.nsets;
+  L.rbar_copies = sch.rbar_copies;
   if (p->mode == ETPC_UVW) {
-    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * rbar_slots(p)));
-    for (int b = 0; b < kSets; ++b) {
+    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * sch.rbar_copies));
+    for (int b = 0; b < sch.nsets; ++b) {
       if (pos) L.wcat[b] = c.take<float>(static_cast<size_t>(d.max_wcat));
       if (xbar) L.wt[b] = c.take<float>(static_cast<size_t>(d.max_wcat));
       if (wt2) L.wt2[b] = c.take<float>(static_cast<size_t>(d.max_wcat));
     }
     if (wbar) {
-      // split-K partial tiles of W_bar: as many splits as wbar_gemm picks for this chunk
+      // split-K partial tiles of W_bar: as many splits as wbar_gemm picks for each block's chunk
       int64_t need = 0;
       for (size_t k = 0; k < p->in.size(); ++k) {
         if (p->by_in[k].empty()) continue;
         const int ni = 2 * p->in[k].l + 1;
-        const int sp = pick_splits(p->in[k].mul, d.block_ncols[k], std::max<int64_t>(chunk, 1) * ni);
+        const int64_t ck = block_chunk(p, d, static_cast<int>(k), std::max<int64_t>(chunk, 1),
+                                       std::max<int64_t>(n_nodes, 1), sch);
+        const int sp = pick_splits(p->in[k].mul, d.block_ncols[k], ck * ni);
         need = std::max<int64_t>(need, static_cast<int64_t>(sp) * p->in[k].mul * d.block_ncols[k]);
       }
-      L.wpart = c.take<float>(static_cast<size_t>((wbar2 ? 2 : 1) * need));
+      L.wpart_cap = (wbar2 ? 2 : 1) * need;
+      L.wpart = c.take<float>(static_cast<size_t>(L.wpart_cap));
     }
-    for (int b = 0; b < kSets; ++b) {
+    for (int b = 0; b < sch.nsets; ++b) {
       if (pos) L.xt[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
       if (need_p) L.P[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
       if (tan) L.Pd[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
     }
     if (xbar) {
-      L.xpart_cap = kGemmSplits * chunk * d.max_xrow;
+      L.xpart_cap = sch.part_slots * chunk * d.max_xrow;
       L.xpart = c.take<float>(static_cast<size_t>(L.xpart_cap));
     }
   } else {
-    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * rbar_slots(p)));
+    if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * sch.rbar_copies));
     int64_t maxbc = 0;
     for (auto& q : p->paths) maxbc = std::max<int64_t>(maxbc, static_cast<int64_t>(p->n_basis) * q.c_in);
     L.wpart_lane = chunk * maxbc;   // chunk = uvu grid size here; one partial set per lane
@@ -231,25 +291,27 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t
 
 constexpr int kUvuGrid = 2048;
 
-size_t fwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t chunk) {
+size_t fwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t chunk, const Sched& sch) {
   Carver c;
   FwdLayout L;
-  fwd_layout(p, d, chunk, c, L);
+  fwd_layout(p, d, chunk, sch, c, L);
   return c.off;
 }
 
-size_t bwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t chunk) {
+size_t bwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t chunk,
+                 const Sched& sch) {
   Carver c;
   BwdLayout L;
-  bwd_layout(p, d, n_edges, chunk, true, true, false, true, false, true, false, c, L);
+  bwd_layout(p, d, n_nodes, n_edges, chunk, sch, true, true, false, true, false, true, false, c, L);
   return c.off;
 }
 
-size_t dbl_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_edges, int64_t chunk) {
+size_t dbl_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t chunk,
+                 const Sched& sch) {
   Carver c;
   BwdLayout L;
-  bwd_layout(p, d, n_edges, chunk, true, true, true, true, true, true, true, c, L);   // every output
-  return std::max(c.off, fwd_bytes(p, d, chunk));
+  bwd_layout(p, d, n_nodes, n_edges, chunk, sch, true, true, true, true, true, true, true, c, L);   // every output
+  return std::max(c.off, fwd_bytes(p, d, chunk, sch));
 }
 
 // largest chunk in [1, n] whose layout fits
@@ -263,6 +325,23 @@ int64_t pick_chunk(int64_t n, size_t ws_bytes, F bytes_of) {
   int64_t c = std::min<int64_t>(n, static_cast<int64_t>((ws_bytes - b0) / per));
   while (c > 1 && bytes_of(c) > ws_bytes) --c;
   return std::max<int64_t>(c, 1);
+}
+
+// The schedule and node chunk of a call given ws_bytes of workspace: the fast schedule
+// when every node fits at once, else the bounded one with its largest chunk that fits
+// (-1 when not even one node does).  bytes_of(chunk, sched) is the call's layout size.
+template <class F>
+void choose_schedule(const etpc_plan_s* p, int64_t n_nodes, int64_t n_edges, size_t ws_bytes, F bytes_of,
+                     Sched* sch, int64_t* chunk) {
+  const Sched f = fast_sched(p);
+  if (n_nodes <= 0 || bytes_of(n_nodes, f) <= ws_bytes) {
+    *sch = f;
+    *chunk = n_nodes;
+    return;
+  }
+  const Sched b = bounded_sched(p, n_edges, ws_bytes);
+  *sch = b;
+  *chunk = pick_chunk(n_nodes, ws_bytes, [&](int64_t c) { return bytes_of(c, b); });
 }
 
 RowMap plain(int64_t ld) { return make_rowmap(ld, 0, 1); }
@@ -401,7 +480,7 @@ std::vector<int> block_order(const etpc_plan_s* p, const Derived& d) {
 // nl: concurrent lanes the call may use (lane_cap, or 1 to stay on the caller's stream).
 etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* xin,
                         const float* pos, const float* pos_dot, const float* win, float* z, bool beta, bool tangent,
-                        const FwdLayout& L, int64_t chunk, int nl, hipStream_t s) {
+                        const FwdLayout& L, int64_t chunk, const Sched& sch, int nl, hipStream_t s) {
   const GeomParams geom = p->geom();
   const int32_t N = g->n_nodes;
   // the channel GEMM of one group runs on the post stream while the next group's
@@ -414,8 +493,9 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     const int no = 2 * p->out[gi].l + 1;
     const int64_t D = d.group_d[gi];
     const int c_out = p->out[gi].mul;
-    for (int64_t r0 = 0; r0 < N; r0 += chunk) {
-      const int nrecv = static_cast<int>(std::min<int64_t>(chunk, N - r0));
+    const int64_t cg = group_chunk(p, d, gi, chunk, N, sch);
+    for (int64_t r0 = 0; r0 < N; r0 += cg) {
+      const int nrecv = static_cast<int>(std::min<int64_t>(cg, N - r0));
       ETPC_HIP(post.wait_slot(set));
       int32_t col0 = 0;
       // the paths of a group fill disjoint column ranges of S: concurrent lanes
@@ -466,7 +546,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       etpc_status st = gemm_auto(ga, L.part, L.part_cap, kGemmSplits, ETPC_KIND_CHANNEL_GEMM, post.stream());
       if (st != ETPC_OK) return st;
       ETPC_HIP(post.mark(set));
-      set ^= 1;
+      if (L.nsets > 1) set ^= 1;
     }
   }
   ETPC_HIP(post.finish());
@@ -597,7 +677,8 @@ etpc_status xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float
 }
 
 etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* pos,
-                        const float* z_bar, const UvwBwdReq& R, const BwdLayout& L, int64_t chunk, hipStream_t s) {
+                        const float* z_bar, const UvwBwdReq& R, const BwdLayout& L, int64_t chunk, const Sched& sch,
+                        hipStream_t s) {
   const GeomParams geom = p->geom();
   const int32_t N = g->n_nodes;
   const bool want_pos = R.rbar != nullptr;
@@ -606,27 +687,38 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   const int nl = std::max(1, R.lanes);
   const int64_t rbar_stride = 3 * g->n_edges;
   if (R.x_out) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
-  // A software pipeline over (sender chunk, input block) items, alternating two buffer
-  // sets: while item i's traversals run on the caller's stream and its lanes, the post
-  // stream re-lays out the weights and forms Xt = x W for item i + 1 in the other set,
-  // then runs item i's x_bar / W_bar GEMMs once its traversals are done.
-  PostStream post(s, nl > 1);
+  // With two buffer sets, a software pipeline over (sender chunk, input block) items: while
+  // item i's traversals run on the caller's stream and its lanes, the post stream
+  // re-lays out the weights and forms Xt = x W for item i + 1 in the other set, then runs
+  // item i's x_bar / W_bar GEMMs once its traversals are done.  With one set (a bounded
+  // workspace) the items run one after another on the caller's stream, input block by
+  // input block, each block in the largest sender chunks its state fits.
+  const bool pipelined = L.nsets > 1;
+  PostStream post(s, nl > 1 && pipelined);
   ETPC_HIP(post.status());
   const std::vector<int> order = block_order(p, d);
   struct Item {
     int64_t j0;
     int k;
+    int nsend;
   };
   std::vector<Item> items;
-  for (int64_t j0 = 0; j0 < N; j0 += chunk)
-    for (const int k : order) items.push_back(Item{j0, k});
+  if (!sch.bounded) {
+    for (int64_t j0 = 0; j0 < N; j0 += chunk)
+      for (const int k : order) items.push_back(Item{j0, k, static_cast<int>(std::min<int64_t>(chunk, N - j0))});
+  } else {
+    for (const int k : order) {
+      const int64_t ck = block_chunk(p, d, k, chunk, N, sch);
+      for (int64_t j0 = 0; j0 < N; j0 += ck) items.push_back(Item{j0, k, static_cast<int>(std::min<int64_t>(ck, N - j0))});
+    }
+  }
   // weight re-layouts and Xt of one item into buffer set `b`, on stream `st`
   auto prep = [&](const Item& it, int b, hipStream_t st) -> etpc_status {
     const int k = it.k;
     const int ni = 2 * p->in[k].l + 1;
     const int64_t ncols = d.block_ncols[k];
     const int c_in = p->in[k].mul;
-    const int nsend = static_cast<int>(std::min<int64_t>(chunk, N - it.j0));
+    const int nsend = it.nsend;
     WPrepArgs wa;
     if (want_pos || R.x_out) {
       wprep_args(p, d, k, R.w, want_pos ? L.wcat[b] : nullptr, R.x_out ? L.wt[b] : nullptr, wa);
@@ -656,29 +748,37 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     }
     return ETPC_OK;
   };
-  if (!items.empty()) {
+  if (pipelined && !items.empty()) {
     etpc_status st0 = prep(items[0], 0, s);
     if (st0 != ETPC_OK) return st0;
   }
-  // each lane's copy of the edge adjoint is first written by its first path of a chunk
+  // Each lane's copy of the edge adjoint is first written by its first path of a chunk.
+  // Block-major items (bounded) cover one sender range several times with different
+  // chunk boundaries, so there every copy starts at zero and every path accumulates.
   bool rbar_started[kLanes];
+  if (want_pos && sch.bounded && !R.rbar_acc)
+    ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(R.rbar, rbar_stride * nl, 0.f, s));
   int t_glob = 0;
   for (size_t ii = 0; ii < items.size(); ++ii) {
     const int64_t j0 = items[ii].j0;
     const int k = items[ii].k;
-    const int set = static_cast<int>(ii & 1);
+    const int set = pipelined ? static_cast<int>(ii & 1) : 0;
     if (ii == 0 || j0 != items[ii - 1].j0) {
-      for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc;
+      for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc || sch.bounded;
       t_glob = 0;
     }
-    const int nsend = static_cast<int>(std::min<int64_t>(chunk, N - j0));
+    const int nsend = items[ii].nsend;
     {
       const auto& paths = p->by_in[k];
       const int64_t ncols = d.block_ncols[k];
       const int c_in = p->in[k].mul;
+      if (!pipelined) {
+        etpc_status stp = prep(items[ii], 0, s);
+        if (stp != ETPC_OK) return stp;
+      }
       // the next item's weights and Xt go into the other set, behind the post work of
       // the item that last used it
-      if (ii + 1 < items.size()) {
+      if (pipelined && ii + 1 < items.size()) {
         // the previous item's traversals (which read that set's Xt) are enqueued before
         // this point: the post stream waits for them first
         ETPC_HIP(post.follow());
@@ -850,16 +950,19 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
 etpc_status forward_impl(const etpc_plan_s* p, const etpc_graph* g, const float* x, const float* pos, const float* w,
                          float* z, void* ws, size_t ws_bytes, int nl, hipStream_t s) {
   const Derived d = derive(p);
-  const int64_t chunk = pick_chunk(g->n_nodes, ws_bytes, [&](int64_t c) { return fwd_bytes(p, d, c); });
+  Sched sch;
+  int64_t chunk = 0;
+  choose_schedule(p, g->n_nodes, g->n_edges, ws_bytes, [&](int64_t c, const Sched& sc) { return fwd_bytes(p, d, c, sc); },
+                  &sch, &chunk);
   if (p->mode == ETPC_UVW) {
-    etpc_status st = check_ws(ws, ws_bytes, fwd_bytes(p, d, 1));
+    etpc_status st = check_ws(ws, ws_bytes, fwd_bytes(p, d, 1, sch));
     if (st != ETPC_OK) return st;
   }
   Carver c{static_cast<char*>(ws), 0};
   FwdLayout L;
-  fwd_layout(p, d, std::max<int64_t>(chunk, 0), c, L);
+  fwd_layout(p, d, std::max<int64_t>(chunk, 0), sch, c, L);
   ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached(p, z, g->n_nodes, s));
-  if (p->mode == ETPC_UVW) return fwd_uvw_run(p, d, g, x, pos, nullptr, w, z, false, false, L, chunk, nl, s);
+  if (p->mode == ETPC_UVW) return fwd_uvw_run(p, d, g, x, pos, nullptr, w, z, false, false, L, chunk, sch, nl, s);
   return fwd_uvu_run(p, g, x, pos, nullptr, w, z, false, false, nl, s);
 }
 
@@ -904,23 +1007,25 @@ etpc_status etpc_workspace_size(etpc_plan p, int32_t pass, int32_t n_nodes, int6
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "unknown pass");
   const Derived d = derive(p);
   // uvu keeps no node state: its layout depends on the persistent grid, not on a chunk
-  auto bytes_of = [&](int64_t c) -> size_t {
+  auto bytes_of = [&](int64_t c, const Sched& sc) -> size_t {
     const int64_t chunk = p->mode == ETPC_UVW ? c : kUvuGrid;
-    if (pass == ETPC_PASS_FWD) return fwd_bytes(p, d, chunk);
-    if (pass == ETPC_PASS_BWD) return bwd_bytes(p, d, n_edges, chunk);
-    return dbl_bytes(p, d, n_edges, chunk);
+    if (pass == ETPC_PASS_FWD) return fwd_bytes(p, d, chunk, sc);
+    if (pass == ETPC_PASS_BWD) return bwd_bytes(p, d, n_nodes, n_edges, chunk, sc);
+    return dbl_bytes(p, d, n_nodes, n_edges, chunk, sc);
   };
-  const size_t full = bytes_of(n_nodes);
+  const size_t full = bytes_of(n_nodes, fast_sched(p));
   if (budget == 0 || full <= budget || n_nodes == 0) {
     *bytes = full;
     return ETPC_OK;
   }
-  const int64_t chunk = pick_chunk(n_nodes, budget, bytes_of);
+  Sched sch;
+  int64_t chunk = 0;
+  choose_schedule(p, n_nodes, n_edges, budget, bytes_of, &sch, &chunk);
   if (chunk < 1) {
-    *bytes = bytes_of(1);
+    *bytes = bytes_of(1, sch);
     ETPC_FAIL(ETPC_ERR_WORKSPACE, "budget below the pass's minimum of " + std::to_string(*bytes) + " bytes");
   }
-  *bytes = bytes_of(chunk);
+  *bytes = bytes_of(chunk, sch);
   return ETPC_OK;
 }
 
@@ -1043,8 +1148,9 @@ etpc_status etpc_forward_noalloc(etpc_plan p, const etpc_graph* g, const float* 
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null x, pos, w or z");
   if (p->mode == ETPC_UVU) return forward_impl(p, g, x, pos, w, z, nullptr, 0, 1, s);   // no scratch
   const Derived d = derive(p);
-  if (fwd_bytes(p, d, 1) > kStaticScratchBytes)
-    ETPC_FAIL(ETPC_ERR_WORKSPACE, "one receiver's state (" + std::to_string(fwd_bytes(p, d, 1)) +
+  const size_t one = fwd_bytes(p, d, 1, bounded_sched(p, g->n_edges, kStaticScratchBytes));
+  if (one > kStaticScratchBytes)
+    ETPC_FAIL(ETPC_ERR_WORKSPACE, "one receiver's state (" + std::to_string(one) +
                                       " bytes) exceeds the fixed scratch of " +
                                       std::to_string(kStaticScratchBytes) + " bytes");
   void* ptr = nullptr;
@@ -1067,26 +1173,29 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
   const Derived d = derive(p);
   const bool want_pos = pos_bar != nullptr;
   const bool need_p = x_bar || w_bar;
-  const int lanes = rbar_lanes(p, g);
   const int32_t N = g->n_nodes;
   if (N == 0) {
     if (w_bar) ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(w_bar, p->w_numel, 0.f, s));
     return ETPC_OK;
   }
-  auto bytes_of = [&](int64_t c) {
+  auto bytes_of = [&](int64_t c, const Sched& sc) {
     Carver cv;
     BwdLayout L;
-    bwd_layout(p, d, g->n_edges, p->mode == ETPC_UVW ? c : kUvuGrid, want_pos, need_p, false, w_bar != nullptr,
-               false, x_bar != nullptr, false, cv, L);
+    bwd_layout(p, d, N, g->n_edges, p->mode == ETPC_UVW ? c : kUvuGrid, sc, want_pos, need_p, false,
+               w_bar != nullptr, false, x_bar != nullptr, false, cv, L);
     return cv.off;
   };
-  const int64_t chunk = pick_chunk(N, ws_bytes, bytes_of);
-  st = check_ws(ws, ws_bytes, bytes_of(1));
+  Sched sch;
+  int64_t chunk = 0;
+  choose_schedule(p, N, g->n_edges, ws_bytes, bytes_of, &sch, &chunk);
+  st = check_ws(ws, ws_bytes, bytes_of(1, sch));
   if (st != ETPC_OK) return st;
+  // concurrent lanes = edge-adjoint copies the schedule keeps
+  const int lanes = want_pos ? std::min(rbar_lanes(p, g), sch.rbar_copies) : rbar_lanes(p, g);
   Carver cv{static_cast<char*>(ws), 0};
   BwdLayout L;
-  bwd_layout(p, d, g->n_edges, p->mode == ETPC_UVW ? chunk : kUvuGrid, want_pos, need_p, false, w_bar != nullptr,
-             false, x_bar != nullptr, false, cv, L);
+  bwd_layout(p, d, N, g->n_edges, p->mode == ETPC_UVW ? chunk : kUvuGrid, sch, want_pos, need_p, false,
+             w_bar != nullptr, false, x_bar != nullptr, false, cv, L);
   if (p->mode == ETPC_UVW) {
     UvwBwdReq R{};
     R.lanes = lanes;
@@ -1095,7 +1204,7 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
     R.x_out = x_bar;
     R.w_out = w_bar;
     R.rbar = want_pos ? L.rbar : nullptr;
-    st = bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, s);
+    st = bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, sch, s);
   } else {
     UvuBwdReq R{};
     R.lanes = lanes;
@@ -1135,27 +1244,29 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     return ETPC_OK;
   }
   const bool want_pos = pos_grad != nullptr;
-  const int lanes = rbar_lanes(p, g);
   const Derived d = derive(p);
   const bool tan = pos_dot != nullptr;
   const bool plain = x_dot != nullptr || w_dot != nullptr;
-  auto bytes_of = [&](int64_t c) {
+  auto bytes_of = [&](int64_t c, const Sched& sc) {
     Carver cv;
     BwdLayout L;
     const int64_t ch = p->mode == ETPC_UVW ? c : kUvuGrid;
-    bwd_layout(p, d, g->n_edges, ch, want_pos, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
+    bwd_layout(p, d, N, g->n_edges, ch, sc, want_pos, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
                x_grad && w_dot && tan, cv, L);
-    return std::max(cv.off, z_bar_grad ? fwd_bytes(p, d, c) : size_t(0));
+    return std::max(cv.off, z_bar_grad ? fwd_bytes(p, d, c, sc) : size_t(0));
   };
-  const int64_t chunk = pick_chunk(N, ws_bytes, bytes_of);
-  st = check_ws(ws, ws_bytes, bytes_of(1));
+  Sched sch;
+  int64_t chunk = 0;
+  choose_schedule(p, N, g->n_edges, ws_bytes, bytes_of, &sch, &chunk);
+  st = check_ws(ws, ws_bytes, bytes_of(1, sch));
   if (st != ETPC_OK) return st;
+  const int lanes = want_pos ? std::min(rbar_lanes(p, g), sch.rbar_copies) : rbar_lanes(p, g);
 
   // d/dz_bar = z_dot = J_pos pos_dot + J_x x_dot + J_W w_dot (forward tangents)
   if (z_bar_grad) {
     Carver cv{static_cast<char*>(ws), 0};
     FwdLayout L;
-    fwd_layout(p, d, chunk, cv, L);
+    fwd_layout(p, d, chunk, sch, cv, L);
     if (!tan && !plain) {
       ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(z_bar_grad, static_cast<int64_t>(N) * p->z_dim, 0.f, s));
     } else {
@@ -1176,7 +1287,8 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
           win = w_dot;
         }
         if (p->mode == ETPC_UVW)
-          st = fwd_uvw_run(p, d, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, L, chunk, lane_cap(p, g), s);
+          st = fwd_uvw_run(p, d, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, L, chunk, sch, lane_cap(p, g),
+                           s);
         else
           st = fwd_uvu_run(p, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, lane_cap(p, g), s);
         if (st != ETPC_OK) return st;
@@ -1195,7 +1307,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     Carver cv{static_cast<char*>(ws), 0};
     BwdLayout L;
     const int64_t ch = p->mode == ETPC_UVW ? chunk : kUvuGrid;
-    bwd_layout(p, d, g->n_edges, ch, want_pos, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
+    bwd_layout(p, d, N, g->n_edges, ch, sch, want_pos, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
                x_grad && w_dot && tan, cv, L);
     if (p->mode == ETPC_UVW) {
       // d/dx = W^T dP + w_dot^T P ;  d/dW = x^T dP + x_dot^T P
@@ -1231,7 +1343,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
         R.x = x_dot ? x_dot : x;
         R.w = w_dot ? w_dot : w;
       }
-      return bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, s);
+      return bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, sch, s);
     }
     // uvu: tangent pass (pos_dot) then plain passes with w -> w_dot (x_grad) and x -> x_dot (w_grad)
     bool xs = false, wsd = false;
@@ -1289,7 +1401,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
   Carver cvp{static_cast<char*>(ws), 0};
   BwdLayout Lp;
   const int64_t chp = p->mode == ETPC_UVW ? chunk : kUvuGrid;
-  bwd_layout(p, d, g->n_edges, chp, true, false, false, false, false, false, false, cvp, Lp);
+  bwd_layout(p, d, N, g->n_edges, chp, sch, true, false, false, false, false, false, false, cvp, Lp);
   bool acc = false;
   for (int term = 0; term < 3; ++term) {
     const float* xin = x;
@@ -1314,7 +1426,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
       R.rbar = Lp.rbar;
       R.hess = hess;
       R.rbar_acc = acc;
-      st = bwd_uvw_run(p, d, g, pos, z_bar, R, Lp, chunk, s);
+      st = bwd_uvw_run(p, d, g, pos, z_bar, R, Lp, chunk, sch, s);
     } else {
       UvuBwdReq R{};
       R.lanes = lanes;

@@ -235,9 +235,11 @@ def test_noalloc_forward_refuses_oversized_state():
     the workspace query first, so the call below can only take the refusal path (its
     pointers are placeholders that nothing dereferences)."""
     import ctypes as C
-    huge = etpc.Plan("300000x0e+300000x1o", "4x0e+4x1o", 1, "uvw", "gaussian", 16, 0.0, 5.0)
-    one_receiver = etpc.etpc_workspace_size(huge, etpc.PASS_FWD, 1, 0)
-    assert one_receiver > (128 << 20)
+    huge = etpc.Plan("600000x0e+600000x1o", "4x0e+4x1o", 1, "uvw", "gaussian", 16, 0.0, 5.0)
+    # the smallest forward workspace of any schedule: a one-byte budget is refused with it
+    one_receiver = C.c_size_t()
+    st = etpc.lib.etpc_workspace_size(huge.handle, etpc.PASS_FWD, 1, 0, 1, C.byref(one_receiver))
+    assert st == 4 and one_receiver.value > (128 << 20)
     g = _binding.etpc_graph()
     g.n_nodes, g.n_edges = 1, 0
     g.rowptr = g.s_rowptr = 4096

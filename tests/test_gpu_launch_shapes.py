@@ -8,8 +8,9 @@ instantiations.  The cases here reach those paths with the oracle still affordab
 - workload 2 and 5 recipes at N = 600 (1200 waves per launch, above the split limit of
   1024, so every traversal runs unsplit): forward, backward with every element of
   W_bar, and workload 5's force double backward;
-- the same graphs with a fraction of the full workspace (node chunks, and for the
-  backward the two-set block pipeline over several chunks);
+- the same graphs with a fraction of the full workspace, and with workspaces sized by a
+  scratch budget (the bounded schedule: one buffer set, node chunks per output group or
+  input block, one or two edge-adjoint copies);
 - a channelwise (uvu) graph of 4096 nodes, so each of the 2048 persistent backward
   workgroups strides over two senders and sums W_bar partials over both;
 - workload 2 at its full size (N = 4096, E = 214,980): z, x_bar, W_bar and pos_bar
@@ -91,10 +92,34 @@ def test_cfg2_chunked_workspace(cfg2_600):
     _check_fwd_bwd(etpc, c, rz, rb, ws_f, ws_b, tag=" (chunked)")
 
 
+@pytest.mark.parametrize("name,n,d,budget_mib", [("cfg2", 600, None, 24), ("cfg4_d64", 300, 64, 3)])
+def test_budgeted_workspace(name, n, d, budget_mib, cfg2_600):
+    """Workspaces sized by a scratch budget well below the full size run the bounded
+    schedule (one buffer set, per-group / per-block node chunks): workload 2 at 24 MiB
+    keeps an edge-adjoint copy per lane; the edge-sweep recipe at 3 MiB keeps one copy and
+    one lane.  Forward and backward against the oracle."""
+    etpc = _etpc()
+    if name == "cfg2":
+        c, rz, rb = cfg2_600
+    else:
+        c = make_case(small_variant(name, n, d))
+        note(f"{c.cfg.name}: N={c.cfg.n_nodes} E={c.wl.n_edges}, oracle forward + backward")
+        rz, rb = _oracle_fwd_bwd(c)
+    N, E = c.cfg.n_nodes, c.wl.n_edges
+    budget = budget_mib << 20
+    sizes = [etpc.etpc_workspace_size(c.plan, p_, N, E, budget) for p_ in (etpc.PASS_FWD, etpc.PASS_BWD)]
+    full = [etpc.etpc_workspace_size(c.plan, p_, N, E) for p_ in (etpc.PASS_FWD, etpc.PASS_BWD)]
+    note(f"{c.cfg.name}: budget {budget_mib} MiB -> fwd {sizes[0] / 2**20:.1f} MiB (full {full[0] / 2**20:.1f}), "
+         f"bwd {sizes[1] / 2**20:.1f} MiB (full {full[1] / 2**20:.1f})")
+    assert all(sz <= budget for sz in sizes) and full[1] > 2 * budget
+    ws_f, ws_b = (torch.empty(sz, dtype=torch.uint8, device="cuda") for sz in sizes)
+    _check_fwd_bwd(etpc, c, rz, rb, ws_f, ws_b, tag=f" (budget {budget_mib} MiB)")
+
+
 @pytest.mark.timeout(600)
 def test_cfg5_unsplit_double_backward():
     """Workload 5's force step at N = 600: forward, backward, and the double backward of
-    L = <c, F> (F = -pos_bar) along pos_dot = -c, whole and with a third of the workspace."""
+    L = <c, F> (F = -pos_bar) along pos_dot = -c, whole and with a 16 MiB scratch budget."""
     etpc = _etpc()
     cfg = small_variant("cfg5", 600)
     c = make_case(cfg)
@@ -106,8 +131,8 @@ def test_cfg5_unsplit_double_backward():
     pd_np = -wl.force_c.astype(np.float64)
     ref = conv.double_backward(c.spec, wl.x, wl.pos, wl.w, wl.src, wl.dst, wl.z_bar, pos_dot=pd_np)
     pos_dot = torch.from_numpy(-wl.force_c).cuda()
-    full = etpc.etpc_workspace_size(c.plan, etpc.PASS_DBL, cfg.n_nodes, wl.n_edges)
-    for tag, ws in (("", None), (" (chunked)", torch.empty(full // 3, dtype=torch.uint8, device="cuda"))):
+    small = etpc.etpc_workspace_size(c.plan, etpc.PASS_DBL, cfg.n_nodes, wl.n_edges, 16 << 20)
+    for tag, ws in (("", None), (" (16 MiB budget)", torch.empty(small, dtype=torch.uint8, device="cuda"))):
         got = etpc.etpc_double_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, pos_dot=pos_dot, ws=ws)
         torch.cuda.synchronize()
         errs = tuple(rel_err(g, r) for g, r in zip(got, ref))

@@ -223,16 +223,21 @@ def test_determinism_and_chunked_workspace():
     b1 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar)
     b2 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar)
     assert torch.equal(z1, z2) and all(torch.equal(a, b) for a, b in zip(b1, b2))
-    # a workspace a fifth of the full size forces receiver/sender chunks
+    # a workspace a fifth of the full size runs the bounded schedule (receiver / sender
+    # chunks, fewer split-K partial slots): the same values up to summation order, and
+    # deterministic for that workspace
     full = etpc.etpc_workspace_size(c.plan, etpc.PASS_FWD, cfg.n_nodes, c.graph.n_edges)
     ws = torch.empty(full // 5, dtype=torch.uint8, device="cuda")
     z3 = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, ws=ws)
-    assert torch.equal(z3, z1)
+    z4 = etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, ws=ws)
+    assert torch.equal(z3, z4) and rel_err(z3, z1.double().cpu().numpy()) < 1e-5
     fullb = etpc.etpc_workspace_size(c.plan, etpc.PASS_BWD, cfg.n_nodes, c.graph.n_edges)
     wsb = torch.empty(fullb // 3, dtype=torch.uint8, device="cuda")
     b3 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, ws=wsb)
-    assert torch.equal(b3[0], b1[0]) and torch.equal(b3[2], b1[2])
-    assert rel_err(b3[1], b1[1].cpu().numpy()) < 1e-6
+    b4 = etpc.etpc_backward(c.plan, c.graph, c.x, c.pos, c.w, c.z_bar, ws=wsb)
+    assert all(torch.equal(u, v) for u, v in zip(b3, b4))
+    for u, v in zip(b3, b1):
+        assert rel_err(u, v.double().cpu().numpy()) < 1e-5
     with pytest.raises(etpc.EtpcError) as ei:
         etpc.etpc_forward(c.plan, c.graph, c.x, c.pos, c.w, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))
     assert ei.value.name == "WORKSPACE"
