@@ -164,24 +164,29 @@ int pick_splits(int64_t M, int64_t N, int64_t K) {
 constexpr int kGemmSplits = 8;   // split-K partial sets kept for the long-K channel / x_bar GEMMs
 
 // Up to two sets of the buffers the node-side GEMMs read (S forward; Xt, P and the
-// re-laid-out weights backward): groups / blocks alternate between them, so one set's
-// GEMMs can run on the post stream while the next traversals fill the other set.
+// re-laid-out weights backward): work items alternate between them, so one item's GEMMs
+// can run on the post stream while the next item's traversals fill the other set.
 constexpr int kSets = 2;
 
-// How a pass uses its workspace.
-//  fast (the workspace holds every node's state): one chunk of all nodes, two buffer sets,
-//    one edge-adjoint copy per concurrent lane, kGemmSplits split-K partial slots.
-//  bounded (less workspace than that, e.g. a scratch budget): one buffer set, node chunks
-//    sized separately for each output group (forward) or input block (backward) so that
-//    each fills the state buffer, two split-K partial slots, and one edge-adjoint copy per
-//    lane only while those copies take at most an eighth of the workspace (else one).
-//    The chunk passed to the layouts is the chunk of the largest group or block; a smaller
-//    one runs bigger chunks in the same buffer (group_chunk / block_chunk).
+// How a uvw pass uses its workspace.  The node-side state (forward: the receiver state S
+// of an output group, Eq. 33; backward: Xt and P of an input block) lives in `nsets`
+// buffers of `cap` floats each, and the pass runs as a list of work items (make_items)
+// that each fit one buffer.
+//  fast (the workspace holds every node's state of the largest group / block): one item
+//    per group or block, two buffer sets, one edge-adjoint copy per lane, kGemmSplits
+//    split-K partial slots.
+//  bounded (a smaller workspace, e.g. one sized by a scratch budget): a group's or
+//    block's paths are split into subsets whose state for every node fits a buffer, so
+//    every traversal launch still covers all nodes (Sobek Sec. 4 keeps complete output
+//    groups inside the scratch budget); only when one path's state for every node does
+//    not fit are the nodes chunked, one path at a time.  Two buffer sets while no node
+//    chunking is needed, else one; one edge-adjoint copy per lane only while those take
+//    at most an eighth of the workspace; split-K partials in a quarter of a buffer (the
+//    GEMMs take fewer splits to fit).
 struct Sched {
   bool bounded = false;
   int nsets = kSets;
   int rbar_copies = 1;
-  int part_slots = kGemmSplits;
 };
 
 Sched fast_sched(const etpc_plan_s* p) {
@@ -190,30 +195,89 @@ Sched fast_sched(const etpc_plan_s* p) {
   return s;
 }
 
-Sched bounded_sched(const etpc_plan_s* p, int64_t n_edges, size_t ws_bytes) {
-  Sched s;
-  s.bounded = true;
-  s.nsets = 1;
-  s.part_slots = 2;
-  const int slots = rbar_slots(p);
-  const size_t all = static_cast<size_t>(3 * sizeof(float)) * static_cast<size_t>(n_edges) * slots;
-  s.rbar_copies = (slots > 1 && all <= ws_bytes / 8) ? slots : 1;
-  return s;
+// One work item of a uvw pass: nodes [n0, n0 + nn) of output group (forward) or input
+// block (backward) `blk`, and its paths [t0, t1) (positions in by_out[blk] / by_in[blk]).
+// Their state columns [col0, col0 + ncols) of the group's or block's column space
+// ((path, q, channel) in plan order) sit in the item's buffer from column 0.
+struct Item {
+  int64_t n0;
+  int32_t nn;
+  int32_t blk, t0, t1;
+  int64_t col0, ncols;
+};
+
+// state columns of each path of a group (forward: B C_in) or block (backward: B C_out)
+std::vector<int64_t> path_cols(const etpc_plan_s* p, int blk, bool fwd) {
+  const auto& paths = fwd ? p->by_out[blk] : p->by_in[blk];
+  std::vector<int64_t> c(paths.size());
+  for (size_t t = 0; t < paths.size(); ++t) {
+    const PathInfo& pi = p->paths[paths[t]];
+    c[t] = static_cast<int64_t>(p->n_basis) * (fwd ? pi.c_in : pi.c_out);
+  }
+  return c;
 }
 
-// receivers per launch of output group g when the S buffer holds `chunk` receivers of the
-// largest group (bounded schedules; the fast schedule runs every node at once)
-int64_t group_chunk(const etpc_plan_s* p, const Derived& d, int g, int64_t chunk, int64_t n, const Sched& sch) {
-  if (!sch.bounded) return chunk;
-  const int64_t per = d.group_d[g] * (2 * p->out[g].l + 1);
-  return std::max<int64_t>(1, std::min<int64_t>(n, per > 0 ? chunk * d.max_s / per : n));
+// rows per node of a group's (forward, 2 l_out + 1) or block's (backward, 2 l_in + 1) state
+int state_rows(const etpc_plan_s* p, int blk, bool fwd) { return 2 * (fwd ? p->out[blk].l : p->in[blk].l) + 1; }
+
+std::vector<int> group_order(const etpc_plan_s* p, const Derived& d);
+std::vector<int> block_order(const etpc_plan_s* p, const Derived& d);
+
+std::vector<Item> make_items(const etpc_plan_s* p, const Derived& d, bool fwd, int64_t n, int64_t cap, bool bounded) {
+  std::vector<Item> items;
+  if (n <= 0) return items;
+  for (const int blk : fwd ? group_order(p, d) : block_order(p, d)) {
+    const std::vector<int64_t> cols = path_cols(p, blk, fwd);
+    const int np = static_cast<int>(cols.size());
+    const int64_t m = state_rows(p, blk, fwd);
+    int64_t total = 0, widest = 0;
+    for (const int64_t c : cols) {
+      total += c;
+      widest = std::max(widest, c);
+    }
+    if (!bounded || n * m * total <= cap) {
+      items.push_back(Item{0, static_cast<int32_t>(n), blk, 0, np, 0, total});
+      continue;
+    }
+    if (n * m * widest <= cap) {   // complete node ranges for subsets of the paths
+      int64_t col0 = 0;
+      for (int t0 = 0; t0 < np;) {
+        int t1 = t0;
+        int64_t c = 0;
+        while (t1 < np && n * m * (c + cols[t1]) <= cap) c += cols[t1++];
+        items.push_back(Item{0, static_cast<int32_t>(n), blk, t0, t1, col0, c});
+        col0 += c;
+        t0 = t1;
+      }
+      continue;
+    }
+    const int64_t nn = std::max<int64_t>(1, cap / (m * widest));   // node chunks of single paths
+    for (int64_t n0 = 0; n0 < n; n0 += nn) {
+      int64_t col0 = 0;
+      for (int t = 0; t < np; ++t) {
+        items.push_back(Item{n0, static_cast<int32_t>(std::min(nn, n - n0)), blk, t, t + 1, col0, cols[t]});
+        col0 += cols[t];
+      }
+    }
+  }
+  return items;
 }
 
-// senders per launch of input block k (likewise for the Xt / P buffers)
-int64_t block_chunk(const etpc_plan_s* p, const Derived& d, int k, int64_t chunk, int64_t n, const Sched& sch) {
-  if (!sch.bounded) return chunk;
-  const int64_t per = d.block_ncols[k] * (2 * p->in[k].l + 1);
-  return std::max<int64_t>(1, std::min<int64_t>(n, per > 0 ? chunk * d.max_state / per : n));
+// smallest buffer of a bounded schedule: one node of the widest path of any group / block
+int64_t min_cap(const etpc_plan_s* p, bool fwd, bool bwd) {
+  int64_t c = 0;
+  if (fwd)
+    for (size_t g = 0; g < p->out.size(); ++g)
+      for (const int64_t w : path_cols(p, static_cast<int>(g), true)) c = std::max(c, w * state_rows(p, g, true));
+  if (bwd)
+    for (size_t k = 0; k < p->in.size(); ++k)
+      for (const int64_t w : path_cols(p, static_cast<int>(k), false)) c = std::max(c, w * state_rows(p, k, false));
+  return c;
+}
+
+// buffer that holds every node's state of the largest group / block (the fast schedule)
+int64_t full_cap(const Derived& d, int64_t n, bool fwd, bool bwd) {
+  return n * std::max(fwd ? d.max_s : int64_t(0), bwd ? d.max_state : int64_t(0));
 }
 
 struct FwdLayout {
@@ -221,12 +285,16 @@ struct FwdLayout {
   float* part = nullptr;
   int64_t part_cap = 0;
   int nsets = kSets;
+  int64_t cap = 0;
 };
-void fwd_layout(const etpc_plan_s* p, const Derived& d, int64_t chunk, const Sched& sch, Carver& c, FwdLayout& L) {
+// n_nodes: the graph's node count (the fast schedule's split-K partials cover all of them)
+void fwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t cap, const Sched& sch, Carver& c,
+                FwdLayout& L) {
   L.nsets = sch.nsets;
+  L.cap = cap;
   if (p->mode == ETPC_UVW) {
-    for (int b = 0; b < sch.nsets; ++b) L.S[b] = c.take<float>(static_cast<size_t>(chunk * d.max_s));
-    L.part_cap = sch.part_slots * chunk * d.max_zrow;
+    for (int b = 0; b < sch.nsets; ++b) L.S[b] = c.take<float>(static_cast<size_t>(cap));
+    L.part_cap = sch.bounded ? cap / 4 : kGemmSplits * n_nodes * d.max_zrow;
     L.part = c.take<float>(static_cast<size_t>(L.part_cap));
   }
 }
@@ -241,15 +309,17 @@ struct BwdLayout {
   int64_t wpart_lane = 0;   // uvu: floats of W_bar partials per lane
   int nsets = kSets;
   int rbar_copies = 1;
+  int64_t cap = 0;
 };
 // flags: pos = edge adjoint (sch.rbar_copies copies) + Xt; p = plain P state; tan = tangent state; wbar = W_bar
-// partials (two sets when wbar2); wt2 = second transposed weight (for w_dot).  n_nodes bounds the per-block
-// chunks of a bounded schedule (the W_bar split count follows each block's chunk).
-void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t chunk,
+// partials (two sets when wbar2); wt2 = second transposed weight (for w_dot).  uvw: cap = floats per state
+// buffer; uvu: cap = the persistent grid size.
+void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t cap,
                 const Sched& sch, bool pos, bool need_p, bool tan, bool wbar, bool wbar2, bool xbar, bool wt2,
                 Carver& c, BwdLayout& L) {
   L.nsets = sch.nsets;
   L.rbar_copies = sch.rbar_copies;
+  L.cap = cap;
   if (p->mode == ETPC_UVW) {
     if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * sch.rbar_copies));
     for (int b = 0; b < sch.nsets; ++b) {
@@ -258,90 +328,131 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t
       if (wt2) L.wt2[b] = c.take<float>(static_cast<size_t>(d.max_wcat));
     }
     if (wbar) {
-      // split-K partial tiles of W_bar: as many splits as wbar_gemm picks for each block's chunk
+      // split-K partial tiles of W_bar: fast, as many splits as wbar_gemm picks for a whole
+      // block; bounded, four sets of the largest block or 32 of its widest path, whichever
+      // is more (an item of one path has few output tiles and needs more splits to fill the
+      // chip; wbar_gemm fits its splits to this room)
       int64_t need = 0;
       for (size_t k = 0; k < p->in.size(); ++k) {
         if (p->by_in[k].empty()) continue;
         const int ni = 2 * p->in[k].l + 1;
-        const int64_t ck = block_chunk(p, d, static_cast<int>(k), std::max<int64_t>(chunk, 1),
-                                       std::max<int64_t>(n_nodes, 1), sch);
-        const int sp = pick_splits(p->in[k].mul, d.block_ncols[k], ck * ni);
-        need = std::max<int64_t>(need, static_cast<int64_t>(sp) * p->in[k].mul * d.block_ncols[k]);
+        const int64_t blockw = static_cast<int64_t>(p->in[k].mul) * d.block_ncols[k];
+        if (sch.bounded) {
+          int64_t widest = 0;
+          for (const int64_t w : path_cols(p, static_cast<int>(k), false)) widest = std::max(widest, w);
+          need = std::max<int64_t>(need, std::max<int64_t>(4 * blockw, 32 * p->in[k].mul * widest));
+        } else {
+          need = std::max<int64_t>(
+              need, pick_splits(p->in[k].mul, d.block_ncols[k], std::max<int64_t>(n_nodes, 1) * ni) * blockw);
+        }
       }
       L.wpart_cap = (wbar2 ? 2 : 1) * need;
       L.wpart = c.take<float>(static_cast<size_t>(L.wpart_cap));
     }
     for (int b = 0; b < sch.nsets; ++b) {
-      if (pos) L.xt[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
-      if (need_p) L.P[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
-      if (tan) L.Pd[b] = c.take<float>(static_cast<size_t>(chunk * d.max_state));
+      if (pos) L.xt[b] = c.take<float>(static_cast<size_t>(cap));
+      if (need_p) L.P[b] = c.take<float>(static_cast<size_t>(cap));
+      if (tan) L.Pd[b] = c.take<float>(static_cast<size_t>(cap));
     }
     if (xbar) {
-      L.xpart_cap = sch.part_slots * chunk * d.max_xrow;
+      L.xpart_cap = sch.bounded ? cap / 4 : kGemmSplits * n_nodes * d.max_xrow;
       L.xpart = c.take<float>(static_cast<size_t>(L.xpart_cap));
     }
   } else {
     if (pos) L.rbar = c.take<float>(static_cast<size_t>(3 * n_edges * sch.rbar_copies));
     int64_t maxbc = 0;
     for (auto& q : p->paths) maxbc = std::max<int64_t>(maxbc, static_cast<int64_t>(p->n_basis) * q.c_in);
-    L.wpart_lane = chunk * maxbc;   // chunk = uvu grid size here; one partial set per lane
+    L.wpart_lane = cap * maxbc;   // cap = uvu grid size here; one partial set per lane
     if (wbar) L.wpart = c.take<float>(static_cast<size_t>(L.wpart_lane * rbar_slots(p)));
   }
 }
 
 constexpr int kUvuGrid = 2048;
 
-size_t fwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t chunk, const Sched& sch) {
+size_t fwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t cap, const Sched& sch) {
   Carver c;
   FwdLayout L;
-  fwd_layout(p, d, chunk, sch, c, L);
+  fwd_layout(p, d, n_nodes, cap, sch, c, L);
   return c.off;
 }
 
-size_t bwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t chunk,
+size_t bwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t cap,
                  const Sched& sch) {
   Carver c;
   BwdLayout L;
-  bwd_layout(p, d, n_nodes, n_edges, chunk, sch, true, true, false, true, false, true, false, c, L);
+  bwd_layout(p, d, n_nodes, n_edges, p->mode == ETPC_UVW ? cap : kUvuGrid, sch, true, true, false, true, false, true,
+             false, c, L);
   return c.off;
 }
 
-size_t dbl_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t chunk,
+size_t dbl_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t n_edges, int64_t cap,
                  const Sched& sch) {
   Carver c;
   BwdLayout L;
-  bwd_layout(p, d, n_nodes, n_edges, chunk, sch, true, true, true, true, true, true, true, c, L);   // every output
-  return std::max(c.off, fwd_bytes(p, d, chunk, sch));
+  bwd_layout(p, d, n_nodes, n_edges, p->mode == ETPC_UVW ? cap : kUvuGrid, sch, true, true, true, true, true, true,
+             true, c, L);   // every output
+  return std::max(c.off, fwd_bytes(p, d, n_nodes, cap, sch));
 }
 
-// largest chunk in [1, n] whose layout fits
+// The schedule and state buffer size of a uvw pass given ws_bytes of workspace:
+// bytes_of(cap, sched) is the pass's layout size; fwd / bwd say which state the pass keeps.
+// The fast schedule when every node fits at once; else the bounded one with the largest
+// buffer that fits (two sets while that needs no node chunks); cap = -1 when not even
+// one node of one path fits.  uvu passes keep no node state (cap unused).
 template <class F>
-int64_t pick_chunk(int64_t n, size_t ws_bytes, F bytes_of) {
-  if (n <= 0) return 0;
-  if (bytes_of(n) <= ws_bytes) return n;
-  const size_t b0 = bytes_of(0), b1 = bytes_of(1);
-  if (b1 > ws_bytes) return -1;
-  const size_t per = std::max<size_t>(1, b1 - b0);
-  int64_t c = std::min<int64_t>(n, static_cast<int64_t>((ws_bytes - b0) / per));
-  while (c > 1 && bytes_of(c) > ws_bytes) --c;
-  return std::max<int64_t>(c, 1);
-}
-
-// The schedule and node chunk of a call given ws_bytes of workspace: the fast schedule
-// when every node fits at once, else the bounded one with its largest chunk that fits
-// (-1 when not even one node does).  bytes_of(chunk, sched) is the call's layout size.
-template <class F>
-void choose_schedule(const etpc_plan_s* p, int64_t n_nodes, int64_t n_edges, size_t ws_bytes, F bytes_of,
-                     Sched* sch, int64_t* chunk) {
+void choose_schedule(const etpc_plan_s* p, const Derived& d, bool fwd, bool bwd, int64_t n_nodes, int64_t n_edges,
+                     size_t ws_bytes, F bytes_of, Sched* sch, int64_t* cap) {
   const Sched f = fast_sched(p);
-  if (n_nodes <= 0 || bytes_of(n_nodes, f) <= ws_bytes) {
+  const int64_t cfull = p->mode == ETPC_UVW ? full_cap(d, n_nodes, fwd, bwd) : 0;
+  if (n_nodes <= 0 || bytes_of(cfull, f) <= ws_bytes) {
     *sch = f;
-    *chunk = n_nodes;
+    *cap = cfull;
     return;
   }
-  const Sched b = bounded_sched(p, n_edges, ws_bytes);
+  Sched b;
+  b.bounded = true;
+  const int slots = rbar_slots(p);
+  const size_t all = static_cast<size_t>(3 * sizeof(float)) * static_cast<size_t>(n_edges) * slots;
+  b.rbar_copies = (slots > 1 && all <= ws_bytes / 8) ? slots : 1;
+  if (p->mode != ETPC_UVW) {
+    b.nsets = 1;
+    *sch = b;
+    *cap = bytes_of(0, b) <= ws_bytes ? 0 : -1;
+    return;
+  }
+  // largest buffer in [lo, hi] that fits (bytes_of grows with cap)
+  auto largest = [&](const Sched& sc) -> int64_t {
+    int64_t lo = min_cap(p, fwd, bwd), hi = cfull;
+    if (bytes_of(lo, sc) > ws_bytes) return -1;
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo + 1) / 2;
+      if (bytes_of(mid, sc) <= ws_bytes)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    return lo;
+  };
+  // two sets while each set still holds the widest path's state for every node
+  int64_t need_all = 0;
+  if (fwd)
+    for (size_t g = 0; g < p->out.size(); ++g)
+      for (const int64_t w : path_cols(p, static_cast<int>(g), true))
+        need_all = std::max(need_all, n_nodes * w * state_rows(p, g, true));
+  if (bwd)
+    for (size_t k = 0; k < p->in.size(); ++k)
+      for (const int64_t w : path_cols(p, static_cast<int>(k), false))
+        need_all = std::max(need_all, n_nodes * w * state_rows(p, k, false));
+  b.nsets = 2;
+  int64_t c2 = largest(b);
+  if (c2 >= need_all) {
+    *sch = b;
+    *cap = c2;
+    return;
+  }
+  b.nsets = 1;
   *sch = b;
-  *chunk = pick_chunk(n_nodes, ws_bytes, [&](int64_t c) { return bytes_of(c, b); });
+  *cap = largest(b);
 }
 
 RowMap plain(int64_t ld) { return make_rowmap(ld, 0, 1); }
@@ -480,74 +591,78 @@ std::vector<int> block_order(const etpc_plan_s* p, const Derived& d) {
 // nl: concurrent lanes the call may use (lane_cap, or 1 to stay on the caller's stream).
 etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* xin,
                         const float* pos, const float* pos_dot, const float* win, float* z, bool beta, bool tangent,
-                        const FwdLayout& L, int64_t chunk, const Sched& sch, int nl, hipStream_t s) {
+                        const FwdLayout& L, const Sched& sch, int nl, hipStream_t s) {
   const GeomParams geom = p->geom();
   const int32_t N = g->n_nodes;
-  // the channel GEMM of one group runs on the post stream while the next group's
-  // traversals fill the other S set; the largest GEMMs go first, so they overlap most
+  // the channel GEMM of one item runs on the post stream while the next item's
+  // traversals fill the other S set; the largest groups go first, so they overlap most
   PostStream post(s, nl > 1);
   ETPC_HIP(post.status());
   int set = 0;
-  for (const int gi : group_order(p, d)) {
+  for (const Item& it : make_items(p, d, true, N, L.cap, sch.bounded)) {
+    const int gi = it.blk;
     const auto& paths = p->by_out[gi];
     const int no = 2 * p->out[gi].l + 1;
-    const int64_t D = d.group_d[gi];
     const int c_out = p->out[gi].mul;
-    const int64_t cg = group_chunk(p, d, gi, chunk, N, sch);
-    for (int64_t r0 = 0; r0 < N; r0 += cg) {
-      const int nrecv = static_cast<int>(std::min<int64_t>(cg, N - r0));
-      ETPC_HIP(post.wait_slot(set));
-      int32_t col0 = 0;
-      // the paths of a group fill disjoint column ranges of S: concurrent lanes
-      LaneGroup lanes(s, std::min(static_cast<int>(paths.size()), nl));
-      ETPC_HIP(lanes.status());
-      for (size_t t = 0; t < paths.size(); ++t) {
-        const PathInfo& pi = p->paths[paths[t]];
-        FwdUvwArgs a{};
-        a.rowptr = g->rowptr;
-        a.col = g->col;
-        a.pos = pos;
-        a.pos_dot = pos_dot;
-        a.x = xin;
-        a.S = L.S[set];
-        a.recv0 = static_cast<int32_t>(r0);
-        a.order = (g->r_order != nullptr && r0 == 0 && nrecv == g->n_nodes) ? g->r_order : nullptr;
-        a.x_dim = static_cast<int32_t>(p->x_dim);
-        a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
-        int ntiles = 1;
-        a.cp = lane_width(pi.c_in, &ntiles, 4);   // 4-lane matrix-core blocks never mix edges
-        a.c_in = pi.c_in;
-        a.ls = pi.l_sh;
-        a.s_row_stride = D;
-        a.s_col0 = col0;
-        // one workgroup per (receiver, channel tile): the tiles are separate workgroups
-        a.nparts = edge_parts(nrecv * ntiles, 1, g, pi.l_out, p->n_basis, 1);
-        a.g = geom;
-        a.cg = pi.cgf;
-        const hipStream_t ls = lanes.lane(static_cast<int>(t));
-        ETPC_LAUNCH_ON(ETPC_KIND_FWD_TRAVERSE, ls, launch_fwd_uvw(a, tangent, pi.l_in, pi.l_out, nrecv, ntiles, ls));
-        col0 += p->n_basis * pi.c_in;
+    const int nrecv = it.nn;
+    ETPC_HIP(post.wait_slot(set));
+    // the item's paths fill disjoint column ranges of S: concurrent lanes
+    LaneGroup lanes(s, std::min(it.t1 - it.t0, nl));
+    ETPC_HIP(lanes.status());
+    int64_t col0 = 0;
+    for (int t = 0; t < it.t1; ++t) {
+      const PathInfo& pi = p->paths[paths[t]];
+      const int64_t cols = static_cast<int64_t>(p->n_basis) * pi.c_in;
+      if (t < it.t0) {
+        col0 += cols;
+        continue;
       }
-      ETPC_HIP(lanes.finish());
-      ETPC_HIP(post.follow());
-      GemmArgs ga{};
-      ga.lowp = p->gemm_precision;
-      ga.A = L.S[set];
-      ga.amap = plain(D);
-      ga.a_mcontig = 0;
-      ga.B = win + p->paths[paths[0]].w_off;
-      ga.ldb = c_out;
-      ga.C = z + r0 * p->z_dim + p->zoff[gi];
-      ga.cmap = irmul(no, p->z_dim, c_out);
-      ga.beta = beta ? 1 : 0;
-      ga.M = nrecv * no;
-      ga.N = c_out;
-      ga.K = static_cast<int32_t>(D);
-      etpc_status st = gemm_auto(ga, L.part, L.part_cap, kGemmSplits, ETPC_KIND_CHANNEL_GEMM, post.stream());
-      if (st != ETPC_OK) return st;
-      ETPC_HIP(post.mark(set));
-      if (L.nsets > 1) set ^= 1;
+      FwdUvwArgs a{};
+      a.rowptr = g->rowptr;
+      a.col = g->col;
+      a.pos = pos;
+      a.pos_dot = pos_dot;
+      a.x = xin;
+      a.S = L.S[set];
+      a.recv0 = static_cast<int32_t>(it.n0);
+      a.order = (g->r_order != nullptr && it.n0 == 0 && nrecv == g->n_nodes) ? g->r_order : nullptr;
+      a.x_dim = static_cast<int32_t>(p->x_dim);
+      a.xoff = static_cast<int32_t>(p->xoff[pi.in_block]);
+      int ntiles = 1;
+      a.cp = lane_width(pi.c_in, &ntiles, 4);   // 4-lane matrix-core blocks never mix edges
+      a.c_in = pi.c_in;
+      a.ls = pi.l_sh;
+      a.s_row_stride = it.ncols;
+      a.s_col0 = static_cast<int32_t>(col0 - it.col0);
+      // one workgroup per (receiver, channel tile): the tiles are separate workgroups
+      a.nparts = edge_parts(nrecv * ntiles, 1, g, pi.l_out, p->n_basis, 1);
+      a.g = geom;
+      a.cg = pi.cgf;
+      const hipStream_t ls = lanes.lane(t - it.t0);
+      ETPC_LAUNCH_ON(ETPC_KIND_FWD_TRAVERSE, ls, launch_fwd_uvw(a, tangent, pi.l_in, pi.l_out, nrecv, ntiles, ls));
+      col0 += cols;
     }
+    ETPC_HIP(lanes.finish());
+    ETPC_HIP(post.follow());
+    // z rows of the item's receivers (+)= S W over the item's paths: the first path subset
+    // of a node range writes (unless the caller accumulates), later ones add
+    GemmArgs ga{};
+    ga.lowp = p->gemm_precision;
+    ga.A = L.S[set];
+    ga.amap = plain(it.ncols);
+    ga.a_mcontig = 0;
+    ga.B = win + p->paths[paths[it.t0]].w_off;
+    ga.ldb = c_out;
+    ga.C = z + it.n0 * p->z_dim + p->zoff[gi];
+    ga.cmap = irmul(no, p->z_dim, c_out);
+    ga.beta = (beta || it.t0 > 0) ? 1 : 0;
+    ga.M = nrecv * no;
+    ga.N = c_out;
+    ga.K = static_cast<int32_t>(it.ncols);
+    etpc_status st = gemm_auto(ga, L.part, L.part_cap, kGemmSplits, ETPC_KIND_CHANNEL_GEMM, post.stream());
+    if (st != ETPC_OK) return st;
+    ETPC_HIP(post.mark(set));
+    if (L.nsets > 1) set ^= 1;
   }
   ETPC_HIP(post.finish());
   return ETPC_OK;
@@ -625,16 +740,23 @@ void wprep_args(const etpc_plan_s* p, const Derived& d, int k, const float* w, f
   }
 }
 
-// W_out block k (+)= A^T S_state (split-K over the chunk's rows), partials at wpart + slot
-hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float* xa, int64_t j0, int nsend,
-                     const float* state, float* wpart, int* splits_out, hipStream_t s) {
+// W_bar split-K partials of an item: wpart[split] = x^T state over the item's sender rows,
+// for the item's ncols state columns; at most max_floats of partials (fewer splits if
+// needed, at least one)
+hipError_t wbar_gemm(const etpc_plan_s* p, int k, const float* xa, int64_t j0, int nsend, const float* state,
+                     int64_t ncols, float* wpart, int64_t max_floats, int* splits_out, hipStream_t s) {
   const int ni = 2 * p->in[k].l + 1;
-  const int64_t ncols = d.block_ncols[k];
   const int c_in = p->in[k].mul;
   const int64_t K = static_cast<int64_t>(nsend) * ni;
-  const int sp = pick_splits(c_in, ncols, K);
+  // enough splits for about 1024 workgroups, at least 256 rows of K each (not capped at
+  // kMaxSplits: an item of one path has few output tiles), within the partials' room
+  const int64_t tiles = ((c_in + 63) / 64) * ((ncols + 63) / 64);
+  int sp = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((1024 + tiles - 1) / tiles, (K + 255) / 256)));
+  const int64_t per = static_cast<int64_t>(c_in) * ncols;
+  sp = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(sp, max_floats / per)));
   int64_t ks = (K + sp - 1) / sp;
   ks = (ks + kGemmBK - 1) / kGemmBK * kGemmBK;
+  sp = static_cast<int>((K + ks - 1) / ks);
   GemmArgs ga{};
   ga.lowp = p->gemm_precision;
   ga.A = xa + j0 * p->x_dim + p->xoff[k];
@@ -649,16 +771,17 @@ hipError_t wbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float*
   ga.N = static_cast<int32_t>(ncols);
   ga.K = static_cast<int32_t>(K);
   ga.k_split = static_cast<int32_t>(ks);
-  ga.c_split_stride = static_cast<int64_t>(c_in) * ncols;
+  ga.c_split_stride = per;
   set_vec4(ga);
   *splits_out = sp;
   return launch_gemm(ga, sp, s);
 }
 
-etpc_status xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float* state, const float* wt, float* xo,
+// x_bar rows of an item (+)= state W^T over its ncols state columns (wt: the item's first
+// row of the block's transposed weights)
+etpc_status xbar_gemm(const etpc_plan_s* p, int k, const float* state, int64_t ncols, const float* wt, float* xo,
                       int64_t j0, int nsend, bool beta, const BwdLayout& L, hipStream_t s) {
   const int ni = 2 * p->in[k].l + 1;
-  const int64_t ncols = d.block_ncols[k];
   const int c_in = p->in[k].mul;
   GemmArgs ga{};
   ga.lowp = p->gemm_precision;
@@ -677,8 +800,7 @@ etpc_status xbar_gemm(const etpc_plan_s* p, const Derived& d, int k, const float
 }
 
 etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph* g, const float* pos,
-                        const float* z_bar, const UvwBwdReq& R, const BwdLayout& L, int64_t chunk, const Sched& sch,
-                        hipStream_t s) {
+                        const float* z_bar, const UvwBwdReq& R, const BwdLayout& L, const Sched& sch, hipStream_t s) {
   const GeomParams geom = p->geom();
   const int32_t N = g->n_nodes;
   const bool want_pos = R.rbar != nullptr;
@@ -687,38 +809,20 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   const int nl = std::max(1, R.lanes);
   const int64_t rbar_stride = 3 * g->n_edges;
   if (R.x_out) ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached_in(p, R.x_out, N, s));
-  // With two buffer sets, a software pipeline over (sender chunk, input block) items: while
-  // item i's traversals run on the caller's stream and its lanes, the post stream
-  // re-lays out the weights and forms Xt = x W for item i + 1 in the other set, then runs
-  // item i's x_bar / W_bar GEMMs once its traversals are done.  With one set (a bounded
-  // workspace) the items run one after another on the caller's stream, input block by
-  // input block, each block in the largest sender chunks its state fits.
+  // With two buffer sets, a software pipeline over the work items: while item i's
+  // traversals run on the caller's stream and its lanes, the post stream re-lays out the
+  // weights and forms Xt = x W for item i + 1 in the other set, then runs item i's x_bar /
+  // W_bar GEMMs once its traversals are done.  With one set the items run one after
+  // another on the caller's stream.
   const bool pipelined = L.nsets > 1;
   PostStream post(s, nl > 1 && pipelined);
   ETPC_HIP(post.status());
-  const std::vector<int> order = block_order(p, d);
-  struct Item {
-    int64_t j0;
-    int k;
-    int nsend;
-  };
-  std::vector<Item> items;
-  if (!sch.bounded) {
-    for (int64_t j0 = 0; j0 < N; j0 += chunk)
-      for (const int k : order) items.push_back(Item{j0, k, static_cast<int>(std::min<int64_t>(chunk, N - j0))});
-  } else {
-    for (const int k : order) {
-      const int64_t ck = block_chunk(p, d, k, chunk, N, sch);
-      for (int64_t j0 = 0; j0 < N; j0 += ck) items.push_back(Item{j0, k, static_cast<int>(std::min<int64_t>(ck, N - j0))});
-    }
-  }
+  const std::vector<Item> items = make_items(p, d, false, N, L.cap, sch.bounded);
   // weight re-layouts and Xt of one item into buffer set `b`, on stream `st`
   auto prep = [&](const Item& it, int b, hipStream_t st) -> etpc_status {
-    const int k = it.k;
+    const int k = it.blk;
     const int ni = 2 * p->in[k].l + 1;
-    const int64_t ncols = d.block_ncols[k];
     const int c_in = p->in[k].mul;
-    const int nsend = it.nsend;
     WPrepArgs wa;
     if (want_pos || R.x_out) {
       wprep_args(p, d, k, R.w, want_pos ? L.wcat[b] : nullptr, R.x_out ? L.wt[b] : nullptr, wa);
@@ -728,19 +832,19 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       wprep_args(p, d, k, R.w2, nullptr, L.wt2[b], wa);
       ETPC_LAUNCH_ON(ETPC_KIND_AUX, st, launch_wprep(wa, st));
     }
-    if (want_pos) {  // Xt = x W
+    if (want_pos) {  // Xt = x W over the item's state columns
       GemmArgs ga{};
       ga.lowp = p->gemm_precision;
-      ga.A = R.x + it.j0 * p->x_dim + p->xoff[k];
+      ga.A = R.x + it.n0 * p->x_dim + p->xoff[k];
       ga.amap = irmul(ni, p->x_dim, c_in);
       ga.a_mcontig = 0;
-      ga.B = L.wcat[b];
-      ga.ldb = ncols;
+      ga.B = L.wcat[b] + it.col0;
+      ga.ldb = d.block_ncols[k];
       ga.C = L.xt[b];
-      ga.cmap = plain(ncols);
+      ga.cmap = plain(it.ncols);
       ga.beta = 0;
-      ga.M = nsend * ni;
-      ga.N = static_cast<int32_t>(ncols);
+      ga.M = it.nn * ni;
+      ga.N = static_cast<int32_t>(it.ncols);
       ga.K = c_in;
       ga.k_split = c_in;
       set_vec4(ga);
@@ -752,117 +856,119 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     etpc_status st0 = prep(items[0], 0, s);
     if (st0 != ETPC_OK) return st0;
   }
-  // Each lane's copy of the edge adjoint is first written by its first path of a chunk.
-  // Block-major items (bounded) cover one sender range several times with different
-  // chunk boundaries, so there every copy starts at zero and every path accumulates.
+  // Each lane's copy of the edge adjoint is first written by its first path (every item of
+  // the fast schedule covers all senders).  Items of a bounded schedule may cover a sender
+  // range several times, so there every copy starts at zero and every path accumulates.
   bool rbar_started[kLanes];
+  for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc || sch.bounded;
   if (want_pos && sch.bounded && !R.rbar_acc)
     ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(R.rbar, rbar_stride * nl, 0.f, s));
   int t_glob = 0;
   for (size_t ii = 0; ii < items.size(); ++ii) {
-    const int64_t j0 = items[ii].j0;
-    const int k = items[ii].k;
+    const Item& it = items[ii];
+    const int k = it.blk;
     const int set = pipelined ? static_cast<int>(ii & 1) : 0;
-    if (ii == 0 || j0 != items[ii - 1].j0) {
-      for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc || sch.bounded;
-      t_glob = 0;
+    const int nsend = it.nn;
+    const auto& paths = p->by_in[k];
+    const int c_in = p->in[k].mul;
+    if (!pipelined) {
+      etpc_status stp = prep(it, 0, s);
+      if (stp != ETPC_OK) return stp;
     }
-    const int nsend = items[ii].nsend;
-    {
-      const auto& paths = p->by_in[k];
-      const int64_t ncols = d.block_ncols[k];
-      const int c_in = p->in[k].mul;
-      if (!pipelined) {
-        etpc_status stp = prep(items[ii], 0, s);
-        if (stp != ETPC_OK) return stp;
-      }
-      // the next item's weights and Xt go into the other set, behind the post work of
-      // the item that last used it
-      if (pipelined && ii + 1 < items.size()) {
-        // the previous item's traversals (which read that set's Xt) are enqueued before
-        // this point: the post stream waits for them first
-        ETPC_HIP(post.follow());
-        etpc_status stp = prep(items[ii + 1], set ^ 1, post.stream());
-        if (stp != ETPC_OK) return stp;
-        ETPC_HIP(post.ready(set ^ 1));
-      }
-      ETPC_HIP(post.wait_ready(set));   // this item's Xt (prefetched, or made above on s)
-      ETPC_HIP(post.wait_slot(set));    // its P set is no longer read by older post work
-      float* const Pset = L.P[set];
-      float* const Pmain = R.tangent ? L.Pd[set] : L.P[set];
-      // the block's paths write disjoint P columns and their own lane's edge adjoint copy
-      LaneGroup lanes(s, nl);
-      ETPC_HIP(lanes.status());
-      for (size_t t = 0; t < paths.size(); ++t, ++t_glob) {
-        const PathInfo& pi = p->paths[paths[t]];
-        const int lane = t_glob % nl;
-        BwdUvwArgs a{};
-        a.s_rowptr = g->s_rowptr;
-        a.s_col = g->s_col;
-        a.s_slot = g->s_slot;
-        a.pos = pos;
-        a.pos_dot = R.pos_dot;
-        a.z_bar = z_bar;
-        a.xt = L.xt[set];
-        a.P = Pset;
-        a.Pdot = L.Pd[set];
-        a.rbar = R.rbar ? R.rbar + lane * rbar_stride : nullptr;
-        a.send0 = static_cast<int32_t>(j0);
-        a.order = (g->s_order != nullptr && j0 == 0 && nsend == g->n_nodes) ? g->s_order : nullptr;
-        a.z_dim = static_cast<int32_t>(p->z_dim);
-        a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
-        int ntiles = 1;
-        a.cp = lane_width(pi.c_out, &ntiles, 16);
-        a.c_out = pi.c_out;
-        a.nparts = edge_parts(nsend, ntiles, g, pi.l_in, p->n_basis,
-                              (R.hess ? 0 : (R.tangent ? need_plain : main_state) ? 1 : 0) + (R.tangent ? 1 : 0));
-        a.ls = pi.l_sh;
-        a.ld_state = ncols;
-        a.state_col0 = d.block_col0[k][t];
-        a.rbar_accumulate = rbar_started[lane] ? 1 : 0;
-        a.g = geom;
-        a.cg = pi.cgf;
-        const bool np = R.tangent ? need_plain : main_state;
-        const hipStream_t ls = lanes.lane(lane);
-        ETPC_LAUNCH_ON(ETPC_KIND_BWD_TRAVERSE, ls,
-                       launch_bwd_uvw(a, R.hess ? false : np, want_pos, R.tangent, R.hess, pi.l_in, pi.l_out, nsend,
-                                      ntiles, ls));
-        if (want_pos) rbar_started[lane] = true;
-      }
-      ETPC_HIP(lanes.finish());
-      if (R.x_out || R.w_out) {
-        ETPC_HIP(post.follow());
-        const hipStream_t ps = post.stream();
-        if (R.x_out) {
-          if (main_state) {
-            etpc_status st = xbar_gemm(p, d, k, Pmain, L.wt[set], R.x_out, j0, nsend, false, L, ps);
-            if (st != ETPC_OK) return st;
-          }
-          if (R.tangent && R.w2) {
-            etpc_status st = xbar_gemm(p, d, k, Pset, L.wt2[set], R.x_out, j0, nsend, true, L, ps);
-            if (st != ETPC_OK) return st;
-          }
+    // the next item's weights and Xt go into the other set, behind the post work of the
+    // item that last used it
+    if (pipelined && ii + 1 < items.size()) {
+      // the previous item's traversals (which read that set's Xt) are enqueued before
+      // this point: the post stream waits for them first
+      ETPC_HIP(post.follow());
+      etpc_status stp = prep(items[ii + 1], set ^ 1, post.stream());
+      if (stp != ETPC_OK) return stp;
+      ETPC_HIP(post.ready(set ^ 1));
+    }
+    ETPC_HIP(post.wait_ready(set));   // this item's Xt (prefetched, or made above on s)
+    ETPC_HIP(post.wait_slot(set));    // its P set is no longer read by older post work
+    float* const Pset = L.P[set];
+    float* const Pmain = R.tangent ? L.Pd[set] : L.P[set];
+    // the item's paths write disjoint P columns and their own lane's edge adjoint copy
+    LaneGroup lanes(s, nl);
+    ETPC_HIP(lanes.status());
+    for (int t = it.t0; t < it.t1; ++t, ++t_glob) {
+      const PathInfo& pi = p->paths[paths[t]];
+      const int lane = t_glob % nl;
+      BwdUvwArgs a{};
+      a.s_rowptr = g->s_rowptr;
+      a.s_col = g->s_col;
+      a.s_slot = g->s_slot;
+      a.pos = pos;
+      a.pos_dot = R.pos_dot;
+      a.z_bar = z_bar;
+      a.xt = L.xt[set];
+      a.P = Pset;
+      a.Pdot = L.Pd[set];
+      a.rbar = R.rbar ? R.rbar + lane * rbar_stride : nullptr;
+      a.send0 = static_cast<int32_t>(it.n0);
+      a.order = (g->s_order != nullptr && it.n0 == 0 && nsend == g->n_nodes) ? g->s_order : nullptr;
+      a.z_dim = static_cast<int32_t>(p->z_dim);
+      a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
+      int ntiles = 1;
+      a.cp = lane_width(pi.c_out, &ntiles, 16);
+      a.c_out = pi.c_out;
+      a.nparts = edge_parts(nsend, ntiles, g, pi.l_in, p->n_basis,
+                            (R.hess ? 0 : (R.tangent ? need_plain : main_state) ? 1 : 0) + (R.tangent ? 1 : 0));
+      a.ls = pi.l_sh;
+      a.ld_state = it.ncols;
+      a.state_col0 = d.block_col0[k][t] - it.col0;
+      a.rbar_accumulate = rbar_started[lane] ? 1 : 0;
+      a.g = geom;
+      a.cg = pi.cgf;
+      const bool np = R.tangent ? need_plain : main_state;
+      const hipStream_t ls = lanes.lane(lane);
+      ETPC_LAUNCH_ON(ETPC_KIND_BWD_TRAVERSE, ls,
+                     launch_bwd_uvw(a, R.hess ? false : np, want_pos, R.tangent, R.hess, pi.l_in, pi.l_out, nsend,
+                                    ntiles, ls));
+      if (want_pos) rbar_started[lane] = true;
+    }
+    ETPC_HIP(lanes.finish());
+    if (R.x_out || R.w_out) {
+      ETPC_HIP(post.follow());
+      const hipStream_t ps = post.stream();
+      if (R.x_out) {
+        // the first path subset of a sender range writes its x_bar rows, later ones add
+        const float* wt_main = L.wt[set] + it.col0 * c_in;
+        if (main_state) {
+          etpc_status st = xbar_gemm(p, k, Pmain, it.ncols, wt_main, R.x_out, it.n0, nsend, it.t0 > 0, L, ps);
+          if (st != ETPC_OK) return st;
         }
-        if (R.w_out) {
-          int sp1 = 0, sp2 = 0;
-          ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, ps, wbar_gemm(p, d, k, R.x, j0, nsend, Pmain, L.wpart, &sp1, ps));
-          if (R.tangent && R.x2)
-            ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, ps,
-                           wbar_gemm(p, d, k, R.x2, j0, nsend, Pset, L.wpart + static_cast<int64_t>(sp1) * c_in * ncols,
-                                     &sp2, ps));
-          int64_t poff[kMaxPaths];
-          int32_t col0[kMaxPaths], cout[kMaxPaths];
-          for (size_t t = 0; t < paths.size(); ++t) {
-            poff[t] = p->paths[paths[t]].w_off;
-            col0[t] = d.block_col0[k][t];
-            cout[t] = p->paths[paths[t]].c_out;
-          }
-          ETPC_LAUNCH_ON(ETPC_KIND_AUX, ps,
-                         launch_reduce_wbar(L.wpart, sp1 + sp2, c_in, static_cast<int>(paths.size()), p->n_basis, poff,
-                                            col0, cout, static_cast<int>(ncols), R.w_out, j0 > 0, ps));
+        if (R.tangent && R.w2) {
+          etpc_status st = xbar_gemm(p, k, Pset, it.ncols, L.wt2[set] + it.col0 * c_in, R.x_out, it.n0, nsend, true,
+                                     L, ps);
+          if (st != ETPC_OK) return st;
         }
-        ETPC_HIP(post.mark(set));
       }
+      if (R.w_out) {
+        int sp1 = 0, sp2 = 0;
+        const bool two = R.tangent && R.x2;
+        const int64_t room = two ? L.wpart_cap / 2 : L.wpart_cap;
+        ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, ps,
+                       wbar_gemm(p, k, R.x, it.n0, nsend, Pmain, it.ncols, L.wpart, room, &sp1, ps));
+        if (two)
+          ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, ps,
+                         wbar_gemm(p, k, R.x2, it.n0, nsend, Pset, it.ncols,
+                                   L.wpart + static_cast<int64_t>(sp1) * c_in * it.ncols, room, &sp2, ps));
+        int64_t poff[kMaxPaths];
+        int32_t col0[kMaxPaths], cout[kMaxPaths];
+        const int npath = it.t1 - it.t0;
+        for (int t = 0; t < npath; ++t) {
+          poff[t] = p->paths[paths[it.t0 + t]].w_off;
+          col0[t] = static_cast<int32_t>(d.block_col0[k][it.t0 + t] - it.col0);
+          cout[t] = p->paths[paths[it.t0 + t]].c_out;
+        }
+        // the first sender range of a path writes its W_bar block, later ones add
+        ETPC_LAUNCH_ON(ETPC_KIND_AUX, ps,
+                       launch_reduce_wbar(L.wpart, sp1 + sp2, c_in, npath, p->n_basis, poff, col0, cout,
+                                          static_cast<int>(it.ncols), R.w_out, it.n0 > 0, ps));
+      }
+      ETPC_HIP(post.mark(set));
     }
   }
   ETPC_HIP(post.finish());
@@ -950,19 +1056,20 @@ etpc_status bwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
 etpc_status forward_impl(const etpc_plan_s* p, const etpc_graph* g, const float* x, const float* pos, const float* w,
                          float* z, void* ws, size_t ws_bytes, int nl, hipStream_t s) {
   const Derived d = derive(p);
+  const int64_t N = g->n_nodes;
+  auto bytes_of = [&](int64_t c, const Sched& sc) { return fwd_bytes(p, d, N, c, sc); };
   Sched sch;
-  int64_t chunk = 0;
-  choose_schedule(p, g->n_nodes, g->n_edges, ws_bytes, [&](int64_t c, const Sched& sc) { return fwd_bytes(p, d, c, sc); },
-                  &sch, &chunk);
+  int64_t cap = 0;
+  choose_schedule(p, d, true, false, N, g->n_edges, ws_bytes, bytes_of, &sch, &cap);
   if (p->mode == ETPC_UVW) {
-    etpc_status st = check_ws(ws, ws_bytes, fwd_bytes(p, d, 1, sch));
+    etpc_status st = check_ws(ws, ws_bytes, bytes_of(cap < 0 ? min_cap(p, true, false) : cap, sch));
     if (st != ETPC_OK) return st;
   }
   Carver c{static_cast<char*>(ws), 0};
   FwdLayout L;
-  fwd_layout(p, d, std::max<int64_t>(chunk, 0), sch, c, L);
+  fwd_layout(p, d, N, std::max<int64_t>(cap, 0), sch, c, L);
   ETPC_LAUNCH(ETPC_KIND_AUX, zero_unreached(p, z, g->n_nodes, s));
-  if (p->mode == ETPC_UVW) return fwd_uvw_run(p, d, g, x, pos, nullptr, w, z, false, false, L, chunk, sch, nl, s);
+  if (p->mode == ETPC_UVW) return fwd_uvw_run(p, d, g, x, pos, nullptr, w, z, false, false, L, sch, nl, s);
   return fwd_uvu_run(p, g, x, pos, nullptr, w, z, false, false, nl, s);
 }
 
@@ -1006,26 +1113,26 @@ etpc_status etpc_workspace_size(etpc_plan p, int32_t pass, int32_t n_nodes, int6
   if (pass != ETPC_PASS_FWD && pass != ETPC_PASS_BWD && pass != ETPC_PASS_DBL)
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "unknown pass");
   const Derived d = derive(p);
-  // uvu keeps no node state: its layout depends on the persistent grid, not on a chunk
+  const bool fwd = pass != ETPC_PASS_BWD, bwd = pass != ETPC_PASS_FWD;
+  // uvu keeps no node state: its layout depends on the persistent grid, not on a buffer size
   auto bytes_of = [&](int64_t c, const Sched& sc) -> size_t {
-    const int64_t chunk = p->mode == ETPC_UVW ? c : kUvuGrid;
-    if (pass == ETPC_PASS_FWD) return fwd_bytes(p, d, chunk, sc);
-    if (pass == ETPC_PASS_BWD) return bwd_bytes(p, d, n_nodes, n_edges, chunk, sc);
-    return dbl_bytes(p, d, n_nodes, n_edges, chunk, sc);
+    if (pass == ETPC_PASS_FWD) return fwd_bytes(p, d, n_nodes, c, sc);
+    if (pass == ETPC_PASS_BWD) return bwd_bytes(p, d, n_nodes, n_edges, c, sc);
+    return dbl_bytes(p, d, n_nodes, n_edges, c, sc);
   };
-  const size_t full = bytes_of(n_nodes, fast_sched(p));
+  const size_t full = bytes_of(p->mode == ETPC_UVW ? full_cap(d, n_nodes, fwd, bwd) : 0, fast_sched(p));
   if (budget == 0 || full <= budget || n_nodes == 0) {
     *bytes = full;
     return ETPC_OK;
   }
   Sched sch;
-  int64_t chunk = 0;
-  choose_schedule(p, n_nodes, n_edges, budget, bytes_of, &sch, &chunk);
-  if (chunk < 1) {
-    *bytes = bytes_of(1, sch);
+  int64_t cap = 0;
+  choose_schedule(p, d, fwd, bwd, n_nodes, n_edges, budget, bytes_of, &sch, &cap);
+  if (cap < 0) {
+    *bytes = bytes_of(min_cap(p, fwd, bwd), sch);
     ETPC_FAIL(ETPC_ERR_WORKSPACE, "budget below the pass's minimum of " + std::to_string(*bytes) + " bytes");
   }
-  *bytes = bytes_of(chunk, sch);
+  *bytes = bytes_of(cap, sch);
   return ETPC_OK;
 }
 
@@ -1148,7 +1255,10 @@ etpc_status etpc_forward_noalloc(etpc_plan p, const etpc_graph* g, const float* 
     ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null x, pos, w or z");
   if (p->mode == ETPC_UVU) return forward_impl(p, g, x, pos, w, z, nullptr, 0, 1, s);   // no scratch
   const Derived d = derive(p);
-  const size_t one = fwd_bytes(p, d, 1, bounded_sched(p, g->n_edges, kStaticScratchBytes));
+  Sched one_set;
+  one_set.bounded = true;
+  one_set.nsets = 1;
+  const size_t one = fwd_bytes(p, d, g->n_nodes, min_cap(p, true, false), one_set);
   if (one > kStaticScratchBytes)
     ETPC_FAIL(ETPC_ERR_WORKSPACE, "one receiver's state (" + std::to_string(one) +
                                       " bytes) exceeds the fixed scratch of " +
@@ -1186,15 +1296,15 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
     return cv.off;
   };
   Sched sch;
-  int64_t chunk = 0;
-  choose_schedule(p, N, g->n_edges, ws_bytes, bytes_of, &sch, &chunk);
-  st = check_ws(ws, ws_bytes, bytes_of(1, sch));
+  int64_t cap = 0;
+  choose_schedule(p, d, false, true, N, g->n_edges, ws_bytes, bytes_of, &sch, &cap);
+  st = check_ws(ws, ws_bytes, bytes_of(cap < 0 ? min_cap(p, false, true) : cap, sch));
   if (st != ETPC_OK) return st;
   // concurrent lanes = edge-adjoint copies the schedule keeps
   const int lanes = want_pos ? std::min(rbar_lanes(p, g), sch.rbar_copies) : rbar_lanes(p, g);
   Carver cv{static_cast<char*>(ws), 0};
   BwdLayout L;
-  bwd_layout(p, d, N, g->n_edges, p->mode == ETPC_UVW ? chunk : kUvuGrid, sch, want_pos, need_p, false,
+  bwd_layout(p, d, N, g->n_edges, p->mode == ETPC_UVW ? cap : kUvuGrid, sch, want_pos, need_p, false,
              w_bar != nullptr, false, x_bar != nullptr, false, cv, L);
   if (p->mode == ETPC_UVW) {
     UvwBwdReq R{};
@@ -1204,7 +1314,7 @@ etpc_status etpc_backward(etpc_plan p, const etpc_graph* g, const float* x, cons
     R.x_out = x_bar;
     R.w_out = w_bar;
     R.rbar = want_pos ? L.rbar : nullptr;
-    st = bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, sch, s);
+    st = bwd_uvw_run(p, d, g, pos, z_bar, R, L, sch, s);
   } else {
     UvuBwdReq R{};
     R.lanes = lanes;
@@ -1253,20 +1363,22 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
     const int64_t ch = p->mode == ETPC_UVW ? c : kUvuGrid;
     bwd_layout(p, d, N, g->n_edges, ch, sc, want_pos, plain, tan, w_grad != nullptr, tan && x_dot, x_grad != nullptr,
                x_grad && w_dot && tan, cv, L);
-    return std::max(cv.off, z_bar_grad ? fwd_bytes(p, d, c, sc) : size_t(0));
+    return std::max(cv.off, z_bar_grad ? fwd_bytes(p, d, N, c, sc) : size_t(0));
   };
   Sched sch;
-  int64_t chunk = 0;
-  choose_schedule(p, N, g->n_edges, ws_bytes, bytes_of, &sch, &chunk);
-  st = check_ws(ws, ws_bytes, bytes_of(1, sch));
+  int64_t cap = 0;
+  const bool fwd_state = z_bar_grad != nullptr;
+  choose_schedule(p, d, fwd_state, true, N, g->n_edges, ws_bytes, bytes_of, &sch, &cap);
+  st = check_ws(ws, ws_bytes, bytes_of(cap < 0 ? min_cap(p, fwd_state, true) : cap, sch));
   if (st != ETPC_OK) return st;
+  const int64_t chunk = p->mode == ETPC_UVW ? cap : kUvuGrid;
   const int lanes = want_pos ? std::min(rbar_lanes(p, g), sch.rbar_copies) : rbar_lanes(p, g);
 
   // d/dz_bar = z_dot = J_pos pos_dot + J_x x_dot + J_W w_dot (forward tangents)
   if (z_bar_grad) {
     Carver cv{static_cast<char*>(ws), 0};
     FwdLayout L;
-    fwd_layout(p, d, chunk, sch, cv, L);
+    fwd_layout(p, d, N, cap, sch, cv, L);
     if (!tan && !plain) {
       ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(z_bar_grad, static_cast<int64_t>(N) * p->z_dim, 0.f, s));
     } else {
@@ -1287,8 +1399,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
           win = w_dot;
         }
         if (p->mode == ETPC_UVW)
-          st = fwd_uvw_run(p, d, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, L, chunk, sch, lane_cap(p, g),
-                           s);
+          st = fwd_uvw_run(p, d, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, L, sch, lane_cap(p, g), s);
         else
           st = fwd_uvu_run(p, g, xin, pos, pos_dot, win, z_bar_grad, beta, tangent, lane_cap(p, g), s);
         if (st != ETPC_OK) return st;
@@ -1343,7 +1454,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
         R.x = x_dot ? x_dot : x;
         R.w = w_dot ? w_dot : w;
       }
-      return bwd_uvw_run(p, d, g, pos, z_bar, R, L, chunk, sch, s);
+      return bwd_uvw_run(p, d, g, pos, z_bar, R, L, sch, s);
     }
     // uvu: tangent pass (pos_dot) then plain passes with w -> w_dot (x_grad) and x -> x_dot (w_grad)
     bool xs = false, wsd = false;
@@ -1426,7 +1537,7 @@ etpc_status etpc_double_backward(etpc_plan p, const etpc_graph* g, const float* 
       R.rbar = Lp.rbar;
       R.hess = hess;
       R.rbar_acc = acc;
-      st = bwd_uvw_run(p, d, g, pos, z_bar, R, Lp, chunk, sch, s);
+      st = bwd_uvw_run(p, d, g, pos, z_bar, R, Lp, sch, s);
     } else {
       UvuBwdReq R{};
       R.lanes = lanes;
