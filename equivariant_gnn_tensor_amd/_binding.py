@@ -417,10 +417,10 @@ def etpc_layout_convert(plan: Plan, features: str, direction: str, x: torch.Tens
     return out
 
 
-def _ws_for(plan, pass_, graph, ws, stream):
+def _ws_for(plan, pass_, graph, ws, stream, budget=0):
     if isinstance(ws, torch.Tensor):
         return ws.data_ptr(), ws.numel() * ws.element_size(), ws
-    n = etpc_workspace_size(plan, pass_, graph.n_nodes, graph.n_edges)
+    n = etpc_workspace_size(plan, pass_, graph.n_nodes, graph.n_edges, budget)
     t, nb = _workspace(n, graph.rowptr.device, stream)
     return (None if t is None else t.data_ptr()), nb, t
 
@@ -440,12 +440,14 @@ def _check_inputs(plan: Plan, graph: Graph, x, pos, w, z_bar=None, **extra):
     return info
 
 
-def etpc_forward(plan: Plan, graph: Graph, x, pos, w, z=None, ws=None, stream=None):
+def etpc_forward(plan: Plan, graph: Graph, x, pos, w, z=None, ws=None, stream=None, budget: int = 0):
+    """z = conv(x, pos, W).  Without ws, a workspace is allocated for the call: the fast
+    schedule's size, or the largest that fits `budget` bytes (the bounded schedule)."""
     _check_inputs(plan, graph, x, pos, w, z=z)
     if z is None:
         with torch.cuda.stream(_torch_stream(stream, x.device)):
             z = torch.empty(graph.n_nodes, plan.info()["z_dim"], dtype=torch.float32, device=x.device)
-    wp, wn, _keep = _ws_for(plan, PASS_FWD, graph, ws, stream)
+    wp, wn, _keep = _ws_for(plan, PASS_FWD, graph, ws, stream, budget)
     _check(lib.etpc_forward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z), wp, wn,
                             _stream(stream)))
     return z
@@ -463,7 +465,7 @@ def etpc_forward_noalloc(plan: Plan, graph: Graph, x, pos, w, z, stream=None):
 
 
 def etpc_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, want=("x", "w", "pos"), outs=None, ws=None,
-                  stream=None):
+                  stream=None, budget: int = 0):
     info = _check_inputs(plan, graph, x, pos, w, z_bar)
     dev = x.device
     if outs is None:
@@ -475,14 +477,14 @@ def etpc_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, want=("x", "w", "p
             )
     xb, wb, pb = outs
     _check_inputs(plan, graph, x, pos, w, z_bar, x_bar=xb, w_bar=wb, pos_bar=pb)
-    wp, wn, _keep = _ws_for(plan, PASS_BWD, graph, ws, stream)
+    wp, wn, _keep = _ws_for(plan, PASS_BWD, graph, ws, stream, budget)
     _check(lib.etpc_backward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z_bar), _ptr(xb),
                              _ptr(wb), _ptr(pb), wp, wn, _stream(stream)))
     return xb, wb, pb
 
 
 def etpc_double_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, x_dot=None, w_dot=None, pos_dot=None,
-                         want=("z_bar", "x", "w", "pos"), outs=None, ws=None, stream=None):
+                         want=("z_bar", "x", "w", "pos"), outs=None, ws=None, stream=None, budget: int = 0):
     """Returns (d/dz_bar, d/dx, d/dW, d/dpos); outputs not in ``want`` are None."""
     info = _check_inputs(plan, graph, x, pos, w, z_bar, x_dot=x_dot, w_dot=w_dot, pos_dot=pos_dot)
     dev = x.device
@@ -499,7 +501,7 @@ def etpc_double_backward(plan: Plan, graph: Graph, x, pos, w, z_bar, x_dot=None,
         outs = tuple(outs) + (None,)
     gz, gx, gw, gp = outs
     _check_inputs(plan, graph, x, pos, w, z_bar, z_bar_grad=gz, x_grad=gx, w_grad=gw, pos_grad=gp)
-    wp, wn, _keep = _ws_for(plan, PASS_DBL, graph, ws, stream)
+    wp, wn, _keep = _ws_for(plan, PASS_DBL, graph, ws, stream, budget)
     _check(lib.etpc_double_backward(plan.handle, C.byref(graph.c), _ptr(x), _ptr(pos), _ptr(w), _ptr(z_bar),
                                     _ptr(x_dot), _ptr(w_dot), _ptr(pos_dot), _ptr(gz), _ptr(gx), _ptr(gw), _ptr(gp),
                                     wp, wn, _stream(stream)))
