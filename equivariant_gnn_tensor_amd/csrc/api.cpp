@@ -367,7 +367,13 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t
   }
 }
 
-constexpr int kUvuGrid = 2048;
+// Persistent grid of the uvu sender traversal (W_bar partials: one per workgroup).  1024
+// or 4096 workgroups run a lone launch ~10% faster, but the channelwise step, whose
+// launches overlap on two lanes, measured 2-3% slower with either.
+#ifndef ETPC_UVU_GRID
+#define ETPC_UVU_GRID 2048
+#endif
+constexpr int kUvuGrid = ETPC_UVU_GRID;
 
 size_t fwd_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t cap, const Sched& sch) {
   Carver c;
@@ -692,7 +698,7 @@ etpc_status fwd_uvu_run(const etpc_plan_s* p, const etpc_graph* g, const float* 
     a.z_dim = static_cast<int32_t>(p->z_dim);
     a.zoff = static_cast<int32_t>(p->zoff[pi.out_block]);
     int ntiles = 1;
-    a.cp = lane_width(pi.c_in, &ntiles);
+    a.cp = lane_width(pi.c_in, &ntiles, 4);   // 4-lane matrix-core blocks never mix edges
     a.c = pi.c_in;
     a.ls = pi.l_sh;
     a.accumulate = (beta || seen[pi.out_block]) ? 1 : 0;

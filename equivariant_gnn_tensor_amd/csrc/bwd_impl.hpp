@@ -42,11 +42,30 @@ constexpr int kPrefetch = ETPC_BWD_PREFETCH;
 #define ETPC_BWD_XT_MFMA 1
 #endif
 constexpr bool kXtMfma = ETPC_BWD_XT_MFMA != 0;
-static_assert(!kXtMfma || kPrefetch == 2, "the matrix-core radial contraction covers two trips");
+static_assert(!kXtMfma || kPrefetch % 2 == 0, "the matrix-core radial contraction covers two trips");
 
 // What may cross the scheduling barrier placed after each pipelined gather: LDS reads and
 // writes (0x80 | 0x100 | 0x200), so record reads can be hoisted; global loads never.
 constexpr int kSchedMask = 0x380;
+
+// First-order uvu backward in the sender-regrouped form (1) or the per-edge form (0).
+// The regrouped form issues 30-70% fewer VALU instructions per edge but the uvu backward
+// waits on its gathers at two waves per SIMD, so it gained 1-2% (channelwise workload,
+// 16.6 -> 16.3 ms per step of backward traversals).
+#ifndef ETPC_BWD_UVU_FIRST
+#define ETPC_BWD_UVU_FIRST 1
+#endif
+constexpr bool kUvuFirst = ETPC_BWD_UVU_FIRST != 0;
+// z_bar gathers in flight per edge slot in the first-order uvu traversal (even; 4 and 6
+// measured 3-7% slower: more registers, no more bandwidth)
+#ifndef ETPC_BWD_UVU_PREFETCH
+#define ETPC_BWD_UVU_PREFETCH 2
+#endif
+constexpr int kUvuPrefetch = ETPC_BWD_UVU_PREFETCH;
+// 1: the sender-regrouped form where it takes fewer FMAs per edge; 0: per-edge form only
+#ifndef ETPC_BWD_UVU_XFORM
+#define ETPC_BWD_UVU_XFORM 1
+#endif
 
 // Edge slots of the sender traversals are at least 16 lanes wide (the host rounds the
 // channel count up), so a per-edge lane sum is a DPP row sum per 16 lanes (no branch, no
@@ -259,28 +278,31 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
       for (int mo = 0; mo < NO; ++mo) zq[pf][mo] += 0.f;
     }
     for (int it0 = 0; it0 < trips; it0 += kPrefetch) {
-      // Position adjoint, radial contractions of both trips of the group at once: with
-      // 4x4x1 matrix-core blocks of four lanes, row r of a block takes phi (r = 0, 1) or
-      // phi' (r = 2, 3) of the edge of trip it0 + (r & 1), and each lane's column is its own
-      // Xt[q][m_in]; so after the NB accumulations register r of a lane holds T (r < 2) or
-      // G (r >= 2) of that edge for the lane's channel.  A padding trip reads edge 0's
-      // record; its results feed only the edge adjoint that is never stored.
       f4v TG[NI];
-      if constexpr (POS && kXtMfma) {
-        const int r4 = lane & 3;
-        const int tt = (it0 + (r4 & 1)) * tslots + gslot;
-        const float* er = s_edge + (tt < ne ? tt : 0) * R::kStride + (r4 < 2 ? R::kPhi : R::kDphi);
-#pragma unroll
-        for (int mi = 0; mi < NI; ++mi) TG[mi] = f4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-          const float aq = er[q];
-#pragma unroll
-          for (int mi = 0; mi < NI; ++mi) TG[mi] = __builtin_amdgcn_mfma_f32_4x4x1f32(aq, xt[q][mi], TG[mi], 0, 0, 0);
-        }
-      }
 #pragma unroll
       for (int pf = 0; pf < kPrefetch; ++pf) {
+        // Position adjoint, radial contractions of two trips at once: with 4x4x1
+        // matrix-core blocks of four lanes, row r of a block takes phi (r = 0, 1) or
+        // phi' (r = 2, 3) of the edge of trip it0 + pf + (r & 1), and each lane's column is
+        // its own Xt[q][m_in]; so after the NB accumulations register r of a lane holds T
+        // (r < 2) or G (r >= 2) of that edge for the lane's channel.  A padding trip reads
+        // edge 0's record; its results feed only the edge adjoint that is never stored.
+        if constexpr (POS && kXtMfma) {
+          if (pf % 2 == 0) {
+            const int r4 = lane & 3;
+            const int tt = (it0 + pf + (r4 & 1)) * tslots + gslot;
+            const float* er = s_edge + (tt < ne ? tt : 0) * R::kStride + (r4 < 2 ? R::kPhi : R::kDphi);
+#pragma unroll
+            for (int mi = 0; mi < NI; ++mi) TG[mi] = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+              const float aq = er[q];
+#pragma unroll
+              for (int mi = 0; mi < NI; ++mi)
+                TG[mi] = __builtin_amdgcn_mfma_f32_4x4x1f32(aq, xt[q][mi], TG[mi], 0, 0, 0);
+            }
+          }
+        }
         // trips run in whole groups of kPrefetch (no exit inside the unrolled body, which
         // would make the compiler copy the loop-carried registers and wait on the loads);
         // a padding trip has t >= ne, gathers zeros and adds exact zeros
@@ -343,8 +365,8 @@ __global__ __launch_bounds__(256) void bwd_uvw_kernel(const BwdUvwArgs a) {
           for (int mi = 0; mi < NI; ++mi) {
             float tq = 0.f, gq = 0.f, g2 = 0.f;
             if constexpr (kXtMfma) {
-              tq = TG[mi][pf];
-              gq = TG[mi][2 + pf];
+              tq = TG[mi][pf & 1];
+              gq = TG[mi][2 + (pf & 1)];
             } else {
 #pragma unroll
               for (int q = 0; q < NB; ++q) {
@@ -689,6 +711,286 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
   }
 }
 
+// Number of nonzero coupling coefficients of a path (compile time).
+template <int LI, int LS, int LO>
+constexpr int cg_nnz() {
+  int n = 0;
+  for (int a = 0; a < 2 * LI + 1; ++a)
+    for (int b = 0; b < 2 * LS + 1; ++b)
+      for (int m = 0; m < 2 * LO + 1; ++m)
+        if (CgTab<LI, LS, LO>::v[a][b][m] != 0.f) ++n;
+  return n;
+}
+
+// First-order uvu sender traversal with the contractions regrouped around the sender.
+// For lane channel u, sender j and edge e = (j -> i), with c the path's coupling tensor:
+//   Ybar_e[b] = sum_{a,m} c[a][b][m] x_j[a] zb_i[m] = sum_m X_j[b][m] zb_i[m],
+//               X_j[b][m] = sum_a c[a][b][m] x_j[a]             (once per sender)
+//   h_e       = <x_j, Q_e> = sum_b Y_e[b] Ybar_e[b]
+//   x_bar_j[a] = sum_e w_e Q_e[a] = sum_{b,m} c[a][b][m] A_j[b][m],
+//               A_j[b][m] = sum_e Y_e[b] (w_e zb_i[m])          (sender accumulator)
+// (Eq. 7 and 17-22 reassociated; exact in exact arithmetic).  A_j is an outer product of
+// the edge's harmonics with the lane's w_e zb and accumulates on the matrix cores as
+// 4x4x1 blocks (lane 4g + r supplies Y[4k + r], every lane its own w_e zb[m]; register r
+// of Ac[k][m] holds b = 4k + r).  The same blocks carry the radial weights of two trips
+// at once (rows phi or phi' of trip pair members, columns the lane's W[q][u]) and the
+// W_bar partials (rows phi[4qq + r], columns h).  Paths whose coupling tensor is sparse
+// enough that the per-edge form V = c zb, Q = Y V, Ybar = x V costs fewer FMAs (l_in = 0)
+// keep that form for Q and Ybar and use the matrix-core weights and W_bar partials.
+template <int LI, int LS, int LO>
+struct UvuSenderForm {
+  static constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1;
+  static constexpr int kPerEdgeV = cg_nnz<LI, LS, LO>() + 2 * NI * NS + 2 * NI;
+  static constexpr int kPerEdgeX = NS * NO + NS + NO;
+  static constexpr bool kX = ETPC_BWD_UVU_XFORM != 0 && kPerEdgeX < kPerEdgeV;
+};
+
+template <int LI, int LS, int LO, int NBQ>
+__global__ __launch_bounds__(256) void bwd_uvu_first_kernel(const BwdUvuArgs a) {
+  constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
+  constexpr int NSQ = (NS + 3) / 4;
+  constexpr bool XF = UvuSenderForm<LI, LS, LO>::kX;
+  static_assert(kUvuPrefetch % 2 == 0, "the radial weights cover two trips");
+  constexpr int kRecAlign = 4;
+  using R = BwdRec<NB, NS, true, false, false, kRecAlign>;
+  using C = CgTab<LI, LS, LO>;
+  __shared__ __attribute__((aligned(16))) float s_edge[64 * R::kStride];
+  __shared__ int s_i[64];
+  __shared__ int s_sl[64];
+  extern __shared__ float s_dyn[];   // [nwaves][64][rows][3]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
+  const int cp = a.cp;
+  const int nslots = kWave / cp;
+  const int slot = lane / cp;
+  const int u = wave * cp + (lane - slot * cp);
+  const bool uvalid = u < a.c;
+  const int rows = rows_per_slot(cp);
+  const int row_in_slot = (lane - slot * cp) >> 4;
+  const bool row_leader = (lane & 15) == 0;
+  const int q4 = lane & 3;
+  const bool want_pos = a.rbar != nullptr;
+  float wv[NB];
+  f4v wb[NBQ];   // W_bar partials: register r of wb[qq] holds q = 4 qq + r
+#pragma unroll
+  for (int q = 0; q < NB; ++q) wv[q] = (uvalid && q < a.g.nb) ? a.w[q * a.c + u] : 0.f;
+#pragma unroll
+  for (int qq = 0; qq < NBQ; ++qq) wb[qq] = f4v{0.f, 0.f, 0.f, 0.f};
+  for (int j = blockIdx.x; j < a.n_nodes; j += gridDim.x) {
+    float xj[NI];
+    const float* xr = a.x + static_cast<int64_t>(j) * a.x_dim + a.xoff + u;
+#pragma unroll
+    for (int mi = 0; mi < NI; ++mi) xj[mi] = uvalid ? xr[mi * a.c] : 0.f;
+    float X[XF ? NS : 1][XF ? NO : 1];
+    f4v Ac[XF ? NSQ : 1][XF ? NO : 1];
+    float xb[NI];
+    if constexpr (XF) {
+#pragma unroll
+      for (int b = 0; b < NS; ++b)
+#pragma unroll
+        for (int m = 0; m < NO; ++m) {
+          float s = 0.f;
+#pragma unroll
+          for (int mi = 0; mi < NI; ++mi)
+            if (C::v[mi][b][m] != 0.f) s += C::v[mi][b][m] * xj[mi];
+          X[b][m] = s;
+        }
+#pragma unroll
+      for (int k = 0; k < NSQ; ++k)
+#pragma unroll
+        for (int m = 0; m < NO; ++m) Ac[k][m] = f4v{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int mi = 0; mi < NI; ++mi) xb[mi] = 0.f;
+    const int k0 = a.s_rowptr[j], k1 = a.s_rowptr[j + 1];
+    for (int base = k0; base < k1; base += kWave) {
+      const int ne = min(kWave, k1 - base);
+      if (tid < ne) {
+        const int i = a.s_col[base + tid];
+        bwd_fill_rec<LS, NB, true, false, true, false, kRecAlign>(a.g, a.pos, a.pos_dot, j, i,
+                                                                  s_edge + tid * R::kStride);
+        s_i[tid] = i;
+        s_sl[tid] = a.s_slot[base + tid];
+      }
+      __syncthreads();
+      const int trips = (ne + nslots - 1) / nslots;
+      float zq[kUvuPrefetch][NO];
+      auto gather = [&](int t, float* dst) {
+        const int i = s_i[t < ne ? t : 0];
+        const float* zr = a.z_bar + static_cast<int64_t>(t < ne ? i : 0) * a.z_dim + a.zoff + (uvalid ? u : 0);
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo) dst[mo] = zr[mo * a.c];
+      };
+#pragma unroll
+      for (int pf = 0; pf < kUvuPrefetch; ++pf) {
+        gather(pf * nslots + slot, zq[pf]);
+#pragma unroll
+        for (int mo = 0; mo < NO; ++mo) zq[pf][mo] += 0.f;   // not a plain load
+      }
+      for (int it0 = 0; it0 < trips; it0 += kUvuPrefetch) {
+        f4v WE;
+#pragma unroll
+        for (int pf = 0; pf < kUvuPrefetch; ++pf) {
+          if (pf % 2 == 0) {
+            // w_e and w_e' = sum_q phi'_q W[q][u] of trips it0 + pf and it0 + pf + 1: row r of a
+            // block takes phi (r < 2) or phi' (r >= 2) of trip it0 + pf + (r & 1)
+            const int tt = (it0 + pf + (q4 & 1)) * nslots + slot;
+            const float* er = s_edge + (tt < ne ? tt : 0) * R::kStride + (q4 < 2 ? R::kPhi : R::kDphi);
+            WE = f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < NB; ++q) WE = __builtin_amdgcn_mfma_f32_4x4x1f32(er[q], wv[q], WE, 0, 0, 0);
+          }
+          const float we = WE[pf & 1], wdr = WE[2 + (pf & 1)];
+          const int t = (it0 + pf) * nslots + slot;
+          const bool tvalid = t < ne;
+          const float* e = s_edge + (tvalid ? t : 0) * R::kStride;
+          float zb[NO];
+#pragma unroll
+          for (int mo = 0; mo < NO; ++mo) zb[mo] = zq[pf][mo];   // masked below, through w_e and h
+          gather(t + kUvuPrefetch * nslots, zq[pf]);
+          __builtin_amdgcn_sched_barrier(kSchedMask);
+          // a padding trip (real but foreign data) adds nothing; lanes past c hold x = 0 and
+          // W = 0, so their h, w_e and lane-sum terms are zero already
+          const float wem = tvalid ? we : 0.f;
+          float wy[NS];
+          float h = 0.f;
+          if constexpr (XF) {
+#pragma unroll
+            for (int b = 0; b < NS; ++b) {
+              float s = 0.f;
+#pragma unroll
+              for (int m = 0; m < NO; ++m) s += X[b][m] * zb[m];
+              wy[b] = s;
+              h += e[R::kY + b] * s;
+            }
+            float tz[NO];
+#pragma unroll
+            for (int m = 0; m < NO; ++m) tz[m] = wem * zb[m];
+#pragma unroll
+            for (int k = 0; k < NSQ; ++k) {
+              const float yv = (4 * k + q4 < NS) ? e[R::kY + 4 * k + q4] : 0.f;
+#pragma unroll
+              for (int m = 0; m < NO; ++m) Ac[k][m] = __builtin_amdgcn_mfma_f32_4x4x1f32(yv, tz[m], Ac[k][m], 0, 0, 0);
+            }
+          } else {
+            float V[NI][NS];
+            cg_contract_out<LI, LS, LO>(zb, V);
+#pragma unroll
+            for (int mi = 0; mi < NI; ++mi) {
+              float s = 0.f;
+#pragma unroll
+              for (int my = 0; my < NS; ++my) s += e[R::kY + my] * V[mi][my];
+              h += xj[mi] * s;
+              xb[mi] += wem * s;
+            }
+#pragma unroll
+            for (int my = 0; my < NS; ++my) {
+              float s = 0.f;
+#pragma unroll
+              for (int mi = 0; mi < NI; ++mi) s += xj[mi] * V[mi][my];
+              wy[my] = s;
+            }
+          }
+          const float hm = tvalid ? h : 0.f;
+#pragma unroll
+          for (int qq = 0; qq < NBQ; ++qq)
+            wb[qq] = __builtin_amdgcn_mfma_f32_4x4x1f32(e[R::kPhi + 4 * qq + q4], hm, wb[qq], 0, 0, 0);
+          if (want_pos) {
+            const float srad = wdr * h;
+            float lanev[3];
+#pragma unroll
+            for (int d = 0; d < 3; ++d) {
+              float s = 0.f;
+#pragma unroll
+              for (int my = 0; my < NS; ++my) s += e[R::kDY + d * R::kNSP + my] * wy[my];
+              // r_bar = w_e' h u + w_e dY^T Ybar
+              lanev[d] = srad * e[R::kU + d] + we * s;
+            }
+            row_sum16x3(lanev[0], lanev[1], lanev[2]);
+            float* sr = s_dyn + ((wave * 64 + (tvalid ? t : 0)) * rows + row_in_slot) * 3;
+            if (tvalid && row_leader) {
+              sr[0] = lanev[0];
+              sr[1] = lanev[1];
+              sr[2] = lanev[2];
+            }
+          }
+        }
+      }
+      __syncthreads();
+      if (want_pos) {
+        if (tid < ne) {
+          float r0 = 0.f, r1 = 0.f, r2 = 0.f;
+          for (int w2 = 0; w2 < nwaves; ++w2)
+            for (int r = 0; r < rows; ++r) {
+              const float* src = s_dyn + ((w2 * 64 + tid) * rows + r) * 3;
+              r0 += src[0];
+              r1 += src[1];
+              r2 += src[2];
+            }
+          float* dst = a.rbar + 3 * static_cast<int64_t>(s_sl[tid]);
+          if (a.rbar_accumulate) {
+            dst[0] += r0;
+            dst[1] += r1;
+            dst[2] += r2;
+          } else {
+            dst[0] = r0;
+            dst[1] = r1;
+            dst[2] = r2;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    if constexpr (XF) {
+      // combine the edge slots of the wave, then x_bar[a] = sum_{b,m} c[a][b][m] A[b][m]
+      for (int off = cp; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < NSQ; ++k)
+#pragma unroll
+          for (int m = 0; m < NO; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Ac[k][m][r] += __shfl_xor(Ac[k][m][r], off);
+#pragma unroll
+      for (int mi = 0; mi < NI; ++mi) {
+        float s = 0.f;
+#pragma unroll
+        for (int b = 0; b < NS; ++b)
+#pragma unroll
+          for (int m = 0; m < NO; ++m)
+            if (C::v[mi][b][m] != 0.f) s += C::v[mi][b][m] * Ac[b / 4][m][b % 4];
+        xb[mi] = s;
+      }
+    } else {
+      for (int off = cp; off < kWave; off <<= 1)
+#pragma unroll
+        for (int mi = 0; mi < NI; ++mi) xb[mi] += __shfl_xor(xb[mi], off);
+    }
+    if (a.x_bar && slot == 0 && uvalid) {
+      float* xo = a.x_bar + static_cast<int64_t>(j) * a.x_dim + a.xoff + u;
+#pragma unroll
+      for (int mi = 0; mi < NI; ++mi) {
+        if (a.xbar_accumulate)
+          xo[mi * a.c] += xb[mi];
+        else
+          xo[mi * a.c] = xb[mi];
+      }
+    }
+  }
+  for (int off = cp; off < kWave; off <<= 1)
+#pragma unroll
+    for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wb[qq][r] += __shfl_xor(wb[qq][r], off);
+  if (a.wbar_part && slot == 0 && uvalid) {
+#pragma unroll
+    for (int qq = 0; qq < NBQ; ++qq)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = 4 * qq + r;
+        if (q < a.g.nb) a.wbar_part[(static_cast<int64_t>(blockIdx.x) * a.g.nb + q) * a.c + u] = wb[qq][r];
+      }
+  }
+}
+
 template <int LI, int LS, int LO, bool NEED_P, bool POS, bool TAN, bool HESS>
 hipError_t bwd_uvw_nb(const BwdUvwArgs& a, int nsend, int ntiles, hipStream_t s) {
   const int nwaves = ntiles * a.nparts;
@@ -717,10 +1019,17 @@ hipError_t bwd_uvu_nb(const BwdUvuArgs& a, int nblocks, int ntiles, hipStream_t 
   dim3 grid(nblocks), block(64 * ntiles);
   const int rows = a.cp / 16;
   const size_t dyn = sizeof(float) * 64 * 3 * rows * ntiles;
-  if (a.g.nb <= 8)
-    hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 2, TAN, HESS>), grid, block, dyn, s, a);
-  else
-    hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 4, TAN, HESS>), grid, block, dyn, s, a);
+  if constexpr (!TAN && !HESS && kUvuFirst) {
+    if (a.g.nb <= 8)
+      hipLaunchKernelGGL((bwd_uvu_first_kernel<LI, LS, LO, 2>), grid, block, dyn, s, a);
+    else
+      hipLaunchKernelGGL((bwd_uvu_first_kernel<LI, LS, LO, 4>), grid, block, dyn, s, a);
+  } else {
+    if (a.g.nb <= 8)
+      hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 2, TAN, HESS>), grid, block, dyn, s, a);
+    else
+      hipLaunchKernelGGL((bwd_uvu_kernel<LI, LS, LO, 4, TAN, HESS>), grid, block, dyn, s, a);
+  }
   return hipGetLastError();
 }
 
