@@ -367,11 +367,12 @@ void bwd_layout(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_t
   }
 }
 
-// Persistent grid of the uvu sender traversal (W_bar partials: one per workgroup).  1024
-// or 4096 workgroups run a lone launch ~10% faster, but the channelwise step, whose
-// launches overlap on two lanes, measured 2-3% slower with either.
+// Persistent grid of the uvu sender traversal (W_bar partials: one per workgroup).  At
+// three resident waves per SIMD (1536 two-wave workgroups) the channelwise workload's
+// backward traversals take 14.5 / 12.9 / 11.8 ms per step with 2048 / 3072 / 4608
+// workgroups (3-4 senders each at 4608, so the launch ends with a short tail).
 #ifndef ETPC_UVU_GRID
-#define ETPC_UVU_GRID 2048
+#define ETPC_UVU_GRID 4608
 #endif
 constexpr int kUvuGrid = ETPC_UVU_GRID;
 

@@ -48,10 +48,8 @@ static_assert(!kXtMfma || kPrefetch % 2 == 0, "the matrix-core radial contractio
 // writes (0x80 | 0x100 | 0x200), so record reads can be hoisted; global loads never.
 constexpr int kSchedMask = 0x380;
 
-// First-order uvu backward in the sender-regrouped form (1) or the per-edge form (0).
-// The regrouped form issues 30-70% fewer VALU instructions per edge but the uvu backward
-// waits on its gathers at two waves per SIMD, so it gained 1-2% (channelwise workload,
-// 16.6 -> 16.3 ms per step of backward traversals).
+// First-order uvu backward: the register-budgeted kernel with matrix-core radial weights
+// and W_bar partials (1) or the general uvu sender traversal (0).
 #ifndef ETPC_BWD_UVU_FIRST
 #define ETPC_BWD_UVU_FIRST 1
 #endif
@@ -62,9 +60,18 @@ constexpr bool kUvuFirst = ETPC_BWD_UVU_FIRST != 0;
 #define ETPC_BWD_UVU_PREFETCH 2
 #endif
 constexpr int kUvuPrefetch = ETPC_BWD_UVU_PREFETCH;
-// 1: the sender-regrouped form where it takes fewer FMAs per edge; 0: per-edge form only
-#ifndef ETPC_BWD_UVU_XFORM
-#define ETPC_BWD_UVU_XFORM 1
+// Register budget of the first-order uvu traversal as resident waves per SIMD (0: the
+// compiler's choice, 2 waves for most paths).  Three waves (168 VGPRs, 0-28 bytes per lane
+// spilled, 48-64 for l_in = l_sh = 3) is what the workgroup's LDS allows; with a persistent
+// grid of 4608 workgroups it measured 28% faster than the compiler's choice on the
+// channelwise workload (backward traversals 16.4 -> 11.8 ms per step).
+#ifndef ETPC_BWD_UVU_WAVES
+#define ETPC_BWD_UVU_WAVES 3
+#endif
+#if ETPC_BWD_UVU_WAVES > 0
+#define ETPC_BWD_UVU_ATTR __attribute__((amdgpu_waves_per_eu(ETPC_BWD_UVU_WAVES)))
+#else
+#define ETPC_BWD_UVU_ATTR
 #endif
 
 // Edge slots of the sender traversals are at least 16 lanes wide (the host rounds the
@@ -711,49 +718,19 @@ __global__ __launch_bounds__(256) void bwd_uvu_kernel(const BwdUvuArgs a) {
   }
 }
 
-// Number of nonzero coupling coefficients of a path (compile time).
-template <int LI, int LS, int LO>
-constexpr int cg_nnz() {
-  int n = 0;
-  for (int a = 0; a < 2 * LI + 1; ++a)
-    for (int b = 0; b < 2 * LS + 1; ++b)
-      for (int m = 0; m < 2 * LO + 1; ++m)
-        if (CgTab<LI, LS, LO>::v[a][b][m] != 0.f) ++n;
-  return n;
-}
-
-// First-order uvu sender traversal with the contractions regrouped around the sender.
-// For lane channel u, sender j and edge e = (j -> i), with c the path's coupling tensor:
-//   Ybar_e[b] = sum_{a,m} c[a][b][m] x_j[a] zb_i[m] = sum_m X_j[b][m] zb_i[m],
-//               X_j[b][m] = sum_a c[a][b][m] x_j[a]             (once per sender)
-//   h_e       = <x_j, Q_e> = sum_b Y_e[b] Ybar_e[b]
-//   x_bar_j[a] = sum_e w_e Q_e[a] = sum_{b,m} c[a][b][m] A_j[b][m],
-//               A_j[b][m] = sum_e Y_e[b] (w_e zb_i[m])          (sender accumulator)
-// (Eq. 7 and 17-22 reassociated; exact in exact arithmetic).  A_j is an outer product of
-// the edge's harmonics with the lane's w_e zb and accumulates on the matrix cores as
-// 4x4x1 blocks (lane 4g + r supplies Y[4k + r], every lane its own w_e zb[m]; register r
-// of Ac[k][m] holds b = 4k + r).  The same blocks carry the radial weights of two trips
-// at once (rows phi or phi' of trip pair members, columns the lane's W[q][u]) and the
-// W_bar partials (rows phi[4qq + r], columns h).  Paths whose coupling tensor is sparse
-// enough that the per-edge form V = c zb, Q = Y V, Ybar = x V costs fewer FMAs (l_in = 0)
-// keep that form for Q and Ybar and use the matrix-core weights and W_bar partials.
-template <int LI, int LS, int LO>
-struct UvuSenderForm {
-  static constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1;
-  static constexpr int kPerEdgeV = cg_nnz<LI, LS, LO>() + 2 * NI * NS + 2 * NI;
-  static constexpr int kPerEdgeX = NS * NO + NS + NO;
-  static constexpr bool kX = ETPC_BWD_UVU_XFORM != 0 && kPerEdgeX < kPerEdgeV;
-};
-
+// First-order uvu sender traversal (x_bar, W_bar partials, r_bar), the same per-edge
+// arithmetic as bwd_uvu_kernel with two parts moved to 4x4x1 matrix-core blocks of four
+// lanes: the radial weights w_e = sum_q phi_q W[q][u] and w_e' = sum_q phi'_q W[q][u] of two
+// trips at once (row r of a block takes phi (r < 2) or phi' (r >= 2) of trip it0 + pf +
+// (r & 1), each lane's column its own W[q][u]), and the W_bar partials sum_e phi_q h_e
+// (rows phi[4qq + r], every lane its own h), which frees the 2B FMAs and B accumulations
+// per edge of the VALU form.  Its register budget (ETPC_BWD_UVU_WAVES) sets the occupancy.
 template <int LI, int LS, int LO, int NBQ>
-__global__ __launch_bounds__(256) void bwd_uvu_first_kernel(const BwdUvuArgs a) {
+__global__ __launch_bounds__(256) ETPC_BWD_UVU_ATTR void bwd_uvu_first_kernel(const BwdUvuArgs a) {
   constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
-  constexpr int NSQ = (NS + 3) / 4;
-  constexpr bool XF = UvuSenderForm<LI, LS, LO>::kX;
   static_assert(kUvuPrefetch % 2 == 0, "the radial weights cover two trips");
   constexpr int kRecAlign = 4;
   using R = BwdRec<NB, NS, true, false, false, kRecAlign>;
-  using C = CgTab<LI, LS, LO>;
   __shared__ __attribute__((aligned(16))) float s_edge[64 * R::kStride];
   __shared__ int s_i[64];
   __shared__ int s_sl[64];
@@ -780,25 +757,7 @@ __global__ __launch_bounds__(256) void bwd_uvu_first_kernel(const BwdUvuArgs a) 
     const float* xr = a.x + static_cast<int64_t>(j) * a.x_dim + a.xoff + u;
 #pragma unroll
     for (int mi = 0; mi < NI; ++mi) xj[mi] = uvalid ? xr[mi * a.c] : 0.f;
-    float X[XF ? NS : 1][XF ? NO : 1];
-    f4v Ac[XF ? NSQ : 1][XF ? NO : 1];
     float xb[NI];
-    if constexpr (XF) {
-#pragma unroll
-      for (int b = 0; b < NS; ++b)
-#pragma unroll
-        for (int m = 0; m < NO; ++m) {
-          float s = 0.f;
-#pragma unroll
-          for (int mi = 0; mi < NI; ++mi)
-            if (C::v[mi][b][m] != 0.f) s += C::v[mi][b][m] * xj[mi];
-          X[b][m] = s;
-        }
-#pragma unroll
-      for (int k = 0; k < NSQ; ++k)
-#pragma unroll
-        for (int m = 0; m < NO; ++m) Ac[k][m] = f4v{0.f, 0.f, 0.f, 0.f};
-    }
 #pragma unroll
     for (int mi = 0; mi < NI; ++mi) xb[mi] = 0.f;
     const int k0 = a.s_rowptr[j], k1 = a.s_rowptr[j + 1];
@@ -853,42 +812,22 @@ __global__ __launch_bounds__(256) void bwd_uvu_first_kernel(const BwdUvuArgs a) 
           const float wem = tvalid ? we : 0.f;
           float wy[NS];
           float h = 0.f;
-          if constexpr (XF) {
+          float V[NI][NS];
+          cg_contract_out<LI, LS, LO>(zb, V);
 #pragma unroll
-            for (int b = 0; b < NS; ++b) {
-              float s = 0.f;
+          for (int mi = 0; mi < NI; ++mi) {
+            float s = 0.f;
 #pragma unroll
-              for (int m = 0; m < NO; ++m) s += X[b][m] * zb[m];
-              wy[b] = s;
-              h += e[R::kY + b] * s;
-            }
-            float tz[NO];
+            for (int my = 0; my < NS; ++my) s += e[R::kY + my] * V[mi][my];
+            h += xj[mi] * s;
+            xb[mi] += wem * s;
+          }
 #pragma unroll
-            for (int m = 0; m < NO; ++m) tz[m] = wem * zb[m];
+          for (int my = 0; my < NS; ++my) {
+            float s = 0.f;
 #pragma unroll
-            for (int k = 0; k < NSQ; ++k) {
-              const float yv = (4 * k + q4 < NS) ? e[R::kY + 4 * k + q4] : 0.f;
-#pragma unroll
-              for (int m = 0; m < NO; ++m) Ac[k][m] = __builtin_amdgcn_mfma_f32_4x4x1f32(yv, tz[m], Ac[k][m], 0, 0, 0);
-            }
-          } else {
-            float V[NI][NS];
-            cg_contract_out<LI, LS, LO>(zb, V);
-#pragma unroll
-            for (int mi = 0; mi < NI; ++mi) {
-              float s = 0.f;
-#pragma unroll
-              for (int my = 0; my < NS; ++my) s += e[R::kY + my] * V[mi][my];
-              h += xj[mi] * s;
-              xb[mi] += wem * s;
-            }
-#pragma unroll
-            for (int my = 0; my < NS; ++my) {
-              float s = 0.f;
-#pragma unroll
-              for (int mi = 0; mi < NI; ++mi) s += xj[mi] * V[mi][my];
-              wy[my] = s;
-            }
+            for (int mi = 0; mi < NI; ++mi) s += xj[mi] * V[mi][my];
+            wy[my] = s;
           }
           const float hm = tvalid ? h : 0.f;
 #pragma unroll
@@ -940,30 +879,9 @@ __global__ __launch_bounds__(256) void bwd_uvu_first_kernel(const BwdUvuArgs a) 
         __syncthreads();
       }
     }
-    if constexpr (XF) {
-      // combine the edge slots of the wave, then x_bar[a] = sum_{b,m} c[a][b][m] A[b][m]
-      for (int off = cp; off < kWave; off <<= 1)
+    for (int off = cp; off < kWave; off <<= 1)
 #pragma unroll
-        for (int k = 0; k < NSQ; ++k)
-#pragma unroll
-          for (int m = 0; m < NO; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Ac[k][m][r] += __shfl_xor(Ac[k][m][r], off);
-#pragma unroll
-      for (int mi = 0; mi < NI; ++mi) {
-        float s = 0.f;
-#pragma unroll
-        for (int b = 0; b < NS; ++b)
-#pragma unroll
-          for (int m = 0; m < NO; ++m)
-            if (C::v[mi][b][m] != 0.f) s += C::v[mi][b][m] * Ac[b / 4][m][b % 4];
-        xb[mi] = s;
-      }
-    } else {
-      for (int off = cp; off < kWave; off <<= 1)
-#pragma unroll
-        for (int mi = 0; mi < NI; ++mi) xb[mi] += __shfl_xor(xb[mi], off);
-    }
+      for (int mi = 0; mi < NI; ++mi) xb[mi] += __shfl_xor(xb[mi], off);
     if (a.x_bar && slot == 0 && uvalid) {
       float* xo = a.x_bar + static_cast<int64_t>(j) * a.x_dim + a.xoff + u;
 #pragma unroll
@@ -1018,7 +936,7 @@ template <int LI, int LS, int LO, bool TAN, bool HESS>
 hipError_t bwd_uvu_nb(const BwdUvuArgs& a, int nblocks, int ntiles, hipStream_t s) {
   dim3 grid(nblocks), block(64 * ntiles);
   const int rows = a.cp / 16;
-  const size_t dyn = sizeof(float) * 64 * 3 * rows * ntiles;
+  const size_t dyn = sizeof(float) * 64 * 3 * rows * ntiles;   // [ntiles][64][rows][3]
   if constexpr (!TAN && !HESS && kUvuFirst) {
     if (a.g.nb <= 8)
       hipLaunchKernelGGL((bwd_uvu_first_kernel<LI, LS, LO, 2>), grid, block, dyn, s, a);
