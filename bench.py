@@ -203,8 +203,8 @@ def _blas_name():
 
 
 KERNEL_FAMILIES = (
-    ("fwd_traverse", ("fwd_uvw_kernel", "fwd_uvu_kernel")),
-    ("bwd_traverse", ("bwd_uvw_kernel", "bwd_uvu_kernel")),
+    ("fwd_traverse", ("fwd_uvw_kernel", "fwd_uvu_kernel", "fwd_uvu_acc_kernel")),
+    ("bwd_traverse", ("bwd_uvw_kernel", "bwd_uvu_kernel", "bwd_uvu_first_kernel")),
     ("gemm", ("gemm_f32_kernel", "gemm_low_kernel")),
     ("csr", ("radix_", "scan_", "lower_bound", "validate_", "iota_", "gather_", "copy_kernel", "degree_key_kernel",
              "window_key_kernel")),

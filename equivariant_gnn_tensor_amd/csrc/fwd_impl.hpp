@@ -44,6 +44,26 @@ constexpr bool kFwdMfma = ETPC_FWD_MFMA != 0;
 #define ETPC_FWD_UVU_ACC 1
 #endif
 constexpr bool kFwdUvuAcc = ETPC_FWD_UVU_ACC != 0;
+// Register budgets as resident waves per SIMD (0: the compiler's choice) of the
+// accumulated uvu forward and of the uvw receiver traversal.  Both forwards measured
+// slower with a budget (uvu at 3 waves: 5.38 -> 5.67 ms per step on the channelwise
+// workload; uvw at 4 waves: 0.597 -> 0.614 ms on workload 2), unlike the uvu backward.
+#ifndef ETPC_FWD_UVU_WAVES
+#define ETPC_FWD_UVU_WAVES 0
+#endif
+#if ETPC_FWD_UVU_WAVES > 0
+#define ETPC_FWD_UVU_ATTR __attribute__((amdgpu_waves_per_eu(ETPC_FWD_UVU_WAVES)))
+#else
+#define ETPC_FWD_UVU_ATTR
+#endif
+#ifndef ETPC_FWD_UVW_WAVES
+#define ETPC_FWD_UVW_WAVES 0
+#endif
+#if ETPC_FWD_UVW_WAVES > 0
+#define ETPC_FWD_UVW_ATTR __attribute__((amdgpu_waves_per_eu(ETPC_FWD_UVW_WAVES)))
+#else
+#define ETPC_FWD_UVW_ATTR
+#endif
 typedef float f4v __attribute__((ext_vector_type(4)));
 
 // LDS per edge: phi[NB], (dphi[NB]), cY[NI*NO], (dcY[NI*NO]), padded by one float.
@@ -108,7 +128,7 @@ __device__ inline void fill_edge(const GeomParams& g, const float* __restrict__ 
 // SPLIT: a.nparts waves share the receiver's edges (small launches); without it the
 // part count is the constant 1 and that code folds away.
 template <int LI, int LS, int LO, int NBQ, bool TANGENT, bool SPLIT = false>
-__global__ __launch_bounds__(SPLIT ? 256 : 64) void fwd_uvw_kernel(const FwdUvwArgs a) {
+__global__ __launch_bounds__(SPLIT ? 256 : 64) ETPC_FWD_UVW_ATTR void fwd_uvw_kernel(const FwdUvwArgs a) {
   constexpr int NI = 2 * LI + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
   using L = EdgeLds<NB, NI * NO, TANGENT>;
   __shared__ float s_edge[64 * L::kStride];
@@ -401,7 +421,7 @@ __device__ inline void fill_edge_y(const GeomParams& g, const float* __restrict_
 }
 
 template <int LI, int LS, int LO, int NBQ>
-__global__ __launch_bounds__(64) void fwd_uvu_acc_kernel(const FwdUvuArgs a) {
+__global__ __launch_bounds__(64) ETPC_FWD_UVU_ATTR void fwd_uvu_acc_kernel(const FwdUvuArgs a) {
   constexpr int NI = 2 * LI + 1, NS = 2 * LS + 1, NO = 2 * LO + 1, NB = 4 * NBQ;
   constexpr int NSQ = (NS + 3) / 4;
   constexpr int kGroup = 4;   // trips per radial-weight group; also the gather distance

@@ -39,17 +39,19 @@ struct ReduceWArgs {
   int32_t cout[kMaxPaths];
 };
 
-// First stage for many partial copies: copy g = blockIdx.y sums copies [g*seg, (g+1)*seg)
-// of each element in order and stores the sum over copy g*seg (only this thread reads or
-// writes that element's copies in the segment, so the update is in place).
-__global__ void segment_sum_kernel(float* __restrict__ part, int splits, int seg, int64_t stride) {
+// Early stage for many partial copies: of the `splits` copies held at copies 0, step,
+// 2 step, ..., group g = blockIdx.y sums copies [g*seg, (g+1)*seg) of each element in order
+// and stores the sum over copy g*seg*step (only this thread reads or writes that element's
+// copies in the group, so the update is in place).
+__global__ void segment_sum_kernel(float* __restrict__ part, int splits, int seg, int64_t stride, int step) {
   const int64_t c = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x;
   if (c >= stride) return;
   const int z0 = blockIdx.y * seg;
   const int z1 = min(splits, z0 + seg);
-  float* p = part + static_cast<int64_t>(z0) * stride + c;
+  const int64_t zs = static_cast<int64_t>(step) * stride;
+  float* p = part + static_cast<int64_t>(z0) * zs + c;
   float s = 0.f;
-  for (int z = z0; z < z1; ++z) s += p[static_cast<int64_t>(z - z0) * stride];
+  for (int z = z0; z < z1; ++z) s += p[static_cast<int64_t>(z - z0) * zs];
   *p = s;
 }
 
@@ -154,15 +156,16 @@ hipError_t launch_reduce_wbar(float* part, int splits, int c_in, int n_paths, in
   a.splits = splits;
   a.split_step = 1;
   constexpr int kSeg = 32;
-  if (splits > 2 * kSeg) {
-    // many copies (one per persistent workgroup): sum segments of kSeg copies in place
-    // first, so the final pass reads splits / kSeg copies with full parallelism
-    const int64_t stride = static_cast<int64_t>(c_in) * ncols;
-    const int groups = (splits + kSeg - 1) / kSeg;
+  // many copies (one per persistent workgroup): sum segments of kSeg copies in place, level
+  // by level, until at most 2 kSeg remain, so every pass reads its copies with full
+  // parallelism and the final pass sums a few per element
+  const int64_t stride = static_cast<int64_t>(c_in) * ncols;
+  while (a.splits > 2 * kSeg) {
+    const int groups = (a.splits + kSeg - 1) / kSeg;
     hipLaunchKernelGGL(segment_sum_kernel, dim3(static_cast<unsigned>((stride + 255) / 256), groups), dim3(256), 0,
-                       s, part, splits, kSeg, stride);
+                       s, part, a.splits, kSeg, stride, a.split_step);
     a.splits = groups;
-    a.split_step = kSeg;
+    a.split_step *= kSeg;
   }
   a.rows = c_in;
   a.ncols = ncols;

@@ -11,8 +11,9 @@ instantiations.  The cases here reach those paths with the oracle still affordab
 - the same graphs with a fraction of the full workspace, and with workspaces sized by a
   scratch budget (the bounded schedule: one buffer set, node chunks per output group or
   input block, one or two edge-adjoint copies);
-- a channelwise (uvu) graph of 4096 nodes, so each of the 2048 persistent backward
-  workgroups strides over two senders and sums W_bar partials over both;
+- a channelwise (uvu) graph of 10240 nodes, so each of the 4608 persistent backward
+  workgroups strides over two or three senders and sums W_bar partials over them, and the
+  4608 partial copies are reduced in three levels;
 - workload 2 at its full size (N = 4096, E = 214,980): z, x_bar, W_bar and pos_bar
   compared with the whole-graph oracle element by element.
 Tolerance (max|d| / max|ref| per output tensor): 1e-4 forward and backward, 1e-3 double
@@ -141,14 +142,14 @@ def test_cfg5_unsplit_double_backward():
         assert max(errs) <= TOL_DBL, errs
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_uvu_persistent_grid_strides():
-    """Channelwise workload recipe at N = 4096 (16 channels per block): the backward's
-    persistent grid of 2048 workgroups takes two senders per workgroup, so every W_bar
-    partial sums over two senders before the fixed-order reduction."""
+    """Channelwise workload recipe at N = 10240 (16 channels per block): the backward's
+    persistent grid of 4608 workgroups takes two or three senders per workgroup, so every
+    W_bar partial sums over several senders before the fixed-order reduction."""
     etpc = _etpc()
-    cfg = dataclasses.replace(small_variant("cfg3", 4096), irreps_in="16x0e+16x1o+16x2e+16x3o",
-                              name="uvu_strided_n4096")
+    cfg = dataclasses.replace(small_variant("cfg3", 10240), irreps_in="16x0e+16x1o+16x2e+16x3o",
+                              name="uvu_strided_n10240")
     c = make_case(cfg)
     note(f"{cfg.name}: N={cfg.n_nodes} E={c.wl.n_edges}, oracle forward + backward")
     rz, rb = _oracle_fwd_bwd(c)
