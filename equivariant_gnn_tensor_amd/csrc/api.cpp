@@ -189,9 +189,13 @@ struct Sched {
   int rbar_copies = 1;
 };
 
-Sched fast_sched(const etpc_plan_s* p) {
+// Above this many bytes per copy the edge adjoint keeps one copy (the traversals that write
+// it then run on one lane): such passes have long launches whose tails a second lane barely
+// fills, and a second copy would add 12 B per edge to a workspace that is otherwise flat in E.
+constexpr int64_t kRbarLaneMaxBytes = int64_t(64) << 20;
+Sched fast_sched(const etpc_plan_s* p, int64_t n_edges) {
   Sched s;
-  s.rbar_copies = rbar_slots(p);
+  s.rbar_copies = 12 * n_edges > kRbarLaneMaxBytes ? 1 : rbar_slots(p);
   return s;
 }
 
@@ -409,7 +413,7 @@ size_t dbl_bytes(const etpc_plan_s* p, const Derived& d, int64_t n_nodes, int64_
 template <class F>
 void choose_schedule(const etpc_plan_s* p, const Derived& d, bool fwd, bool bwd, int64_t n_nodes, int64_t n_edges,
                      size_t ws_bytes, F bytes_of, Sched* sch, int64_t* cap) {
-  const Sched f = fast_sched(p);
+  const Sched f = fast_sched(p, n_edges);
   const int64_t cfull = p->mode == ETPC_UVW ? full_cap(d, n_nodes, fwd, bwd) : 0;
   if (n_nodes <= 0 || bytes_of(cfull, f) <= ws_bytes) {
     *sch = f;
@@ -1127,7 +1131,7 @@ etpc_status etpc_workspace_size(etpc_plan p, int32_t pass, int32_t n_nodes, int6
     if (pass == ETPC_PASS_BWD) return bwd_bytes(p, d, n_nodes, n_edges, c, sc);
     return dbl_bytes(p, d, n_nodes, n_edges, c, sc);
   };
-  const size_t full = bytes_of(p->mode == ETPC_UVW ? full_cap(d, n_nodes, fwd, bwd) : 0, fast_sched(p));
+  const size_t full = bytes_of(p->mode == ETPC_UVW ? full_cap(d, n_nodes, fwd, bwd) : 0, fast_sched(p, n_edges));
   if (budget == 0 || full <= budget || n_nodes == 0) {
     *bytes = full;
     return ETPC_OK;
