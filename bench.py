@@ -432,12 +432,16 @@ def measure(args, name):
     src, dst = T(wl.src), T(wl.dst)
     torch.cuda.synchronize()
 
-    # CSR build, timed on its own (not part of a step)
-    graph = etpc.etpc_csr_build(N, src, dst, order=args.sender_order == "degree")
+    # CSR build (with the dispatch orders), timed on its own (not part of a step).  The
+    # spatial base order needs one shared frame: batches of cells that overlap in space
+    # (workload 6) keep the index base, whose cell-major numbering is already local.
+    spatial = args.dispatch_base == "spatial" and cfg.n_graphs == 1
+    sp_kw = dict(pos=pos, box=(cfg.box,) * 3 if cfg.box else None) if spatial else {}
+    graph = etpc.etpc_csr_build(N, src, dst, order=args.sender_order == "degree", **sp_kw)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(3):
-        graph = etpc.etpc_csr_build(N, src, dst, order=args.sender_order == "degree")
+        graph = etpc.etpc_csr_build(N, src, dst, order=args.sender_order == "degree", **sp_kw)
     torch.cuda.synchronize()
     csr_ms = (time.perf_counter() - t0) / 3 * 1e3
 
@@ -551,6 +555,7 @@ def measure(args, name):
             "launch": "hip graph replay" if args.graph else "eager",
             "node_order": args.node_order,
             "sender_order": args.sender_order,
+            "dispatch_base": "spatial" if spatial and args.sender_order == "degree" else "index",
             "lanes": timed_lanes,
         },
         "roofline": {
@@ -715,6 +720,9 @@ def main():
                     help="concurrent launch lanes per pass for the timed steps (0 = library default)")
     ap.add_argument("--node-order", choices=("given", "morton"), default="given",
                     help="node numbering: as generated (random in space) or Morton order of the positions")
+    ap.add_argument("--dispatch-base", choices=("spatial", "index"), default="spatial",
+                    help="base sequence of the degree-windowed dispatch orders: the Morton order of the "
+                         "positions (single graphs) or the node index")
     ap.add_argument("--sender-order", choices=("degree", "index"), default="degree",
                     help="traversal dispatch: nodes by decreasing degree (the graph's s_order and r_order) "
                          "or in index order")

@@ -12,4 +12,5 @@ from ._binding import (  # noqa: F401
     etpc_profile_enable, etpc_profile_read, etpc_workspace_size, lib, parse_irreps,
     etpc_layout_convert, etpc_radius_graph, etpc_radius_graph_workspace_size,
     etpc_degree_order, etpc_degree_order_workspace_size, RECV_ORDER_WINDOW, SEND_ORDER_WINDOW,
+    etpc_spatial_order, etpc_spatial_order_workspace_size,
 )

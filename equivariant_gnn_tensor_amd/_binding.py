@@ -72,6 +72,7 @@ SYMBOLS = (
     "etpc_forward", "etpc_forward_noalloc", "etpc_backward", "etpc_double_backward",
     "etpc_profile_enable", "etpc_profile_read", "etpc_radius_graph_workspace_size", "etpc_radius_graph",
     "etpc_layout_convert", "etpc_last_error", "etpc_degree_order_workspace_size", "etpc_degree_order",
+    "etpc_degree_order_within", "etpc_spatial_order_workspace_size", "etpc_spatial_order",
 )
 KINDS = ("csr", "fwd_traverse", "channel_gemm", "bwd_traverse", "node_gemm", "aux", "prep")
 
@@ -97,6 +98,9 @@ def _load():
         "etpc_graph_validate": [P(etpc_graph), vp],
         "etpc_degree_order_workspace_size": [i32, P(sz)],
         "etpc_degree_order": [i32, vp, i32, vp, vp, sz, vp],
+        "etpc_degree_order_within": [i32, vp, i32, vp, vp, vp, sz, vp],
+        "etpc_spatial_order_workspace_size": [i32, P(sz)],
+        "etpc_spatial_order": [i32, vp, P(C.c_float), vp, vp, sz, vp],
         "etpc_forward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, sz, vp],
         "etpc_forward_noalloc": [vp, P(etpc_graph), vp, vp, vp, vp, vp],
         "etpc_backward": [vp, P(etpc_graph), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
@@ -332,9 +336,11 @@ def _workspace(nbytes: int, device, stream=None) -> Tuple[Optional[torch.Tensor]
     return t, nbytes
 
 
-def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=None, order: bool = True) -> Graph:
+def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=None, order: bool = True,
+                   pos: torch.Tensor = None, box=None) -> Graph:
     """Both CSR views of the COO list; with `order`, also the sender and receiver
-    dispatch orders (etpc_degree_order of s_rowptr and rowptr)."""
+    dispatch orders (etpc_degree_order of s_rowptr and rowptr, or, given positions,
+    etpc_degree_order_within along their etpc_spatial_order, box = periodic lengths or None)."""
     dev = src.device
     e = int(src.shape[0])
     _check_shape("dst", dst, (e,), dev)
@@ -345,8 +351,9 @@ def etpc_csr_build(n_nodes: int, src: torch.Tensor, dst: torch.Tensor, stream=No
                               _ptr(col, torch.int32), _ptr(eid, torch.int32), _ptr(s_rowptr, torch.int32),
                               _ptr(s_col, torch.int32), _ptr(s_slot, torch.int32),
                               None if ws is None else ws.data_ptr(), nb, _stream(stream)))
-    s_order = etpc_degree_order(s_rowptr, window=SEND_ORDER_WINDOW, stream=stream) if order else None
-    r_order = etpc_degree_order(rowptr, window=RECV_ORDER_WINDOW, stream=stream) if order else None
+    base = etpc_spatial_order(pos, box, stream=stream) if (order and pos is not None) else None
+    s_order = etpc_degree_order(s_rowptr, window=SEND_ORDER_WINDOW, base=base, stream=stream) if order else None
+    r_order = etpc_degree_order(rowptr, window=RECV_ORDER_WINDOW, base=base, stream=stream) if order else None
     return Graph(n_nodes, rowptr, col, s_rowptr, s_col, s_slot, eid=eid, s_order=s_order, r_order=r_order)
 
 
@@ -356,14 +363,41 @@ def etpc_degree_order_workspace_size(n_nodes: int) -> int:
     return b.value
 
 
-def etpc_degree_order(rowptr: torch.Tensor, window: int = 0, stream=None) -> torch.Tensor:
+def etpc_degree_order(rowptr: torch.Tensor, window: int = 0, base: torch.Tensor = None, stream=None) -> torch.Tensor:
     """Nodes by decreasing row length rowptr[v+1] - rowptr[v], ties by index (int32 [N]);
-    with window > 0, within each aligned window of that many nodes."""
+    with window > 0, within each aligned window of that many nodes.  With `base` (a
+    permutation, e.g. etpc_spatial_order), windows and ties follow the base sequence."""
     n = int(rowptr.shape[0]) - 1
     order = _empty_i32(n, rowptr.device)
     ws, nb = _workspace(etpc_degree_order_workspace_size(n), rowptr.device, stream)
-    _check(lib.etpc_degree_order(n, _ptr(rowptr, torch.int32), window, _ptr(order, torch.int32) if n > 0 else None,
-                                 None if ws is None else ws.data_ptr(), nb, _stream(stream)))
+    wsp = None if ws is None else ws.data_ptr()
+    out = _ptr(order, torch.int32) if n > 0 else None
+    if base is None:
+        _check(lib.etpc_degree_order(n, _ptr(rowptr, torch.int32), window, out, wsp, nb, _stream(stream)))
+    else:
+        _check_shape("base", base, (n,), rowptr.device)
+        _check(lib.etpc_degree_order_within(n, _ptr(rowptr, torch.int32), window, _ptr(base, torch.int32), out, wsp,
+                                            nb, _stream(stream)))
+    return order
+
+
+def etpc_spatial_order_workspace_size(n_nodes: int) -> int:
+    b = C.c_size_t()
+    _check(lib.etpc_spatial_order_workspace_size(n_nodes, C.byref(b)))
+    return b.value
+
+
+def etpc_spatial_order(pos: torch.Tensor, box=None, stream=None) -> torch.Tensor:
+    """Nodes by the Morton code of their position (int32 [N]): over the periodic box
+    (box = three lengths) or the bounding box (box = None); ties by index."""
+    n = int(pos.shape[0])
+    _check_shape("pos", pos, (n, 3), pos.device)
+    order = _empty_i32(n, pos.device)
+    ws, nb = _workspace(etpc_spatial_order_workspace_size(n), pos.device, stream)
+    bx = None if box is None else (C.c_float * 3)(*[float(v) for v in box])
+    _check(lib.etpc_spatial_order(n, _ptr(pos, torch.float32) if n > 0 else None, bx,
+                                  _ptr(order, torch.int32) if n > 0 else None,
+                                  None if ws is None else ws.data_ptr(), nb, _stream(stream)))
     return order
 
 

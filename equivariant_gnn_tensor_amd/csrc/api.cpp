@@ -37,8 +37,11 @@ etpc_status csr_build_impl(int32_t n_nodes, int64_t n_edges, const int32_t* src,
                            hipStream_t s);
 etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s);
 size_t degree_order_bytes(int32_t n);
-etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t window, int32_t* order, void* ws,
-                              hipStream_t s);
+etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t window, const int32_t* base_order,
+                              int32_t* order, void* ws, hipStream_t s);
+size_t spatial_order_bytes(int32_t n);
+etpc_status spatial_order_impl(int32_t n, const float* pos, const float* box, int32_t* order, void* ws,
+                               hipStream_t s);
 size_t radius_workspace_bytes(int32_t n_nodes, int64_t max_edges);
 etpc_status radius_graph_impl(int32_t n, const float* pos, float cutoff, const float* box, int64_t max_edges,
                               int32_t* src, int32_t* dst, int64_t* n_edges, void* ws, hipStream_t s);
@@ -1186,7 +1189,40 @@ etpc_status etpc_degree_order(int32_t n_nodes, const int32_t* rowptr, int32_t wi
   etpc_status st = check_ws(ws, ws_bytes, degree_order_bytes(n_nodes));
   if (st != ETPC_OK) return st;
   ::etpc::ProfScope ps(ETPC_KIND_CSR, stream);
-  return degree_order_impl(n_nodes, rowptr, window, order, ws, stream);
+  return degree_order_impl(n_nodes, rowptr, window, nullptr, order, ws, stream);
+}
+
+etpc_status etpc_degree_order_within(int32_t n_nodes, const int32_t* rowptr, int32_t window, const int32_t* base,
+                                     int32_t* order, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (n_nodes < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative node count");
+  if (window < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative window");
+  if (n_nodes == 0) return ETPC_OK;
+  if (rowptr == nullptr || base == nullptr || order == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null arrays");
+  etpc_status st = check_ws(ws, ws_bytes, degree_order_bytes(n_nodes));
+  if (st != ETPC_OK) return st;
+  ::etpc::ProfScope ps(ETPC_KIND_CSR, stream);
+  return degree_order_impl(n_nodes, rowptr, window, base, order, ws, stream);
+}
+
+etpc_status etpc_spatial_order_workspace_size(int32_t n_nodes, size_t* bytes) {
+  if (bytes == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null output");
+  if (n_nodes < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative node count");
+  *bytes = spatial_order_bytes(n_nodes);
+  return ETPC_OK;
+}
+
+etpc_status etpc_spatial_order(int32_t n_nodes, const float* pos, const float* box, int32_t* order, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  if (n_nodes < 0) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "negative node count");
+  if (n_nodes == 0) return ETPC_OK;
+  if (pos == nullptr || order == nullptr) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "null arrays");
+  if (box != nullptr)
+    for (int d = 0; d < 3; ++d)
+      if (!(box[d] > 0.f) || !std::isfinite(box[d])) ETPC_FAIL(ETPC_ERR_INVALID_ARG, "box lengths must be finite and > 0");
+  etpc_status st = check_ws(ws, ws_bytes, spatial_order_bytes(n_nodes));
+  if (st != ETPC_OK) return st;
+  ::etpc::ProfScope ps(ETPC_KIND_CSR, stream);
+  return spatial_order_impl(n_nodes, pos, box, order, ws, stream);
 }
 
 etpc_status etpc_graph_validate(const etpc_graph* g, hipStream_t stream) {

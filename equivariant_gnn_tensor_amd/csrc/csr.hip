@@ -242,35 +242,158 @@ __global__ void degree_key_kernel(const int32_t* __restrict__ rowptr, int32_t n,
   val[v] = v;
 }
 
-// second key: the window of the node each entry now holds
-__global__ void window_key_kernel(const int32_t* __restrict__ val, int32_t n, int32_t window,
-                                  int32_t* __restrict__ key) {
+// the same over a base sequence: entry k takes node base[k]; rank[base[k]] = k
+__global__ void degree_key_base_kernel(const int32_t* __restrict__ rowptr, const int32_t* __restrict__ base, int32_t n,
+                                       int32_t* __restrict__ key, int32_t* __restrict__ val,
+                                       int32_t* __restrict__ rank) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  const int v = base[k];
+  key[k] = 0x7fffffff - (rowptr[v + 1] - rowptr[v]);
+  val[k] = v;
+  rank[v] = k;
+}
+
+// second key: the window of the node each entry now holds (by its index, or by its
+// position in the base sequence)
+__global__ void window_key_kernel(const int32_t* __restrict__ val, const int32_t* __restrict__ rank, int32_t n,
+                                  int32_t window, int32_t* __restrict__ key) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t < n) key[t] = val[t] / window;
+  if (t < n) key[t] = (rank ? rank[val[t]] : val[t]) / window;
+}
+
+// Morton (Z-order) key of a position: 10 bits per axis of the cell of the point in a
+// 1024^3 grid over the box (periodic: the coordinate wrapped into [0, L)) or over the
+// bounding box lo[3] / ext[3] found by bbox_dev_kernel.
+__device__ inline uint32_t spread_bits10(uint32_t v) {
+  v &= 0x3ffu;
+  v = (v | (v << 16)) & 0x030000ffu;
+  v = (v | (v << 8)) & 0x0300f00fu;
+  v = (v | (v << 4)) & 0x030c30c3u;
+  v = (v | (v << 2)) & 0x09249249u;
+  return v;
+}
+
+// one workgroup: lo[3], ext[3] of the points (ext >= a tiny positive floor)
+__global__ __launch_bounds__(1024) void bbox_dev_kernel(const float* __restrict__ pos, int32_t n,
+                                                        float* __restrict__ box6) {
+  __shared__ float red[6][1024];
+  float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+  for (int64_t i = threadIdx.x; i < n; i += 1024)
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const float v = pos[3 * i + a];
+      mn[a] = fminf(mn[a], v);
+      mx[a] = fmaxf(mx[a], v);
+    }
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    red[a][threadIdx.x] = mn[a];
+    red[3 + a][threadIdx.x] = mx[a];
+  }
+  __syncthreads();
+  for (int h = 512; h > 0; h >>= 1) {
+    if (threadIdx.x < h)
+#pragma unroll
+      for (int a = 0; a < 3; ++a) {
+        red[a][threadIdx.x] = fminf(red[a][threadIdx.x], red[a][threadIdx.x + h]);
+        red[3 + a][threadIdx.x] = fmaxf(red[3 + a][threadIdx.x], red[3 + a][threadIdx.x + h]);
+      }
+    __syncthreads();
+  }
+  if (threadIdx.x < 3) {
+    const int a = threadIdx.x;
+    box6[a] = red[a][0];
+    box6[3 + a] = fmaxf(red[3 + a][0] - red[a][0], 1e-30f);
+  }
+}
+
+struct MortonFrame {
+  float box[3];       // periodic box lengths (periodic = 1)
+  int32_t periodic;
+};
+
+__global__ void morton_key_kernel(const float* __restrict__ pos, int32_t n, const MortonFrame f,
+                                  const float* __restrict__ box6, int32_t* __restrict__ key,
+                                  int32_t* __restrict__ val) {
+  // each operation rounded on its own (no fused multiply-add), so the cell of a point is
+  // the one that plain IEEE single-precision arithmetic gives
+#pragma clang fp contract(off)
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= n) return;
+  uint32_t code = 0;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float p = pos[3 * v + a];
+    float t;
+    if (f.periodic) {
+      const float L = f.box[a];
+      t = (p - L * floorf(p / L)) / L;
+    } else {
+      t = (p - box6[a]) / box6[3 + a];
+    }
+    const float c = fminf(fmaxf(t * 1024.f, 0.f), 1023.f);
+    code |= spread_bits10(static_cast<uint32_t>(c)) << a;
+  }
+  key[v] = static_cast<int32_t>(code);
+  val[v] = v;
 }
 
 }  // namespace
 
 size_t degree_order_bytes(int32_t n) {
   const size_t a = (static_cast<size_t>(n) + 63) & ~size_t(63);
-  return sizeof(int32_t) * (4 * a + sort_scratch_ints(n));
+  return sizeof(int32_t) * (5 * a + sort_scratch_ints(n));
 }
 
-etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t window, int32_t* order, void* ws,
-                              hipStream_t s) {
+etpc_status degree_order_impl(int32_t n, const int32_t* rowptr, int32_t window, const int32_t* base_order,
+                              int32_t* order, void* ws, hipStream_t s) {
   if (n == 0) return ETPC_OK;
   const size_t a = (static_cast<size_t>(n) + 63) & ~size_t(63);
   int32_t* base = static_cast<int32_t*>(ws);
-  SortBufs b = make_sort_bufs(base, base + a, base + 2 * a, base + 3 * a, base + 4 * a, n);
-  hipLaunchKernelGGL(degree_key_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, rowptr, n, b.k0, b.v0);
-  // a stable LSD sort over all four key bytes: ties keep increasing node index
+  int32_t* rank = base + 4 * a;
+  SortBufs b = make_sort_bufs(base, base + a, base + 2 * a, base + 3 * a, base + 5 * a, n);
+  if (base_order)
+    hipLaunchKernelGGL(degree_key_base_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, rowptr, base_order, n, b.k0,
+                       b.v0, rank);
+  else
+    hipLaunchKernelGGL(degree_key_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, rowptr, n, b.k0, b.v0);
+  // a stable LSD sort over all four key bytes: ties keep increasing node index (or the
+  // base sequence)
   ETPC_HIP(radix_sort(b, n, 4, s));
   if (window > 0 && window < n) {
     // then stably by window (radix sort keys must be non-negative: v / window is):
     // window-major, heaviest first inside each window
-    hipLaunchKernelGGL(window_key_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, b.v0, n, window, b.k0);
+    hipLaunchKernelGGL(window_key_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, b.v0,
+                       base_order ? rank : nullptr, n, window, b.k0);
     ETPC_HIP(radix_sort(b, n, radix_passes((n + window - 1) / window), s));
   }
+  ETPC_HIP(launch_copy(b.v0, order, n, s));
+  return ETPC_OK;
+}
+
+size_t spatial_order_bytes(int32_t n) {
+  const size_t a = (static_cast<size_t>(n) + 63) & ~size_t(63);
+  return sizeof(int32_t) * (4 * a + sort_scratch_ints(n) + 64);
+}
+
+etpc_status spatial_order_impl(int32_t n, const float* pos, const float* box, int32_t* order, void* ws,
+                               hipStream_t s) {
+  if (n == 0) return ETPC_OK;
+  const size_t a = (static_cast<size_t>(n) + 63) & ~size_t(63);
+  int32_t* base = static_cast<int32_t*>(ws);
+  float* box6 = reinterpret_cast<float*>(base + 4 * a);
+  SortBufs b = make_sort_bufs(base, base + a, base + 2 * a, base + 3 * a, base + 4 * a + 64, n);
+  MortonFrame f{};
+  if (box) {
+    f.periodic = 1;
+    for (int d = 0; d < 3; ++d) f.box[d] = box[d];
+  } else {
+    hipLaunchKernelGGL(bbox_dev_kernel, dim3(1), dim3(1024), 0, s, pos, n, box6);
+  }
+  hipLaunchKernelGGL(morton_key_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, pos, n, f, box6, b.k0, b.v0);
+  // 30-bit keys: four stable digit passes, ties in increasing node index
+  ETPC_HIP(radix_sort(b, n, 4, s));
   ETPC_HIP(launch_copy(b.v0, order, n, s));
   return ETPC_OK;
 }
@@ -319,25 +442,36 @@ __global__ void validate_slots_kernel(const etpc_graph g) {
 }
 
 // sender rows: strictly increasing slots in range
-// order with windows of w nodes: every entry in range and in the
-// window of its position, and each adjacent pair of a window in (decreasing degree,
-// increasing index) order; a window's strictly ordered entries, all from that window
-// and as many as its positions, are a permutation of it
+// order with windows of w positions: every entry in range, counted once per occurrence
+// (count[], zeroed by the caller), and the degrees of each window's entries
+// non-increasing (ties in any order: index order or a base order such as the spatial one)
 __global__ void validate_order_kernel(const int32_t* __restrict__ order, const int32_t* __restrict__ rp, int n,
-                                      int w) {
+                                      int w, int32_t* __restrict__ count) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
   if (k >= n) return;
   const int v = order[k];
-  if (v < 0 || v >= n || v / w != k / w) {
+  if (v < 0 || v >= n) {
     atomicMax(&g_graph_error, 7);
     return;
   }
+  atomicAdd(&count[v], 1);
   if (k + 1 < n && (k + 1) / w == k / w) {
     const int u = order[k + 1];
     if (u < 0 || u >= n) return;   // reported by thread k + 1
     const int dv = rp[v + 1] - rp[v], du = rp[u + 1] - rp[u];
-    if (!(dv > du || (dv == du && v < u))) atomicMax(&g_graph_error, 7);
+    if (dv < du) atomicMax(&g_graph_error, 7);
   }
+}
+
+// every node counted exactly once: the order is a permutation
+__global__ void validate_count_kernel(const int32_t* __restrict__ count, int n) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v < n && count[v] != 1) atomicMax(&g_graph_error, 7);
+}
+
+__global__ void zero_i32_kernel(int32_t* p, int n) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v < n) p[v] = 0;
 }
 
 __global__ void validate_sender_rows_kernel(const etpc_graph g) {
@@ -420,13 +554,26 @@ etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s) {
   if (err == 0) {
     hipLaunchKernelGGL(validate_sender_rows_kernel, dim3(blocks), dim3(threads), 0, s, g);
     hipLaunchKernelGGL(validate_slots_kernel, dim3(blocks), dim3(threads), 0, s, g);
-    if (g.s_order != nullptr && g.n_nodes > 0)
-      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g.s_order, g.s_rowptr, g.n_nodes,
-                         static_cast<int>(ETPC_SEND_ORDER_WINDOW));
-    if (g.r_order != nullptr && g.n_nodes > 0)
-      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, g.r_order, g.rowptr, g.n_nodes,
-                         static_cast<int>(ETPC_RECV_ORDER_WINDOW));
-    ETPC_HIP(hipGetLastError());
+    int32_t* count = nullptr;
+    if ((g.s_order != nullptr || g.r_order != nullptr) && g.n_nodes > 0)
+      ETPC_HIP(hipMalloc(&count, sizeof(int32_t) * static_cast<size_t>(g.n_nodes)));
+    const int32_t* orders[2] = {g.s_order, g.r_order};
+    const int32_t* rps[2] = {g.s_rowptr, g.rowptr};
+    const int windows[2] = {static_cast<int>(ETPC_SEND_ORDER_WINDOW), static_cast<int>(ETPC_RECV_ORDER_WINDOW)};
+    for (int o = 0; o < 2; ++o) {
+      if (orders[o] == nullptr || g.n_nodes == 0) continue;
+      hipLaunchKernelGGL(zero_i32_kernel, dim3(blocks), dim3(threads), 0, s, count, g.n_nodes);
+      hipLaunchKernelGGL(validate_order_kernel, dim3(blocks), dim3(threads), 0, s, orders[o], rps[o], g.n_nodes,
+                         windows[o], count);
+      hipLaunchKernelGGL(validate_count_kernel, dim3(blocks), dim3(threads), 0, s, count, g.n_nodes);
+    }
+    const hipError_t launched = hipGetLastError();
+    if (count != nullptr) {
+      const hipError_t synced = hipStreamSynchronize(s);
+      ETPC_HIP(hipFree(count));
+      ETPC_HIP(synced);
+    }
+    ETPC_HIP(launched);
     ETPC_HIP(hipMemcpyFromSymbolAsync(&err, HIP_SYMBOL(g_graph_error), sizeof(int), 0, hipMemcpyDeviceToHost, s));
     ETPC_HIP(hipStreamSynchronize(s));
   }
@@ -437,7 +584,7 @@ etpc_status graph_validate_impl(const etpc_graph& g, hipStream_t s) {
                                "self loop (sender == receiver)",
                                "sender view does not hold a receiver slot (or s_col mismatch)",
                                "sender row slots out of range or not strictly increasing",
-                               "s_order or r_order is not the decreasing-degree order of its row pointers"};
+                               "s_order or r_order is not a permutation with decreasing degree within windows"};
   if (err != 0) ETPC_FAIL(ETPC_ERR_GRAPH, what[err]);
   return ETPC_OK;
 }

@@ -117,20 +117,23 @@ typedef struct {
 /* Receiver-sorted CSR plus the sender (source) view; all DEVICE pointers.
  * rowptr[N+1], col[E] = sender of each receiver slot;
  * s_rowptr[N+1], s_col[E] = receiver of each sender slot, s_slot[E] = the receiver slot.
- * s_order[N] (optional, NULL = index order): the senders by decreasing out-degree, ties
- * in index order, within aligned windows of ETPC_SEND_ORDER_WINDOW senders:
- * etpc_degree_order(s_rowptr, ETPC_SEND_ORDER_WINDOW).  r_order[N] (optional): likewise
- * the receivers by in-degree within windows of ETPC_RECV_ORDER_WINDOW:
- * etpc_degree_order(rowptr, ETPC_RECV_ORDER_WINDOW).  The uvw traversals then start the
- * longest rows first, which shortens the tail of each launch.  The orders stay
- * window-local so that nodes numbered close together (cells of a batch, a
- * space-filling-curve numbering) still run close together in time and share cache; the
- * sender window is about the number of waves resident on the chip at once, the receiver
- * window a fraction of one XCD's share (the receiver traversals also give each XCD a
- * contiguous range of node slots).  Results are bit-identical either way.
+ * s_order[N] (optional, NULL = index order): the senders by decreasing out-degree within
+ * aligned windows of ETPC_SEND_ORDER_WINDOW senders, ties in index order
+ * (etpc_degree_order(s_rowptr, ETPC_SEND_ORDER_WINDOW)) or windows and ties taken along a
+ * base sequence such as the spatial order (etpc_degree_order_within(s_rowptr,
+ * ETPC_SEND_ORDER_WINDOW, etpc_spatial_order(pos))).  r_order[N] (optional): likewise the
+ * receivers by in-degree within windows of ETPC_RECV_ORDER_WINDOW.  The uvw traversals then
+ * start the longest rows first, which shortens the tail of each launch.  The orders stay
+ * window-local so that nodes that are close (numbered together, as the cells of a batch or
+ * a space-filling-curve numbering, or consecutive in a spatial base order) still run close
+ * together in time and share cache; the sender window is about the number of waves resident
+ * on the chip at once, the receiver window a fraction of one XCD's share (the receiver
+ * traversals also give each XCD a contiguous range of node slots).  Results are
+ * bit-identical for any order.
  * Preconditions (checked only by etpc_graph_validate): indices in range, both views
  * describe the same edge multiset, no self loops, |r_e| > 0 on every edge, s_order and
- * r_order (when given) equal to the etpc_degree_order results named above. */
+ * r_order (when given) permutations of the nodes whose degrees do not increase within each
+ * aligned window of positions. */
 enum { ETPC_SEND_ORDER_WINDOW = 4096, ETPC_RECV_ORDER_WINDOW = 512 };
 typedef struct {
   int32_t n_nodes;
@@ -212,6 +215,27 @@ etpc_status etpc_csr_build(int32_t n_nodes, int64_t n_edges, const int32_t* src,
 etpc_status etpc_degree_order_workspace_size(int32_t n_nodes, size_t* bytes);
 etpc_status etpc_degree_order(int32_t n_nodes, const int32_t* rowptr, int32_t window, int32_t* order, void* ws,
                               size_t ws_bytes, hipStream_t stream);
+/* The same along a base sequence: base [device] int32 [N], a permutation of the nodes
+ * (e.g. etpc_spatial_order).  window = 0: all nodes by decreasing degree, ties in base
+ * order; window > 0: positions [k w, (k+1) w) hold the nodes base[k w .. (k+1) w), heaviest
+ * first, ties in base order.  Workspace from etpc_degree_order_workspace_size; the same
+ * errors, and ETPC_ERR_INVALID_ARG for a null base (base is not checked to be a
+ * permutation). */
+etpc_status etpc_degree_order_within(int32_t n_nodes, const int32_t* rowptr, int32_t window, const int32_t* base,
+                                     int32_t* order, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Spatial node order: the nodes by the Morton (Z-order) code of their position, 10 bits per
+ * axis over a 1024^3 grid, ties in increasing node index.  With box [host] float[3]
+ * (periodic lengths > 0) each coordinate is wrapped into [0, L) first; with box = NULL the
+ * grid spans the points' bounding box.  As the base of the dispatch orders it puts nodes
+ * that share neighbours next to each other, so the workgroups that one XCD runs together
+ * gather overlapping rows through that XCD's L2 (the traversals' gathers of Sec. 4 read
+ * sender rows forward and receiver rows backward).  pos [device] float [N][3]; order
+ * [device] int32 [N] out.  Bit-exact and deterministic; no host synchronization.
+ * Workspace from etpc_spatial_order_workspace_size; ETPC_ERR_INVALID_ARG for N < 0, null
+ * pointers with N > 0, a non-positive or non-finite box length, or a workspace too small. */
+etpc_status etpc_spatial_order_workspace_size(int32_t n_nodes, size_t* bytes);
+etpc_status etpc_spatial_order(int32_t n_nodes, const float* pos, const float* box, int32_t* order, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
 /* Debug check of the graph preconditions listed with etpc_graph (Sec. 4: the traversals
  * own whole rows of cached, stable receiver and source CSR views, so both views must
  * describe one edge multiset in the stable orders etpc_csr_build produces; Eq. 8 needs
@@ -219,8 +243,9 @@ etpc_status etpc_degree_order(int32_t n_nodes, const int32_t* rowptr, int32_t wi
  * and end at n_edges; col / s_col in [0, N); no self loops; s_slot a permutation of the
  * receiver slots with s_col[k] = receiver of slot s_slot[k] and col[s_slot[k]] = the
  * sender of row k; each sender row in increasing slot order; s_order / r_order (when
- * given) equal to their etpc_degree_order results.  Positions are not read, so |r_e| > 0
- * stays the caller's precondition.  Synchronizes the stream and needs no workspace.
+ * given) permutations with non-increasing degree inside each window of positions.
+ * Positions are not read, so |r_e| > 0 stays the caller's precondition.  Synchronizes the
+ * stream; needs no workspace (it allocates N ints of its own while checking the orders).
  * ETPC_ERR_GRAPH with a description of the first violation found; ETPC_ERR_INVALID_ARG
  * for null arrays or negative sizes. */
 etpc_status etpc_graph_validate(const etpc_graph* graph, hipStream_t stream);

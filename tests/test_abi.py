@@ -229,6 +229,30 @@ def test_degree_order_argument_errors():
     assert st != 0 and "workspace" in etpc.lib.etpc_last_error().decode().lower()
 
 
+def test_spatial_and_based_order_argument_errors():
+    """The spatial order and the degree order along a base sequence check their arguments
+    on the host before any launch (placeholder pointers are never dereferenced)."""
+    import ctypes as C
+    lib = _binding.lib
+    assert etpc.etpc_spatial_order_workspace_size(4096) > 0
+    with pytest.raises(etpc.EtpcError):
+        etpc.etpc_spatial_order_workspace_size(-1)
+    assert lib.etpc_spatial_order(0, None, None, None, None, 0, None) == 0     # empty: nothing to do
+    assert lib.etpc_spatial_order(-1, None, None, None, None, 0, None) != 0
+    assert lib.etpc_spatial_order(8, None, None, None, None, 0, None) != 0     # null arrays
+    bad_box = (C.c_float * 3)(10.0, 0.0, 10.0)
+    assert lib.etpc_spatial_order(8, 16, bad_box, 16, 16, 1 << 20, None) != 0
+    assert "box" in lib.etpc_last_error().decode()
+    good_box = (C.c_float * 3)(10.0, 10.0, 10.0)
+    assert lib.etpc_spatial_order(8, 16, good_box, 16, 16, 8, None) != 0      # workspace too small
+    assert "workspace" in lib.etpc_last_error().decode().lower()
+    assert lib.etpc_degree_order_within(0, None, 0, None, None, None, 0, None) == 0
+    assert lib.etpc_degree_order_within(8, 16, 0, None, 16, 16, 1 << 20, None) != 0   # null base
+    assert lib.etpc_degree_order_within(8, 16, -1, 16, 16, 16, 1 << 20, None) != 0    # negative window
+    assert lib.etpc_degree_order_within(8, 16, 0, 16, 16, 16, 8, None) != 0           # workspace too small
+    assert "workspace" in lib.etpc_last_error().decode().lower()
+
+
 def test_noalloc_forward_refuses_oversized_state():
     """The allocation-free forward refuses, on the host and before any HIP call, a plan whose
     single-receiver state exceeds its fixed 128 MiB scratch.  The size is confirmed through

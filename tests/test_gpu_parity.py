@@ -184,9 +184,10 @@ def test_double_backward_all_cotangents(name, n):
 
 @pytest.mark.parametrize("name,n", [("cfg2", 256), ("cfg2", None), ("cfg3", 128)])
 def test_dispatch_order_is_bit_identical(name, n):
-    """Dispatching nodes in decreasing degree (the graph's s_order and r_order) changes only
-    which workgroup takes which node: forward, backward and double backward are
-    bit-identical to the index-order dispatch (the small graph takes the edge-split
+    """Dispatching nodes in decreasing degree (the graph's s_order and r_order, along the
+    node index or along the spatial order of the positions) changes only which workgroup
+    takes which node: forward, backward and double backward are bit-identical to the
+    index-order dispatch (the small graph takes the edge-split
     launches, the full one the plain ones; workload 3 is the channelwise forward)."""
     etpc = _etpc()
     cfg = CONFIGS[name] if n is None else small_variant(name, n)
@@ -201,6 +202,17 @@ def test_dispatch_order_is_bit_identical(name, n):
     torch.cuda.synchronize()
     assert torch.equal(za, zb)
     for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    # the same along the spatial order of the positions
+    box = (cfg.box,) * 3 if cfg.box else None
+    gsp = etpc.etpc_csr_build(cfg.n_nodes, torch.from_numpy(c.wl.src).cuda(), torch.from_numpy(c.wl.dst).cuda(),
+                              pos=c.pos, box=box)
+    etpc.etpc_graph_validate(gsp)
+    zs = etpc.etpc_forward(c.plan, gsp, c.x, c.pos, c.w)
+    s_ = etpc.etpc_backward(c.plan, gsp, c.x, c.pos, c.w, c.z_bar)
+    torch.cuda.synchronize()
+    assert torch.equal(zs, zb)
+    for u, v in zip(s_, b):
         assert torch.equal(u, v)
     if n is not None and name == "cfg2":
         rng = np.random.default_rng(5)

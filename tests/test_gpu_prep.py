@@ -11,7 +11,9 @@ the whole list is checked for order, symmetry and validity.
 
 Degree order: the dispatch orders (decreasing degree, ties by index; over all nodes or
 in aligned windows) equal the oracle's stable sorts bit for bit; etpc_graph_validate
-accepts the graph's orders and rejects wrong ones.
+accepts the graph's orders and rejects wrong ones.  Spatial order: the Morton sort of the
+positions and the degree orders along it equal a direct numpy sort (a dispatch heuristic,
+not part of the method, so the reference lives here rather than in the oracle).
 
 Layout: mul_ir <-> ir_mul of the workloads' input and output irreps, ragged row counts,
 round trips.
@@ -222,23 +224,84 @@ def test_degree_order_matches_oracle(n, e):
     for w, o in s_win.items():
         assert np.array_equal(o.cpu().numpy(), ocsr.degree_order(ref["s_rowptr"], window=w)), w
     etpc.etpc_graph_validate(g)
+    # any permutation whose degrees do not increase inside a window is a valid dispatch
+    # order (the global degree order too); the validator rejects the others
+    etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot,
+                                        s_order=s_win[10 ** 6], r_order=r_all))
     if n > 1:
+        deg = np.diff(ref["s_rowptr"])
         bad = g.s_order.clone()
         bad[[0, -1]] = bad[[-1, 0]]
-        with pytest.raises(etpc.EtpcError) as ei:
-            etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot, s_order=bad))
-        assert ei.value.name == "GRAPH"
+        if deg[int(bad[0])] < deg[int(bad[1])]:          # the swap raised a degree inside window 0
+            with pytest.raises(etpc.EtpcError) as ei:
+                etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot, s_order=bad))
+            assert ei.value.name == "GRAPH"
         bad = g.s_order.clone()
         bad[1] = n
         with pytest.raises(etpc.EtpcError):
             etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot, s_order=bad))
-        if n > etpc.RECV_ORDER_WINDOW and not torch.equal(r_all, g.r_order):
-            # the receiver order is the windowed one
-            with pytest.raises(etpc.EtpcError):
-                etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot,
-                                                    s_order=g.s_order, r_order=r_all))
-        s_all = s_win[10 ** 6]
-        if n > etpc.SEND_ORDER_WINDOW and not torch.equal(s_all, g.s_order):
-            with pytest.raises(etpc.EtpcError):
-                etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot,
-                                                    s_order=s_all, r_order=g.r_order))
+        bad = g.r_order.clone()
+        bad[-1] = bad[-2]                                  # a node twice, another never
+        with pytest.raises(etpc.EtpcError):
+            etpc.etpc_graph_validate(etpc.Graph(n, g.rowptr, g.col, g.s_rowptr, g.s_col, g.s_slot, r_order=bad))
+
+
+def _morton_reference(pos, box):
+    """Morton keys as the spatial order defines them, in float32 with every operation rounded
+    on its own; returns the stable argsort (ties by index)."""
+    p = pos.astype(np.float32)
+    if box is None:
+        lo = p.min(axis=0)
+        ext = np.maximum(p.max(axis=0) - lo, np.float32(1e-30)).astype(np.float32)
+        t = (p - lo) / ext
+    else:
+        L = np.asarray(box, dtype=np.float32)
+        t = (p - L * np.floor(p / L)) / L
+    c = np.minimum(np.maximum(t * np.float32(1024.0), np.float32(0.0)), np.float32(1023.0)).astype(np.uint32)
+
+    def spread(v):
+        v = v & np.uint32(0x3FF)
+        v = (v | (v << np.uint32(16))) & np.uint32(0x030000FF)
+        v = (v | (v << np.uint32(8))) & np.uint32(0x0300F00F)
+        v = (v | (v << np.uint32(4))) & np.uint32(0x030C30C3)
+        v = (v | (v << np.uint32(2))) & np.uint32(0x09249249)
+        return v
+
+    code = spread(c[:, 0]) | (spread(c[:, 1]) << np.uint32(1)) | (spread(c[:, 2]) << np.uint32(2))
+    return np.argsort(code, kind="stable").astype(np.int32)
+
+
+def _degree_order_along(rowptr, window, base):
+    """Windows of positions along `base`, heaviest first inside each, ties in base order."""
+    deg = np.diff(rowptr)[base]
+    win = np.arange(base.size) // window if window > 0 else np.zeros(base.size, dtype=np.int64)
+    return base[np.lexsort((np.arange(base.size), -deg, win))].astype(np.int32)
+
+
+@pytest.mark.parametrize("n,periodic", [(1, True), (4096, True), (16384, True), (5000, False)])
+def test_spatial_order_and_orders_along_it(n, periodic):
+    """etpc_spatial_order equals the Morton sort of the positions (periodic wrap or bounding
+    box, including atoms outside the box), and etpc_degree_order_within takes windows and
+    ties along it; a CSR build given positions carries these orders and validates."""
+    etpc = _etpc()
+    rng = np.random.default_rng(n + 11)
+    L = (n / 0.1) ** (1.0 / 3.0)
+    pos = rng.uniform(-0.2 * L, 1.2 * L, (n, 3)).astype(np.float32)
+    box = (L, L, L) if periodic else None
+    note(f"spatial order N={n} periodic={periodic}")
+    pt = torch.from_numpy(pos).cuda()
+    got = etpc.etpc_spatial_order(pt, box).cpu().numpy()
+    ref = _morton_reference(pos, box)
+    assert np.array_equal(got, ref)
+    e = 40 * n
+    src = rng.integers(0, n, e).astype(np.int32)
+    dst = rng.integers(0, n, e).astype(np.int32)
+    keep = src != dst
+    src, dst = src[keep], dst[keep]
+    g = etpc.etpc_csr_build(n, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda(), pos=pt, box=box)
+    cref = ocsr.csr_build(n, src, dst)
+    assert np.array_equal(g.s_order.cpu().numpy(), _degree_order_along(cref["s_rowptr"], etpc.SEND_ORDER_WINDOW, ref))
+    assert np.array_equal(g.r_order.cpu().numpy(), _degree_order_along(cref["rowptr"], etpc.RECV_ORDER_WINDOW, ref))
+    whole = etpc.etpc_degree_order(g.rowptr, window=0, base=torch.from_numpy(ref).cuda())
+    assert np.array_equal(whole.cpu().numpy(), _degree_order_along(cref["rowptr"], 0, ref))
+    etpc.etpc_graph_validate(g)
