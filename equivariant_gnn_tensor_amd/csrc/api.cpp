@@ -832,8 +832,10 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   PostStream post(s, nl > 1 && pipelined);
   ETPC_HIP(post.status());
   const std::vector<Item> items = make_items(p, d, false, N, L.cap, sch.bounded);
-  // weight re-layouts and Xt of one item into buffer set `b`, on stream `st`
-  auto prep = [&](const Item& it, int b, hipStream_t st) -> etpc_status {
+  // weight re-layouts and Xt of one item into buffer set `b`, on stream `st`; with
+  // `per_path`, one Xt GEMM per path of the item, each marked as a part of the post
+  // work (st is then the post stream)
+  auto prep = [&](const Item& it, int b, hipStream_t st, bool per_path) -> etpc_status {
     const int k = it.blk;
     const int ni = 2 * p->in[k].l + 1;
     const int c_in = p->in[k].mul;
@@ -861,13 +863,33 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       ga.N = static_cast<int32_t>(it.ncols);
       ga.K = c_in;
       ga.k_split = c_in;
-      set_vec4(ga);
-      ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, st, launch_gemm(ga, 1, st));
+      if (!per_path) {
+        set_vec4(ga);
+        ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, st, launch_gemm(ga, 1, st));
+      } else {
+        for (int t = it.t0; t < it.t1; ++t) {
+          const int64_t c0 = d.block_col0[k][t] - it.col0;
+          GemmArgs gp = ga;
+          gp.B = ga.B + c0;
+          gp.C = ga.C + c0;
+          gp.N = static_cast<int32_t>(p->n_basis) * p->paths[p->by_in[k][t]].c_out;
+          set_vec4(gp);
+          ETPC_LAUNCH_ON(ETPC_KIND_NODE_GEMM, st, launch_gemm(gp, 1, st));
+          ETPC_HIP(post.mark_part(t - it.t0));
+        }
+      }
     }
     return ETPC_OK;
   };
+  // The first item's Xt has no earlier traversals to hide behind: with a post stream it
+  // is formed there one path at a time, and each path's traversal waits only for its own
+  // columns, so the traversals start after the first path's GEMM instead of the whole
+  // item's.
+  const bool split_first = pipelined && post.enabled() && want_pos && !items.empty() &&
+                           items[0].t1 - items[0].t0 <= PostStream::kPostParts;
   if (pipelined && !items.empty()) {
-    etpc_status st0 = prep(items[0], 0, s);
+    if (split_first) ETPC_HIP(post.follow());
+    etpc_status st0 = split_first ? prep(items[0], 0, post.stream(), true) : prep(items[0], 0, s, false);
     if (st0 != ETPC_OK) return st0;
   }
   // Each lane's copy of the edge adjoint is first written by its first path (every item of
@@ -886,7 +908,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     const auto& paths = p->by_in[k];
     const int c_in = p->in[k].mul;
     if (!pipelined) {
-      etpc_status stp = prep(it, 0, s);
+      etpc_status stp = prep(it, 0, s, false);
       if (stp != ETPC_OK) return stp;
     }
     // the next item's weights and Xt go into the other set, behind the post work of the
@@ -895,7 +917,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       // the previous item's traversals (which read that set's Xt) are enqueued before
       // this point: the post stream waits for them first
       ETPC_HIP(post.follow());
-      etpc_status stp = prep(items[ii + 1], set ^ 1, post.stream());
+      etpc_status stp = prep(items[ii + 1], set ^ 1, post.stream(), false);
       if (stp != ETPC_OK) return stp;
       ETPC_HIP(post.ready(set ^ 1));
     }
@@ -937,6 +959,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       a.cg = pi.cgf;
       const bool np = R.tangent ? need_plain : main_state;
       const hipStream_t ls = lanes.lane(lane);
+      if (split_first && ii == 0) ETPC_HIP(post.wait_part(ls, t - it.t0));
       ETPC_LAUNCH_ON(ETPC_KIND_BWD_TRAVERSE, ls,
                      launch_bwd_uvw(a, R.hess ? false : np, want_pos, R.tangent, R.hess, pi.l_in, pi.l_out, nsend,
                                     ntiles, ls));

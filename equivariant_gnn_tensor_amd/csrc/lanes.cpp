@@ -22,6 +22,7 @@ struct DeviceLanes {
   hipEvent_t post_slot[2] = {};
   hipEvent_t post_ready[2] = {};
   hipEvent_t post_join = nullptr;
+  hipEvent_t post_part[PostStream::kPostParts] = {};
 };
 
 DeviceLanes g_dev[kMaxDevices];
@@ -49,6 +50,8 @@ bool ensure_post(DeviceLanes& dl) {
   for (int i = 0; ok && i < 2; ++i)
     ok = hipEventCreateWithFlags(&dl.post_slot[i], hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&dl.post_ready[i], hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; ok && i < PostStream::kPostParts; ++i)
+    ok = hipEventCreateWithFlags(&dl.post_part[i], hipEventDisableTiming) == hipSuccess;
   dl.post_ok = ok;
   return ok;
 }
@@ -112,6 +115,7 @@ PostStream::PostStream(hipStream_t main, bool enable) : main_(main) {
   ready_ev_[0] = dl.post_ready[0];
   ready_ev_[1] = dl.post_ready[1];
   join_ev_ = dl.post_join;
+  for (int i = 0; i < kPostParts; ++i) part_ev_[i] = dl.post_part[i];
   on_ = true;
 }
 
@@ -145,6 +149,19 @@ hipError_t PostStream::ready(int slot) {
 hipError_t PostStream::wait_ready(int slot) {
   if (!on_ || err_ != hipSuccess || !readied_[slot & 1]) return err_;
   err_ = hipStreamWaitEvent(main_, ready_ev_[slot & 1], 0);
+  return err_;
+}
+
+hipError_t PostStream::mark_part(int i) {
+  if (!on_ || err_ != hipSuccess || i < 0 || i >= kPostParts) return err_;
+  err_ = hipEventRecord(part_ev_[i], post_);
+  if (err_ == hipSuccess) part_marked_[i] = true;
+  return err_;
+}
+
+hipError_t PostStream::wait_part(hipStream_t st, int i) {
+  if (!on_ || err_ != hipSuccess || i < 0 || i >= kPostParts || !part_marked_[i]) return err_;
+  err_ = hipStreamWaitEvent(st, part_ev_[i], 0);
   return err_;
 }
 

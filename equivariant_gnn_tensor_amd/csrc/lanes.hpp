@@ -68,9 +68,16 @@ class PostStream {
   hipError_t ready(int slot);
   // ...and the caller's stream waits for that before reading it.
   hipError_t wait_ready(int slot);
+  // Part `i` (< kPostParts) of the post work has been enqueued so far...
+  hipError_t mark_part(int i);
+  // ...and stream `st` waits for it (a no-op if part `i` was never marked).
+  hipError_t wait_part(hipStream_t st, int i);
   // The caller's stream waits for all post work (idempotent).
   hipError_t finish();
   hipError_t status() const { return err_; }
+  bool enabled() const { return on_; }
+
+  static constexpr int kPostParts = 16;
 
  private:
   hipStream_t main_;
@@ -83,6 +90,8 @@ class PostStream {
   hipEvent_t slot_ev_[2] = {nullptr, nullptr};
   hipEvent_t ready_ev_[2] = {nullptr, nullptr};
   hipEvent_t join_ev_ = nullptr;
+  hipEvent_t part_ev_[kPostParts] = {};
+  bool part_marked_[kPostParts] = {};
   hipError_t err_ = hipSuccess;
   std::unique_lock<std::mutex> lock_;
 };
