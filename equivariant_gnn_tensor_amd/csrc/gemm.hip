@@ -24,140 +24,28 @@ __device__ inline int64_t rowoff(const RowMap& m, int r) {
   return static_cast<int64_t>(q) * m.s1 + static_cast<int64_t>(r - q * m.div) * m.s2;
 }
 
-// A(m, k) and B(k, n) tiles: each of the 256 threads moves KB / 4 elements of A and of B
-// per K slice, in groups of 4 consecutive elements (float4 when aligned).
-__global__ __launch_bounds__(256) void gemm_f32_kernel(const GemmArgs a) {
-  constexpr int BM = 64, BN = 64, KB = kGemmBK;
+// One workgroup of four wavefronts arranged WGM x WGN computes a (32 WGM) x (32 WGN) tile
+// of C: 64 x 64, or 128 x 32 / 32 x 128 against a 32-channel side.  Per K slice of KB
+// values every thread moves groups of 4 consecutive elements (float4 when aligned) from
+// global memory into LDS tiles As[k][m] and Bs[k][n]; the 32x32x2 MFMA reads k = kk + kh
+// from lane half kh (32 consecutive m or n of one row: no bank conflict).  Groups along m
+// or n (B, and an m-contiguous A) go in as one 16-byte LDS store (row stride 32 WGM + 4 or
+// 32 WGN + 4).  A K-contiguous A is read with eight consecutive lanes per row (full
+// 128-byte row segments) and stored transposed, four 4-byte stores per group, into rows
+// of odd stride 32 WGM + 1, so the 32 lanes of a half-wave (eight k groups x four rows)
+// hit 32 distinct banks.  MC: A is m-contiguous (GemmArgs::a_mcontig).  The wave budget
+// keeps the 64 x 64 tile within 64 VGPRs (eight waves per SIMD: the short-K node GEMMs
+// are latency-bound) and the narrow tiles within 80.
+template <int WGM, int WGN, bool MC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WGM == 2 ? 8 : 6))) void gemm_f32_kernel(
+    const GemmArgs a) {
+  constexpr int BM = 32 * WGM, BN = 32 * WGN, KB = kGemmBK;
   static_assert(KB == 32 || KB == 64, "K slice of 32 or 64");
-  constexpr int TPR = KB / 4;          // threads per A row (K-contiguous A), 4 k each
-  constexpr int RP = 256 / TPR;        // A rows per pass
-  constexpr int HA = BM / RP;          // passes (groups of 4) per thread, K-contiguous A
-  constexpr int HK = KB / 16;          // passes per thread for k-major tiles (16 k rows each)
-  __shared__ float As[KB][BM + 4];
-  __shared__ float Bs[KB][BN + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid & 1, wn = wid >> 1;
-  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
-  const int kz0 = blockIdx.z * a.k_split;
-  const int kz1 = min(a.K, kz0 + a.k_split);
-  float* C = a.C + static_cast<int64_t>(blockIdx.z) * a.c_split_stride;
-
-  // K-contiguous A: rows a_row + RP h, k offset a_k4 (4 consecutive k; TPR threads span
-  // the slice, so a row's slice is one contiguous KB * 4-byte segment)
-  const int a_row = tid / TPR, a_k4 = (tid % TPR) * 4;
-  // k-major tiles: k rows t_k + 16 h, 4 consecutive columns at t_c4
-  const int t_k = tid >> 4, t_c4 = (tid & 15) * 4;
-  constexpr int HAM = HA > HK ? HA : HK;
-  int64_t a_off[HAM];
-  bool a_ok[HAM];
-#pragma unroll
-  for (int h = 0; h < HAM; ++h) {
-    a_off[h] = 0;
-    a_ok[h] = false;
-  }
-  if (!a.a_mcontig) {
-#pragma unroll
-    for (int h = 0; h < HA; ++h) {
-      const int m = m0 + a_row + RP * h;
-      a_ok[h] = m < a.M;
-      if (a_ok[h]) a_off[h] = rowoff(a.amap, m);
-    }
-  }
-  const bool vec = a.vec4 != 0;
-
-  float ra[4 * HAM], rb[4 * HK];
-  auto load4 = [&](const float* p, bool full, int valid, float* dst) {
-    if (full && vec) {
-      const float4 v = *reinterpret_cast<const float4*>(p);
-      dst[0] = v.x;
-      dst[1] = v.y;
-      dst[2] = v.z;
-      dst[3] = v.w;
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) dst[t] = t < valid ? p[t] : 0.f;
-    }
-  };
-  auto load = [&](int k0) {
-    if (!a.a_mcontig) {
-#pragma unroll
-      for (int h = 0; h < HA; ++h) {
-        const int k = k0 + a_k4;
-        const int valid = a_ok[h] ? min(4, kz1 - k) : 0;
-        load4(a.A + a_off[h] + k, valid == 4, valid, ra + 4 * h);
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < HK; ++h) {
-        const int k = k0 + t_k + 16 * h;
-        const int m = m0 + t_c4;
-        const int valid = k < kz1 ? min(4, a.M - m) : 0;
-        load4(a.A + (valid > 0 ? rowoff(a.amap, k) : 0) + m, valid == 4, valid, ra + 4 * h);
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < HK; ++h) {
-      const int k = k0 + t_k + 16 * h;
-      const int n = n0 + t_c4;
-      const int valid = k < kz1 ? min(4, a.N - n) : 0;
-      load4(a.B + static_cast<int64_t>(k < kz1 ? k : 0) * a.ldb + n, valid == 4, valid, rb + 4 * h);
-    }
-  };
-  auto store = [&]() {
-    if (!a.a_mcontig) {
-#pragma unroll
-      for (int h = 0; h < HA; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) As[a_k4 + t][a_row + RP * h] = ra[4 * h + t];
-    } else {
-#pragma unroll
-      for (int h = 0; h < HK; ++h)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) As[t_k + 16 * h][t_c4 + t] = ra[4 * h + t];
-    }
-#pragma unroll
-    for (int h = 0; h < HK; ++h)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) Bs[t_k + 16 * h][t_c4 + t] = rb[4 * h + t];
-  };
-
-  f16v acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  if (kz0 < kz1) load(kz0);
-  const int am = wm * 32 + (lane & 31), bn = wn * 32 + (lane & 31), kh = lane >> 5;
-  for (int k0 = kz0; k0 < kz1; k0 += KB) {
-    store();
-    __syncthreads();
-    if (k0 + KB < kz1) load(k0 + KB);
-#pragma unroll
-    for (int kk = 0; kk < KB; kk += 2)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + kh][am], Bs[kk + kh][bn], acc, 0, 0, 0);
-    __syncthreads();
-  }
-  const int n = n0 + wn * 32 + (lane & 31);
-  if (n < a.N) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (m < a.M) {
-        float* p = C + rowoff(a.cmap, m) + n;
-        *p = a.beta ? (*p + acc[r]) : acc[r];
-      }
-    }
-  }
-}
-
-// The same scheme with the four wavefronts arranged WGM x WGN (4 x 1 or 1 x 4): 128 x 32 or
-// 32 x 128 tiles for products with a 32-channel side.
-// Per K slice each thread moves groups of 4 consecutive elements of A and B (float4 when
-// aligned): BM / 32 groups of A and BN / 32 of B.
-template <int WGM, int WGN>
-__global__ __launch_bounds__(256) void gemm_f32_narrow_kernel(const GemmArgs a) {
-  constexpr int BM = 32 * WGM, BN = 32 * WGN;
-  constexpr int AG = BM / 32, BG = BN / 32;
-  __shared__ float As[BK][BM + 4];
-  __shared__ float Bs[BK][BN + 4];
+  static_assert(WGM * WGN == 4, "four wavefronts per workgroup");
+  constexpr int AG = BM * KB / 1024, BG = BN * KB / 1024;  // float4 groups per thread and slice
+  constexpr int LKM = MC ? BM + 4 : BM + 1, LKN = BN + 4;   // As[k][m] / Bs[k][n] row strides
+  __shared__ __attribute__((aligned(16))) float As[KB * LKM];
+  __shared__ __attribute__((aligned(16))) float Bs[KB * LKN];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid % WGM, wn = wid / WGM;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
@@ -166,44 +54,43 @@ __global__ __launch_bounds__(256) void gemm_f32_narrow_kernel(const GemmArgs a) 
   float* C = a.C + static_cast<int64_t>(blockIdx.z) * a.c_split_stride;
   const bool vec = a.vec4 != 0;
 
-  // group h of this thread (g = tid + 256 h): K-contiguous A -> row g / 8, k4 = 4 (g % 8);
-  // m-contiguous A -> k = g / (BM / 4), m4 = 4 (g % (BM / 4)); B (k-major) -> k = g / (BN / 4),
-  // n4 = 4 (g % (BN / 4)).  Only the A row offsets are kept; the rest is recomputed.
+  // group h of this thread (g = tid + 256 h): K-contiguous A -> row g / (KB / 4),
+  // k4 = 4 (g % (KB / 4)); m-contiguous A -> k = g / (BM / 4), m4 = 4 (g % (BM / 4));
+  // B -> k = g / (BN / 4), n4 = 4 (g % (BN / 4)).  Only the A row offsets are kept.
   int64_t a_off[AG];
   bool a_ok[AG];
-  if (!a.a_mcontig) {
 #pragma unroll
-    for (int h = 0; h < AG; ++h) {
-      const int m = m0 + ((tid + 256 * h) >> 3);
+  for (int h = 0; h < AG; ++h) {
+    a_off[h] = 0;
+    a_ok[h] = false;
+    if constexpr (!MC) {
+      const int m = m0 + (tid + 256 * h) / (KB / 4);
       a_ok[h] = m < a.M;
-      a_off[h] = a_ok[h] ? rowoff(a.amap, m) : 0;
+      if (a_ok[h]) a_off[h] = rowoff(a.amap, m);
     }
   }
-  float ra[AG][4], rb[BG][4];
-  auto load4 = [&](const float* p, int valid, float* dst) {
-    if (valid == 4 && vec) {
-      const float4 v = *reinterpret_cast<const float4*>(p);
-      dst[0] = v.x;
-      dst[1] = v.y;
-      dst[2] = v.z;
-      dst[3] = v.w;
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) dst[t] = t < valid ? p[t] : 0.f;
-    }
+  float4 ra[AG], rb[BG];
+  auto load4 = [&](const float* p, int valid) -> float4 {
+    if (valid == 4 && vec) return *reinterpret_cast<const float4*>(p);
+    float4 v;
+    v.x = valid > 0 ? p[0] : 0.f;
+    v.y = valid > 1 ? p[1] : 0.f;
+    v.z = valid > 2 ? p[2] : 0.f;
+    v.w = valid > 3 ? p[3] : 0.f;
+    return v;
   };
   auto load = [&](int k0) {
 #pragma unroll
     for (int h = 0; h < AG; ++h) {
       const int g = tid + 256 * h;
-      if (!a.a_mcontig) {
-        const int k = k0 + (g & 7) * 4;
-        load4(a.A + a_off[h] + k, a_ok[h] ? min(4, kz1 - k) : 0, ra[h]);
+      if constexpr (!MC) {
+        const int k = k0 + (g % (KB / 4)) * 4;
+        ra[h] = load4(a.A + a_off[h] + k, a_ok[h] ? min(4, kz1 - k) : 0);
       } else {
         const int k = k0 + g / (BM / 4);
         const int m = m0 + (g % (BM / 4)) * 4;
         const int valid = k < kz1 ? min(4, a.M - m) : 0;
-        load4(a.A + (valid > 0 ? rowoff(a.amap, k) : 0) + m, valid, ra[h]);
+        ra[h] = load4(a.A + (valid > 0 ? rowoff(a.amap, k) : 0) + m, valid);
       }
     }
 #pragma unroll
@@ -212,26 +99,27 @@ __global__ __launch_bounds__(256) void gemm_f32_narrow_kernel(const GemmArgs a) 
       const int k = k0 + g / (BN / 4);
       const int n = n0 + (g % (BN / 4)) * 4;
       const int valid = k < kz1 ? min(4, a.N - n) : 0;
-      load4(a.B + static_cast<int64_t>(k < kz1 ? k : 0) * a.ldb + n, valid, rb[h]);
+      rb[h] = load4(a.B + static_cast<int64_t>(k < kz1 ? k : 0) * a.ldb + n, valid);
     }
   };
   auto store = [&]() {
 #pragma unroll
     for (int h = 0; h < AG; ++h) {
       const int g = tid + 256 * h;
-      if (!a.a_mcontig) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) As[(g & 7) * 4 + t][g >> 3] = ra[h][t];
+      if constexpr (!MC) {
+        const int row = g / (KB / 4), k4 = (g % (KB / 4)) * 4;
+        As[k4 * LKM + row] = ra[h].x;
+        As[(k4 + 1) * LKM + row] = ra[h].y;
+        As[(k4 + 2) * LKM + row] = ra[h].z;
+        As[(k4 + 3) * LKM + row] = ra[h].w;
       } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) As[g / (BM / 4)][(g % (BM / 4)) * 4 + t] = ra[h][t];
+        *reinterpret_cast<float4*>(As + (g / (BM / 4)) * LKM + (g % (BM / 4)) * 4) = ra[h];
       }
     }
 #pragma unroll
     for (int h = 0; h < BG; ++h) {
       const int g = tid + 256 * h;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) Bs[g / (BN / 4)][(g % (BN / 4)) * 4 + t] = rb[h][t];
+      *reinterpret_cast<float4*>(Bs + (g / (BN / 4)) * LKN + (g % (BN / 4)) * 4) = rb[h];
     }
   };
 
@@ -240,13 +128,14 @@ __global__ __launch_bounds__(256) void gemm_f32_narrow_kernel(const GemmArgs a) 
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
   if (kz0 < kz1) load(kz0);
   const int am = wm * 32 + (lane & 31), bn = wn * 32 + (lane & 31), kh = lane >> 5;
-  for (int k0 = kz0; k0 < kz1; k0 += BK) {
+  const int a_rd = kh * LKM + am, b_rd = kh * LKN + bn;   // row kh of As[k][m] / Bs[k][n]
+  for (int k0 = kz0; k0 < kz1; k0 += KB) {
     store();
     __syncthreads();
-    if (k0 + BK < kz1) load(k0 + BK);
+    if (k0 + KB < kz1) load(k0 + KB);
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[kk + kh][am], Bs[kk + kh][bn], acc, 0, 0, 0);
+    for (int kk = 0; kk < KB; kk += 2)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[a_rd + kk * LKM], Bs[b_rd + kk * LKN], acc, 0, 0, 0);
     __syncthreads();
   }
   const int n = n0 + wn * 32 + (lane & 31);
@@ -457,15 +346,25 @@ hipError_t launch_gemm(const GemmArgs& a, int splits, hipStream_t s) {
   }
   // a side of at most 32 (a 32-channel operand) gets a 32-wide tile, so no half tile of
   // MFMA work and loads is wasted on padding
+  const bool mc = a.a_mcontig != 0;
   if (a.N <= 32 && a.M > 32) {
     dim3 grid((a.M + 127) / 128, (a.N + 31) / 32, splits);
-    hipLaunchKernelGGL((gemm_f32_narrow_kernel<4, 1>), grid, dim3(256), 0, s, a);
+    if (mc)
+      hipLaunchKernelGGL((gemm_f32_kernel<4, 1, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_f32_kernel<4, 1, false>), grid, dim3(256), 0, s, a);
   } else if (a.M <= 32 && a.N > 32) {
     dim3 grid((a.M + 31) / 32, (a.N + 127) / 128, splits);
-    hipLaunchKernelGGL((gemm_f32_narrow_kernel<1, 4>), grid, dim3(256), 0, s, a);
+    if (mc)
+      hipLaunchKernelGGL((gemm_f32_kernel<1, 4, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_f32_kernel<1, 4, false>), grid, dim3(256), 0, s, a);
   } else {
     dim3 grid((a.M + 63) / 64, (a.N + 63) / 64, splits);
-    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, a);
+    if (mc)
+      hipLaunchKernelGGL((gemm_f32_kernel<2, 2, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_f32_kernel<2, 2, false>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
