@@ -21,6 +21,7 @@
 //                  same traversals in tangent mode plus the same GEMMs.
 #include <algorithm>
 #include <cmath>
+#include <optional>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -600,6 +601,14 @@ std::vector<int> block_order(const etpc_plan_s* p, const Derived& d) {
   return order;
 }
 
+// Whether work enqueued on s is being captured into a HIP graph.  Passes keep their
+// lanes forked across work items only outside capture: under capture they join the lanes
+// at every item, the form whose captured graphs are tested to replay bit-identically.
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+}
+
 // One uvw forward evaluation into z (beta: accumulate into z).  With tangent, the
 // receiver traversal builds dS along pos_dot.  xin / win select the operands.
 // nl: concurrent lanes the call may use (lane_cap, or 1 to stay on the caller's stream).
@@ -609,20 +618,34 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   const GeomParams geom = p->geom();
   const int32_t N = g->n_nodes;
   // the channel GEMM of one item runs on the post stream while the next item's
-  // traversals fill the other S set; the largest groups go first, so they overlap most
+  // traversals fill the other S set; the largest groups go first, so they overlap most.
+  // With the post stream the lanes stay forked for the whole pass: a lane goes on to the
+  // next item's paths as soon as its own are done (only the GEMM waits for every lane),
+  // and waits for the GEMM that last read the S set it is about to fill.
   PostStream post(s, nl > 1);
   ETPC_HIP(post.status());
-  int set = 0;
+  const bool keep = post.enabled() && !capturing(s);
+  std::optional<LaneGroup> pass_lanes;
+  if (keep) {
+    pass_lanes.emplace(s, nl);
+    ETPC_HIP(pass_lanes->status());
+  }
+  int set = 0, t_glob = 0;
   for (const Item& it : make_items(p, d, true, N, L.cap, sch.bounded)) {
     const int gi = it.blk;
     const auto& paths = p->by_out[gi];
     const int no = 2 * p->out[gi].l + 1;
     const int c_out = p->out[gi].mul;
     const int nrecv = it.nn;
-    ETPC_HIP(post.wait_slot(set));
     // the item's paths fill disjoint column ranges of S: concurrent lanes
-    LaneGroup lanes(s, std::min(it.t1 - it.t0, nl));
-    ETPC_HIP(lanes.status());
+    std::optional<LaneGroup> item_lanes;
+    if (!keep) {
+      ETPC_HIP(post.wait_slot(set));
+      item_lanes.emplace(s, std::min(it.t1 - it.t0, nl));
+      ETPC_HIP(item_lanes->status());
+    }
+    LaneGroup& lanes = keep ? *pass_lanes : *item_lanes;
+    unsigned waited = 0;   // kept lanes that already wait for this item's S set
     int64_t col0 = 0;
     for (int t = 0; t < it.t1; ++t) {
       const PathInfo& pi = p->paths[paths[t]];
@@ -652,11 +675,19 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       a.nparts = edge_parts(nrecv * ntiles, 1, g, pi.l_out, p->n_basis, 1);
       a.g = geom;
       a.cg = pi.cgf;
-      const hipStream_t ls = lanes.lane(t - it.t0);
+      const int lane = keep ? t_glob++ % nl : t - it.t0;
+      const hipStream_t ls = lanes.lane(lane);
+      if (keep && !(waited & (1u << lane))) {
+        ETPC_HIP(post.wait_slot_on(ls, set));
+        waited |= 1u << lane;
+      }
       ETPC_LAUNCH_ON(ETPC_KIND_FWD_TRAVERSE, ls, launch_fwd_uvw(a, tangent, pi.l_in, pi.l_out, nrecv, ntiles, ls));
       col0 += cols;
     }
-    ETPC_HIP(lanes.finish());
+    if (keep)
+      ETPC_HIP(lanes.signal(post.stream()));
+    else
+      ETPC_HIP(lanes.finish());
     ETPC_HIP(post.follow());
     // z rows of the item's receivers (+)= S W over the item's paths: the first path subset
     // of a node range writes (unless the caller accumulates), later ones add
@@ -678,6 +709,7 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     ETPC_HIP(post.mark(set));
     if (L.nsets > 1) set ^= 1;
   }
+  if (keep) ETPC_HIP(pass_lanes->finish());
   ETPC_HIP(post.finish());
   return ETPC_OK;
 }
@@ -899,6 +931,16 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   for (int l = 0; l < kLanes; ++l) rbar_started[l] = R.rbar_acc || sch.bounded;
   if (want_pos && sch.bounded && !R.rbar_acc)
     ETPC_LAUNCH(ETPC_KIND_AUX, launch_fill(R.rbar, rbar_stride * nl, 0.f, s));
+  // With the post stream the lanes stay forked for the whole pass: a lane goes on to the
+  // next item's paths as soon as its own are done, after waiting for that item's Xt and
+  // for the post work that last read the P set it writes; the post stream waits for every
+  // lane before it reads P or overwrites an Xt set.
+  const bool keep = post.enabled() && !capturing(s);
+  std::optional<LaneGroup> pass_lanes;
+  if (keep) {
+    pass_lanes.emplace(s, nl);
+    ETPC_HIP(pass_lanes->status());
+  }
   int t_glob = 0;
   for (size_t ii = 0; ii < items.size(); ++ii) {
     const Item& it = items[ii];
@@ -916,18 +958,26 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     if (pipelined && ii + 1 < items.size()) {
       // the previous item's traversals (which read that set's Xt) are enqueued before
       // this point: the post stream waits for them first
+      if (keep) ETPC_HIP(pass_lanes->signal(post.stream()));
       ETPC_HIP(post.follow());
       etpc_status stp = prep(items[ii + 1], set ^ 1, post.stream(), false);
       if (stp != ETPC_OK) return stp;
       ETPC_HIP(post.ready(set ^ 1));
     }
-    ETPC_HIP(post.wait_ready(set));   // this item's Xt (prefetched, or made above on s)
-    ETPC_HIP(post.wait_slot(set));    // its P set is no longer read by older post work
+    if (!keep) {
+      ETPC_HIP(post.wait_ready(set));   // this item's Xt (prefetched, or made above on s)
+      ETPC_HIP(post.wait_slot(set));    // its P set is no longer read by older post work
+    }
     float* const Pset = L.P[set];
     float* const Pmain = R.tangent ? L.Pd[set] : L.P[set];
     // the item's paths write disjoint P columns and their own lane's edge adjoint copy
-    LaneGroup lanes(s, nl);
-    ETPC_HIP(lanes.status());
+    std::optional<LaneGroup> item_lanes;
+    if (!keep) {
+      item_lanes.emplace(s, nl);
+      ETPC_HIP(item_lanes->status());
+    }
+    LaneGroup& lanes = keep ? *pass_lanes : *item_lanes;
+    unsigned waited = 0;   // kept lanes that already wait for this item's Xt and P sets
     for (int t = it.t0; t < it.t1; ++t, ++t_glob) {
       const PathInfo& pi = p->paths[paths[t]];
       const int lane = t_glob % nl;
@@ -959,13 +1009,21 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       a.cg = pi.cgf;
       const bool np = R.tangent ? need_plain : main_state;
       const hipStream_t ls = lanes.lane(lane);
+      if (keep && !(waited & (1u << lane))) {
+        ETPC_HIP(post.wait_ready_on(ls, set));
+        ETPC_HIP(post.wait_slot_on(ls, set));
+        waited |= 1u << lane;
+      }
       if (split_first && ii == 0) ETPC_HIP(post.wait_part(ls, t - it.t0));
       ETPC_LAUNCH_ON(ETPC_KIND_BWD_TRAVERSE, ls,
                      launch_bwd_uvw(a, R.hess ? false : np, want_pos, R.tangent, R.hess, pi.l_in, pi.l_out, nsend,
                                     ntiles, ls));
       if (want_pos) rbar_started[lane] = true;
     }
-    ETPC_HIP(lanes.finish());
+    if (keep)
+      ETPC_HIP(lanes.signal(post.stream()));
+    else
+      ETPC_HIP(lanes.finish());
     if (R.x_out || R.w_out) {
       ETPC_HIP(post.follow());
       const hipStream_t ps = post.stream();
@@ -1008,6 +1066,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
       ETPC_HIP(post.mark(set));
     }
   }
+  if (keep) ETPC_HIP(pass_lanes->finish());
   ETPC_HIP(post.finish());
   return ETPC_OK;
 }

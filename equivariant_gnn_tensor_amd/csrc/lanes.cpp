@@ -82,6 +82,15 @@ LaneGroup::LaneGroup(hipStream_t main, int n) : main_(main) {
   forked_ = true;
 }
 
+hipError_t LaneGroup::signal(hipStream_t target) {
+  if (!forked_ || done_ || err_ != hipSuccess) return err_;
+  for (int i = 0; i < n_ && err_ == hipSuccess; ++i) {
+    err_ = hipEventRecord(join_[i], side_[i]);
+    if (err_ == hipSuccess) err_ = hipStreamWaitEvent(target, join_[i], 0);
+  }
+  return err_;
+}
+
 hipError_t LaneGroup::finish() {
   if (done_) return err_;
   done_ = true;
@@ -149,6 +158,18 @@ hipError_t PostStream::ready(int slot) {
 hipError_t PostStream::wait_ready(int slot) {
   if (!on_ || err_ != hipSuccess || !readied_[slot & 1]) return err_;
   err_ = hipStreamWaitEvent(main_, ready_ev_[slot & 1], 0);
+  return err_;
+}
+
+hipError_t PostStream::wait_slot_on(hipStream_t st, int slot) {
+  if (!on_ || err_ != hipSuccess || !marked_[slot & 1]) return err_;
+  err_ = hipStreamWaitEvent(st, slot_ev_[slot & 1], 0);
+  return err_;
+}
+
+hipError_t PostStream::wait_ready_on(hipStream_t st, int slot) {
+  if (!on_ || err_ != hipSuccess || !readied_[slot & 1]) return err_;
+  err_ = hipStreamWaitEvent(st, ready_ev_[slot & 1], 0);
   return err_;
 }
 

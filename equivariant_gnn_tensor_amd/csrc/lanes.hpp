@@ -27,6 +27,9 @@ class LaneGroup {
 
   int size() const { return n_; }
   hipStream_t lane(int i) const { return forked_ ? side_[i % n_] : main_; }
+  // Stream `target` waits for everything enqueued on the lanes so far; the lanes stay
+  // forked, so a pass can keep them across its work items (a no-op when not forked).
+  hipError_t signal(hipStream_t target);
   // Joins the lanes back into the caller's stream (idempotent).
   hipError_t finish();
   hipError_t status() const { return err_; }
@@ -68,6 +71,9 @@ class PostStream {
   hipError_t ready(int slot);
   // ...and the caller's stream waits for that before reading it.
   hipError_t wait_ready(int slot);
+  // wait_slot / wait_ready for another stream `st` (a lane kept across work items)
+  hipError_t wait_slot_on(hipStream_t st, int slot);
+  hipError_t wait_ready_on(hipStream_t st, int slot);
   // Part `i` (< kPostParts) of the post work has been enqueued so far...
   hipError_t mark_part(int i);
   // ...and stream `st` waits for it (a no-op if part `i` was never marked).
