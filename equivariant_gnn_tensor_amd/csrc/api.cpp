@@ -156,16 +156,27 @@ Derived derive(const etpc_plan_s* p) {
   return d;
 }
 
+// Workgroups a split-K GEMM aims for (split count = this / output tiles, at least 256 rows
+// of K per split).
+#ifndef ETPC_GEMM_TARGET_WG
+#define ETPC_GEMM_TARGET_WG 1024
+#endif
+constexpr int64_t kGemmTargetWg = ETPC_GEMM_TARGET_WG;
+
 int pick_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
-  int64_t sp = (1024 + tiles - 1) / tiles;
+  int64_t sp = (kGemmTargetWg + tiles - 1) / tiles;
   sp = std::min<int64_t>(sp, (K + 255) / 256);
   sp = std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
   return static_cast<int>(sp);
 }
 
 // ---------------------------------------------------------------- workspace layouts
-constexpr int kGemmSplits = 8;   // split-K partial sets kept for the long-K channel / x_bar GEMMs
+// split-K partial sets kept for the long-K channel / x_bar GEMMs
+#ifndef ETPC_GEMM_SPLIT_SLOTS
+#define ETPC_GEMM_SPLIT_SLOTS 8
+#endif
+constexpr int kGemmSplits = ETPC_GEMM_SPLIT_SLOTS;
 
 // Up to two sets of the buffers the node-side GEMMs read (S forward; Xt, P and the
 // re-laid-out weights backward): work items alternate between them, so one item's GEMMs
@@ -794,10 +805,11 @@ hipError_t wbar_gemm(const etpc_plan_s* p, int k, const float* xa, int64_t j0, i
   const int ni = 2 * p->in[k].l + 1;
   const int c_in = p->in[k].mul;
   const int64_t K = static_cast<int64_t>(nsend) * ni;
-  // enough splits for about 1024 workgroups, at least 256 rows of K each (not capped at
-  // kMaxSplits: an item of one path has few output tiles), within the partials' room
+  // enough splits for about kGemmTargetWg workgroups, at least 256 rows of K each (not
+  // capped at kMaxSplits: an item of one path has few output tiles), within the partials' room
   const int64_t tiles = ((c_in + 63) / 64) * ((ncols + 63) / 64);
-  int sp = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((1024 + tiles - 1) / tiles, (K + 255) / 256)));
+  int sp = static_cast<int>(
+      std::max<int64_t>(1, std::min<int64_t>((kGemmTargetWg + tiles - 1) / tiles, (K + 255) / 256)));
   const int64_t per = static_cast<int64_t>(c_in) * ncols;
   sp = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(sp, max_floats / per)));
   int64_t ks = (K + sp - 1) / sp;
