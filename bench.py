@@ -318,6 +318,85 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
     print(json.dumps(out, indent=1))
 
 
+def summarize_timeline(d, workload, steps, warmup):
+    """Concurrency of one step as run (default lanes and post stream) from a rocprofv3 kernel
+    trace, DIR/timeline_<workload>, into profiles/timeline_<workload>.md: for each timed step
+    the wall span, the time any kernel runs, the time a traversal runs, and per pass (forward:
+    up to the backward's first weight re-layout; backward: the rest) the span, the traversal
+    time and the tail after the last traversal."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, f"timeline_{workload}", "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {d}/timeline_{workload}")
+    ev = []
+    for r in csv.DictReader(open(files[0])):
+        fam = kernel_family(r["Kernel_Name"])
+        ev.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), fam, "wprep" in r["Kernel_Name"]))
+    ev.sort()
+    # a step starts at a forward traversal that follows backward work
+    starts, prev = [], None
+    for i, (_, _, fam, _) in enumerate(ev):
+        if fam == "fwd_traverse" and prev in (None, "bwd_traverse"):
+            starts.append(i)
+        if fam in ("fwd_traverse", "bwd_traverse"):
+            prev = fam
+    segs = [ev[a:b] for a, b in zip(starts, starts[1:] + [len(ev)])]
+
+    def union(iv):
+        tot, cs, ce = 0, None, None
+        for s0, e0 in sorted(iv):
+            if cs is None or s0 > ce:
+                tot += 0 if cs is None else ce - cs
+                cs, ce = s0, e0
+            else:
+                ce = max(ce, e0)
+        return tot + (0 if cs is None else ce - cs)
+
+    trav = ("fwd_traverse", "bwd_traverse")
+    cmd_args = f"--steps {steps} --warmup {warmup} --no-cpu-baseline --workload {workload}"
+    lines = [f"# Concurrency of a step as run (two lanes and the post stream), workload {workload}", "",
+             "Commands (repo root, one MI355X):", "", "```",
+             f"rocprofv3 --kernel-trace --output-format csv -d DIR/timeline_{workload} -o run -- "
+             f"python3 bench.py {cmd_args}",
+             f"python bench.py --summarize-timeline DIR --steps {steps} --warmup {warmup} --workload {workload}",
+             "```", "",
+             f"Steps {warmup}..{warmup + steps - 1} of the run (after {warmup} warmup steps) are the timed, concurrent "
+             "ones; times in us from the kernel trace (the profiler itself adds launch overhead). "
+             "`busy`: some kernel runs; `traversal`: some traversal runs; `tail`: from the pass's last traversal "
+             "end to its last kernel end (node-side GEMMs and reductions left after the traversals). "
+             "Sums are kernel durations added up (concurrent kernels each count in full).", "",
+             "| step | span | busy | traversal | fwd span | fwd traversal | fwd tail | bwd span | bwd traversal | "
+             "bwd tail | sum fwd_traverse | sum bwd_traverse | sum gemm | sum aux |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in range(warmup, min(warmup + steps, len(segs))):
+        seg = segs[k]
+        t0, t1 = seg[0][0], max(e for _, e, _, _ in seg)
+        b0 = next((s0 for s0, _, _, w in seg if w), t1)
+        fw = [x for x in seg if x[0] < b0]
+        bw = [x for x in seg if x[0] >= b0]
+
+        def part(xs):
+            if not xs:
+                return 0, 0, 0
+            a0, a1 = xs[0][0], max(e for _, e, _, _ in xs)
+            tr = [(s0, e0) for s0, e0, f, _ in xs if f in trav]
+            last = max((e0 for _, e0 in tr), default=a0)
+            return (a1 - a0) / 1e3, union(tr) / 1e3, (a1 - last) / 1e3
+
+        fs, ft, ftl = part(fw)
+        bs, bt, btl = part(bw)
+        sums = {f: sum(e0 - s0 for s0, e0, g, _ in seg if g == f) / 1e3 for f in ("fwd_traverse", "bwd_traverse",
+                                                                               "gemm", "aux")}
+        lines.append(f"| {k} | {(t1 - t0) / 1e3:.1f} | {union([(s0, e0) for s0, e0, _, _ in seg]) / 1e3:.1f} | "
+                     f"{union([(s0, e0) for s0, e0, f, _ in seg if f in trav]) / 1e3:.1f} | {fs:.1f} | {ft:.1f} | "
+                     f"{ftl:.1f} | {bs:.1f} | {bt:.1f} | {btl:.1f} | {sums['fwd_traverse']:.1f} | "
+                     f"{sums['bwd_traverse']:.1f} | {sums['gemm']:.1f} | {sums['aux']:.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"timeline_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 SQ_RUNS = {
     # one rocprofv3 --pmc pass each (at most 8 SQ counters per pass)
     "sq1": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAVES "
@@ -736,7 +815,12 @@ def main():
                     help="time the graph-preparation steps (radius graph, layout conversion)")
     ap.add_argument("--summarize-profile", metavar="DIR", default=None,
                     help="summarize rocprofv3 output under DIR into profiles/ and exit (no GPU needed)")
+    ap.add_argument("--summarize-timeline", metavar="DIR", default=None,
+                    help="summarize a rocprofv3 kernel trace of a concurrent run under DIR into profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_timeline:
+        summarize_timeline(args.summarize_timeline, args.workload, args.steps, args.warmup)
+        return
     if args.summarize_profile:
         summarize_profile(args.summarize_profile, args.workload, args.steps, args.warmup, args.copy_calibration_mib)
         return
