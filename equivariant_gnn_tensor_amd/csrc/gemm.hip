@@ -44,8 +44,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WGM == 2 ? 
   static_assert(WGM * WGN == 4, "four wavefronts per workgroup");
   constexpr int AG = BM * KB / 1024, BG = BN * KB / 1024;  // float4 groups per thread and slice
   constexpr int LKM = MC ? BM + 4 : BM + 1, LKN = BN + 4;   // As[k][m] / Bs[k][n] row strides
-  __shared__ __attribute__((aligned(16))) float As[KB * LKM];
-  __shared__ __attribute__((aligned(16))) float Bs[KB * LKN];
+  // the operand tiles, then (after the last slice) the C tile on its way out
+  __shared__ __attribute__((aligned(16))) float smem[KB * LKM + KB * LKN];
+  float* const As = smem;
+  float* const Bs = smem + KB * LKM;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid % WGM, wn = wid / WGM;
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
@@ -138,15 +140,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WGM == 2 ? 
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[a_rd + kk * LKM], Bs[b_rd + kk * LKN], acc, 0, 0, 0);
     __syncthreads();
   }
-  const int n = n0 + wn * 32 + (lane & 31);
-  if (n < a.N) {
+  // C leaves through LDS (the last slice ended with a barrier, so the operand tiles are
+  // free): each thread writes four consecutive columns of a row as one 16-byte store, where
+  // the MFMA layout would give 4-byte stores of 32-column half rows (16 store instructions
+  // per wave instead of 4).
+  constexpr int LC = BN + 1;
+  static_assert(BM * LC <= KB * LKM + KB * LKN, "the C tile fits the operand tiles");
+  float* const Cs = smem;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (m < a.M) {
-        float* p = C + rowoff(a.cmap, m) + n;
-        *p = a.beta ? (*p + acc[r]) : acc[r];
+  for (int r = 0; r < 16; ++r)
+    Cs[(wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * LC + wn * 32 + (lane & 31)] = acc[r];
+  __syncthreads();
+  const bool cvec = (reinterpret_cast<uintptr_t>(C) & 15) == 0 && a.cmap.s1 % 4 == 0 &&
+                    (a.cmap.div == 1 || a.cmap.s2 % 4 == 0);
+#pragma unroll
+  for (int it = 0; it < BM * BN / 1024; ++it) {
+    const int idx = (it * 256 + tid) * 4;
+    const int row = idx / BN, col = idx % BN;
+    const int m = m0 + row, n = n0 + col;
+    if (m >= a.M) continue;
+    float v[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = Cs[row * LC + col + c];
+    float* p = C + rowoff(a.cmap, m) + n;
+    if (cvec && n + 3 < a.N) {
+      float4 o = make_float4(v[0], v[1], v[2], v[3]);
+      if (a.beta) {
+        const float4 q = *reinterpret_cast<const float4*>(p);
+        o.x += q.x;
+        o.y += q.y;
+        o.z += q.z;
+        o.w += q.w;
       }
+      *reinterpret_cast<float4*>(p) = o;
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (n + c < a.N) p[c] = a.beta ? (p[c] + v[c]) : v[c];
     }
   }
 }
