@@ -44,8 +44,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WGM == 2 ? 
   static_assert(WGM * WGN == 4, "four wavefronts per workgroup");
   constexpr int AG = BM * KB / 1024, BG = BN * KB / 1024;  // float4 groups per thread and slice
   constexpr int LKM = MC ? BM + 4 : BM + 1, LKN = BN + 4;   // As[k][m] / Bs[k][n] row strides
-  // the operand tiles, then (after the last slice) the C tile on its way out
-  __shared__ __attribute__((aligned(16))) float smem[KB * LKM + KB * LKN];
+  // the operand tiles, then (after the last slice) the C tile on its way out (row stride
+  // BN + 4: the MFMA-layout writes and the 16-byte row reads are both free of bank conflicts)
+  constexpr int LC = BN + 4;
+  constexpr int kSmem = KB * LKM + KB * LKN > BM * LC ? KB * LKM + KB * LKN : BM * LC;
+  __shared__ __attribute__((aligned(16))) float smem[kSmem];
   float* const As = smem;
   float* const Bs = smem + KB * LKM;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -144,8 +147,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WGM == 2 ? 
   // free): each thread writes four consecutive columns of a row as one 16-byte store, where
   // the MFMA layout would give 4-byte stores of 32-column half rows (16 store instructions
   // per wave instead of 4).
-  constexpr int LC = BN + 1;
-  static_assert(BM * LC <= KB * LKM + KB * LKN, "the C tile fits the operand tiles");
   float* const Cs = smem;
 #pragma unroll
   for (int r = 0; r < 16; ++r)
@@ -159,12 +160,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WGM == 2 ? 
     const int row = idx / BN, col = idx % BN;
     const int m = m0 + row, n = n0 + col;
     if (m >= a.M) continue;
-    float v[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = Cs[row * LC + col + c];
+    const float4 cv = *reinterpret_cast<const float4*>(Cs + row * LC + col);
+    const float v[4] = {cv.x, cv.y, cv.z, cv.w};
     float* p = C + rowoff(a.cmap, m) + n;
     if (cvec && n + 3 < a.N) {
-      float4 o = make_float4(v[0], v[1], v[2], v[3]);
+      float4 o = cv;
       if (a.beta) {
         const float4 q = *reinterpret_cast<const float4*>(p);
         o.x += q.x;
