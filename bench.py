@@ -318,7 +318,7 @@ def summarize_profile(d, workload, steps, warmup, copy_mib):
     print(json.dumps(out, indent=1))
 
 
-def summarize_timeline(d, workload, steps, warmup):
+def summarize_timeline(d, workload, steps, warmup, out_dir=None):
     """Concurrency of one step as run (default lanes and post stream) from a rocprofv3 kernel
     trace, DIR/timeline_<workload>, into profiles/timeline_<workload>.md: for each timed step
     the wall span, the time any kernel runs, the time a traversal runs, and per pass (forward:
@@ -392,9 +392,10 @@ def summarize_timeline(d, workload, steps, warmup):
                      f"{union([(s0, e0) for s0, e0, f, _ in seg if f in trav]) / 1e3:.1f} | {fs:.1f} | {ft:.1f} | "
                      f"{ftl:.1f} | {bs:.1f} | {bt:.1f} | {btl:.1f} | {sums['fwd_traverse']:.1f} | "
                      f"{sums['bwd_traverse']:.1f} | {sums['gemm']:.1f} | {sums['aux']:.1f} |")
-    with open(os.path.join(ROOT, "profiles", f"timeline_{workload}.md"), "w") as fh:
+    with open(os.path.join(out_dir or os.path.join(ROOT, "profiles"), f"timeline_{workload}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+    return lines
 
 
 SQ_RUNS = {
