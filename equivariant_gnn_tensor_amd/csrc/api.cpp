@@ -635,7 +635,9 @@ etpc_status fwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   // and waits for the GEMM that last read the S set it is about to fill.
   PostStream post(s, nl > 1);
   ETPC_HIP(post.status());
-  const bool keep = post.enabled() && !capturing(s);
+  // Bounded schedules (many small items) join the lanes per item: keeping them measured
+  // 6% slower there (workload 2 at a 256 MiB budget) and neutral elsewhere.
+  const bool keep = post.enabled() && !capturing(s) && !sch.bounded;
   std::optional<LaneGroup> pass_lanes;
   if (keep) {
     pass_lanes.emplace(s, nl);
@@ -947,7 +949,7 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
   // next item's paths as soon as its own are done, after waiting for that item's Xt and
   // for the post work that last read the P set it writes; the post stream waits for every
   // lane before it reads P or overwrites an Xt set.
-  const bool keep = post.enabled() && !capturing(s);
+  const bool keep = post.enabled() && !capturing(s) && !sch.bounded;   // as in the forward
   std::optional<LaneGroup> pass_lanes;
   if (keep) {
     pass_lanes.emplace(s, nl);
