@@ -601,14 +601,17 @@ std::vector<int> group_order(const etpc_plan_s* p, const Derived& d) {
   return order;
 }
 
-// Input blocks with paths, by decreasing node-GEMM work per node ((2l+1) C_in ncols), ties
-// in plan order.
+// Input blocks with paths, by increasing node-GEMM work per node ((2l+1) C_in ncols), ties
+// in plan order: the first block's Xt product, which no traversal hides, is the smallest,
+// and the largest products run beside the traversals of the blocks after them (workload 2
+// 2.62-2.63 -> 2.58-2.59 ms against the decreasing order; the pass then ends on the
+// largest block's x_bar / W_bar products, which cost less than the first Xt they replace).
 std::vector<int> block_order(const etpc_plan_s* p, const Derived& d) {
   std::vector<int> order;
   for (size_t k = 0; k < p->in.size(); ++k)
     if (!p->by_in[k].empty()) order.push_back(static_cast<int>(k));
   auto work = [&](int k) { return int64_t(2 * p->in[k].l + 1) * p->in[k].mul * d.block_ncols[k]; };
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) > work(b); });
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) < work(b); });
   return order;
 }
 
