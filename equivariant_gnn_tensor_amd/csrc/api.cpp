@@ -1044,16 +1044,26 @@ etpc_status bwd_uvw_run(const etpc_plan_s* p, const Derived& d, const etpc_graph
     if (R.x_out || R.w_out) {
       ETPC_HIP(post.follow());
       const hipStream_t ps = post.stream();
+      // The last item's products end the pass with nothing beside them: its x_bar GEMM runs
+      // on the caller's stream (once every lane and the previous item's post work, which
+      // used the same split-K partials, are done) beside its W_bar GEMM on the post stream
+      // (workload 2 2.60 -> 2.58 ms, workload 5 3.29 -> 3.26 ms).
+      hipStream_t xs = ps;
+      if (keep && ii + 1 == items.size() && R.x_out && R.w_out) {
+        ETPC_HIP(pass_lanes->signal(s));
+        ETPC_HIP(post.wait_slot(set ^ 1));
+        xs = s;
+      }
       if (R.x_out) {
         // the first path subset of a sender range writes its x_bar rows, later ones add
         const float* wt_main = L.wt[set] + it.col0 * c_in;
         if (main_state) {
-          etpc_status st = xbar_gemm(p, k, Pmain, it.ncols, wt_main, R.x_out, it.n0, nsend, it.t0 > 0, L, ps);
+          etpc_status st = xbar_gemm(p, k, Pmain, it.ncols, wt_main, R.x_out, it.n0, nsend, it.t0 > 0, L, xs);
           if (st != ETPC_OK) return st;
         }
         if (R.tangent && R.w2) {
           etpc_status st = xbar_gemm(p, k, Pset, it.ncols, L.wt2[set] + it.col0 * c_in, R.x_out, it.n0, nsend, true,
-                                     L, ps);
+                                     L, xs);
           if (st != ETPC_OK) return st;
         }
       }
